@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the routed MXFP4 MoE feed-forward.
+
+This module holds only input generation: shapes, value distributions and seeds. It contains none of
+the method's arithmetic (no decoding, routing, grouping or GEMM) and is shared by the tests, the
+benchmark and the smoke check, which feed the same arrays to the CPU oracle and to the HIP library.
+
+Workloads (the pages measure decode at concurrency 1, 10, 256 and 1024 on Blackwell — "Chunk 8.0";
+c8 decode at matched M=8 — vllm.cpp PR #52; MTP1 decode with M=2 — "MTP1 Post-Portfolio Eager-Cycle
+Profile"; no dataset or weights are used, every value is drawn here):
+
+  name           T     H     I     E    k  routing            logits
+  tiny           4   256   128     8    2  softmax, renorm    N(0,1)
+  decode_c1      1  2048   768   128    8  softmax, renorm    N(0,1)
+  decode_m2      2  4096  2048   256    8  softmax, renorm    U[-1,1)
+  decode_m8      8  4096  2048   256    8  softmax, renorm    U[-1,1)
+  medium_zipf  256  4096  2048   256    8  softmax, renorm    N(0,1) + Zipf(1.1) popularity bias
+  high_c4     1024  7168  2048   256    8  sigmoid, renorm    N(0,1); gate/up clamped to [-7, 7]
+  m1024       1024  7168  2048     8    8  softmax, renorm    N(0,1) (every expert sees every token)
+
+Draw order from numpy PCG64(seed): logits, x, w13 codes, w13 scales, w2 codes, w2 scales, then the
+Zipf expert-rank permutation. x is N(0,1) rounded to bfloat16 (nearest-even). Codes are uniform bytes
+(both nibbles uniform over the 16 E2M1 codes); scales are integers uniform in [120, 124].
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+SEED_BASE = 20261203
+SCORE_SOFTMAX = 0
+SCORE_SIGMOID = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    score_fn: int = SCORE_SOFTMAX
+    renorm: bool = True
+    clamp: float = 0.0
+    logits: str = "normal"  # normal | uniform | zipf
+    index: int = 0
+
+    @property
+    def P(self) -> int:
+        return self.T * self.k
+
+    def with_tokens(self, T: int) -> "Config":
+        return dataclasses.replace(self, T=T)
+
+
+CONFIGS = {
+    c.name: c
+    for c in [
+        Config("tiny", 4, 256, 128, 8, 2, index=0),
+        Config("decode_c1", 1, 2048, 768, 128, 8, index=1),
+        Config("decode_m2", 2, 4096, 2048, 256, 8, logits="uniform", index=2),
+        Config("decode_m8", 8, 4096, 2048, 256, 8, logits="uniform", index=2),
+        Config("medium_zipf", 256, 4096, 2048, 256, 8, logits="zipf", index=3),
+        Config("high_c4", 1024, 7168, 2048, 256, 8, score_fn=SCORE_SIGMOID, clamp=7.0,
+               logits="normal", index=4),
+        Config("m1024", 1024, 7168, 2048, 8, 8, index=5),
+    ]
+}
+
+ZIPF_S = 1.1
+ZIPF_BETA = 0.25
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even) and return the 16-bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def zipf_bias(E: int, rank_perm: np.ndarray, s: float = ZIPF_S, beta: float = ZIPF_BETA) -> np.ndarray:
+    """Per-expert logit bias beta*ln(E*p_rank) with p_r proportional to r^-s over ranks 1..E."""
+    r = np.arange(1, E + 1, dtype=np.float64)
+    p = r ** (-s)
+    p /= p.sum()
+    return (beta * np.log(E * p[rank_perm])).astype(np.float32)
+
+
+def make_inputs(cfg: Config, seed: int | None = None, weights: bool = True,
+                scale_lo: int = 120, scale_hi: int = 124) -> dict:
+    """Draw one workload. Returns numpy arrays; weights are omitted when ``weights`` is False."""
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + cfg.index if seed is None else seed))
+    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
+    if cfg.logits == "uniform":
+        logits = rng.uniform(-1.0, 1.0, size=(T, E)).astype(np.float32)
+    else:
+        logits = rng.standard_normal(size=(T, E), dtype=np.float32)
+    x = f32_to_bf16_bits(rng.standard_normal(size=(T, H), dtype=np.float32))
+    out = dict(logits=logits, x=x)
+    if weights:
+        out["w13_q"] = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
+        out["w13_s"] = rng.integers(scale_lo, scale_hi + 1, size=(E, 2 * I, H // 32), dtype=np.uint8)
+        out["w2_q"] = rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8)
+        out["w2_s"] = rng.integers(scale_lo, scale_hi + 1, size=(E, H, I // 32), dtype=np.uint8)
+    if cfg.logits == "zipf":
+        perm = rng.permutation(E)
+        out["logits"] = (logits + zipf_bias(E, perm)[None, :]).astype(np.float32)
+        out["zipf_rank"] = perm
+    return out
+
+
+def make_weights(E: int, H: int, I: int, seed: int, scale_lo: int = 120, scale_hi: int = 124) -> dict:
+    """Weights only, from their own seed (used for small random-shape cases)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return dict(
+        w13_q=rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8),
+        w13_s=rng.integers(scale_lo, scale_hi + 1, size=(E, 2 * I, H // 32), dtype=np.uint8),
+        w2_q=rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8),
+        w2_s=rng.integers(scale_lo, scale_hi + 1, size=(E, H, I // 32), dtype=np.uint8),
+    )
+
+
+def small_case(T: int, H: int, I: int, E: int, k: int, seed: int, logits: str = "normal",
+               score_fn: int = SCORE_SOFTMAX, clamp: float = 0.0) -> tuple[Config, dict]:
+    """A random small workload with explicit shape (ragged shapes, edge cases)."""
+    cfg = Config(f"case_T{T}_H{H}_I{I}_E{E}_k{k}_s{seed}", T, H, I, E, k, score_fn=score_fn,
+                 clamp=clamp, logits=logits)
+    return cfg, make_inputs(cfg, seed=seed)
+
+
+def active_weight_bytes(counts: np.ndarray, H: int, I: int) -> int:
+    """Weight bytes the layer must stream: every expert with at least one routed pair reads its
+    3*H*I codes (half a byte each) and 3*H*I/32 scale bytes."""
+    n_active = int(np.count_nonzero(np.asarray(counts)))
+    per_expert = 3 * H * I // 2 + 3 * H * I // 32
+    return n_active * per_expert
