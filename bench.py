@@ -1,0 +1,258 @@
+"""Benchmark of the routed MXFP4 MoE layer on one MI355X.
+
+One step = one whole layer (router top-k, grouping, fused gate_up + SwiGLU, down, weighted combine)
+on one batch of seeded synthetic input resident in HBM. The default workload is decode at M=8:
+T=8 tokens, H=4096, I=2048, E=256 experts, top-8 softmax routing (the c8 decode shape the vllm.cpp
+PR #52 node-trace diff measures). Weights are random MXFP4 of that shape, rotated over enough
+device replicas that every step streams them cold from HBM (no step finds its weights in the 256 MB
+last-level cache). Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config decode_m8] [--mode graph|eager]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+LLC_BYTES = 256 << 20           # MI355X Infinity Cache
+METRIC = "µs/MoE layer + weight-stream GB/s (% HBM peak) at M=8 decode, 1 GPU"
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode_m8")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="which timing is reported as value (both are measured)")
+    ap.add_argument("--flags", type=int, default=0, help="moe_mxfp4_ffn flags (1 = unfused gate/up)")
+    ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough for cold weights)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="also run one plain device copy of this many bytes (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp4_mixture_experts_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(config: str, src_hash: str):
+    """HBM traffic per launch of the dominant kernel from the committed counter summary, if it was
+    taken on the current kernel sources (otherwise None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gateup_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard by "
+              "experts or by the intermediate dimension, with one all-to-all or all-reduce per layer); "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_synth
+    import mxfp4_mixture_experts_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.load_library()
+    cfg = moe_synth.CONFIGS[args.config]
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    t0 = time.time()
+    inp = moe_synth.make_inputs(cfg)
+    log(f"generated {cfg.name} inputs in {time.time() - t0:.1f}s")
+
+    per_expert = 3 * H * I // 2 + 3 * H * I // 32
+    replica_bytes = E * per_expert
+    R = args.replicas or max(2, math.ceil((2 << 30) / replica_bytes), math.ceil(8 * LLC_BYTES / replica_bytes))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    host = [inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"]]
+    first = moe.Mxfp4Weights(*(dev(a) for a in host))
+    replicas = [first] + [moe.Mxfp4Weights(*(t.clone() for t in (first.w13_q, first.w13_s, first.w2_q, first.w2_s)))
+                          for _ in range(R - 1)]
+    del host
+    x = dev(inp["x"].view(np.int16)).view(torch.bfloat16)
+    logits = dev(inp["logits"])
+    layer = moe.MoELayer(first, k, T, cfg.score_fn, cfg.renorm, cfg.clamp, args.flags)
+    torch.cuda.synchronize()
+    log(f"{R} weight replicas of {replica_bytes / 1e9:.2f} GB on device")
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step(i):
+        layer.forward(x, logits, replicas[i % R], stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+    counts = layer.grp.counts.cpu().numpy()
+    n_active = int(np.count_nonzero(counts))
+    weight_bytes = n_active * per_expert
+    gateup_bytes = n_active * 2 * I * (H // 2 + H // 32)
+    flops = 2 * T * k * 3 * H * I
+    gateup_flops = 2 * T * k * 2 * I * H
+
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_bytes} bytes done")
+
+    # eager: per-step HIP events around the gate_up stage, recorded on the stream it runs on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:  # create the underlying events
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            moe.set_stage_events(moe.STAGE_GATE_UP, ev[i][0], ev[i][1])
+            step(i)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t_start
+    moe.set_stage_events(moe.STAGE_GATE_UP, None, None)
+    gateup_ms = [a.elapsed_time(b) for a, b in ev]
+    gateup_mean_s = statistics.fmean(gateup_ms) / 1e3
+    log(f"eager: {eager_s / args.steps * 1e6:.1f} us/layer, gate_up stage {gateup_mean_s * 1e6:.1f} us")
+
+    # graph: one captured layer per replica, replayed in rotation
+    graph_s = None
+    try:
+        graphs = []
+        for rr in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                layer.forward(x, logits, replicas[rr], stream=stream)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        graph_s = time.perf_counter() - t_start
+        log(f"graph: {graph_s / args.steps * 1e6:.1f} us/layer")
+    except Exception as exc:  # capture unsupported: report eager
+        log(f"graph capture failed: {exc!r}")
+
+    use_graph = args.mode == "graph" and graph_s is not None
+    total_s = graph_s if use_graph else eager_s
+    us_layer = total_s / args.steps * 1e6
+    gbps = weight_bytes / (us_layer * 1e-6) / 1e9
+
+    large = int(T > 8 or args.flags & moe.FORCE_LARGE_M)
+    mfma_bound = cfg.name == "m1024"
+    if mfma_bound:
+        achieved = gateup_flops / gateup_mean_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = gateup_bytes / gateup_mean_s / 1e9
+        traffic = committed_traffic(cfg.name, kernel_source_hash())
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    roofline["kernel"] = "gate_up stage (" + ("MFMA" if large else "weight-streaming") + " kernel)"
+    roofline["bytes_per_launch" if not mfma_bound else "flops_per_launch"] = (
+        gateup_bytes if not mfma_bound else gateup_flops)
+    roofline["avg_launch_us"] = round(gateup_mean_s * 1e6, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = min(16, os.cpu_count() or 1)
+        times = []
+        sample_tokens = T if cfg.T <= 8 else 1
+        for rep in range(args.cpu_reps):
+            t_c = time.perf_counter()
+            oracle.moe_layer(inp["logits"][:sample_tokens], inp["x"][:sample_tokens], inp["w13_q"], inp["w13_s"],
+                             inp["w2_q"], inp["w2_s"], k, cfg.score_fn, cfg.renorm, cfg.clamp, threads)
+            times.append(time.perf_counter() - t_c)
+            log(f"oracle rep {rep}: {times[-1]:.2f}s")
+        per_layer_us = statistics.median(times) * 1e6 * (T / sample_tokens)
+        cpu = {"value": round(per_layer_us, 1), "unit": "µs/layer", "cores": oracle.num_threads(threads),
+               "kind": "oracle",
+               "sample": (f"{sample_tokens} of {T} tokens of one {cfg.name} layer (route+group+ffn+combine, "
+                          f"fp64), median of {args.cpu_reps}, scaled to the whole layer")}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(us_layer, 2),
+        "unit": "µs/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_s / args.steps * 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 weights, bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded; random MXFP4 weights, no checkpoint)",
+        "config": {"workload": f"{cfg.name}: T={T} H={H} I={I} E={E} top-{k} "
+                               f"{'sigmoid' if cfg.score_fn else 'softmax'} renorm"
+                               + (f", clamp {cfg.clamp}" if cfg.clamp else ""),
+                   "timing": "hipGraph replay" if use_graph else "eager",
+                   "flags": args.flags, "weight_replicas": R, "parallelism": "none (1 GPU)"},
+        "weight_stream_GBps": round(gbps, 1),
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "active_experts": n_active,
+        "weight_bytes_per_layer": weight_bytes,
+        "tflops": round(flops / (us_layer * 1e-6) / 1e12, 2),
+        "us_per_layer_eager": round(eager_s / args.steps * 1e6, 2),
+        "us_per_layer_graph": round(graph_s / args.steps * 1e6, 2) if graph_s else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+// C ABI of the routed MXFP4 MoE layer: host-side validation, workspace layout, launch plan and
+// stream-ordered launches. Nothing here allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+
+#include "kernels.hpp"
+#include "moe_mxfp4.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+// Experts with at most this many rows run on the weight-streaming kernels; more rows go to the MFMA
+// kernels (the launch table keyed by token count, tokenspeed PR #661 "What the sweep found").
+std::atomic<int> g_small_m_max{8};
+
+std::atomic<void*> g_stage_start[MOE_NUM_STAGES];
+std::atomic<void*> g_stage_stop[MOE_NUM_STAGES];
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct WsLayout {
+  size_t h_f32, g_f32, y, total;
+};
+
+WsLayout ws_layout(long P, int H, int I, int flags) {
+  WsLayout w;
+  size_t off = 0;
+  w.h_f32 = off;
+  off = align_up(off + (size_t)P * I * sizeof(float));
+  w.g_f32 = off;
+  if (flags & MOE_UNFUSED_GATE_UP) off = align_up(off + (size_t)P * I * sizeof(float));
+  w.y = off;
+  off = align_up(off + (size_t)P * H * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+bool ffn_sizes_ok(int T, int H, int I, int E, int k) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E) return false;
+  if (H < 32 || H > MOE_MAX_HIDDEN || H % 32) return false;
+  if (I < 32 || I > MOE_MAX_INTER || I % 32) return false;
+  if ((long)T * k > MOE_MAX_PAIRS) return false;
+  return true;
+}
+
+constexpr int kKnownFlags = MOE_UNFUSED_GATE_UP | MOE_FORCE_SMALL_M | MOE_FORCE_LARGE_M;
+
+int effective_small_m_max(int flags) {
+  if (flags & MOE_FORCE_SMALL_M) return INT_MAX;
+  if (flags & MOE_FORCE_LARGE_M) return 0;
+  return g_small_m_max.load();
+}
+
+void fill_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan) {
+  const int thr = effective_small_m_max(flags);
+  const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k);
+  const moe::LargePlan lp = moe::plan_large(T, H, I, E, k, thr == INT_MAX ? INT_MAX - 1 : thr);
+  plan->small_m_max = thr;
+  plan->launch_small = (flags & MOE_FORCE_LARGE_M) ? 0 : 1;
+  plan->launch_large = (flags & MOE_FORCE_LARGE_M) ? 1 : ((flags & MOE_FORCE_SMALL_M) ? 0 : (T > thr));
+  if (T == 0) plan->launch_small = plan->launch_large = 0;
+  const int gu_launches = (flags & MOE_UNFUSED_GATE_UP) ? 2 : 1;
+  plan->small_gateup_grid = plan->launch_small ? sp.gu_grid_x * sp.slots : 0;
+  plan->small_down_grid = plan->launch_small ? sp.dn_grid_x * sp.slots : 0;
+  plan->large_gateup_grid = plan->launch_large ? lp.gu_grid_x * lp.tile_slots : 0;
+  plan->large_down_grid = plan->launch_large ? lp.dn_grid_x * lp.tile_slots : 0;
+  plan->combine_grid = T > 0 ? moe::combine_grid(T, H) : 0;
+  plan->n_launches = (plan->launch_small ? gu_launches + 1 : 0) + (plan->launch_large ? 2 : 0) +
+                     (T > 0 ? 1 : 0);
+}
+
+void record(int stage, bool start, hipStream_t stream) {
+  void* ev = start ? g_stage_start[stage].load() : g_stage_stop[stage].load();
+  if (ev) (void)hipEventRecord((hipEvent_t)ev, stream);
+}
+
+}  // namespace
+
+MOE_API int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is out of range";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: misaligned pointer or unsupported option";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: the HIP runtime reported a launch error";
+    default: return "unknown moe_status";
+  }
+}
+
+MOE_API int moe_set_small_m_max(int v) {
+  if (v < 0) return MOE_ERR_SHAPE;
+  return g_small_m_max.exchange(v);
+}
+
+MOE_API int moe_set_stage_events(int stage, void* start_event, void* stop_event) {
+  if (stage < 0 || stage >= MOE_NUM_STAGES) return MOE_ERR_SHAPE;
+  g_stage_start[stage].store(start_event);
+  g_stage_stop[stage].store(stop_event);
+  return MOE_OK;
+}
+
+MOE_API int moe_route_topk(const float* logits, int T, int E, int k, int score_fn, int renorm,
+                           int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E ||
+      (long)T * k > MOE_MAX_PAIRS)
+    return MOE_ERR_SHAPE;
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_NULL;
+  if (moe::launch_route_topk(logits, T, E, k, score_fn, renorm, topk_ids, topk_w,
+                             (hipStream_t)stream) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}
+
+MOE_API int moe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                             int32_t* active, int32_t* n_active, void* stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK ||
+      (long)T * k > MOE_MAX_PAIRS)
+    return MOE_ERR_SHAPE;
+  if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return MOE_ERR_NULL;
+  if (moe::launch_group_tokens(topk_ids, T * k, E, counts, offsets, sorted_pair, pair_pos, active,
+                               n_active, (hipStream_t)stream) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}
+
+MOE_API size_t moe_mxfp4_ffn_workspace_size(int T, int H, int I, int E, int k, int flags) {
+  if (!ffn_sizes_ok(T, H, I, E, k) || (flags & ~kKnownFlags)) return 0;
+  return ws_layout((long)T * k, H, I, flags).total;
+}
+
+MOE_API int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan) {
+  if (!plan) return MOE_ERR_NULL;
+  if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
+  if ((flags & ~kKnownFlags) || ((flags & MOE_FORCE_SMALL_M) && (flags & MOE_FORCE_LARGE_M)))
+    return MOE_ERR_UNSUPPORTED;
+  fill_plan(T, H, I, E, k, flags, plan);
+  return MOE_OK;
+}
+
+MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                          const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                          const uint8_t* w2_s, const float* topk_w, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* sorted_pair,
+                          const int32_t* pair_pos, const int32_t* active, const int32_t* n_active,
+                          float clamp_limit, int flags, uint16_t* out_bf16, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
+  if ((flags & ~kKnownFlags) || ((flags & MOE_FORCE_SMALL_M) && (flags & MOE_FORCE_LARGE_M)))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !w13_q || !w13_s || !w2_q || !w2_s || !topk_w || !counts || !offsets ||
+      !sorted_pair || !pair_pos || !active || !n_active || !out_bf16 || !workspace)
+    return MOE_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(out_bf16, 16) || !aligned(w13_q, 16) || !aligned(w2_q, 16) ||
+      !aligned(workspace, kAlign))
+    return MOE_ERR_UNSUPPORTED;
+  const long P = (long)T * k;
+  const WsLayout wl = ws_layout(P, H, I, flags);
+  if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+
+  moe_ffn_plan plan;
+  fill_plan(T, H, I, E, k, flags, &plan);
+  const int thr = plan.small_m_max;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* h_f32 = (float*)(ws + wl.h_f32);
+  float* g_f32 = (float*)(ws + wl.g_f32);
+  float* y = (float*)(ws + wl.y);
+
+  const moe::Routed r{x_bf16, counts, offsets, sorted_pair, active, n_active, k};
+  const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k);
+  const moe::LargePlan lp = moe::plan_large(T, H, I, E, k, thr == INT_MAX ? INT_MAX - 1 : thr);
+  const int check_m = plan.launch_large;
+  bool ok = true;
+
+  record(MOE_STAGE_GATE_UP, true, s);
+  if (plan.launch_small) {
+    if (flags & MOE_UNFUSED_GATE_UP) {
+      ok &= moe::launch_small_gateup(sp, r, H, I, w13_q, w13_s, thr, check_m, clamp_limit,
+                                     moe::kGateOnly, h_f32, g_f32, s) == hipSuccess;
+      ok &= moe::launch_small_gateup(sp, r, H, I, w13_q, w13_s, thr, check_m, clamp_limit,
+                                     moe::kUpWithGate, h_f32, g_f32, s) == hipSuccess;
+    } else {
+      ok &= moe::launch_small_gateup(sp, r, H, I, w13_q, w13_s, thr, check_m, clamp_limit,
+                                     moe::kGateUpFused, h_f32, g_f32, s) == hipSuccess;
+    }
+  }
+  if (plan.launch_large)
+    ok &= moe::launch_large_gateup(lp, r, H, I, w13_q, w13_s, thr, clamp_limit, h_f32, s) ==
+          hipSuccess;
+  record(MOE_STAGE_GATE_UP, false, s);
+
+  record(MOE_STAGE_DOWN, true, s);
+  if (plan.launch_small)
+    ok &= moe::launch_small_down(sp, r, H, I, w2_q, w2_s, thr, check_m, h_f32, y, s) == hipSuccess;
+  if (plan.launch_large)
+    ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, thr, h_f32, y, s) == hipSuccess;
+  record(MOE_STAGE_DOWN, false, s);
+
+  record(MOE_STAGE_COMBINE, true, s);
+  ok &= moe::launch_combine(y, topk_w, pair_pos, T, H, k, out_bf16, nullptr, s) == hipSuccess;
+  record(MOE_STAGE_COMBINE, false, s);
+  return ok ? MOE_OK : MOE_ERR_LAUNCH;
+}

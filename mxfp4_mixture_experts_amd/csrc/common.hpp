@@ -1,0 +1,87 @@
+// Device helpers shared by the gfx950 kernels of the routed MXFP4 MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// E8M0 scale byte s -> the binary32 2^(s-127), built from its exponent field. Exact for s in
+// [1, 254]; the library's contract covers s in [2, 254] (decoded values stay normal binary32).
+__device__ __forceinline__ float e8m0_to_float(uint32_t s) {
+  return __builtin_bit_cast(float, s << 23);
+}
+
+// Round a binary32 to bfloat16, nearest-even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+// Two E2M1 codes (byte `sel` of `w`: low nibble = even element) times `scale` -> two bf16 in one
+// dword, the even element in the low half. Exact for normal results.
+template <int sel>
+__device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, sel);
+}
+
+template <int sel>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, sel);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
+// acc + a.lo*b.lo + a.hi*b.hi in fp32 (products of two bf16 are exact in fp32).
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__device__ __forceinline__ float clampf(float v, float c) { return fminf(fmaxf(v, -c), c); }
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Lanes of the wave holding the same key (keys in [0, 1024)), restricted to lanes with `valid`.
+__device__ __forceinline__ uint64_t match_key(int key, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {
+    bool bit = (key >> b) & 1;
+    uint64_t ones = __ballot(bit);
+    m &= bit ? ones : ~ones;
+  }
+  return valid ? m : 0ull;
+}
+
+}  // namespace moe

@@ -1,0 +1,89 @@
+// Internal launchers of the gfx950 kernels (host side). Only api.hip calls them; shapes and pointers
+// have been validated there.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int score_fn, int renorm,
+                             int32_t* ids, float* weights, hipStream_t stream);
+
+hipError_t launch_group_tokens(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
+                               int32_t* n_active, hipStream_t stream);
+
+// Grouping results and activations every FFN kernel reads.
+struct Routed {
+  const uint16_t* x;         // bf16 [T, H]
+  const int32_t* counts;     // [E]
+  const int32_t* offsets;    // [E + 1]
+  const int32_t* sorted_pair;// [P]
+  const int32_t* active;     // [E]
+  const int32_t* n_active;   // [1]
+  int k;
+};
+
+// How one K-long weight row is spread over a wave: `lpr` lanes share a row (a power of two dividing
+// 64), each lane owning the 32-element blocks q, q + lpr, q + 2*lpr, ... (`bpl` of them at most).
+struct RowSplit {
+  int nb;   // 32-element blocks per row (K / 32)
+  int lpr;  // lanes per row
+  int bpl;  // blocks per lane, ceil(nb / lpr), at most 8
+};
+
+RowSplit choose_row_split(int K);
+
+// Weight-streaming kernels for experts with at most `small_m_max` rows.
+enum SmallGateUpMode { kGateUpFused = 0, kGateOnly = 1, kUpWithGate = 2 };
+
+struct SmallPlan {
+  RowSplit gu, dn;
+  int gu_tile;    // gate rows per gate_up workgroup
+  int dn_tile;    // down rows per down workgroup
+  int gu_grid_x;  // gate_up workgroups per expert
+  int dn_grid_x;  // down workgroups per expert
+  int slots;      // expert slots in the grid (min(E, P))
+  int mt_gu, mt_dn;  // tokens per pass
+};
+
+SmallPlan plan_small(int T, int H, int I, int E, int k);
+
+// check_m: the MFMA kernels are launched too, so experts above small_m_max must be skipped here.
+hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, int H, int I,
+                               const uint8_t* w13_q, const uint8_t* w13_s, int small_m_max,
+                               int check_m, float clamp, int mode, float* h, float* g_ws,
+                               hipStream_t stream);
+
+hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, int H, int I, const uint8_t* w2_q,
+                             const uint8_t* w2_s, int small_m_max, int check_m, const float* h,
+                             float* y, hipStream_t stream);
+
+// bf16-MFMA kernels for experts with more than `small_m_max` rows: tiles of up to 64 rows of one
+// expert; the weight rows are decoded from MXFP4 to bf16 in registers, the activation tile is staged
+// in LDS (x for gate_up; h as a bf16 hi/lo pair for down). h is fp32 [P, I] on both kernel families.
+struct LargePlan {
+  int tile_m;        // rows per tile
+  int gu_tile_n;     // gate columns per gate_up workgroup (the matching up columns come with them)
+  int dn_tile_n;     // output columns per down workgroup
+  int gu_grid_x, dn_grid_x;
+  int tile_slots;    // upper bound on the number of (expert, row-tile) pairs
+};
+
+LargePlan plan_large(int T, int H, int I, int E, int k, int small_m_max);
+
+hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int I,
+                               const uint8_t* w13_q, const uint8_t* w13_s, int small_m_max,
+                               float clamp, float* h, hipStream_t stream);
+
+hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I, const uint8_t* w2_q,
+                             const uint8_t* w2_s, int small_m_max, const float* h, float* y,
+                             hipStream_t stream);
+
+// out[t] = bf16(sum_j topk_w[t, j] * y[pair_pos[t*k + j]])
+hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* pair_pos, int T, int H,
+                          int k, uint16_t* out, int* grid_out, hipStream_t stream);
+int combine_grid(int T, int H);
+
+}  // namespace moe

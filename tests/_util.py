@@ -95,12 +95,28 @@ def numpy_bruteforce_ffn(x_bits, w13_q, w13_s, w2_q, w2_s, ids, w, clamp=0.0):
     return out
 
 
+def rne_bf16(ref: np.ndarray) -> np.ndarray:
+    """ref rounded to bfloat16 (nearest-even) as float64, via torch's CPU conversion."""
+    import torch
+
+    return torch.from_numpy(np.asarray(ref, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def parity_metrics(out_bf16_bits, ref):
-    """max |out - ref| / rms(ref) and sum|out - ref| / sum|ref| (ref = unrounded oracle output)."""
+    """Error of a bfloat16 output against the unrounded fp64 oracle output `ref`:
+      max_raw    = max |out - ref| / rms(ref)
+      max_excess = max (|out - ref| - |bf16(ref) - ref|) / rms(ref): the error beyond what rounding
+                   the exact value to bfloat16 already costs at that element
+      l1         = sum |out - ref| / sum |ref|
+    """
     out = bf16_to_f64(out_bf16_bits)
     ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return dict(max_raw=0.0, max_excess=0.0, l1=0.0)
     err = np.abs(out - ref)
-    rms = math.sqrt(float(np.mean(ref * ref))) if ref.size else 0.0
-    max_rel = float(err.max()) / rms if ref.size and rms > 0 else 0.0
-    l1 = float(err.sum()) / float(np.abs(ref).sum()) if ref.size and np.abs(ref).sum() > 0 else 0.0
-    return max_rel, l1
+    own = np.abs(rne_bf16(ref) - ref)
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    den = float(np.abs(ref).sum())
+    return dict(max_raw=float(err.max()) / rms if rms > 0 else float(err.max()),
+                max_excess=float((err - own).max()) / rms if rms > 0 else float((err - own).max()),
+                l1=float(err.sum()) / den if den > 0 else float(err.sum()))

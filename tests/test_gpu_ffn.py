@@ -1,0 +1,136 @@
+"""GPU parity of the whole layer (route -> group -> moe_mxfp4_ffn) against the fp64 oracle.
+
+Small workloads are compared element by element on every output; the full-size decode workloads too
+(the oracle finishes them in seconds); the T=256/1024 workloads on sampled tokens, whose outputs the
+oracle computes one token at a time (a token's output depends only on its own row, ids and weights).
+Every case also runs with the weight-streaming and the MFMA kernels forced, and the unfused gate/up
+variant, on the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from _gpu import assert_output_parity, dev, run_layer, weights_to_device, x_to_device, out_bits
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("mxfp4_mixture_experts_amd")
+
+FLAG_SETS = {"default": 0, "small": moe.FORCE_SMALL_M, "large": moe.FORCE_LARGE_M,
+             "unfused": moe.UNFUSED_GATE_UP, "unfused_small": moe.UNFUSED_GATE_UP | moe.FORCE_SMALL_M}
+
+
+def oracle_full(orc, inp, cfg):
+    return orc.moe_layer(inp["logits"], inp["x"], inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"],
+                         cfg.k, cfg.score_fn, cfg.renorm, cfg.clamp)
+
+
+def check_full(orc, cfg, inp, flags_names=tuple(FLAG_SETS)):
+    ref = oracle_full(orc, inp, cfg)
+    w = weights_to_device(inp)
+    outs = {}
+    for fname in flags_names:
+        print(f"ffn {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} flags={fname}", flush=True)
+        g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, FLAG_SETS[fname], w=w, renorm=cfg.renorm)
+        np.testing.assert_array_equal(g["topk_ids"], ref["topk_ids"])
+        np.testing.assert_array_equal(g["sorted_pair"], ref["sorted_pair"])
+        assert_output_parity(g["out_bf16"], ref["out_ref"], f"{cfg.name}/{fname}")
+        outs[fname] = g["out_bf16"]
+    if "unfused" in outs and "default" in outs:
+        np.testing.assert_array_equal(outs["unfused"], outs["default"])  # fused == unfused bitwise
+    if "unfused_small" in outs and "small" in outs:
+        np.testing.assert_array_equal(outs["unfused_small"], outs["small"])
+    return outs
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_c1", "decode_m2"])
+def test_configs_full(orc, name):
+    cfg = moe_synth.CONFIGS[name]
+    check_full(orc, cfg, moe_synth.make_inputs(cfg))
+
+
+def test_decode_m8_full(orc):
+    cfg = moe_synth.CONFIGS["decode_m8"]
+    check_full(orc, cfg, moe_synth.make_inputs(cfg), ("default", "large", "unfused"))
+
+
+CASES = [
+    # T, H, I, E, k, score_fn, clamp, seed: ragged shapes, blocks per lane 1..8, tails of every tile
+    (5, 96, 160, 6, 3, 0, 0.0, 1),
+    (3, 32, 32, 1, 1, 0, 0.0, 2),
+    (7, 288, 96, 9, 4, 1, 7.0, 3),
+    (2, 224, 736, 4, 2, 0, 0.0, 4),
+    (9, 1024, 544, 12, 5, 1, 3.0, 5),
+    (16, 512, 256, 16, 16, 0, 0.0, 6),
+    (1, 7168, 256, 4, 2, 1, 7.0, 7),
+    (40, 256, 128, 4, 2, 0, 0.0, 8),     # experts with ~20 rows each: both kernel families
+    (130, 160, 96, 3, 2, 0, 0.0, 9),     # >64 rows per expert: several MFMA row tiles, ragged
+    (33, 8192, 64, 5, 3, 0, 0.0, 10),
+    (4, 128, 8192, 3, 2, 0, 0.0, 11),
+    (6, 16384, 32, 2, 1, 0, 0.0, 12),   # 8 blocks per lane at the largest hidden size
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_H%d_I%d_E%d_k%d" % c[:5])
+def test_small_shapes(orc, case):
+    T, H, I, E, k, fn, clamp, seed = case
+    cfg, inp = moe_synth.small_case(T, H, I, E, k, seed, score_fn=fn, clamp=clamp)
+    check_full(orc, cfg, inp)
+
+
+def test_threshold_sweep_same_result(orc):
+    """Every launch-table threshold gives an oracle-matching output on a mixed-M workload."""
+    cfg, inp = moe_synth.small_case(48, 512, 256, 8, 3, 21)
+    ref = oracle_full(orc, inp, cfg)
+    w = weights_to_device(inp)
+    prev = moe.set_small_m_max(8)
+    try:
+        for thr in (0, 1, 2, 4, 8, 16, 32, 1000):
+            moe.set_small_m_max(thr)
+            print(f"threshold {thr}", flush=True)
+            g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w)
+            assert_output_parity(g["out_bf16"], ref["out_ref"], f"thr={thr}")
+    finally:
+        moe.set_small_m_max(prev)
+
+
+def sample_tokens(ref_ids, counts, T, n=6):
+    """Tokens to check at full size: first, last, and tokens routed to the most and least loaded
+    active experts (so both kernel families are covered)."""
+    loads = counts[ref_ids].max(axis=1)
+    picks = {0, T - 1, int(np.argmax(loads)), int(np.argmin(loads))}
+    rng = np.random.default_rng(T)
+    while len(picks) < n:
+        picks.add(int(rng.integers(0, T)))
+    return np.array(sorted(picks))
+
+
+@pytest.mark.parametrize("name", ["medium_zipf", "high_c4", "m1024"])
+def test_large_configs_sampled(orc, name):
+    cfg = moe_synth.CONFIGS[name]
+    inp = moe_synth.make_inputs(cfg)
+    ids, wts = orc.route_topk(inp["logits"], cfg.k, cfg.score_fn, cfg.renorm)
+    grp = orc.group_tokens(ids, cfg.E)
+    toks = sample_tokens(ids, grp["counts"], cfg.T)
+    ref = orc.mxfp4_ffn(inp["x"][toks], inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"], ids[toks],
+                        wts[toks], cfg.clamp)
+    w = weights_to_device(inp)
+    for fname in ("default", "large", "small"):
+        print(f"ffn {name} flags={fname} sampled tokens {toks.tolist()}", flush=True)
+        g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, FLAG_SETS[fname], w=w, renorm=cfg.renorm)
+        np.testing.assert_array_equal(g["topk_ids"], ids)
+        np.testing.assert_array_equal(g["counts"], grp["counts"])
+        np.testing.assert_array_equal(g["sorted_pair"], grp["sorted_pair"])
+        assert_output_parity(g["out_bf16"][toks], ref["out_ref"], f"{name}/{fname}")
+
+
+def test_empty_batch():
+    w = moe.Mxfp4Weights(*(torch.zeros(s, dtype=torch.uint8, device="cuda")
+                           for s in [(2, 64, 16), (2, 64, 1), (2, 32, 16), (2, 32, 1)]))
+    x = torch.zeros((0, 32), dtype=torch.bfloat16, device="cuda")
+    ids, tw = moe.route_topk(torch.zeros((0, 2), device="cuda"), 1)
+    grp = moe.group_tokens(ids, 2)
+    out = moe.mxfp4_ffn(x, w, tw, grp)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 32)
+    assert int(grp.n_active.item()) == 0 and int(grp.counts.sum().item()) == 0
