@@ -20,16 +20,34 @@ std::atomic<void*> g_stage_start[MOE_NUM_STAGES];
 std::atomic<void*> g_stage_stop[MOE_NUM_STAGES];
 
 constexpr size_t kAlign = 256;
+
+// Compute units of the current device (the persistent grids are sized from it); 256 (MI355X) if it
+// cannot be queried, e.g. on a host without a GPU.
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
-  size_t h_f32, g_f32, y, total;
+  size_t h_f32, g_f32, y, sched, total;
+  int tile_slots_max;
 };
 
-WsLayout ws_layout(long P, int H, int I, int flags) {
+// Every region is sized for the worst case over routings and launch-table thresholds, so one
+// workspace serves every call with the same sizes and flags.
+WsLayout ws_layout(long P, int H, int I, int E, int k, int flags) {
   WsLayout w;
   size_t off = 0;
+  w.tile_slots_max = moe::tile_slots_bound((int)(P / k), E, k, 0);
+  w.sched = off;  // small_list[E], n_small[1], tile_e[slots], tile_m0[slots]
+  off = align_up(off + sizeof(int32_t) * ((size_t)E + 1 + 2 * (size_t)w.tile_slots_max));
   w.h_f32 = off;
   off = align_up(off + (size_t)P * I * sizeof(float));
   w.g_f32 = off;
@@ -58,19 +76,20 @@ int effective_small_m_max(int flags) {
 
 void fill_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan) {
   const int thr = effective_small_m_max(flags);
-  const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k);
+  const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k, num_cus());
   const moe::LargePlan lp = moe::plan_large(T, H, I, E, k, thr == INT_MAX ? INT_MAX - 1 : thr);
   plan->small_m_max = thr;
   plan->launch_small = (flags & MOE_FORCE_LARGE_M) ? 0 : 1;
   plan->launch_large = (flags & MOE_FORCE_LARGE_M) ? 1 : ((flags & MOE_FORCE_SMALL_M) ? 0 : (T > thr));
   if (T == 0) plan->launch_small = plan->launch_large = 0;
   const int gu_launches = (flags & MOE_UNFUSED_GATE_UP) ? 2 : 1;
-  plan->small_gateup_grid = plan->launch_small ? sp.gu_grid_x * sp.slots : 0;
-  plan->small_down_grid = plan->launch_small ? sp.dn_grid_x * sp.slots : 0;
+  plan->small_gateup_grid = plan->launch_small ? sp.gu_grid : 0;
+  plan->small_down_grid = plan->launch_small ? sp.dn_grid : 0;
   plan->large_gateup_grid = plan->launch_large ? lp.gu_grid_x * lp.tile_slots : 0;
   plan->large_down_grid = plan->launch_large ? lp.dn_grid_x * lp.tile_slots : 0;
   plan->combine_grid = T > 0 ? moe::combine_grid(T, H) : 0;
-  plan->n_launches = (plan->launch_small ? gu_launches + 1 : 0) + (plan->launch_large ? 2 : 0) +
+  // the MFMA kernels need the schedule kernel's tile list first
+  plan->n_launches = (plan->launch_small ? gu_launches + 1 : 0) + (plan->launch_large ? 3 : 0) +
                      (T > 0 ? 1 : 0);
 }
 
@@ -137,7 +156,7 @@ MOE_API int moe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32
 
 MOE_API size_t moe_mxfp4_ffn_workspace_size(int T, int H, int I, int E, int k, int flags) {
   if (!ffn_sizes_ok(T, H, I, E, k) || (flags & ~kKnownFlags)) return 0;
-  return ws_layout((long)T * k, H, I, flags).total;
+  return ws_layout((long)T * k, H, I, E, k, flags).total;
 }
 
 MOE_API int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan) {
@@ -167,7 +186,7 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
       !aligned(workspace, kAlign))
     return MOE_ERR_UNSUPPORTED;
   const long P = (long)T * k;
-  const WsLayout wl = ws_layout(P, H, I, flags);
+  const WsLayout wl = ws_layout(P, H, I, E, k, flags);
   if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
 
   moe_ffn_plan plan;
@@ -180,33 +199,43 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   float* y = (float*)(ws + wl.y);
 
   const moe::Routed r{x_bf16, counts, offsets, sorted_pair, active, n_active, k};
-  const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k);
+  const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k, num_cus());
   const moe::LargePlan lp = moe::plan_large(T, H, I, E, k, thr == INT_MAX ? INT_MAX - 1 : thr);
-  const int check_m = plan.launch_large;
+  int32_t* small_list = (int32_t*)(ws + wl.sched);
+  int32_t* n_small = small_list + E;
+  int32_t* tile_e = n_small + 1;
+  int32_t* tile_m0 = tile_e + wl.tile_slots_max;
+  // without MFMA kernels every active expert is small: the grouping's active list is the work list
+  const int32_t* list = plan.launch_large ? small_list : active;
+  const int32_t* list_count = plan.launch_large ? n_small : n_active;
   bool ok = true;
+
+  if (plan.launch_large)
+    ok &= moe::launch_schedule(r, E, thr, wl.tile_slots_max, small_list, n_small, tile_e, tile_m0, s) ==
+          hipSuccess;
 
   record(MOE_STAGE_GATE_UP, true, s);
   if (plan.launch_small) {
     if (flags & MOE_UNFUSED_GATE_UP) {
-      ok &= moe::launch_small_gateup(sp, r, H, I, w13_q, w13_s, thr, check_m, clamp_limit,
+      ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
                                      moe::kGateOnly, h_f32, g_f32, s) == hipSuccess;
-      ok &= moe::launch_small_gateup(sp, r, H, I, w13_q, w13_s, thr, check_m, clamp_limit,
+      ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
                                      moe::kUpWithGate, h_f32, g_f32, s) == hipSuccess;
     } else {
-      ok &= moe::launch_small_gateup(sp, r, H, I, w13_q, w13_s, thr, check_m, clamp_limit,
+      ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
                                      moe::kGateUpFused, h_f32, g_f32, s) == hipSuccess;
     }
   }
   if (plan.launch_large)
-    ok &= moe::launch_large_gateup(lp, r, H, I, w13_q, w13_s, thr, clamp_limit, h_f32, s) ==
+    ok &= moe::launch_large_gateup(lp, r, H, I, w13_q, w13_s, tile_e, tile_m0, clamp_limit, h_f32, s) ==
           hipSuccess;
   record(MOE_STAGE_GATE_UP, false, s);
 
   record(MOE_STAGE_DOWN, true, s);
   if (plan.launch_small)
-    ok &= moe::launch_small_down(sp, r, H, I, w2_q, w2_s, thr, check_m, h_f32, y, s) == hipSuccess;
+    ok &= moe::launch_small_down(sp, r, list, list_count, H, I, w2_q, w2_s, h_f32, y, s) == hipSuccess;
   if (plan.launch_large)
-    ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, thr, h_f32, y, s) == hipSuccess;
+    ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, tile_e, tile_m0, h_f32, y, s) == hipSuccess;
   record(MOE_STAGE_DOWN, false, s);
 
   record(MOE_STAGE_COMBINE, true, s);

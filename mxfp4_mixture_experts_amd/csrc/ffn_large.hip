@@ -17,9 +17,9 @@
 //     lo = bf16(h - hi)), two MFMAs per operand: a single bf16 rounding of h alone can cost up to
 //     ~2% of the output's rms at small I or k (no averaging over many terms), while these medium-M
 //     GEMMs are bound by the weight stream, so the extra MFMAs are free.
-// Tile schedule: the (expert, row-tile) pairs of experts above small_m_max are enumerated on the
-// device from the grouping (counts, active list) with a wave-wide scan, so the grid comes from host
-// bounds only and the launch needs no host synchronisation.
+// Tile schedule: a one-wave kernel lists the (expert, row-tile) pairs of experts above small_m_max
+// (and the remaining experts for the weight-streaming kernels) on the device, so the grids come from
+// host bounds only and no launch needs a host synchronisation.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,46 +32,50 @@ constexpr int kKStep = 128;     // K elements per step (4 MX blocks)
 constexpr int kLdsRow = 272;    // bytes per LDS activation row (256 + 16 padding)
 constexpr int kColBlocks = 4;   // 16-column MFMA blocks per wave
 
-struct TileRef {
-  int e, m0, rows;
-};
-
-// The blockIdx.y-th (expert, row tile) pair among experts with more than small_m_max rows.
-__device__ __forceinline__ bool find_tile(const Routed& r, int small_m_max, int target, TileRef& out) {
-  const int lane = threadIdx.x & 63;
-  const int na = *r.n_active;
-  int base = 0;
+// One wave: split the active experts into those for the weight-streaming kernels (at most
+// small_m_max rows) and the row tiles of the others, in ascending expert order. Unused tail entries
+// are -1, so consumers need not read the counts.
+__global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ active,
+                                                      const int32_t* __restrict__ n_active, int E,
+                                                      int small_m_max, int tile_slots,
+                                                      int32_t* __restrict__ small_list,
+                                                      int32_t* __restrict__ n_small,
+                                                      int32_t* __restrict__ tile_e,
+                                                      int32_t* __restrict__ tile_m0) {
+  const int lane = threadIdx.x;
+  const int na = *n_active;
+  int ns = 0, nt = 0;
   for (int i0 = 0; i0 < na; i0 += 64) {
     const int i = i0 + lane;
-    int e = -1, c = 0, nt = 0;
-    if (i < na) {
-      e = r.active[i];
-      c = r.counts[e];
-      nt = c > small_m_max ? (c + kTileM - 1) / kTileM : 0;
+    const int e = i < na ? active[i] : -1;
+    const int c = e >= 0 ? counts[e] : 0;
+    const bool small = e >= 0 && c <= small_m_max;
+    const uint64_t sm = __ballot(small);
+    if (small) small_list[ns + __popcll(sm & lanemask_lt(lane))] = e;
+    ns += __popcll(sm);
+    const int tiles = (e >= 0 && !small) ? (c + kTileM - 1) / kTileM : 0;
+    const int incl = wave_inclusive_scan(tiles, lane);
+    for (int t = 0; t < tiles; ++t) {
+      const int slot = nt + incl - tiles + t;
+      if (slot < tile_slots) {
+        tile_e[slot] = e;
+        tile_m0[slot] = t * kTileM;
+      }
     }
-    const int incl = wave_inclusive_scan(nt, lane);
-    const int total = __shfl(incl, 63, 64);
-    if (target < base + total) {
-      const uint64_t hit = __ballot(target < base + incl);
-      const int L = __ffsll((unsigned long long)hit) - 1;
-      const int sel_e = __shfl(e, L, 64);
-      const int sel_c = __shfl(c, L, 64);
-      const int first = base + __shfl(incl - nt, L, 64);
-      out.e = sel_e;
-      out.m0 = (target - first) * kTileM;
-      out.rows = min(kTileM, sel_c - out.m0);
-      return true;
-    }
-    base += total;
+    nt += __shfl(incl, 63, 64);
   }
-  return false;
+  for (int i = ns + lane; i < E; i += 64) small_list[i] = -1;
+  for (int i = nt + lane; i < tile_slots; i += 64) tile_e[i] = -1;
+  if (lane == 0) *n_small = ns;
 }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void large_kernel(Routed r, int H, int I,
                                                     const uint8_t* __restrict__ wq_all,
                                                     const uint8_t* __restrict__ ws_all,
-                                                    int small_m_max, float clamp,
+                                                    const int32_t* __restrict__ tile_e,
+                                                    const int32_t* __restrict__ tile_m0, float clamp,
                                                     const float* __restrict__ h_in,
                                                     float* __restrict__ h_out,
                                                     float* __restrict__ y_out) {
@@ -79,8 +83,13 @@ __global__ __launch_bounds__(256) void large_kernel(Routed r, int H, int I,
   constexpr int kATiles = GATEUP ? 1 : 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[kATiles * kTileM * kLdsRow];
 
-  TileRef tr;
-  if (!find_tile(r, small_m_max, blockIdx.y, tr)) return;
+  struct {
+    int e, m0, rows;
+  } tr;
+  tr.e = tile_e[blockIdx.y];
+  if (tr.e < 0) return;
+  tr.m0 = tile_m0[blockIdx.y];
+  tr.rows = min(kTileM, r.counts[tr.e] - tr.m0);
   const int row0 = r.offsets[tr.e] + tr.m0;
   const int msub_n = (tr.rows + 15) >> 4;
 
@@ -276,31 +285,42 @@ LargePlan plan_large(int T, int H, int I, int E, int k, int small_m_max) {
   lp.dn_tile_n = 256;
   lp.gu_grid_x = (I + lp.gu_tile_n - 1) / lp.gu_tile_n;
   lp.dn_grid_x = (H + lp.dn_tile_n - 1) / lp.dn_tile_n;
-  const long P = (long)T * k;
-  // sum over large experts of ceil(M_e / 64) <= P/64 + (number of large experts)
-  long n_large = P / (small_m_max + 1);
-  if (n_large > E) n_large = E;
-  lp.tile_slots = (int)((P + kTileM - 1) / kTileM + n_large);
+  lp.tile_slots = tile_slots_bound(T, E, k, small_m_max);
   return lp;
 }
 
+int tile_slots_bound(int T, int E, int k, int small_m_max) {
+  // sum over experts above the threshold of ceil(M_e / 64) <= P/64 + (number of such experts)
+  const long P = (long)T * k;
+  long n_large = P / ((long)small_m_max + 1);
+  if (n_large > E) n_large = E;
+  return (int)((P + kTileM - 1) / kTileM + n_large);
+}
+
+hipError_t launch_schedule(const Routed& r, int E, int small_m_max, int tile_slots, int32_t* small_list,
+                           int32_t* n_small, int32_t* tile_e, int32_t* tile_m0, hipStream_t stream) {
+  schedule_kernel<<<1, 64, 0, stream>>>(r.counts, r.active, r.n_active, E, small_m_max, tile_slots,
+                                        small_list, n_small, tile_e, tile_m0);
+  return hipGetLastError();
+}
+
 hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int I,
-                               const uint8_t* w13_q, const uint8_t* w13_s, int small_m_max,
-                               float clamp, float* h, hipStream_t stream) {
+                               const uint8_t* w13_q, const uint8_t* w13_s, const int32_t* tile_e,
+                               const int32_t* tile_m0, float clamp, float* h, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
   const dim3 grid(lp.gu_grid_x, lp.tile_slots), block(256);
-  large_kernel<true><<<grid, block, 0, stream>>>(r, H, I, w13_q, w13_s, small_m_max, clamp, nullptr,
-                                                 h, nullptr);
+  large_kernel<true><<<grid, block, 0, stream>>>(r, H, I, w13_q, w13_s, tile_e, tile_m0, clamp,
+                                                 nullptr, h, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I, const uint8_t* w2_q,
-                             const uint8_t* w2_s, int small_m_max, const float* h, float* y,
-                             hipStream_t stream) {
+                             const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
+                             const float* h, float* y, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
   const dim3 grid(lp.dn_grid_x, lp.tile_slots), block(256);
-  large_kernel<false><<<grid, block, 0, stream>>>(r, H, I, w2_q, w2_s, small_m_max, 0.0f, h, nullptr,
-                                                  y);
+  large_kernel<false><<<grid, block, 0, stream>>>(r, H, I, w2_q, w2_s, tile_e, tile_m0, 0.0f, h,
+                                                  nullptr, y);
   return hipGetLastError();
 }
 

@@ -2,22 +2,25 @@
 //
 // At small per-expert M the expert GEMMs are bound by HBM bandwidth ("Chunk 8.0": the small
 // per-expert GEMMs are memory-bandwidth-bound; "MTP1 Post-Portfolio Eager-Cycle Profile": the compact
-// routed MXFP4 GEMM is the largest open kernel family at M=2). Every weight byte is used by at most
-// a handful of rows, so these kernels are organised around streaming the expert's packed weights
-// once, at full width:
-//   - each lane loads whole 32-element MX blocks: 16 bytes of E2M1 codes (one 128-bit load, a wave
-//     load covering up to 1 KB of consecutive bytes of a row) and the block's E8M0 scale byte;
+// routed MXFP4 GEMM is the largest open kernel family at M=2). Each weight byte is used by at most a
+// handful of rows, so these kernels are organised around streaming the expert weights once, at full
+// width, with loads always in flight:
+//   - each lane loads whole 32-element MX blocks: 16 bytes of E2M1 codes (one 128-bit load; a wave
+//     load covers up to 1 KB of consecutive bytes of a row) plus the block's E8M0 scale byte;
 //   - a row of K elements is split over `lpr` lanes (in-wave split-K), each owning fixed blocks, so
-//     the lane's slice of the activations is loaded into registers once and reused for every row;
+//     the lane's slice of the activations stays in registers for every row of an expert;
 //   - the codes are decoded in registers with the gfx950 scaled FP4 conversion (two codes and the
-//     scale per instruction) and consumed by bf16 dot2 (gate/up; products exact in fp32) or fp32 FMA
-//     (down, whose activations h are fp32);
-//   - partial sums are reduced across the row's lanes with a butterfly, deterministically;
+//     scale per instruction) and consumed by bf16 dot2 (gate/up; bf16 products are exact in fp32) or
+//     fp32 FMA (down, whose activations h are fp32);
+//   - partial sums are reduced across the row's lanes with DPP adds, deterministically;
 //   - gate row i and up row I+i are handled by the same lanes, so SwiGLU (with the optional clamp) is
 //     applied in registers and only h is written (gate_up fusion as in vllm.cpp PR #52; clamp-SwiGLU
-//     epilogue per the routed clamp-SwiGLU row of the Post-Portfolio Device Attribution table).
-// Grid: x = row tiles of the expert, y = active-expert slot. Slots past n_active and experts with more
-// than small_m_max rows exit at once; the grid is sized from host-known bounds only.
+//     epilogue as the routed clamp-SwiGLU row of the Post-Portfolio Device Attribution table).
+// Scheduling: the work is a list of items (expert, tile of rows). The grid is persistent (two
+// workgroups per CU); each workgroup takes a contiguous range of items and double-buffers them: the
+// weights of item i+1 are loaded into a second register set while item i is computed, so a wave
+// always has a tile of loads outstanding. A contiguous range stays mostly within one expert, so the
+// activations are reloaded only when the expert changes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,18 +42,20 @@ RowSplit choose_row_split(int K) {
 
 namespace {
 
-constexpr int gateup_slots(int bpl) { return bpl >= 8 ? 1 : 8 / bpl; }
-constexpr int down_slots(int bpl) { return bpl >= 16 ? 1 : 16 / bpl; }
+// Row slots per wave and item: each gate_up slot is a (gate row, up row) pair; down slots are rows.
+// Chosen so one item's loads per lane are about 8 x 16 bytes.
+constexpr int gateup_slots(int bpl) { return bpl >= 4 ? 1 : 4 / bpl; }
+constexpr int down_slots(int bpl) { return bpl >= 8 ? 1 : 8 / bpl; }
 
 __device__ __forceinline__ int ilog2(int v) { return 31 - __clz(v); }
 
-// acc[m] += <decoded block, x block of token m> for MTC tokens (gate/up: bf16 dot2).
 // The packed block is passed through an empty asm so the compiler cannot hoist its decode out of
 // the token loop (that would keep up to 32 decoded registers per block alive and spill).
 __device__ __forceinline__ void opaque(uint4& w) {
   asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
 }
 
+// acc[m] += <decoded block, x block of token m> for MTC tokens (gate/up: bf16 dot2).
 template <int MTC>
 __device__ __forceinline__ void dot_block_bf16(uint4 w, float scale, const uint4 (&xb)[MTC][4],
                                                float (&acc)[MTC]) {
@@ -104,24 +109,64 @@ __device__ __forceinline__ void dot_block_f32(uint4 w, float scale, const float4
   }
 }
 
-__device__ __forceinline__ float reduce_row(float v, int lpr) {
-  for (int off = lpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// v plus a DPP lane permutation of v (lanes outside row_mask add 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false);
+  return v + __builtin_bit_cast(float, moved);
+}
+
+// Sum over each aligned segment of `lpr` lanes (lpr a power of two); the total lands in the
+// segment's last lane (lane % lpr == lpr - 1), which is the lane that writes the result.
+__device__ __forceinline__ float segment_sum(float v, int lpr) {
+  if (lpr >= 2) v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  if (lpr >= 4) v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  if (lpr >= 8) v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+  if (lpr >= 16) v = dpp_add<0x140, 0xF>(v); // row_mirror
+  if (lpr >= 32) v = dpp_add<0x142, 0xA>(v); // row_bcast15 into rows 1 and 3
+  if (lpr >= 64) v = dpp_add<0x143, 0xC>(v); // row_bcast31 into rows 2 and 3
   return v;
 }
 
+struct ItemRange {
+  int begin, end;  // items [begin, end) of this workgroup
+};
+
+__device__ __forceinline__ bool my_items(const int* count_ptr, int tiles, ItemRange& ir) {
+  const int total = *count_ptr * tiles;
+  const int per = (total + gridDim.x - 1) / gridDim.x;
+  ir.begin = blockIdx.x * per;
+  ir.end = min(total, ir.begin + per);
+  return ir.begin < ir.end;
+}
+
+// ---------------------------------------------------------------------------------------------
+// gate_up
+
+template <int S, int BPL>
+struct GuStage {
+  uint4 w[S][2][BPL];
+  uint32_t sc[S][2][BPL];
+  int e;     // expert
+  int tile;  // row tile within the expert
+};
+
+// Two waves per SIMD where the double-buffered registers fit in 256 VGPRs; wide rows (many blocks
+// per lane) get one wave per SIMD and the full register file instead of spilling.
+constexpr int waves_per_simd(int bpl) { return bpl <= 4 ? 2 : 1; }
+// down keeps 32 fp32 activations per block and token in registers
+constexpr int down_waves_per_simd(int bpl) { return bpl <= 1 ? 2 : 1; }
+
 template <int BPL, int MT, int MODE>
-__global__ __launch_bounds__(256) void small_gateup_kernel(
-    Routed r, int H, int I, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s,
-    int lpr, int small_m_max, int check_m, float clamp, float* __restrict__ h_out,
-    float* __restrict__ g_ws) {
+__global__ __launch_bounds__(256, waves_per_simd(BPL)) void small_gateup_kernel(
+    Routed r, const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
+    int tiles, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s, int lpr,
+    float clamp, float* __restrict__ h_out, float* __restrict__ g_ws) {
   constexpr int S = gateup_slots(BPL);
   constexpr bool kGate = MODE != kUpWithGate;
   constexpr bool kUp = MODE != kGateOnly;
-
-  // active[] holds -1 past n_active, and the grid has at most E slots: no n_active read needed
-  const int e = r.active[blockIdx.y];
-  if (e < 0) return;
-  if (check_m && r.counts[e] > small_m_max) return;  // that expert runs on the MFMA kernels
+  ItemRange ir;
+  if (!my_items(list_count, tiles, ir)) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -130,142 +175,166 @@ __global__ __launch_bounds__(256) void small_gateup_kernel(
   const int sub = lane >> lg;
   const int rpw = 64 >> lg;
   const int NB = H >> 5;
-  const int tile = 4 * S * rpw;
+  const int tile_rows = 4 * S * rpw;
   const size_t qrow = (size_t)(H >> 1), srow = (size_t)NB;
-  const uint8_t* qe = w13_q + (size_t)e * 2 * I * qrow;
-  const uint8_t* se = w13_s + (size_t)e * 2 * I * srow;
+  const size_t qexp = (size_t)2 * I * qrow, sexp = (size_t)2 * I * srow;
 
-  // Every load below is unconditional at a clamped, in-bounds address, and out-of-range lanes are
-  // zeroed afterwards: a load under a branch would have to complete before the branch joins, which
-  // serialises the loads instead of keeping them all in flight.
-  int n[S];
-  uint4 wq[S][2][BPL];
-  uint32_t sc[S][2][BPL];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    n[s] = blockIdx.x * tile + (wave * S + s) * rpw + sub;
-    const int nc = min(n[s], I - 1);
-#pragma unroll
-    for (int gu = 0; gu < 2; ++gu) {
-      if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
-      const size_t row = (size_t)(gu ? I + nc : nc);
-#pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        const int kb = min(q + lpr * b, NB - 1);
-        wq[s][gu][b] = *reinterpret_cast<const uint4*>(qe + row * qrow + (size_t)kb * 16);
-        sc[s][gu][b] = (uint32_t)se[row * srow + kb];
-      }
+  int cur_slot = -1, cur_e = -1;
+  // Loads are unconditional at clamped in-bounds addresses; lanes past the end of a row or of the
+  // expert get a zero scale at use (a load under a branch would serialise the loads).
+  auto load = [&](GuStage<S, BPL>& st, int item) {
+    const int slot = item / tiles;
+    if (slot != cur_slot) {
+      cur_slot = slot;
+      cur_e = list[slot];
     }
-  }
+    st.e = cur_e;
+    st.tile = item - slot * tiles;
+    const uint8_t* qe = w13_q + (size_t)st.e * qexp;
+    const uint8_t* se = w13_s + (size_t)st.e * sexp;
 #pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int gu = 0; gu < 2; ++gu)
-#pragma unroll
-      for (int b = 0; b < BPL; ++b)
-        if (!(n[s] < I && q + lpr * b < NB)) wq[s][gu][b] = make_uint4(0, 0, 0, 0);
-
-  const int M = r.counts[e];
-  const int row0 = r.offsets[e];
-  for (int m0 = 0; m0 < M; m0 += MT) {
-    const int mc = min(MT, M - m0);
-    uint4 xb[MT][BPL][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int t = r.sorted_pair[row0 + m0 + min(m, mc - 1)] / r.k;
-#pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        const int kb = min(q + lpr * b, NB - 1);
-        const uint4* xp = reinterpret_cast<const uint4*>(r.x + (size_t)t * H + (size_t)kb * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xb[m][b][i] = xp[i];
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int b = 0; b < BPL; ++b)
-        if (!(m < mc && q + lpr * b < NB))
-#pragma unroll
-          for (int i = 0; i < 4; ++i) xb[m][b][i] = make_uint4(0, 0, 0, 0);
-
-    float acc[S][2][MT];
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int gu = 0; gu < 2; ++gu)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[s][gu][m] = 0.0f;
-
-#pragma unroll
-    for (int s = 0; s < S; ++s)
+    for (int s = 0; s < S; ++s) {
+      const int nc = min(st.tile * tile_rows + (wave * S + s) * rpw + sub, I - 1);
 #pragma unroll
       for (int gu = 0; gu < 2; ++gu) {
         if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
+        const size_t row = (size_t)(gu ? I + nc : nc);
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
-          const float scale = e8m0_to_float(sc[s][gu][b]);
-          if (MT == 1 || mc == MT) {
-            uint4 xs[MT][4];
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) xs[m][i] = xb[m][b][i];
-            dot_block_bf16<MT>(wq[s][gu][b], scale, xs, acc[s][gu]);
-          } else {
-            // fewer tokens left than MT: skip the empty ones (uniform branch)
-            uint4 xs[1][4];
-            float a1[1];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              if (m >= mc) break;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) xs[0][i] = xb[m][b][i];
-              a1[0] = acc[s][gu][m];
-              dot_block_bf16<1>(wq[s][gu][b], scale, xs, a1);
-              acc[s][gu][m] = a1[0];
-            }
-          }
-          // keep each block's decode next to its use (bounds the decoded values' live range)
-          __builtin_amdgcn_sched_barrier(0);
+          const int kb = min(q + lpr * b, NB - 1);
+          st.w[s][gu][b] = *reinterpret_cast<const uint4*>(qe + row * qrow + (size_t)kb * 16);
+          st.sc[s][gu][b] = (uint32_t)se[row * srow + kb];
         }
       }
+    }
+  };
 
+  int x_e = -1, x_m0 = -1, M = 0, row0 = 0;
+  uint4 xb[MT][BPL][4];
+
+  auto compute = [&](const GuStage<S, BPL>& st) {
+    if (st.e != x_e) {  // new expert: its row count and first row
+      x_e = st.e;
+      x_m0 = -1;
+      M = r.counts[x_e];
+      row0 = r.offsets[x_e];
+    }
+    for (int m0 = 0; m0 < M; m0 += MT) {
+      const int mc = min(MT, M - m0);
+      if (m0 != x_m0) {
+        // activation slices of tokens m0 .. m0+mc-1 (L2 hits; reloaded only when the expert or the
+        // token chunk changes, which a contiguous item range rarely does)
+        x_m0 = m0;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+        for (int m = 0; m < MT; ++m) {
+          const int t = r.sorted_pair[row0 + m0 + min(m, mc - 1)] / r.k;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        float g = kGate ? reduce_row(acc[s][0][m], lpr) : 0.0f;
-        float u = kUp ? reduce_row(acc[s][1][m], lpr) : 0.0f;
-        if (q == 0 && m < mc && n[s] < I) {
-          const size_t o = (size_t)(row0 + m0 + m) * I + n[s];
-          if (MODE == kGateOnly) {
-            g_ws[o] = g;
-          } else {
-            if (MODE == kUpWithGate) g = g_ws[o];
-            if (clamp > 0.0f) {
-              g = clampf(g, clamp);
-              u = clampf(u, clamp);
+          for (int b = 0; b < BPL; ++b) {
+            const int kb = min(q + lpr * b, NB - 1);
+            const uint4* xp = reinterpret_cast<const uint4*>(r.x + (size_t)t * H + (size_t)kb * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xb[m][b][i] = xp[i];
+          }
+        }
+      }
+      float acc[S][2][MT];
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[s][gu][m] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = st.tile * tile_rows + (wave * S + s) * rpw + sub;
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu) {
+          if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
+#pragma unroll
+          for (int b = 0; b < BPL; ++b) {
+            const bool ok = n < I && q + lpr * b < NB;
+            const float scale = ok ? e8m0_to_float(st.sc[s][gu][b]) : 0.0f;
+            if (MT == 1 || mc == MT) {
+              uint4 xs[MT][4];
+#pragma unroll
+              for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xs[m][i] = xb[m][b][i];
+              dot_block_bf16<MT>(st.w[s][gu][b], scale, xs, acc[s][gu]);
+            } else {
+              uint4 xs[1][4];
+              float a1[1];
+#pragma unroll
+              for (int m = 0; m < MT; ++m) {
+                if (m >= mc) break;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xs[0][i] = xb[m][b][i];
+                a1[0] = acc[s][gu][m];
+                dot_block_bf16<1>(st.w[s][gu][b], scale, xs, a1);
+                acc[s][gu][m] = a1[0];
+              }
             }
-            h_out[o] = silu_mul(g, u);
+            // keep each block's decode next to its use (bounds the decoded values' live range)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = st.tile * tile_rows + (wave * S + s) * rpw + sub;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float g = kGate ? segment_sum(acc[s][0][m], lpr) : 0.0f;
+          float u = kUp ? segment_sum(acc[s][1][m], lpr) : 0.0f;
+          if (q == lpr - 1 && m < mc && n < I) {
+            const size_t o = (size_t)(row0 + m0 + m) * I + n;
+            if (MODE == kGateOnly) {
+              g_ws[o] = g;
+            } else {
+              if (MODE == kUpWithGate) g = g_ws[o];
+              if (clamp > 0.0f) {
+                g = clampf(g, clamp);
+                u = clampf(u, clamp);
+              }
+              h_out[o] = silu_mul(g, u);
+            }
           }
         }
       }
     }
+  };
+
+  GuStage<S, BPL> sa, sb;
+  int it = ir.begin;
+  load(sa, it);
+  while (true) {
+    if (it + 1 < ir.end) load(sb, it + 1);
+    compute(sa);
+    if (++it >= ir.end) break;
+    if (it + 1 < ir.end) load(sa, it + 1);
+    compute(sb);
+    if (++it >= ir.end) break;
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// down
+
+template <int S, int BPL>
+struct DnStage {
+  uint4 w[S][BPL];
+  uint32_t sc[S][BPL];
+  int e, tile;
+};
+
 template <int BPL, int MT>
-__global__ __launch_bounds__(256) void small_down_kernel(Routed r, int H, int I,
-                                                         const uint8_t* __restrict__ w2_q,
-                                                         const uint8_t* __restrict__ w2_s, int lpr,
-                                                         int small_m_max, int check_m,
-                                                         const float* __restrict__ h,
-                                                         float* __restrict__ y) {
+__global__ __launch_bounds__(256, down_waves_per_simd(BPL)) void small_down_kernel(
+    Routed r, const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
+    int tiles, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s, int lpr,
+    const float* __restrict__ h, float* __restrict__ y) {
   constexpr int S = down_slots(BPL);
-  const int e = r.active[blockIdx.y];
-  if (e < 0) return;
-  if (check_m && r.counts[e] > small_m_max) return;
+  ItemRange ir;
+  if (!my_items(list_count, tiles, ir)) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -274,115 +343,138 @@ __global__ __launch_bounds__(256) void small_down_kernel(Routed r, int H, int I,
   const int sub = lane >> lg;
   const int rpw = 64 >> lg;
   const int NB = I >> 5;
-  const int tile = 4 * S * rpw;
+  const int tile_rows = 4 * S * rpw;
   const size_t qrow = (size_t)(I >> 1), srow = (size_t)NB;
-  const uint8_t* qe = w2_q + (size_t)e * H * qrow;
-  const uint8_t* se = w2_s + (size_t)e * H * srow;
+  const size_t qexp = (size_t)H * qrow, sexp = (size_t)H * srow;
 
-  int n[S];
-  uint4 wq[S][BPL];
-  uint32_t sc[S][BPL];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    n[s] = blockIdx.x * tile + (wave * S + s) * rpw + sub;
-    const size_t nc = (size_t)min(n[s], H - 1);
-#pragma unroll
-    for (int b = 0; b < BPL; ++b) {
-      const int kb = min(q + lpr * b, NB - 1);
-      wq[s][b] = *reinterpret_cast<const uint4*>(qe + nc * qrow + (size_t)kb * 16);
-      sc[s][b] = (uint32_t)se[nc * srow + kb];
+  int cur_slot = -1, cur_e = -1;
+  auto load = [&](DnStage<S, BPL>& st, int item) {
+    const int slot = item / tiles;
+    if (slot != cur_slot) {
+      cur_slot = slot;
+      cur_e = list[slot];
     }
-  }
+    st.e = cur_e;
+    st.tile = item - slot * tiles;
+    const uint8_t* qe = w2_q + (size_t)st.e * qexp;
+    const uint8_t* se = w2_s + (size_t)st.e * sexp;
 #pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int b = 0; b < BPL; ++b)
-      if (!(n[s] < H && q + lpr * b < NB)) wq[s][b] = make_uint4(0, 0, 0, 0);
-
-  const int M = r.counts[e];
-  const int row0 = r.offsets[e];
-
-  for (int m0 = 0; m0 < M; m0 += MT) {
-    const int mc = min(MT, M - m0);
-    float4 hb[MT][BPL][8];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
+    for (int s = 0; s < S; ++s) {
+      const size_t nc = (size_t)min(st.tile * tile_rows + (wave * S + s) * rpw + sub, H - 1);
 #pragma unroll
       for (int b = 0; b < BPL; ++b) {
         const int kb = min(q + lpr * b, NB - 1);
-        const float4* hp = reinterpret_cast<const float4*>(h + (size_t)(row0 + m0 + min(m, mc - 1)) * I +
-                                                           (size_t)kb * 32);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hb[m][b][i] = hp[i];
+        st.w[s][b] = *reinterpret_cast<const uint4*>(qe + nc * qrow + (size_t)kb * 16);
+        st.sc[s][b] = (uint32_t)se[nc * srow + kb];
       }
     }
+  };
+
+  int h_e = -1, h_m0 = -1, M = 0, row0 = 0;
+  float4 hb[MT][BPL][8];
+
+  auto compute = [&](const DnStage<S, BPL>& st) {
+    if (st.e != h_e) {
+      h_e = st.e;
+      h_m0 = -1;
+      M = r.counts[h_e];
+      row0 = r.offsets[h_e];
+    }
+    for (int m0 = 0; m0 < M; m0 += MT) {
+      const int mc = min(MT, M - m0);
+      if (m0 != h_m0) {
+        h_m0 = m0;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m) {
 #pragma unroll
-      for (int b = 0; b < BPL; ++b)
-        if (!(m < mc && q + lpr * b < NB))
+          for (int b = 0; b < BPL; ++b) {
+            const int kb = min(q + lpr * b, NB - 1);
+            const float4* hp = reinterpret_cast<const float4*>(
+                h + (size_t)(row0 + m0 + min(m, mc - 1)) * I + (size_t)kb * 32);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) hb[m][b][i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    float acc[S][MT];
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[s][m] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        const float scale = e8m0_to_float(sc[s][b]);
-        if (MT == 1 || mc == MT) {
-          float4 hs[MT][8];
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) hs[m][i] = hb[m][b][i];
-          dot_block_f32<MT>(wq[s][b], scale, hs, acc[s]);
-        } else {
-          float4 hs[1][8];
-          float a1[1];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            if (m >= mc) break;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) hs[0][i] = hb[m][b][i];
-            a1[0] = acc[s][m];
-            dot_block_f32<1>(wq[s][b], scale, hs, a1);
-            acc[s][m] = a1[0];
+            for (int i = 0; i < 8; ++i) hb[m][b][i] = hp[i];
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
+      }
+      float acc[S][MT];
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[s][m] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = st.tile * tile_rows + (wave * S + s) * rpw + sub;
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+          const bool ok = n < H && q + lpr * b < NB;
+          const float scale = ok ? e8m0_to_float(st.sc[s][b]) : 0.0f;
+          if (MT == 1 || mc == MT) {
+            float4 hs[MT][8];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) hs[m][i] = hb[m][b][i];
+            dot_block_f32<MT>(st.w[s][b], scale, hs, acc[s]);
+          } else {
+            float4 hs[1][8];
+            float a1[1];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              if (m >= mc) break;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) hs[0][i] = hb[m][b][i];
+              a1[0] = acc[s][m];
+              dot_block_f32<1>(st.w[s][b], scale, hs, a1);
+              acc[s][m] = a1[0];
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 #pragma unroll
-    for (int s = 0; s < S; ++s)
+      for (int s = 0; s < S; ++s) {
+        const int n = st.tile * tile_rows + (wave * S + s) * rpw + sub;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const float v = reduce_row(acc[s][m], lpr);
-        if (q == 0 && m < mc && n[s] < H) y[(size_t)(row0 + m0 + m) * H + n[s]] = v;
+        for (int m = 0; m < MT; ++m) {
+          const float v = segment_sum(acc[s][m], lpr);
+          if (q == lpr - 1 && m < mc && n < H) y[(size_t)(row0 + m0 + m) * H + n] = v;
+        }
       }
+    }
+  };
+
+  DnStage<S, BPL> sa, sb;
+  int it = ir.begin;
+  load(sa, it);
+  while (true) {
+    if (it + 1 < ir.end) load(sb, it + 1);
+    compute(sa);
+    if (++it >= ir.end) break;
+    if (it + 1 < ir.end) load(sa, it + 1);
+    compute(sb);
+    if (++it >= ir.end) break;
   }
 }
 
 template <int MODE>
-hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, int H, int I, const uint8_t* wq,
-                           const uint8_t* ws, int small_m_max, int check_m, float clamp, float* h,
-                           float* g_ws, hipStream_t stream) {
-  const dim3 grid(sp.gu_grid_x, sp.slots), block(256);
-  const int lpr = sp.gu.lpr;
+hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* list,
+                           const int32_t* list_count, int H, int I, const uint8_t* wq,
+                           const uint8_t* ws, float clamp, float* h, float* g_ws,
+                           hipStream_t stream) {
+  const dim3 grid(sp.gu_grid), block(256);
+  const int lpr = sp.gu.lpr, tiles = sp.gu_tiles;
 #define MOE_GU(BPL, MT)                                                                           \
-  small_gateup_kernel<BPL, MT, MODE><<<grid, block, 0, stream>>>(r, H, I, wq, ws, lpr, small_m_max, \
-                                                                 check_m, clamp, h, g_ws)
-#define MOE_GU_MT(BPL)   \
-  if (sp.mt_gu == 2)     \
-    MOE_GU(BPL, 2);      \
-  else                   \
+  small_gateup_kernel<BPL, MT, MODE><<<grid, block, 0, stream>>>(r, list, list_count, H, I, tiles, \
+                                                                 wq, ws, lpr, clamp, h, g_ws)
+#define MOE_GU_MT(BPL) \
+  if (sp.mt_gu == 2)   \
+    MOE_GU(BPL, 2);    \
+  else                 \
     MOE_GU(BPL, 1);
   switch (sp.gu.bpl) {
     case 1: MOE_GU_MT(1) break;
     case 2: MOE_GU_MT(2) break;
-    case 3: MOE_GU_MT(3) break;
+    case 3: MOE_GU(3, 1); break;
     case 4: MOE_GU(4, 1); break;
     case 5: MOE_GU(5, 1); break;
     case 6: MOE_GU(6, 1); break;
@@ -397,49 +489,56 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, int H, int I, c
 
 }  // namespace
 
-SmallPlan plan_small(int T, int H, int I, int E, int k) {
+SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
   SmallPlan sp;
   sp.gu = choose_row_split(H);
   sp.dn = choose_row_split(I);
   const int rpw_gu = 64 / sp.gu.lpr, rpw_dn = 64 / sp.dn.lpr;
   sp.gu_tile = 4 * gateup_slots(sp.gu.bpl) * rpw_gu;
   sp.dn_tile = 4 * down_slots(sp.dn.bpl) * rpw_dn;
-  sp.gu_grid_x = (I + sp.gu_tile - 1) / sp.gu_tile;
-  sp.dn_grid_x = (H + sp.dn_tile - 1) / sp.dn_tile;
+  sp.gu_tiles = (I + sp.gu_tile - 1) / sp.gu_tile;
+  sp.dn_tiles = (H + sp.dn_tile - 1) / sp.dn_tile;
   const long P = (long)T * k;
   sp.slots = (int)(P < E ? P : E);
-  sp.mt_gu = (T >= 2 && sp.gu.bpl <= 3) ? 2 : 1;
+  // persistent grid: two workgroups per CU, never more than there can be items
+  const long cap = 2L * num_cus;
+  const long gu_items = (long)sp.slots * sp.gu_tiles, dn_items = (long)sp.slots * sp.dn_tiles;
+  sp.gu_grid = (int)(gu_items < cap ? gu_items : cap);
+  sp.dn_grid = (int)(dn_items < cap ? dn_items : cap);
+  sp.mt_gu = (T >= 2 && sp.gu.bpl <= 2) ? 2 : 1;
   sp.mt_dn = (T >= 2 && sp.dn.bpl <= 2) ? 2 : 1;
   return sp;
 }
 
-hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, int H, int I,
-                               const uint8_t* w13_q, const uint8_t* w13_s, int small_m_max,
-                               int check_m, float clamp, int mode, float* h, float* g_ws,
+hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32_t* list,
+                               const int32_t* list_count, int H, int I, const uint8_t* w13_q,
+                               const uint8_t* w13_s, float clamp, int mode, float* h, float* g_ws,
                                hipStream_t stream) {
+  if (sp.gu_grid <= 0) return hipSuccess;
   switch (mode) {
     case kGateUpFused:
-      return gateup_dispatch<kGateUpFused>(sp, r, H, I, w13_q, w13_s, small_m_max, check_m, clamp, h, g_ws,
-                                       stream);
+      return gateup_dispatch<kGateUpFused>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h, g_ws,
+                                           stream);
     case kGateOnly:
-      return gateup_dispatch<kGateOnly>(sp, r, H, I, w13_q, w13_s, small_m_max, check_m, clamp, h, g_ws,
-                                       stream);
+      return gateup_dispatch<kGateOnly>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h, g_ws,
+                                        stream);
     case kUpWithGate:
-      return gateup_dispatch<kUpWithGate>(sp, r, H, I, w13_q, w13_s, small_m_max, check_m, clamp, h, g_ws,
-                                       stream);
+      return gateup_dispatch<kUpWithGate>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h, g_ws,
+                                          stream);
     default:
       return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, int H, int I, const uint8_t* w2_q,
-                             const uint8_t* w2_s, int small_m_max, int check_m, const float* h,
-                             float* y, hipStream_t stream) {
-  const dim3 grid(sp.dn_grid_x, sp.slots), block(256);
-  const int lpr = sp.dn.lpr;
-#define MOE_DN(BPL, MT) \
-  small_down_kernel<BPL, MT><<<grid, block, 0, stream>>>(r, H, I, w2_q, w2_s, lpr, small_m_max, \
-                                                         check_m, h, y)
+hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t* list,
+                             const int32_t* list_count, int H, int I, const uint8_t* w2_q,
+                             const uint8_t* w2_s, const float* h, float* y, hipStream_t stream) {
+  if (sp.dn_grid <= 0) return hipSuccess;
+  const dim3 grid(sp.dn_grid), block(256);
+  const int lpr = sp.dn.lpr, tiles = sp.dn_tiles;
+#define MOE_DN(BPL, MT)                                                                          \
+  small_down_kernel<BPL, MT><<<grid, block, 0, stream>>>(r, list, list_count, H, I, tiles, w2_q, \
+                                                         w2_s, lpr, h, y)
   switch (sp.dn.bpl) {
     case 1:
       if (sp.mt_dn == 2) MOE_DN(1, 2); else MOE_DN(1, 1);

@@ -35,30 +35,29 @@ struct RowSplit {
 
 RowSplit choose_row_split(int K);
 
-// Weight-streaming kernels for experts with at most `small_m_max` rows.
+// Weight-streaming kernels for experts with at most `small_m_max` rows. They work through the
+// experts of `list` (the first *list_count entries; the active list, or the schedule's small list).
 enum SmallGateUpMode { kGateUpFused = 0, kGateOnly = 1, kUpWithGate = 2 };
 
 struct SmallPlan {
   RowSplit gu, dn;
-  int gu_tile;    // gate rows per gate_up workgroup
-  int dn_tile;    // down rows per down workgroup
-  int gu_grid_x;  // gate_up workgroups per expert
-  int dn_grid_x;  // down workgroups per expert
-  int slots;      // expert slots in the grid (min(E, P))
-  int mt_gu, mt_dn;  // tokens per pass
+  int gu_tile, dn_tile;    // rows per item (gate rows for gate_up, output rows for down)
+  int gu_tiles, dn_tiles;  // items per expert
+  int gu_grid, dn_grid;    // persistent workgroups
+  int slots;               // bound on the number of experts in the list (min(E, P))
+  int mt_gu, mt_dn;        // tokens per pass
 };
 
-SmallPlan plan_small(int T, int H, int I, int E, int k);
+SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus);
 
-// check_m: the MFMA kernels are launched too, so experts above small_m_max must be skipped here.
-hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, int H, int I,
-                               const uint8_t* w13_q, const uint8_t* w13_s, int small_m_max,
-                               int check_m, float clamp, int mode, float* h, float* g_ws,
+hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32_t* list,
+                               const int32_t* list_count, int H, int I, const uint8_t* w13_q,
+                               const uint8_t* w13_s, float clamp, int mode, float* h, float* g_ws,
                                hipStream_t stream);
 
-hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, int H, int I, const uint8_t* w2_q,
-                             const uint8_t* w2_s, int small_m_max, int check_m, const float* h,
-                             float* y, hipStream_t stream);
+hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t* list,
+                             const int32_t* list_count, int H, int I, const uint8_t* w2_q,
+                             const uint8_t* w2_s, const float* h, float* y, hipStream_t stream);
 
 // bf16-MFMA kernels for experts with more than `small_m_max` rows: tiles of up to 64 rows of one
 // expert; the weight rows are decoded from MXFP4 to bf16 in registers, the activation tile is staged
@@ -71,15 +70,21 @@ struct LargePlan {
   int tile_slots;    // upper bound on the number of (expert, row-tile) pairs
 };
 
+int tile_slots_bound(int T, int E, int k, int small_m_max);
 LargePlan plan_large(int T, int H, int I, int E, int k, int small_m_max);
 
+// Splits the active experts by row count: small_list/n_small for the weight-streaming kernels,
+// tile_e/tile_m0 (tile_slots entries, -1 past the last tile) for the MFMA kernels.
+hipError_t launch_schedule(const Routed& r, int E, int small_m_max, int tile_slots, int32_t* small_list,
+                           int32_t* n_small, int32_t* tile_e, int32_t* tile_m0, hipStream_t stream);
+
 hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int I,
-                               const uint8_t* w13_q, const uint8_t* w13_s, int small_m_max,
-                               float clamp, float* h, hipStream_t stream);
+                               const uint8_t* w13_q, const uint8_t* w13_s, const int32_t* tile_e,
+                               const int32_t* tile_m0, float clamp, float* h, hipStream_t stream);
 
 hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I, const uint8_t* w2_q,
-                             const uint8_t* w2_s, int small_m_max, const float* h, float* y,
-                             hipStream_t stream);
+                             const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
+                             const float* h, float* y, hipStream_t stream);
 
 // out[t] = bf16(sum_j topk_w[t, j] * y[pair_pos[t*k + j]])
 hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* pair_pos, int T, int H,

@@ -121,11 +121,13 @@ def test_launch_plan(lib):
 
     p = m.ffn_plan(8, 4096, 2048, 256, 8)
     assert p["launch_small"] == 1 and p["launch_large"] == 0 and p["n_launches"] == 3
-    assert p["small_gateup_grid"] == (2048 // 16) * 64  # 16 gate rows per workgroup, 64 expert slots
+    # persistent grid: two workgroups per CU (256 CUs when no device can be queried)
+    assert p["small_gateup_grid"] == 512 and p["small_down_grid"] == 512
+    assert m.ffn_plan(1, 2048, 768, 128, 8)["small_gateup_grid"] <= 8 * 768
     p = m.ffn_plan(8, 4096, 2048, 256, 8, m.UNFUSED_GATE_UP)
     assert p["n_launches"] == 4
     p = m.ffn_plan(1024, 7168, 2048, 256, 8)
-    assert p["launch_small"] == 1 and p["launch_large"] == 1 and p["n_launches"] == 5
+    assert p["launch_small"] == 1 and p["launch_large"] == 1 and p["n_launches"] == 6
     p = m.ffn_plan(1024, 7168, 2048, 256, 8, m.FORCE_LARGE_M)
     assert p["launch_small"] == 0 and p["launch_large"] == 1 and p["small_m_max"] == 0
     p = m.ffn_plan(1024, 7168, 2048, 256, 8, m.FORCE_SMALL_M)
