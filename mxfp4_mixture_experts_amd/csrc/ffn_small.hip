@@ -16,11 +16,11 @@
 //   - gate row i and up row I+i are handled by the same lanes, so SwiGLU (with the optional clamp) is
 //     applied in registers and only h is written (gate_up fusion as in vllm.cpp PR #52; clamp-SwiGLU
 //     epilogue as the routed clamp-SwiGLU row of the Post-Portfolio Device Attribution table).
-// Scheduling: the work is a list of items (expert, tile of rows). The grid is persistent (two
-// workgroups per CU); each workgroup takes a contiguous range of items and double-buffers them: the
-// weights of item i+1 are loaded into a second register set while item i is computed, so a wave
-// always has a tile of loads outstanding. A contiguous range stays mostly within one expert, so the
-// activations are reloaded only when the expert changes.
+// Scheduling: the work is a list of items (expert, tile of rows). The grid is persistent (as many
+// workgroups per CU as the register budget allows waves per SIMD); each workgroup takes a contiguous
+// range of items. A wave issues all loads of an item before consuming them, and the other resident
+// waves hide its latency. A contiguous range stays mostly within one expert, so the activations are
+// reloaded only when the expert changes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,12 +42,21 @@ RowSplit choose_row_split(int K) {
 
 namespace {
 
-// Row slots per wave and item: each gate_up slot is a (gate row, up row) pair; down slots are rows.
-// Chosen so one item's loads per lane are about 8 x 16 bytes.
+// Row slots per wave and item (gate_up slot = a gate row and its up row): about 8 block loads per
+// lane per item, so that 3-4 waves fit per SIMD.
 constexpr int gateup_slots(int bpl) { return bpl >= 4 ? 1 : 4 / bpl; }
 constexpr int down_slots(int bpl) { return bpl >= 8 ? 1 : 8 / bpl; }
 
 __device__ __forceinline__ int ilog2(int v) { return 31 - __clz(v); }
+
+// Waves per SIMD each variant's registers allow without spilling (4 waves x 128 VGPRs, 3 x 168,
+// 2 x 256, 1 x 512), read off the compiler's resource usage for these tile shapes.
+constexpr int gu_waves(int bpl, int mt, int) {
+  return bpl == 1 ? 4 : bpl == 2 ? (mt == 1 ? 4 : 3) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
+}
+constexpr int dn_waves(int bpl, int mt, int) {
+  return bpl == 1 ? 3 : bpl == 2 ? (mt == 1 ? 2 : 2) : bpl == 3 ? 2 : 1;
+}
 
 // The packed block is passed through an empty asm so the compiler cannot hoist its decode out of
 // the token loop (that would keep up to 32 decoded registers per block alive and spill).
@@ -140,29 +149,34 @@ __device__ __forceinline__ bool my_items(const int* count_ptr, int tiles, ItemRa
   return ir.begin < ir.end;
 }
 
-// ---------------------------------------------------------------------------------------------
-// gate_up
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int S, int BPL>
-struct GuStage {
-  uint4 w[S][2][BPL];
-  uint32_t sc[S][2][BPL];
-  int e;     // expert
-  int tile;  // row tile within the expert
+// 16 bytes / 1 byte at a uniform base plus a 32-bit per-lane offset (lets the compiler use the
+// scalar-base addressing form, one VGPR per address)
+__device__ __forceinline__ uint4 ld16(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+__device__ __forceinline__ uint32_t ld8(const uint8_t* base, uint32_t off) { return base[off]; }
+
+// The item currently streamed: its expert and row tile, and the expert's weight bases.
+struct Item {
+  int slot, e, tile;
+  const uint8_t* q;
+  const uint8_t* s;
 };
 
-// Two waves per SIMD where the double-buffered registers fit in 256 VGPRs; wide rows (many blocks
-// per lane) get one wave per SIMD and the full register file instead of spilling.
-constexpr int waves_per_simd(int bpl) { return bpl <= 4 ? 2 : 1; }
-// down keeps 32 fp32 activations per block and token in registers
-constexpr int down_waves_per_simd(int bpl) { return bpl <= 1 ? 2 : 1; }
+// ---------------------------------------------------------------------------------------------
+// gate_up
+//
+// Each wave streams items of S (gate row, up row) slot pairs: it issues all of the item's block loads
+// at once, then decodes and consumes them. There is no second register set: latency is hidden by the
+// other waves of the CU (3-4 per SIMD), which is why the register budget is kept small.
 
-template <int BPL, int MT, int MODE>
-__global__ __launch_bounds__(256, waves_per_simd(BPL)) void small_gateup_kernel(
+template <int BPL, int MT, int S, int MODE>
+__global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel(
     Routed r, const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
     int tiles, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s, int lpr,
     float clamp, float* __restrict__ h_out, float* __restrict__ g_ws) {
-  constexpr int S = gateup_slots(BPL);
   constexpr bool kGate = MODE != kUpWithGate;
   constexpr bool kUp = MODE != kGateOnly;
   ItemRange ir;
@@ -176,64 +190,58 @@ __global__ __launch_bounds__(256, waves_per_simd(BPL)) void small_gateup_kernel(
   const int rpw = 64 >> lg;
   const int NB = H >> 5;
   const int tile_rows = 4 * S * rpw;
-  const size_t qrow = (size_t)(H >> 1), srow = (size_t)NB;
+  const uint32_t qrow = (uint32_t)(H >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)2 * I * qrow, sexp = (size_t)2 * I * srow;
 
-  int cur_slot = -1, cur_e = -1;
-  // Loads are unconditional at clamped in-bounds addresses; lanes past the end of a row or of the
-  // expert get a zero scale at use (a load under a branch would serialise the loads).
-  auto load = [&](GuStage<S, BPL>& st, int item) {
-    const int slot = item / tiles;
-    if (slot != cur_slot) {
-      cur_slot = slot;
-      cur_e = list[slot];
+  int slot_c = -1, e = -1, M = 0, row0 = 0, x_m0 = -1;
+  uint4 xb[MT][BPL][4];
+
+  for (int item = ir.begin; item < ir.end; ++item) {
+    const int slot = uniform(item / tiles);
+    const int tile = uniform(item - slot * tiles);
+    if (slot != slot_c) {  // new expert
+      slot_c = slot;
+      e = uniform(list[slot]);
+      M = uniform(r.counts[e]);
+      row0 = uniform(r.offsets[e]);
+      x_m0 = -1;
     }
-    st.e = cur_e;
-    st.tile = item - slot * tiles;
-    const uint8_t* qe = w13_q + (size_t)st.e * qexp;
-    const uint8_t* se = w13_s + (size_t)st.e * sexp;
+    const uint8_t* qe = w13_q + (size_t)e * qexp;
+    const uint8_t* se = w13_s + (size_t)e * sexp;
+
+    // all loads of the item first (unconditional, clamped in-bounds; lanes past a row end or the
+    // expert's last row get a zero scale at use)
+    uint4 w[S][2][BPL];
+    uint32_t sc[S][2][BPL];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int nc = min(st.tile * tile_rows + (wave * S + s) * rpw + sub, I - 1);
+      const int nc = min(tile * tile_rows + (wave * S + s) * rpw + sub, I - 1);
 #pragma unroll
       for (int gu = 0; gu < 2; ++gu) {
         if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
-        const size_t row = (size_t)(gu ? I + nc : nc);
+        const uint32_t row = (uint32_t)(gu ? I + nc : nc);
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
-          const int kb = min(q + lpr * b, NB - 1);
-          st.w[s][gu][b] = *reinterpret_cast<const uint4*>(qe + row * qrow + (size_t)kb * 16);
-          st.sc[s][gu][b] = (uint32_t)se[row * srow + kb];
+          const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
+          w[s][gu][b] = ld16(qe, row * qrow + kb * 16);
+          sc[s][gu][b] = ld8(se, row * srow + kb);
         }
       }
     }
-  };
 
-  int x_e = -1, x_m0 = -1, M = 0, row0 = 0;
-  uint4 xb[MT][BPL][4];
-
-  auto compute = [&](const GuStage<S, BPL>& st) {
-    if (st.e != x_e) {  // new expert: its row count and first row
-      x_e = st.e;
-      x_m0 = -1;
-      M = r.counts[x_e];
-      row0 = r.offsets[x_e];
-    }
     for (int m0 = 0; m0 < M; m0 += MT) {
       const int mc = min(MT, M - m0);
-      if (m0 != x_m0) {
-        // activation slices of tokens m0 .. m0+mc-1 (L2 hits; reloaded only when the expert or the
-        // token chunk changes, which a contiguous item range rarely does)
+      if (m0 != x_m0) {  // activation slices of this token chunk (L2 hits)
         x_m0 = m0;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const int t = r.sorted_pair[row0 + m0 + min(m, mc - 1)] / r.k;
+          const int t = uniform(r.sorted_pair[row0 + m0 + min(m, mc - 1)]) / r.k;
+          const uint8_t* xbase = reinterpret_cast<const uint8_t*>(r.x + (size_t)t * H);
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
-            const int kb = min(q + lpr * b, NB - 1);
-            const uint4* xp = reinterpret_cast<const uint4*>(r.x + (size_t)t * H + (size_t)kb * 32);
+            const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xb[m][b][i] = xp[i];
+            for (int i = 0; i < 4; ++i) xb[m][b][i] = ld16(xbase, kb * 64 + i * 16);
           }
         }
       }
@@ -246,47 +254,43 @@ __global__ __launch_bounds__(256, waves_per_simd(BPL)) void small_gateup_kernel(
           for (int m = 0; m < MT; ++m) acc[s][gu][m] = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = st.tile * tile_rows + (wave * S + s) * rpw + sub;
+        const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int gu = 0; gu < 2; ++gu) {
           if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
             const bool ok = n < I && q + lpr * b < NB;
-            const float scale = ok ? e8m0_to_float(st.sc[s][gu][b]) : 0.0f;
+            const float scale = ok ? e8m0_to_float(sc[s][gu][b]) : 0.0f;
             if (MT == 1 || mc == MT) {
               uint4 xs[MT][4];
 #pragma unroll
               for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) xs[m][i] = xb[m][b][i];
-              dot_block_bf16<MT>(st.w[s][gu][b], scale, xs, acc[s][gu]);
+              dot_block_bf16<MT>(w[s][gu][b], scale, xs, acc[s][gu]);
             } else {
               uint4 xs[1][4];
               float a1[1];
 #pragma unroll
-              for (int m = 0; m < MT; ++m) {
-                if (m >= mc) break;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) xs[0][i] = xb[m][b][i];
-                a1[0] = acc[s][gu][m];
-                dot_block_bf16<1>(st.w[s][gu][b], scale, xs, a1);
-                acc[s][gu][m] = a1[0];
-              }
+              for (int i = 0; i < 4; ++i) xs[0][i] = xb[0][b][i];
+              a1[0] = acc[s][gu][0];
+              dot_block_bf16<1>(w[s][gu][b], scale, xs, a1);
+              acc[s][gu][0] = a1[0];
             }
-            // keep each block's decode next to its use (bounds the decoded values' live range)
             __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = st.tile * tile_rows + (wave * S + s) * rpw + sub;
+        const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+          if (m >= mc) break;
           float g = kGate ? segment_sum(acc[s][0][m], lpr) : 0.0f;
           float u = kUp ? segment_sum(acc[s][1][m], lpr) : 0.0f;
-          if (q == lpr - 1 && m < mc && n < I) {
+          if (q == lpr - 1 && n < I) {
             const size_t o = (size_t)(row0 + m0 + m) * I + n;
             if (MODE == kGateOnly) {
               g_ws[o] = g;
@@ -302,37 +306,17 @@ __global__ __launch_bounds__(256, waves_per_simd(BPL)) void small_gateup_kernel(
         }
       }
     }
-  };
-
-  GuStage<S, BPL> sa, sb;
-  int it = ir.begin;
-  load(sa, it);
-  while (true) {
-    if (it + 1 < ir.end) load(sb, it + 1);
-    compute(sa);
-    if (++it >= ir.end) break;
-    if (it + 1 < ir.end) load(sa, it + 1);
-    compute(sb);
-    if (++it >= ir.end) break;
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// down
+// down (same structure; rows of W2, activations h in fp32)
 
-template <int S, int BPL>
-struct DnStage {
-  uint4 w[S][BPL];
-  uint32_t sc[S][BPL];
-  int e, tile;
-};
-
-template <int BPL, int MT>
-__global__ __launch_bounds__(256, down_waves_per_simd(BPL)) void small_down_kernel(
+template <int BPL, int MT, int S>
+__global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
     Routed r, const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
     int tiles, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s, int lpr,
     const float* __restrict__ h, float* __restrict__ y) {
-  constexpr int S = down_slots(BPL);
   ItemRange ir;
   if (!my_items(list_count, tiles, ir)) return;
 
@@ -344,55 +328,52 @@ __global__ __launch_bounds__(256, down_waves_per_simd(BPL)) void small_down_kern
   const int rpw = 64 >> lg;
   const int NB = I >> 5;
   const int tile_rows = 4 * S * rpw;
-  const size_t qrow = (size_t)(I >> 1), srow = (size_t)NB;
+  const uint32_t qrow = (uint32_t)(I >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)H * qrow, sexp = (size_t)H * srow;
 
-  int cur_slot = -1, cur_e = -1;
-  auto load = [&](DnStage<S, BPL>& st, int item) {
-    const int slot = item / tiles;
-    if (slot != cur_slot) {
-      cur_slot = slot;
-      cur_e = list[slot];
-    }
-    st.e = cur_e;
-    st.tile = item - slot * tiles;
-    const uint8_t* qe = w2_q + (size_t)st.e * qexp;
-    const uint8_t* se = w2_s + (size_t)st.e * sexp;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const size_t nc = (size_t)min(st.tile * tile_rows + (wave * S + s) * rpw + sub, H - 1);
-#pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        const int kb = min(q + lpr * b, NB - 1);
-        st.w[s][b] = *reinterpret_cast<const uint4*>(qe + nc * qrow + (size_t)kb * 16);
-        st.sc[s][b] = (uint32_t)se[nc * srow + kb];
-      }
-    }
-  };
-
-  int h_e = -1, h_m0 = -1, M = 0, row0 = 0;
+  int slot_c = -1, e = -1, M = 0, row0 = 0, h_m0 = -1;
   float4 hb[MT][BPL][8];
 
-  auto compute = [&](const DnStage<S, BPL>& st) {
-    if (st.e != h_e) {
-      h_e = st.e;
+  for (int item = ir.begin; item < ir.end; ++item) {
+    const int slot = uniform(item / tiles);
+    const int tile = uniform(item - slot * tiles);
+    if (slot != slot_c) {
+      slot_c = slot;
+      e = uniform(list[slot]);
+      M = uniform(r.counts[e]);
+      row0 = uniform(r.offsets[e]);
       h_m0 = -1;
-      M = r.counts[h_e];
-      row0 = r.offsets[h_e];
     }
+    const uint8_t* qe = w2_q + (size_t)e * qexp;
+    const uint8_t* se = w2_s + (size_t)e * sexp;
+
+    uint4 w[S][BPL];
+    uint32_t sc[S][BPL];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint32_t row = (uint32_t)min(tile * tile_rows + (wave * S + s) * rpw + sub, H - 1);
+#pragma unroll
+      for (int b = 0; b < BPL; ++b) {
+        const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
+        w[s][b] = ld16(qe, row * qrow + kb * 16);
+        sc[s][b] = ld8(se, row * srow + kb);
+      }
+    }
+
     for (int m0 = 0; m0 < M; m0 += MT) {
       const int mc = min(MT, M - m0);
       if (m0 != h_m0) {
         h_m0 = m0;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+          const uint8_t* hbase =
+              reinterpret_cast<const uint8_t*>(h + (size_t)(row0 + m0 + min(m, mc - 1)) * I);
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
-            const int kb = min(q + lpr * b, NB - 1);
-            const float4* hp = reinterpret_cast<const float4*>(
-                h + (size_t)(row0 + m0 + min(m, mc - 1)) * I + (size_t)kb * 32);
+            const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) hb[m][b][i] = hp[i];
+            for (int i = 0; i < 8; ++i)
+              hb[m][b][i] = __builtin_bit_cast(float4, ld16(hbase, kb * 128 + i * 16));
           }
         }
       }
@@ -403,56 +384,41 @@ __global__ __launch_bounds__(256, down_waves_per_simd(BPL)) void small_down_kern
         for (int m = 0; m < MT; ++m) acc[s][m] = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = st.tile * tile_rows + (wave * S + s) * rpw + sub;
+        const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
           const bool ok = n < H && q + lpr * b < NB;
-          const float scale = ok ? e8m0_to_float(st.sc[s][b]) : 0.0f;
+          const float scale = ok ? e8m0_to_float(sc[s][b]) : 0.0f;
           if (MT == 1 || mc == MT) {
             float4 hs[MT][8];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
               for (int i = 0; i < 8; ++i) hs[m][i] = hb[m][b][i];
-            dot_block_f32<MT>(st.w[s][b], scale, hs, acc[s]);
+            dot_block_f32<MT>(w[s][b], scale, hs, acc[s]);
           } else {
             float4 hs[1][8];
             float a1[1];
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              if (m >= mc) break;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) hs[0][i] = hb[m][b][i];
-              a1[0] = acc[s][m];
-              dot_block_f32<1>(st.w[s][b], scale, hs, a1);
-              acc[s][m] = a1[0];
-            }
+            for (int i = 0; i < 8; ++i) hs[0][i] = hb[0][b][i];
+            a1[0] = acc[s][0];
+            dot_block_f32<1>(w[s][b], scale, hs, a1);
+            acc[s][0] = a1[0];
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = st.tile * tile_rows + (wave * S + s) * rpw + sub;
+        const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+          if (m >= mc) break;
           const float v = segment_sum(acc[s][m], lpr);
-          if (q == lpr - 1 && m < mc && n < H) y[(size_t)(row0 + m0 + m) * H + n] = v;
+          if (q == lpr - 1 && n < H) y[(size_t)(row0 + m0 + m) * H + n] = v;
         }
       }
     }
-  };
-
-  DnStage<S, BPL> sa, sb;
-  int it = ir.begin;
-  load(sa, it);
-  while (true) {
-    if (it + 1 < ir.end) load(sb, it + 1);
-    compute(sa);
-    if (++it >= ir.end) break;
-    if (it + 1 < ir.end) load(sa, it + 1);
-    compute(sb);
-    if (++it >= ir.end) break;
   }
 }
 
@@ -463,9 +429,9 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
                            hipStream_t stream) {
   const dim3 grid(sp.gu_grid), block(256);
   const int lpr = sp.gu.lpr, tiles = sp.gu_tiles;
-#define MOE_GU(BPL, MT)                                                                           \
-  small_gateup_kernel<BPL, MT, MODE><<<grid, block, 0, stream>>>(r, list, list_count, H, I, tiles, \
-                                                                 wq, ws, lpr, clamp, h, g_ws)
+#define MOE_GU(BPL, MT)                                                                        \
+  small_gateup_kernel<BPL, MT, gateup_slots(BPL), MODE><<<grid, block, 0, stream>>>(            \
+      r, list, list_count, H, I, tiles, wq, ws, lpr, clamp, h, g_ws)
 #define MOE_GU_MT(BPL) \
   if (sp.mt_gu == 2)   \
     MOE_GU(BPL, 2);    \
@@ -487,6 +453,9 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
   return hipGetLastError();
 }
 
+int gu_waves_rt(int bpl, int mt) { return gu_waves(bpl, mt, gateup_slots(bpl)); }
+int dn_waves_rt(int bpl, int mt) { return dn_waves(bpl, mt, down_slots(bpl)); }
+
 }  // namespace
 
 SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
@@ -500,13 +469,15 @@ SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
   sp.dn_tiles = (H + sp.dn_tile - 1) / sp.dn_tile;
   const long P = (long)T * k;
   sp.slots = (int)(P < E ? P : E);
-  // persistent grid: two workgroups per CU, never more than there can be items
-  const long cap = 2L * num_cus;
-  const long gu_items = (long)sp.slots * sp.gu_tiles, dn_items = (long)sp.slots * sp.dn_tiles;
-  sp.gu_grid = (int)(gu_items < cap ? gu_items : cap);
-  sp.dn_grid = (int)(dn_items < cap ? dn_items : cap);
   sp.mt_gu = (T >= 2 && sp.gu.bpl <= 2) ? 2 : 1;
   sp.mt_dn = (T >= 2 && sp.dn.bpl <= 2) ? 2 : 1;
+  // persistent grid: one workgroup (4 waves) per CU per wave/SIMD of occupancy, never more than
+  // there can be items
+  const long gu_cap = (long)gu_waves_rt(sp.gu.bpl, sp.mt_gu) * num_cus;
+  const long dn_cap = (long)dn_waves_rt(sp.dn.bpl, sp.mt_dn) * num_cus;
+  const long gu_items = (long)sp.slots * sp.gu_tiles, dn_items = (long)sp.slots * sp.dn_tiles;
+  sp.gu_grid = (int)(gu_items < gu_cap ? gu_items : gu_cap);
+  sp.dn_grid = (int)(dn_items < dn_cap ? dn_items : dn_cap);
   return sp;
 }
 
@@ -536,9 +507,9 @@ hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t
   if (sp.dn_grid <= 0) return hipSuccess;
   const dim3 grid(sp.dn_grid), block(256);
   const int lpr = sp.dn.lpr, tiles = sp.dn_tiles;
-#define MOE_DN(BPL, MT)                                                                          \
-  small_down_kernel<BPL, MT><<<grid, block, 0, stream>>>(r, list, list_count, H, I, tiles, w2_q, \
-                                                         w2_s, lpr, h, y)
+#define MOE_DN(BPL, MT)                                                                       \
+  small_down_kernel<BPL, MT, down_slots(BPL)><<<grid, block, 0, stream>>>(r, list, list_count, H, \
+                                                                        I, tiles, w2_q, w2_s, lpr, h, y)
   switch (sp.dn.bpl) {
     case 1:
       if (sp.mt_dn == 2) MOE_DN(1, 2); else MOE_DN(1, 1);

@@ -121,8 +121,8 @@ def test_launch_plan(lib):
 
     p = m.ffn_plan(8, 4096, 2048, 256, 8)
     assert p["launch_small"] == 1 and p["launch_large"] == 0 and p["n_launches"] == 3
-    # persistent grid: two workgroups per CU (256 CUs when no device can be queried)
-    assert p["small_gateup_grid"] == 512 and p["small_down_grid"] == 512
+    # persistent grid: one workgroup per CU per wave/SIMD (256 CUs when no device can be queried)
+    assert p["small_gateup_grid"] % 256 == 0 and p["small_down_grid"] % 256 == 0
     assert m.ffn_plan(1, 2048, 768, 128, 8)["small_gateup_grid"] <= 8 * 768
     p = m.ffn_plan(8, 4096, 2048, 256, 8, m.UNFUSED_GATE_UP)
     assert p["n_launches"] == 4
