@@ -50,7 +50,12 @@ __device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// silu(g) * u = g * u / (1 + exp(-g)), with the hardware exp2 and reciprocal (each about 1 ulp);
+// exp(-g) overflowing to +inf for very negative g gives the correct limit -0.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 __device__ __forceinline__ float clampf(float v, float c) { return fminf(fmaxf(v, -c), c); }
 

@@ -193,6 +193,20 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
   const uint32_t qrow = (uint32_t)(H >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)2 * I * qrow, sexp = (size_t)2 * I * srow;
 
+  // Per-lane parts of the block addresses, fixed for the whole kernel: the item's row tile and the
+  // expert only move the (scalar) base. Rows past I (the last tile of an expert) are clamped.
+  const bool k_exact = (NB % lpr) == 0;
+  uint32_t qoff[S][BPL], soff[S][BPL];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+      const uint32_t rr = (uint32_t)((wave * S + s) * rpw + sub);
+      const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
+      qoff[s][b] = rr * qrow + kb * 16;
+      soff[s][b] = rr * srow + kb;
+    }
+
   int slot_c = -1, e = -1, M = 0, row0 = 0, x_m0 = -1;
   uint4 xb[MT][BPL][4];
 
@@ -206,28 +220,51 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
       row0 = uniform(r.offsets[e]);
       x_m0 = -1;
     }
-    const uint8_t* qe = w13_q + (size_t)e * qexp;
-    const uint8_t* se = w13_s + (size_t)e * sexp;
+    const int n0 = tile * tile_rows;
+    const bool full = n0 + tile_rows <= I;
+    // gate rows of the tile start at row n0, up rows at row I + n0
+    const uint8_t* qg = w13_q + (size_t)e * qexp + (size_t)n0 * qrow;
+    const uint8_t* sg = w13_s + (size_t)e * sexp + (size_t)n0 * srow;
+    const uint8_t* qu = qg + (size_t)I * qrow;
+    const uint8_t* su = sg + (size_t)I * srow;
 
-    // all loads of the item first (unconditional, clamped in-bounds; lanes past a row end or the
-    // expert's last row get a zero scale at use)
-    uint4 w[S][2][BPL];
-    uint32_t sc[S][2][BPL];
+    // all loads of the item first; a partial last tile clamps its rows (offsets only, the loads
+    // themselves stay unconditional) and zeroes their scales at use
+    uint32_t qo[S][BPL], so[S][BPL];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int nc = min(tile * tile_rows + (wave * S + s) * rpw + sub, I - 1);
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int gu = 0; gu < 2; ++gu) {
-        if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
-        const uint32_t row = (uint32_t)(gu ? I + nc : nc);
+      for (int b = 0; b < BPL; ++b) {
+        qo[s][b] = qoff[s][b];
+        so[s][b] = soff[s][b];
+      }
+    if (!full) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const uint32_t rr = (uint32_t)min((wave * S + s) * rpw + sub, I - 1 - n0);
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
           const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
-          w[s][gu][b] = ld16(qe, row * qrow + kb * 16);
-          sc[s][gu][b] = ld8(se, row * srow + kb);
+          qo[s][b] = rr * qrow + kb * 16;
+          so[s][b] = rr * srow + kb;
         }
       }
     }
+    uint4 w[S][2][BPL];
+    uint32_t sc[S][2][BPL];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int b = 0; b < BPL; ++b) {
+        if (kGate) {
+          w[s][0][b] = ld16(qg, qo[s][b]);
+          sc[s][0][b] = ld8(sg, so[s][b]);
+        }
+        if (kUp) {
+          w[s][1][b] = ld16(qu, qo[s][b]);
+          sc[s][1][b] = ld8(su, so[s][b]);
+        }
+      }
 
     for (int m0 = 0; m0 < M; m0 += MT) {
       const int mc = min(MT, M - m0);
@@ -260,8 +297,8 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
           if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
-            const bool ok = n < I && q + lpr * b < NB;
-            const float scale = ok ? e8m0_to_float(sc[s][gu][b]) : 0.0f;
+            float scale = e8m0_to_float(sc[s][gu][b]);
+            if (!(full && k_exact) && !(n < I && q + lpr * b < NB)) scale = 0.0f;
             if (MT == 1 || mc == MT) {
               uint4 xs[MT][4];
 #pragma unroll
@@ -331,6 +368,7 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
   const uint32_t qrow = (uint32_t)(I >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)H * qrow, sexp = (size_t)H * srow;
 
+  const bool k_exact = (NB % lpr) == 0;
   int slot_c = -1, e = -1, M = 0, row0 = 0, h_m0 = -1;
   float4 hb[MT][BPL][8];
 
@@ -344,19 +382,23 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
       row0 = uniform(r.offsets[e]);
       h_m0 = -1;
     }
-    const uint8_t* qe = w2_q + (size_t)e * qexp;
-    const uint8_t* se = w2_s + (size_t)e * sexp;
+    const int n0 = tile * tile_rows;
+    const bool full = n0 + tile_rows <= H;
+    const uint8_t* qe = w2_q + (size_t)e * qexp + (size_t)n0 * qrow;
+    const uint8_t* se = w2_s + (size_t)e * sexp + (size_t)n0 * srow;
 
+    // offsets are rebuilt per item here (registers are tight); rows of a partial last tile clamp
     uint4 w[S][BPL];
     uint32_t sc[S][BPL];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const uint32_t row = (uint32_t)min(tile * tile_rows + (wave * S + s) * rpw + sub, H - 1);
+      const int rr0 = (wave * S + s) * rpw + sub;
+      const uint32_t rr = (uint32_t)(full ? rr0 : min(rr0, H - 1 - n0));
 #pragma unroll
       for (int b = 0; b < BPL; ++b) {
         const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
-        w[s][b] = ld16(qe, row * qrow + kb * 16);
-        sc[s][b] = ld8(se, row * srow + kb);
+        w[s][b] = ld16(qe, rr * qrow + kb * 16);
+        sc[s][b] = ld8(se, rr * srow + kb);
       }
     }
 
@@ -387,8 +429,8 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
         const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
-          const bool ok = n < H && q + lpr * b < NB;
-          const float scale = ok ? e8m0_to_float(sc[s][b]) : 0.0f;
+          float scale = e8m0_to_float(sc[s][b]);
+          if (!(full && k_exact) && !(n < H && q + lpr * b < NB)) scale = 0.0f;
           if (MT == 1 || mc == MT) {
             float4 hs[MT][8];
 #pragma unroll
