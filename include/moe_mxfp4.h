@@ -196,8 +196,10 @@ int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_pla
 
 /*
  * Launch-table threshold (host only, process-wide): experts with at most `small_m_max` rows run on
- * the weight-streaming kernels, the rest on the MFMA kernels. Returns the previous value, or
- * MOE_ERR_SHAPE for a negative value. Not synchronised with calls in flight on other host threads.
+ * the weight-streaming kernels, the rest on the MFMA kernels. By default (-1) the threshold follows
+ * the token count: 8 for T <= 8 (every expert streams), 2 above. Returns the previous setting (-1
+ * for the default table), or MOE_ERR_SHAPE for a value below -1. Not synchronised with calls in
+ * flight on other host threads.
  */
 int moe_set_small_m_max(int small_m_max);
 

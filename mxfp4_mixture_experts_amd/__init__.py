@@ -118,8 +118,10 @@ def ffn_plan(T: int, H: int, I: int, E: int, k: int, flags: int = 0) -> dict:
 
 
 def set_small_m_max(v: int) -> int:
+    """Override the launch-table threshold (-1 restores the token-count table); returns the
+    previous setting."""
     prev = load_library().moe_set_small_m_max(int(v))
-    if prev < 0:
+    if prev < -1:
         _check(prev, "moe_set_small_m_max")
     return prev
 

@@ -12,9 +12,15 @@
 
 namespace {
 
-// Experts with at most this many rows run on the weight-streaming kernels; more rows go to the MFMA
-// kernels (the launch table keyed by token count, tokenspeed PR #661 "What the sweep found").
-std::atomic<int> g_small_m_max{8};
+// Launch table keyed by token count (tokenspeed PR #661, "What the sweep found"): experts with at
+// most small_m_max rows run on the weight-streaming kernels, the others on the MFMA kernels. With
+// T <= 8 every expert stays on the streaming kernels (no schedule or MFMA launches at decode); above
+// that, experts with more than 2 rows go to the MFMA kernels (the streaming kernels hold two
+// tokens' activations in registers, and each further pair of tokens costs another decode pass and a
+// reload). A value set through moe_set_small_m_max overrides the table; -1 restores it.
+std::atomic<int> g_small_m_max{-1};
+
+int table_small_m_max(int T) { return T <= 8 ? 8 : 2; }
 
 std::atomic<void*> g_stage_start[MOE_NUM_STAGES];
 std::atomic<void*> g_stage_stop[MOE_NUM_STAGES];
@@ -68,14 +74,15 @@ bool ffn_sizes_ok(int T, int H, int I, int E, int k) {
 
 constexpr int kKnownFlags = MOE_UNFUSED_GATE_UP | MOE_FORCE_SMALL_M | MOE_FORCE_LARGE_M;
 
-int effective_small_m_max(int flags) {
+int effective_small_m_max(int T, int flags) {
   if (flags & MOE_FORCE_SMALL_M) return INT_MAX;
   if (flags & MOE_FORCE_LARGE_M) return 0;
-  return g_small_m_max.load();
+  const int v = g_small_m_max.load();
+  return v >= 0 ? v : table_small_m_max(T);
 }
 
 void fill_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan) {
-  const int thr = effective_small_m_max(flags);
+  const int thr = effective_small_m_max(T, flags);
   const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k, num_cus());
   const moe::LargePlan lp = moe::plan_large(T, H, I, E, k, thr == INT_MAX ? INT_MAX - 1 : thr);
   plan->small_m_max = thr;
@@ -115,7 +122,7 @@ MOE_API const char* moe_status_string(int status) {
 }
 
 MOE_API int moe_set_small_m_max(int v) {
-  if (v < 0) return MOE_ERR_SHAPE;
+  if (v < -1) return MOE_ERR_SHAPE;
   return g_small_m_max.exchange(v);
 }
 

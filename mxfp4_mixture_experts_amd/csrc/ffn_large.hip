@@ -30,7 +30,12 @@ namespace {
 constexpr int kTileM = 64;      // rows per tile (4 MFMA row blocks of 16)
 constexpr int kKStep = 128;     // K elements per step (4 MX blocks)
 constexpr int kLdsRow = 272;    // bytes per LDS activation row (256 + 16 padding)
-constexpr int kColBlocks = 4;   // 16-column MFMA blocks per wave
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint4 ld16(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+__device__ __forceinline__ uint32_t ld8(const uint8_t* base, uint32_t off) { return base[off]; }
 
 // One wave: split the active experts into those for the weight-streaming kernels (at most
 // small_m_max rows) and the row tiles of the others, in ascending expert order. Unused tail entries
@@ -70,127 +75,139 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
   if (lane == 0) *n_small = ns;
 }
 
+// Staging of the activation tile: gate_up stages 64 rows x 128 bf16 of gathered x per K-step
+// (16 KB: 4 x 16 B per thread); down stages 64 rows x 128 fp32 of h (32 KB: 8 x 16 B per thread)
+// and writes them to LDS as a bf16 hi tile and a bf16 lo tile.
 template <bool GATEUP>
-__global__ __launch_bounds__(256) void large_kernel(Routed r, int H, int I,
-                                                    const uint8_t* __restrict__ wq_all,
-                                                    const uint8_t* __restrict__ ws_all,
-                                                    const int32_t* __restrict__ tile_e,
-                                                    const int32_t* __restrict__ tile_m0, float clamp,
-                                                    const float* __restrict__ h_in,
-                                                    float* __restrict__ h_out,
-                                                    float* __restrict__ y_out) {
-  // gate_up: one bf16 tile of gathered x rows; down: h split into a hi and a lo bf16 tile
-  constexpr int kATiles = GATEUP ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[kATiles * kTileM * kLdsRow];
+struct AStage {
+  static constexpr int kLoads = GATEUP ? 4 : 8;
+};
 
-  struct {
-    int e, m0, rows;
-  } tr;
-  tr.e = tile_e[blockIdx.y];
-  if (tr.e < 0) return;
-  tr.m0 = tile_m0[blockIdx.y];
-  tr.rows = min(kTileM, r.counts[tr.e] - tr.m0);
-  const int row0 = r.offsets[tr.e] + tr.m0;
-  const int msub_n = (tr.rows + 15) >> 4;
+template <bool GATEUP, int CB, int D>
+__global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
+                                                       const uint8_t* __restrict__ wq_all,
+                                                       const uint8_t* __restrict__ ws_all,
+                                                       const int32_t* __restrict__ tile_e,
+                                                       const int32_t* __restrict__ tile_m0,
+                                                       float clamp, const float* __restrict__ h_in,
+                                                       float* __restrict__ h_out,
+                                                       float* __restrict__ y_out) {
+  constexpr int kATiles = GATEUP ? 1 : 2;  // bf16 x, or bf16 hi + lo of h
+  constexpr int kTileBytes = kTileM * kLdsRow;
+  constexpr int NA = AStage<GATEUP>::kLoads;
+  // two LDS buffers (double-buffered across K-steps), each kATiles tiles
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kATiles * kTileBytes];
 
-  const int K = GATEUP ? H : I;      // reduction length
+  const int te = tile_e[blockIdx.y];
+  if (te < 0) return;
+  const int e = uniform(te);
+  const int m0 = uniform(tile_m0[blockIdx.y]);
+  const int rows = min(kTileM, uniform(r.counts[e]) - m0);
+  const int row0 = uniform(r.offsets[e]) + m0;
+  const int msub_n = (rows + 15) >> 4;
+
+  const int K = GATEUP ? H : I;     // reduction length
   const int NB = K >> 5;
-  const int NCOL = GATEUP ? I : H;   // output columns (gate columns for gate_up)
-  const size_t qrow = (size_t)(K >> 1), srow = (size_t)NB;
+  const uint32_t qrow = (uint32_t)(K >> 1), srow = (uint32_t)NB;
   const size_t nrows_w = GATEUP ? (size_t)2 * I : (size_t)H;
-  const uint8_t* qe = wq_all + (size_t)tr.e * nrows_w * qrow;
-  const uint8_t* se = ws_all + (size_t)tr.e * nrows_w * srow;
+  const uint8_t* qe = wq_all + (size_t)e * nrows_w * qrow;
+  const uint8_t* se = ws_all + (size_t)e * nrows_w * srow;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int j16 = lane & 15;   // MFMA column / row within a 16-block
-  const int g = lane >> 4;     // K group: block (4*step + g)
+  const int j16 = lane & 15;  // MFMA column (weight row) / A row within a 16-block
+  const int g = lane >> 4;    // K group: this lane's block within a step is 4*step + g
 
-  // output columns of this wave's four column blocks, and the weight row each lane loads for them
-  int col[kColBlocks];
-  int wrow[kColBlocks];
-  bool cval[kColBlocks];
+  // weight rows of this wave's CB column blocks (gate_up: CB/2 gate blocks, then the matching up
+  // blocks), the per-lane part of their addresses, and whether the column exists
+  int col[CB];
+  bool cval[CB];
+  uint32_t bq[CB], bs[CB];  // byte offset of the weight row's codes and scales
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
+    int wrow;
     if (GATEUP) {
-      const int gc = blockIdx.x * 128 + wave * 32 + (cb & 1) * 16 + j16;  // gate column
+      const int gc = blockIdx.x * (32 * CB) + wave * (8 * CB) + (cb % (CB / 2)) * 16 + j16;
       col[cb] = gc;
       cval[cb] = gc < I;
-      const int gcc = min(gc, I - 1);
-      wrow[cb] = (cb < 2) ? gcc : I + gcc;
+      wrow = (cb < CB / 2) ? min(gc, I - 1) : I + min(gc, I - 1);
     } else {
-      const int c = blockIdx.x * 256 + wave * 64 + cb * 16 + j16;
+      const int c = blockIdx.x * (64 * CB) + wave * (16 * CB) + cb * 16 + j16;
       col[cb] = c;
       cval[cb] = c < H;
-      wrow[cb] = min(c, H - 1);
+      wrow = min(c, H - 1);
     }
+    bq[cb] = (uint32_t)wrow * qrow;
+    bs[cb] = (uint32_t)wrow * srow;
   }
 
-  // activation rows this thread stages. gate_up: idx = tid + 256*i (i < 4) -> row idx/16, 8 bf16 of
-  // x at column chunk idx%16; down: idx = tid + 256*i (i < 8) -> row idx/32, 4 fp32 of h at idx%32.
-  constexpr int kStage = GATEUP ? 4 : 8;
-  const uint16_t* xrow[kStage];
-  const float* hrow[kStage];
-  bool aval[kStage];
+  // activation rows this thread stages (rows past the tile repeat its last row: their results
+  // are never written); each stages one 16-byte chunk of its row per K-step
+  const uint8_t* arow[NA];
 #pragma unroll
-  for (int i = 0; i < kStage; ++i) {
-    const int lr = GATEUP ? (tid + 256 * i) >> 4 : (tid + 256 * i) >> 5;
-    aval[i] = lr < tr.rows;
-    const int lrc = min(lr, tr.rows - 1);
+  for (int i = 0; i < NA; ++i) {
+    const int idx = tid + 256 * i;
+    const int lr = min(GATEUP ? idx >> 4 : idx >> 5, rows - 1);
     if (GATEUP) {
-      xrow[i] = r.x + (size_t)(r.sorted_pair[row0 + lrc] / r.k) * (size_t)H;
-      hrow[i] = nullptr;
+      const int t = r.sorted_pair[row0 + lr] / r.k;
+      arow[i] = reinterpret_cast<const uint8_t*>(r.x + (size_t)t * H);
     } else {
-      hrow[i] = h_in + (size_t)(row0 + lrc) * (size_t)I;
-      xrow[i] = nullptr;
+      arow[i] = reinterpret_cast<const uint8_t*>(h_in + (size_t)(row0 + lr) * I);
     }
   }
 
-  f32x4_t acc[4][kColBlocks];
+  const int nsteps = (NB + 3) >> 2;
+  // ring of D K-steps of loads in flight: weight blocks, scale bytes, activation slices
+  uint4 rb[D][CB];
+  uint32_t rs[D][CB];
+  uint4 ra[D][NA];
+
+  // issue every load of step `step` into ring slot `slot`. Block and element indices are clamped
+  // into the row (a partial last step re-reads in-bounds data that is masked at use); steps past
+  // the end load one shared location (no branch around the loads, negligible traffic).
+  auto issue = [&](int slot, int step) {
+    const bool live = step < nsteps;
+    const uint32_t blk = (uint32_t)min(step * 4 + g, NB - 1);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      rb[slot][cb] = ld16(qe, live ? bq[cb] + blk * 16 : 0u);
+      rs[slot][cb] = ld8(se, live ? bs[cb] + blk : 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int idx = tid + 256 * i;
+      const uint32_t el = GATEUP ? (uint32_t)min(step * 128 + (idx & 15) * 8, K - 8)
+                                 : (uint32_t)min(step * 128 + (idx & 31) * 4, K - 4);
+      ra[slot][i] = ld16(arow[i], live ? el * (GATEUP ? 2 : 4) : 0u);
+    }
+  };
+
+  f32x4_t acc[4][CB];
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) acc[ms][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) acc[ms][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = (NB + 3) >> 2;
-  uint4 wnext[kColBlocks];
-  uint32_t snext[kColBlocks];
-  auto load_b = [&](int step) {
-    const int kb_raw = step * 4 + g;
-    const int kb = min(kb_raw, NB - 1);  // unconditional in-bounds loads, zeroed below if unused
 #pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) {
-      wnext[cb] = *reinterpret_cast<const uint4*>(qe + (size_t)wrow[cb] * qrow + (size_t)kb * 16);
-      snext[cb] = (uint32_t)se[(size_t)wrow[cb] * srow + kb];
-    }
-#pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb)
-      if (!(cval[cb] && kb_raw < NB)) wnext[cb] = make_uint4(0, 0, 0, 0);
-  };
-  load_b(0);
+  for (int d = 0; d < D; ++d) issue(d, d);
 
-  for (int step = 0; step < nsteps; ++step) {
-    // stage the activation tile(s) of this step
-    __syncthreads();
-    if (GATEUP) {
+  auto step_body = [&](int slot, int step) {
+    uint8_t* lb = lds_a + (step & 1) * (kATiles * kTileBytes);
+    // the oldest ring slot: its activation slice goes to LDS (zero past K), visible after the barrier
+    const bool k_tail = (step * 4 + 4) > NB;
 #pragma unroll
-      for (int i = 0; i < kStage; ++i) {
-        const int idx = tid + 256 * i;
+    for (int i = 0; i < NA; ++i) {
+      const int idx = tid + 256 * i;
+      if (GATEUP) {
         const int lr = idx >> 4, c16 = idx & 15;
-        const int kelem = step * kKStep + c16 * 8;
-        uint4 v = *reinterpret_cast<const uint4*>(xrow[i] + min(kelem, K - 8));
-        if (!(aval[i] && kelem < K)) v = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(lds_a + lr * kLdsRow + c16 * 16) = v;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kStage; ++i) {
-        const int idx = tid + 256 * i;
+        uint4 v = ra[slot][i];
+        if (k_tail && step * 128 + c16 * 8 >= K) v = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(lb + lr * kLdsRow + c16 * 16) = v;
+      } else {
         const int lr = idx >> 5, c4 = idx & 31;
-        const int kelem = step * kKStep + c4 * 4;
-        float4 v = *reinterpret_cast<const float4*>(hrow[i] + min(kelem, K - 4));
-        if (!(aval[i] && kelem < K)) v = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 v = __builtin_bit_cast(float4, ra[slot][i]);
+        if (k_tail && step * 128 + c4 * 4 >= K) v = make_float4(0.f, 0.f, 0.f, 0.f);
         const uint16_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
         const uint16_t h2 = f32_to_bf16_rne(v.z), h3 = f32_to_bf16_rne(v.w);
         auto up = [](uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); };
@@ -199,68 +216,68 @@ __global__ __launch_bounds__(256) void large_kernel(Routed r, int H, int I,
         hi.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
         lo.x = pack_bf16x2(v.x - up(h0), v.y - up(h1));
         lo.y = pack_bf16x2(v.z - up(h2), v.w - up(h3));
-        *reinterpret_cast<uint2*>(lds_a + lr * kLdsRow + c4 * 8) = hi;
-        *reinterpret_cast<uint2*>(lds_a + kTileM * kLdsRow + lr * kLdsRow + c4 * 8) = lo;
+        *reinterpret_cast<uint2*>(lb + lr * kLdsRow + c4 * 8) = hi;
+        *reinterpret_cast<uint2*>(lb + kTileBytes + lr * kLdsRow + c4 * 8) = lo;
       }
     }
-    uint4 wcur[kColBlocks];
-    uint32_t scur[kColBlocks];
-#pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) {
-      wcur[cb] = wnext[cb];
-      scur[cb] = snext[cb];
-    }
-    if (step + 1 < nsteps) load_b(step + 1);
     __syncthreads();
+    // decode the weight blocks straight into MFMA B operands (operand s = elements 8s..8s+7)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t aop[kATiles][4];
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+        if (ms < msub_n)
+#pragma unroll
+          for (int at = 0; at < kATiles; ++at)
+            aop[at][ms] = *reinterpret_cast<const bf16x8_t*>(lb + at * kTileBytes +
+                                                              (ms * 16 + j16) * kLdsRow + g * 64 + s * 16);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const bool ok = cval[cb] && step * 4 + g < NB;
+        const float scale = ok ? e8m0_to_float(rs[slot][cb]) : 0.0f;
+        uint32_t wd = s == 0 ? rb[slot][cb].x : s == 1 ? rb[slot][cb].y : s == 2 ? rb[slot][cb].z : rb[slot][cb].w;
+        const bf16x2_t p0 = fp4x2_to_bf16x2<0>(wd, scale);
+        const bf16x2_t p1 = fp4x2_to_bf16x2<1>(wd, scale);
+        const bf16x2_t p2 = fp4x2_to_bf16x2<2>(wd, scale);
+        const bf16x2_t p3 = fp4x2_to_bf16x2<3>(wd, scale);
+        const bf16x8_t bop = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+          if (ms < msub_n)
+#pragma unroll
+            for (int at = 0; at < kATiles; ++at)
+              acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[at][ms], bop, acc[ms][cb], 0, 0, 0);
+      }
+    }
+    // the slot's registers are consumed: refill it with step + D
+    issue(slot, step + D);
+  };
 
-    // decode this step's weight blocks into MFMA B operands: operand s = elements 8s..8s+7
-    bf16x8_t bop[kColBlocks][4];
+  int step = 0;
+  for (; step + D <= nsteps; step += D) {
 #pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) {
-      const float scale = e8m0_to_float(scur[cb]);
-      const uint32_t wd[4] = {wcur[cb].x, wcur[cb].y, wcur[cb].z, wcur[cb].w};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x2_t p0 = fp4x2_to_bf16x2<0>(wd[s], scale);
-        const bf16x2_t p1 = fp4x2_to_bf16x2<1>(wd[s], scale);
-        const bf16x2_t p2 = fp4x2_to_bf16x2<2>(wd[s], scale);
-        const bf16x2_t p3 = fp4x2_to_bf16x2<3>(wd[s], scale);
-        bop[cb][s] = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      }
-    }
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms) {
-      if (ms >= msub_n) break;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int at = 0; at < kATiles; ++at) {
-          const bf16x8_t aop = *reinterpret_cast<const bf16x8_t*>(
-              lds_a + at * kTileM * kLdsRow + (ms * 16 + j16) * kLdsRow + g * 64 + s * 16);
-#pragma unroll
-          for (int cb = 0; cb < kColBlocks; ++cb)
-            acc[ms][cb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[cb][s], acc[ms][cb], 0, 0, 0);
-        }
-      }
-    }
+    for (int d = 0; d < D; ++d) step_body(d, step + d);
   }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (step + d < nsteps) step_body(d, step + d);
 
-  // epilogue: lane holds rows 4*g + i (i < 4) of each 16-row block, column j16 of each column block
+  // epilogue: lane holds rows 4*g + i (i < 4) of each 16-row block, column j16 of each block
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms) {
     if (ms >= msub_n) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int lr = ms * 16 + g * 4 + i;
-      if (lr >= tr.rows) continue;
+      if (lr >= rows) continue;
       const size_t orow = (size_t)(row0 + lr);
       if (GATEUP) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < CB / 2; ++cb) {
           if (!cval[cb]) continue;
           float gv = acc[ms][cb][i];
-          float uv = acc[ms][cb + 2][i];
+          float uv = acc[ms][cb + CB / 2][i];
           if (clamp > 0.0f) {
             gv = clampf(gv, clamp);
             uv = clampf(uv, clamp);
@@ -269,20 +286,23 @@ __global__ __launch_bounds__(256) void large_kernel(Routed r, int H, int I,
         }
       } else {
 #pragma unroll
-        for (int cb = 0; cb < kColBlocks; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
           if (cval[cb]) y_out[orow * H + col[cb]] = acc[ms][cb][i];
       }
     }
   }
 }
 
+constexpr int kGuCB = 4, kGuD = 3;  // gate_up: 4 column blocks per wave, 3 K-steps in flight
+constexpr int kDnCB = 4, kDnD = 2;  // down: its activation slices are twice as large
+
 }  // namespace
 
 LargePlan plan_large(int T, int H, int I, int E, int k, int small_m_max) {
   LargePlan lp;
   lp.tile_m = kTileM;
-  lp.gu_tile_n = 128;
-  lp.dn_tile_n = 256;
+  lp.gu_tile_n = 32 * kGuCB;
+  lp.dn_tile_n = 64 * kDnCB;
   lp.gu_grid_x = (I + lp.gu_tile_n - 1) / lp.gu_tile_n;
   lp.dn_grid_x = (H + lp.dn_tile_n - 1) / lp.dn_tile_n;
   lp.tile_slots = tile_slots_bound(T, E, k, small_m_max);
@@ -309,8 +329,8 @@ hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int 
                                const int32_t* tile_m0, float clamp, float* h, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
   const dim3 grid(lp.gu_grid_x, lp.tile_slots), block(256);
-  large_kernel<true><<<grid, block, 0, stream>>>(r, H, I, w13_q, w13_s, tile_e, tile_m0, clamp,
-                                                 nullptr, h, nullptr);
+  large_kernel<true, kGuCB, kGuD><<<grid, block, 0, stream>>>(r, H, I, w13_q, w13_s, tile_e, tile_m0,
+                                                              clamp, nullptr, h, nullptr);
   return hipGetLastError();
 }
 
@@ -319,8 +339,8 @@ hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I,
                              const float* h, float* y, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
   const dim3 grid(lp.dn_grid_x, lp.tile_slots), block(256);
-  large_kernel<false><<<grid, block, 0, stream>>>(r, H, I, w2_q, w2_s, tile_e, tile_m0, 0.0f, h,
-                                                  nullptr, y);
+  large_kernel<false, kDnCB, kDnD><<<grid, block, 0, stream>>>(r, H, I, w2_q, w2_s, tile_e, tile_m0,
+                                                               0.0f, h, nullptr, y);
   return hipGetLastError();
 }
 

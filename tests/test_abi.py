@@ -134,11 +134,15 @@ def test_launch_plan(lib):
     assert p["launch_large"] == 0
     p = m.ffn_plan(0, 4096, 2048, 256, 8)
     assert p["n_launches"] == 0
+    assert m.ffn_plan(8, 4096, 2048, 256, 8)["small_m_max"] == 8
+    assert m.ffn_plan(256, 4096, 2048, 256, 8)["small_m_max"] == 2
     prev = m.set_small_m_max(2)
     try:
+        assert prev == -1
         assert m.ffn_plan(8, 4096, 2048, 256, 8)["launch_large"] == 1
     finally:
         m.set_small_m_max(prev)
+    assert m.ffn_plan(8, 4096, 2048, 256, 8)["launch_large"] == 0
     with pytest.raises(m.MoeError):
         m.ffn_plan(8, 4096, 2048, 256, 8, 6)
 

@@ -83,7 +83,7 @@ def test_threshold_sweep_same_result(orc):
     cfg, inp = moe_synth.small_case(48, 512, 256, 8, 3, 21)
     ref = oracle_full(orc, inp, cfg)
     w = weights_to_device(inp)
-    prev = moe.set_small_m_max(8)
+    prev = moe.set_small_m_max(-1)
     try:
         for thr in (0, 1, 2, 4, 8, 16, 32, 1000):
             moe.set_small_m_max(thr)
