@@ -92,8 +92,8 @@ void fill_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan)
   const int gu_launches = (flags & MOE_UNFUSED_GATE_UP) ? 2 : 1;
   plan->small_gateup_grid = plan->launch_small ? sp.gu_grid : 0;
   plan->small_down_grid = plan->launch_small ? sp.dn_grid : 0;
-  plan->large_gateup_grid = plan->launch_large ? lp.gu_grid_x * lp.tile_slots : 0;
-  plan->large_down_grid = plan->launch_large ? lp.dn_grid_x * lp.tile_slots : 0;
+  plan->large_gateup_grid = plan->launch_large ? lp.gu_blocks : 0;
+  plan->large_down_grid = plan->launch_large ? lp.dn_blocks : 0;
   plan->combine_grid = T > 0 ? moe::combine_grid(T, H) : 0;
   // the MFMA kernels need the schedule kernel's tile list first
   plan->n_launches = (plan->launch_small ? gu_launches + 1 : 0) + (plan->launch_large ? 3 : 0) +

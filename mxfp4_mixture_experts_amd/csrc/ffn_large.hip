@@ -75,43 +75,34 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
   if (lane == 0) *n_small = ns;
 }
 
-// Staging of the activation tile: gate_up stages 64 rows x 128 bf16 of gathered x per K-step
-// (16 KB: 4 x 16 B per thread); down stages 64 rows x 128 fp32 of h (32 KB: 8 x 16 B per thread)
-// and writes them to LDS as a bf16 hi tile and a bf16 lo tile.
-template <bool GATEUP>
-struct AStage {
-  static constexpr int kLoads = GATEUP ? 4 : 8;
-};
+// Ring depth (K-steps of loads in flight) by tile height: the fewer MFMAs a step holds, the more
+// steps must be in flight to cover the memory latency with one workgroup per CU.
+constexpr int ring_depth(bool gateup, int msub) {
+  return gateup ? (msub == 1 ? 6 : msub == 2 ? 5 : msub == 3 ? 4 : 3)
+                : (msub == 1 ? 5 : msub == 2 ? 4 : msub == 3 ? 3 : 2);
+}
 
-template <bool GATEUP, int CB, int D>
-__global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
-                                                       const uint8_t* __restrict__ wq_all,
-                                                       const uint8_t* __restrict__ ws_all,
-                                                       const int32_t* __restrict__ tile_e,
-                                                       const int32_t* __restrict__ tile_m0,
-                                                       float clamp, const float* __restrict__ h_in,
-                                                       float* __restrict__ h_out,
-                                                       float* __restrict__ y_out) {
+// One (expert, row tile) x column block, with MSUB blocks of 16 rows fixed at compile time so the
+// step is straight-line code (no per-row-block branches between MFMAs).
+// Staging: gate_up stages MSUB*16 rows x 128 bf16 of gathered x per K-step (one 16-byte chunk per
+// thread and 16-row block); down stages MSUB*16 rows x 128 fp32 of h (two chunks per thread and
+// block) and writes them to LDS as a bf16 hi tile and a bf16 lo tile.
+template <bool GATEUP, int MSUB, int CB>
+__device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const uint8_t* __restrict__ qe,
+                                           const uint8_t* __restrict__ se, int e, int m0, int xblk,
+                                           float clamp, const float* __restrict__ h_in,
+                                           float* __restrict__ h_out, float* __restrict__ y_out,
+                                           uint8_t* lds_a) {
+  constexpr int D = ring_depth(GATEUP, MSUB);
   constexpr int kATiles = GATEUP ? 1 : 2;  // bf16 x, or bf16 hi + lo of h
   constexpr int kTileBytes = kTileM * kLdsRow;
-  constexpr int NA = AStage<GATEUP>::kLoads;
-  // two LDS buffers (double-buffered across K-steps), each kATiles tiles
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kATiles * kTileBytes];
+  constexpr int NA = GATEUP ? MSUB : 2 * MSUB;
 
-  const int te = tile_e[blockIdx.y];
-  if (te < 0) return;
-  const int e = uniform(te);
-  const int m0 = uniform(tile_m0[blockIdx.y]);
   const int rows = min(kTileM, uniform(r.counts[e]) - m0);
   const int row0 = uniform(r.offsets[e]) + m0;
-  const int msub_n = (rows + 15) >> 4;
-
-  const int K = GATEUP ? H : I;     // reduction length
+  const int K = GATEUP ? H : I;  // reduction length
   const int NB = K >> 5;
   const uint32_t qrow = (uint32_t)(K >> 1), srow = (uint32_t)NB;
-  const size_t nrows_w = GATEUP ? (size_t)2 * I : (size_t)H;
-  const uint8_t* qe = wq_all + (size_t)e * nrows_w * qrow;
-  const uint8_t* se = ws_all + (size_t)e * nrows_w * srow;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,12 +119,12 @@ __global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
   for (int cb = 0; cb < CB; ++cb) {
     int wrow;
     if (GATEUP) {
-      const int gc = blockIdx.x * (32 * CB) + wave * (8 * CB) + (cb % (CB / 2)) * 16 + j16;
+      const int gc = xblk * (32 * CB) + wave * (8 * CB) + (cb % (CB / 2)) * 16 + j16;
       col[cb] = gc;
       cval[cb] = gc < I;
       wrow = (cb < CB / 2) ? min(gc, I - 1) : I + min(gc, I - 1);
     } else {
-      const int c = blockIdx.x * (64 * CB) + wave * (16 * CB) + cb * 16 + j16;
+      const int c = xblk * (64 * CB) + wave * (16 * CB) + cb * 16 + j16;
       col[cb] = c;
       cval[cb] = c < H;
       wrow = min(c, H - 1);
@@ -143,12 +134,11 @@ __global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
   }
 
   // activation rows this thread stages (rows past the tile repeat its last row: their results
-  // are never written); each stages one 16-byte chunk of its row per K-step
+  // are never written)
   const uint8_t* arow[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int idx = tid + 256 * i;
-    const int lr = min(GATEUP ? idx >> 4 : idx >> 5, rows - 1);
+    const int lr = min(GATEUP ? (tid >> 4) + 16 * i : (tid >> 5) + 8 * i, rows - 1);
     if (GATEUP) {
       const int t = r.sorted_pair[row0 + lr] / r.k;
       arow[i] = reinterpret_cast<const uint8_t*>(r.x + (size_t)t * H);
@@ -176,16 +166,15 @@ __global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
     }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int idx = tid + 256 * i;
-      const uint32_t el = GATEUP ? (uint32_t)min(step * 128 + (idx & 15) * 8, K - 8)
-                                 : (uint32_t)min(step * 128 + (idx & 31) * 4, K - 4);
+      const uint32_t el = GATEUP ? (uint32_t)min(step * 128 + (tid & 15) * 8, K - 8)
+                                 : (uint32_t)min(step * 128 + (tid & 31) * 4, K - 4);
       ra[slot][i] = ld16(arow[i], live ? el * (GATEUP ? 2 : 4) : 0u);
     }
   };
 
-  f32x4_t acc[4][CB];
+  f32x4_t acc[MSUB][CB];
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms)
+  for (int ms = 0; ms < MSUB; ++ms)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[ms][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -198,14 +187,13 @@ __global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
     const bool k_tail = (step * 4 + 4) > NB;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int idx = tid + 256 * i;
       if (GATEUP) {
-        const int lr = idx >> 4, c16 = idx & 15;
+        const int lr = (tid >> 4) + 16 * i, c16 = tid & 15;
         uint4 v = ra[slot][i];
         if (k_tail && step * 128 + c16 * 8 >= K) v = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(lb + lr * kLdsRow + c16 * 16) = v;
       } else {
-        const int lr = idx >> 5, c4 = idx & 31;
+        const int lr = (tid >> 5) + 8 * i, c4 = tid & 31;
         float4 v = __builtin_bit_cast(float4, ra[slot][i]);
         if (k_tail && step * 128 + c4 * 4 >= K) v = make_float4(0.f, 0.f, 0.f, 0.f);
         const uint16_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
@@ -224,30 +212,28 @@ __global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
     // decode the weight blocks straight into MFMA B operands (operand s = elements 8s..8s+7)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8_t aop[kATiles][4];
+      bf16x8_t aop[kATiles][MSUB];
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
-        if (ms < msub_n)
+      for (int ms = 0; ms < MSUB; ++ms)
 #pragma unroll
-          for (int at = 0; at < kATiles; ++at)
-            aop[at][ms] = *reinterpret_cast<const bf16x8_t*>(lb + at * kTileBytes +
-                                                              (ms * 16 + j16) * kLdsRow + g * 64 + s * 16);
+        for (int at = 0; at < kATiles; ++at)
+          aop[at][ms] = *reinterpret_cast<const bf16x8_t*>(lb + at * kTileBytes +
+                                                            (ms * 16 + j16) * kLdsRow + g * 64 + s * 16);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const bool ok = cval[cb] && step * 4 + g < NB;
         const float scale = ok ? e8m0_to_float(rs[slot][cb]) : 0.0f;
-        uint32_t wd = s == 0 ? rb[slot][cb].x : s == 1 ? rb[slot][cb].y : s == 2 ? rb[slot][cb].z : rb[slot][cb].w;
+        const uint32_t wd = s == 0 ? rb[slot][cb].x : s == 1 ? rb[slot][cb].y : s == 2 ? rb[slot][cb].z : rb[slot][cb].w;
         const bf16x2_t p0 = fp4x2_to_bf16x2<0>(wd, scale);
         const bf16x2_t p1 = fp4x2_to_bf16x2<1>(wd, scale);
         const bf16x2_t p2 = fp4x2_to_bf16x2<2>(wd, scale);
         const bf16x2_t p3 = fp4x2_to_bf16x2<3>(wd, scale);
         const bf16x8_t bop = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-          if (ms < msub_n)
+        for (int ms = 0; ms < MSUB; ++ms)
 #pragma unroll
-            for (int at = 0; at < kATiles; ++at)
-              acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[at][ms], bop, acc[ms][cb], 0, 0, 0);
+          for (int at = 0; at < kATiles; ++at)
+            acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[at][ms], bop, acc[ms][cb], 0, 0, 0);
       }
     }
     // the slot's registers are consumed: refill it with step + D
@@ -265,8 +251,7 @@ __global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
 
   // epilogue: lane holds rows 4*g + i (i < 4) of each 16-row block, column j16 of each block
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-    if (ms >= msub_n) break;
+  for (int ms = 0; ms < MSUB; ++ms) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int lr = ms * 16 + g * 4 + i;
@@ -293,8 +278,49 @@ __global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I,
   }
 }
 
-constexpr int kGuCB = 4, kGuD = 3;  // gate_up: 4 column blocks per wave, 3 K-steps in flight
-constexpr int kDnCB = 4, kDnD = 2;  // down: its activation slices are twice as large
+// Grid: 8 * nx * ceil(tile_slots / 8) one-dimensional workgroups. Consecutive workgroups go to the
+// 8 XCDs in turn, so workgroup b runs on XCD b % 8; the mapping below gives XCD x the row tiles
+// y = x, x + 8, ... and dispatches all nx column blocks of one tile back to back on it, so a tile's
+// activation rows are fetched into that XCD's L2 once and reused by every column block.
+template <bool GATEUP, int CB>
+__global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I, int nx, int tile_slots,
+                                                       const uint8_t* __restrict__ wq_all,
+                                                       const uint8_t* __restrict__ ws_all,
+                                                       const int32_t* __restrict__ tile_e,
+                                                       const int32_t* __restrict__ tile_m0,
+                                                       float clamp, const float* __restrict__ h_in,
+                                                       float* __restrict__ h_out,
+                                                       float* __restrict__ y_out) {
+  constexpr int kATiles = GATEUP ? 1 : 2;
+  // two LDS buffers (double-buffered across K-steps), each kATiles tiles
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kATiles * kTileM * kLdsRow];
+
+  const int b = blockIdx.x;
+  const int j = b >> 3;
+  const int y = (b & 7) + 8 * (j / nx);
+  const int xblk = j % nx;
+  if (y >= tile_slots) return;
+  const int te = tile_e[y];
+  if (te < 0) return;
+  const int e = uniform(te);
+  const int m0 = uniform(tile_m0[y]);
+  const int rows = min(kTileM, uniform(r.counts[e]) - m0);
+  const int msub_n = (rows + 15) >> 4;
+
+  const int K = GATEUP ? H : I;
+  const size_t nrows_w = GATEUP ? (size_t)2 * I : (size_t)H;
+  const uint8_t* qe = wq_all + (size_t)e * nrows_w * (size_t)(K >> 1);
+  const uint8_t* se = ws_all + (size_t)e * nrows_w * (size_t)(K >> 5);
+  switch (msub_n) {
+    case 1: large_tile<GATEUP, 1, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_in, h_out, y_out, lds_a); break;
+    case 2: large_tile<GATEUP, 2, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_in, h_out, y_out, lds_a); break;
+    case 3: large_tile<GATEUP, 3, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_in, h_out, y_out, lds_a); break;
+    default: large_tile<GATEUP, 4, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_in, h_out, y_out, lds_a); break;
+  }
+}
+
+constexpr int kGuCB = 4;  // gate_up: 4 column blocks per wave (2 gate + 2 up)
+constexpr int kDnCB = 4;  // down: 4 column blocks per wave
 
 }  // namespace
 
@@ -306,6 +332,9 @@ LargePlan plan_large(int T, int H, int I, int E, int k, int small_m_max) {
   lp.gu_grid_x = (I + lp.gu_tile_n - 1) / lp.gu_tile_n;
   lp.dn_grid_x = (H + lp.dn_tile_n - 1) / lp.dn_tile_n;
   lp.tile_slots = tile_slots_bound(T, E, k, small_m_max);
+  const int groups = (lp.tile_slots + 7) / 8;
+  lp.gu_blocks = 8 * lp.gu_grid_x * groups;
+  lp.dn_blocks = 8 * lp.dn_grid_x * groups;
   return lp;
 }
 
@@ -328,9 +357,9 @@ hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int 
                                const uint8_t* w13_q, const uint8_t* w13_s, const int32_t* tile_e,
                                const int32_t* tile_m0, float clamp, float* h, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
-  const dim3 grid(lp.gu_grid_x, lp.tile_slots), block(256);
-  large_kernel<true, kGuCB, kGuD><<<grid, block, 0, stream>>>(r, H, I, w13_q, w13_s, tile_e, tile_m0,
-                                                              clamp, nullptr, h, nullptr);
+  large_kernel<true, kGuCB><<<lp.gu_blocks, 256, 0, stream>>>(r, H, I, lp.gu_grid_x, lp.tile_slots, w13_q,
+                                                               w13_s, tile_e, tile_m0, clamp, nullptr, h,
+                                                               nullptr);
   return hipGetLastError();
 }
 
@@ -338,9 +367,9 @@ hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I,
                              const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
                              const float* h, float* y, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
-  const dim3 grid(lp.dn_grid_x, lp.tile_slots), block(256);
-  large_kernel<false, kDnCB, kDnD><<<grid, block, 0, stream>>>(r, H, I, w2_q, w2_s, tile_e, tile_m0,
-                                                               0.0f, h, nullptr, y);
+  large_kernel<false, kDnCB><<<lp.dn_blocks, 256, 0, stream>>>(r, H, I, lp.dn_grid_x, lp.tile_slots, w2_q,
+                                                                w2_s, tile_e, tile_m0, 0.0f, h, nullptr,
+                                                                y);
   return hipGetLastError();
 }
 

@@ -66,8 +66,9 @@ struct LargePlan {
   int tile_m;        // rows per tile
   int gu_tile_n;     // gate columns per gate_up workgroup (the matching up columns come with them)
   int dn_tile_n;     // output columns per down workgroup
-  int gu_grid_x, dn_grid_x;
+  int gu_grid_x, dn_grid_x;  // column blocks per row tile
   int tile_slots;    // upper bound on the number of (expert, row-tile) pairs
+  int gu_blocks, dn_blocks;  // one-dimensional grids (XCD-interleaved tile order)
 };
 
 int tile_slots_bound(int T, int E, int k, int small_m_max);
