@@ -143,23 +143,32 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.copy_bytes} bytes done")
 
-    # eager: per-step HIP events around the gate_up stage, recorded on the stream it runs on
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in ev:  # create the underlying events
-        a.record(stream)
-        b.record(stream)
+    # eager: per-step HIP events around the gate_up, down and combine stages, recorded on the stream
+    # the kernels run on
+    stages = (moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
+          for _ in range(args.steps)]
+    for per_step in ev:  # create the underlying events
+        for a, b in per_step:
+            a.record(stream)
+            b.record(stream)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     with torch.cuda.stream(stream):
         for i in range(args.steps):
-            moe.set_stage_events(moe.STAGE_GATE_UP, ev[i][0], ev[i][1])
+            for st, (a, b) in zip(stages, ev[i]):
+                moe.set_stage_events(st, a, b)
             step(i)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t_start
-    moe.set_stage_events(moe.STAGE_GATE_UP, None, None)
-    gateup_ms = [a.elapsed_time(b) for a, b in ev]
-    gateup_mean_s = statistics.fmean(gateup_ms) / 1e3
-    log(f"eager: {eager_s / args.steps * 1e6:.1f} us/layer, gate_up stage {gateup_mean_s * 1e6:.1f} us")
+    for st in stages:
+        moe.set_stage_events(st, None, None)
+    stage_us = [[ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e3 for i in range(args.steps)] for j in range(len(stages))]
+    gateup_mean_s = statistics.fmean(stage_us[0]) / 1e6
+    down_mean_us = statistics.fmean(stage_us[1])
+    combine_mean_us = statistics.fmean(stage_us[2])
+    log(f"eager: {eager_s / args.steps * 1e6:.1f} us/layer, gate_up stage {gateup_mean_s * 1e6:.1f} us, "
+        f"down stage {down_mean_us:.1f} us, combine {combine_mean_us:.1f} us")
 
     # graph: one captured layer per replica, replayed in rotation
     graph_s = None

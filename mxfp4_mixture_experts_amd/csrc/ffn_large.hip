@@ -154,21 +154,20 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
   uint4 ra[D][NA];
 
   // issue every load of step `step` into ring slot `slot`. Block and element indices are clamped
-  // into the row (a partial last step re-reads in-bounds data that is masked at use); steps past
-  // the end load one shared location (no branch around the loads, negligible traffic).
+  // into the row: a partial last step re-reads in-bounds data that is masked at use, and the steps
+  // past the end re-read the last step (L2 hits spread over the channels; no branch around the loads).
   auto issue = [&](int slot, int step) {
-    const bool live = step < nsteps;
     const uint32_t blk = (uint32_t)min(step * 4 + g, NB - 1);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      rb[slot][cb] = ld16(qe, live ? bq[cb] + blk * 16 : 0u);
-      rs[slot][cb] = ld8(se, live ? bs[cb] + blk : 0u);
+      rb[slot][cb] = ld16(qe, bq[cb] + blk * 16);
+      rs[slot][cb] = ld8(se, bs[cb] + blk);
     }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const uint32_t el = GATEUP ? (uint32_t)min(step * 128 + (tid & 15) * 8, K - 8)
                                  : (uint32_t)min(step * 128 + (tid & 31) * 4, K - 4);
-      ra[slot][i] = ld16(arow[i], live ? el * (GATEUP ? 2 : 4) : 0u);
+      ra[slot][i] = ld16(arow[i], el * (GATEUP ? 2 : 4));
     }
   };
 

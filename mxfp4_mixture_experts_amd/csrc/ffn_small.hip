@@ -44,23 +44,29 @@ namespace {
 
 // Row slots per wave and item (gate_up slot = a gate row and its up row): about 8 block loads per
 // lane per item, so that 3-4 waves fit per SIMD.
-constexpr int gateup_slots(int bpl) { return bpl >= 4 ? 1 : 4 / bpl; }
-constexpr int down_slots(int bpl) { return bpl >= 8 ? 1 : 8 / bpl; }
+constexpr int gateup_slots(int bpl) { return bpl >= 2 ? 1 : 2; }
+constexpr int down_slots(int bpl) { return bpl >= 4 ? 1 : 4 / bpl; }
+// Items in flight per wave (ring depth).
+constexpr int gateup_ring(int bpl) { return 2; }
+constexpr int down_ring(int bpl) { return 2; }
 
 __device__ __forceinline__ int ilog2(int v) { return 31 - __clz(v); }
 
 // Waves per SIMD each variant's registers allow without spilling (4 waves x 128 VGPRs, 3 x 168,
 // 2 x 256, 1 x 512), read off the compiler's resource usage for these tile shapes.
 constexpr int gu_waves(int bpl, int mt, int) {
-  return bpl == 1 ? 4 : bpl == 2 ? (mt == 1 ? 4 : 3) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
+  return bpl <= 2 ? (mt == 1 ? 5 : 4) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
 }
 constexpr int dn_waves(int bpl, int mt, int) {
-  return bpl == 1 ? 3 : bpl == 2 ? (mt == 1 ? 2 : 2) : bpl == 3 ? 2 : 1;
+  return bpl == 1 ? (mt == 1 ? 4 : 3) : bpl == 2 ? (mt == 1 ? 3 : 2) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
 }
 
 // The packed block is passed through an empty asm so the compiler cannot hoist its decode out of
 // the token loop (that would keep up to 32 decoded registers per block alive and spill).
 __device__ __forceinline__ void opaque(uint4& w) {
+  asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+}
+__device__ __forceinline__ void opaque(float4& w) {
   asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
 }
 
@@ -166,15 +172,36 @@ struct Item {
 };
 
 // ---------------------------------------------------------------------------------------------
-// gate_up
+// Item pipeline shared by both kernels.
 //
-// Each wave streams items of S (gate row, up row) slot pairs: it issues all of the item's block loads
-// at once, then decodes and consumes them. There is no second register set: latency is hidden by the
-// other waves of the CU (3-4 per SIMD), which is why the register budget is kept small.
+// A wave keeps the weight loads of the next D items in flight in a ring of register sets: it
+// consumes ring entry d (item i) and then refills it with item i + D, so the loads of D items are
+// always outstanding while it decodes. Entries past the end of the workgroup's range re-load its
+// last item (L2 hits spread over the channels; no branch around the loads). The activations of the
+// current expert and token chunk stay in registers and are reloaded only when the item changes
+// expert (or an expert has more rows than one chunk holds); a reload waits for its loads at once,
+// so the decode paths never wait on anything but the ring entry they consume.
 
-template <int BPL, int MT, int S, int MODE>
+struct Prefetch {
+  int next;                  // next item to prefetch
+  int slot;                  // expert slot whose bases are cached
+  const uint8_t* q;          // that expert's code and scale bases
+  const uint8_t* s;
+};
+
+// Expert state of the item being consumed.
+struct Current {
+  int slot, e, M, row0, a_m0;
+};
+
+// ---------------------------------------------------------------------------------------------
+// gate_up: an item is S (gate row, up row) slot pairs per wave.
+
+template <int BPL, int MT, int S, int D, int MODE>
 __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel(
-    Routed r, const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
     int tiles, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s, int lpr,
     float clamp, float* __restrict__ h_out, float* __restrict__ g_ws) {
   constexpr bool kGate = MODE != kUpWithGate;
@@ -192,88 +219,72 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
   const int tile_rows = 4 * S * rpw;
   const uint32_t qrow = (uint32_t)(H >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)2 * I * qrow, sexp = (size_t)2 * I * srow;
-
-  // Per-lane parts of the block addresses, fixed for the whole kernel: the item's row tile and the
-  // expert only move the (scalar) base. Rows past I (the last tile of an expert) are clamped.
+  const uint32_t up_q = (uint32_t)I * qrow, up_s = (uint32_t)I * srow;  // up rows follow the gate rows
   const bool k_exact = (NB % lpr) == 0;
-  uint32_t qoff[S][BPL], soff[S][BPL];
-#pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int b = 0; b < BPL; ++b) {
-      const uint32_t rr = (uint32_t)((wave * S + s) * rpw + sub);
-      const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
-      qoff[s][b] = rr * qrow + kb * 16;
-      soff[s][b] = rr * srow + kb;
-    }
 
-  int slot_c = -1, e = -1, M = 0, row0 = 0, x_m0 = -1;
+  uint4 w[D][S][2][BPL];
+  uint32_t sc[D][S][2][BPL];
+  Prefetch pf{ir.begin, -1, w13_q, w13_s};
+
+  // loads of item pf.next into ring entry d; rows of a partial last tile are clamped (their
+  // results are never stored)
+  auto prefetch = [&](int d) {
+    const int it = min(pf.next, ir.end - 1);
+    const int slot = uniform(it / tiles);
+    const int tile = uniform(it - slot * tiles);
+    if (slot != pf.slot) {
+      pf.slot = slot;
+      const int e = uniform(list[slot]);
+      pf.q = w13_q + (size_t)e * qexp;
+      pf.s = w13_s + (size_t)e * sexp;
+    }
+    const uint8_t* bq = pf.q;
+    const uint8_t* bs = pf.s;
+    const int n0 = tile * tile_rows;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint32_t rr = (uint32_t)min(n0 + (wave * S + s) * rpw + sub, I - 1);
+#pragma unroll
+      for (int b = 0; b < BPL; ++b) {
+        const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
+        const uint32_t oq = rr * qrow + kb * 16;
+        const uint32_t os = rr * srow + kb;
+        if (kGate) {
+          w[d][s][0][b] = ld16(bq, oq);
+          sc[d][s][0][b] = ld8(bs, os);
+        }
+        if (kUp) {
+          w[d][s][1][b] = ld16(bq, oq + up_q);
+          sc[d][s][1][b] = ld8(bs, os + up_s);
+        }
+      }
+    }
+    ++pf.next;
+  };
+
+  Current cur{-1, -1, 0, 0, -1};
   uint4 xb[MT][BPL][4];
 
-  for (int item = ir.begin; item < ir.end; ++item) {
+  auto consume = [&](int d, int item) {
     const int slot = uniform(item / tiles);
     const int tile = uniform(item - slot * tiles);
-    if (slot != slot_c) {  // new expert
-      slot_c = slot;
-      e = uniform(list[slot]);
-      M = uniform(r.counts[e]);
-      row0 = uniform(r.offsets[e]);
-      x_m0 = -1;
+    if (slot != cur.slot) {  // new expert
+      cur.slot = slot;
+      cur.e = uniform(list[slot]);
+      cur.M = uniform(counts[cur.e]);
+      cur.row0 = uniform(offsets[cur.e]);
+      cur.a_m0 = -1;
     }
     const int n0 = tile * tile_rows;
     const bool full = n0 + tile_rows <= I;
-    // gate rows of the tile start at row n0, up rows at row I + n0
-    const uint8_t* qg = w13_q + (size_t)e * qexp + (size_t)n0 * qrow;
-    const uint8_t* sg = w13_s + (size_t)e * sexp + (size_t)n0 * srow;
-    const uint8_t* qu = qg + (size_t)I * qrow;
-    const uint8_t* su = sg + (size_t)I * srow;
-
-    // all loads of the item first; a partial last tile clamps its rows (offsets only, the loads
-    // themselves stay unconditional) and zeroes their scales at use
-    uint32_t qo[S][BPL], so[S][BPL];
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        qo[s][b] = qoff[s][b];
-        so[s][b] = soff[s][b];
-      }
-    if (!full) {
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const uint32_t rr = (uint32_t)min((wave * S + s) * rpw + sub, I - 1 - n0);
-#pragma unroll
-        for (int b = 0; b < BPL; ++b) {
-          const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
-          qo[s][b] = rr * qrow + kb * 16;
-          so[s][b] = rr * srow + kb;
-        }
-      }
-    }
-    uint4 w[S][2][BPL];
-    uint32_t sc[S][2][BPL];
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        if (kGate) {
-          w[s][0][b] = ld16(qg, qo[s][b]);
-          sc[s][0][b] = ld8(sg, so[s][b]);
-        }
-        if (kUp) {
-          w[s][1][b] = ld16(qu, qo[s][b]);
-          sc[s][1][b] = ld8(su, so[s][b]);
-        }
-      }
-
-    for (int m0 = 0; m0 < M; m0 += MT) {
-      const int mc = min(MT, M - m0);
-      if (m0 != x_m0) {  // activation slices of this token chunk (L2 hits)
-        x_m0 = m0;
+    for (int m0 = 0; m0 < cur.M; m0 += MT) {
+      const int mc = min(MT, cur.M - m0);
+      if (m0 != cur.a_m0) {  // activation slices of this token chunk (L2 hits)
+        cur.a_m0 = m0;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const int t = uniform(r.sorted_pair[row0 + m0 + min(m, mc - 1)]) / r.k;
-          const uint8_t* xbase = reinterpret_cast<const uint8_t*>(r.x + (size_t)t * H);
+          const int t = uniform(sorted_pair[cur.row0 + m0 + min(m, mc - 1)]) / k;
+          const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
             const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
@@ -281,6 +292,12 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
             for (int i = 0; i < 4; ++i) xb[m][b][i] = ld16(xbase, kb * 64 + i * 16);
           }
         }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int b = 0; b < BPL; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) opaque(xb[m][b][i]);
       }
       float acc[S][2][MT];
 #pragma unroll
@@ -291,13 +308,13 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
           for (int m = 0; m < MT; ++m) acc[s][gu][m] = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
+        const int n = n0 + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int gu = 0; gu < 2; ++gu) {
           if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
-            float scale = e8m0_to_float(sc[s][gu][b]);
+            float scale = e8m0_to_float(sc[d][s][gu][b]);
             if (!(full && k_exact) && !(n < I && q + lpr * b < NB)) scale = 0.0f;
             if (MT == 1 || mc == MT) {
               uint4 xs[MT][4];
@@ -305,14 +322,14 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
               for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) xs[m][i] = xb[m][b][i];
-              dot_block_bf16<MT>(w[s][gu][b], scale, xs, acc[s][gu]);
+              dot_block_bf16<MT>(w[d][s][gu][b], scale, xs, acc[s][gu]);
             } else {
               uint4 xs[1][4];
               float a1[1];
 #pragma unroll
               for (int i = 0; i < 4; ++i) xs[0][i] = xb[0][b][i];
               a1[0] = acc[s][gu][0];
-              dot_block_bf16<1>(w[s][gu][b], scale, xs, a1);
+              dot_block_bf16<1>(w[d][s][gu][b], scale, xs, a1);
               acc[s][gu][0] = a1[0];
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -321,14 +338,14 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
       }
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
+        const int n = n0 + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m >= mc) break;
           float g = kGate ? segment_sum(acc[s][0][m], lpr) : 0.0f;
           float u = kUp ? segment_sum(acc[s][1][m], lpr) : 0.0f;
           if (q == lpr - 1 && n < I) {
-            const size_t o = (size_t)(row0 + m0 + m) * I + n;
+            const size_t o = (size_t)(cur.row0 + m0 + m) * I + n;
             if (MODE == kGateOnly) {
               g_ws[o] = g;
             } else {
@@ -343,15 +360,26 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
         }
       }
     }
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d) prefetch(d);
+  for (int base = ir.begin; base < ir.end; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (base + d < ir.end) consume(d, base + d);
+      prefetch(d);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// down (same structure; rows of W2, activations h in fp32)
+// down: an item is S rows of W2 per wave; activations h in fp32.
 
-template <int BPL, int MT, int S>
+template <int BPL, int MT, int S, int D>
 __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
-    Routed r, const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
     int tiles, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s, int lpr,
     const float* __restrict__ h, float* __restrict__ y) {
   ItemRange ir;
@@ -367,49 +395,61 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
   const int tile_rows = 4 * S * rpw;
   const uint32_t qrow = (uint32_t)(I >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)H * qrow, sexp = (size_t)H * srow;
-
   const bool k_exact = (NB % lpr) == 0;
-  int slot_c = -1, e = -1, M = 0, row0 = 0, h_m0 = -1;
-  float4 hb[MT][BPL][8];
 
-  for (int item = ir.begin; item < ir.end; ++item) {
-    const int slot = uniform(item / tiles);
-    const int tile = uniform(item - slot * tiles);
-    if (slot != slot_c) {
-      slot_c = slot;
-      e = uniform(list[slot]);
-      M = uniform(r.counts[e]);
-      row0 = uniform(r.offsets[e]);
-      h_m0 = -1;
+  uint4 w[D][S][BPL];
+  uint32_t sc[D][S][BPL];
+  Prefetch pf{ir.begin, -1, w2_q, w2_s};
+
+  auto prefetch = [&](int d) {
+    const int it = min(pf.next, ir.end - 1);
+    const int slot = uniform(it / tiles);
+    const int tile = uniform(it - slot * tiles);
+    if (slot != pf.slot) {
+      pf.slot = slot;
+      const int e = uniform(list[slot]);
+      pf.q = w2_q + (size_t)e * qexp;
+      pf.s = w2_s + (size_t)e * sexp;
     }
+    const uint8_t* bq = pf.q;
+    const uint8_t* bs = pf.s;
     const int n0 = tile * tile_rows;
-    const bool full = n0 + tile_rows <= H;
-    const uint8_t* qe = w2_q + (size_t)e * qexp + (size_t)n0 * qrow;
-    const uint8_t* se = w2_s + (size_t)e * sexp + (size_t)n0 * srow;
-
-    // offsets are rebuilt per item here (registers are tight); rows of a partial last tile clamp
-    uint4 w[S][BPL];
-    uint32_t sc[S][BPL];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int rr0 = (wave * S + s) * rpw + sub;
-      const uint32_t rr = (uint32_t)(full ? rr0 : min(rr0, H - 1 - n0));
+      const uint32_t rr = (uint32_t)min(n0 + (wave * S + s) * rpw + sub, H - 1);
 #pragma unroll
       for (int b = 0; b < BPL; ++b) {
         const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
-        w[s][b] = ld16(qe, rr * qrow + kb * 16);
-        sc[s][b] = ld8(se, rr * srow + kb);
+        w[d][s][b] = ld16(bq, rr * qrow + kb * 16);
+        sc[d][s][b] = ld8(bs, rr * srow + kb);
       }
     }
+    ++pf.next;
+  };
 
-    for (int m0 = 0; m0 < M; m0 += MT) {
-      const int mc = min(MT, M - m0);
-      if (m0 != h_m0) {
-        h_m0 = m0;
+  Current cur{-1, -1, 0, 0, -1};
+  float4 hb[MT][BPL][8];
+
+  auto consume = [&](int d, int item) {
+    const int slot = uniform(item / tiles);
+    const int tile = uniform(item - slot * tiles);
+    if (slot != cur.slot) {
+      cur.slot = slot;
+      cur.e = uniform(list[slot]);
+      cur.M = uniform(counts[cur.e]);
+      cur.row0 = uniform(offsets[cur.e]);
+      cur.a_m0 = -1;
+    }
+    const int n0 = tile * tile_rows;
+    const bool full = n0 + tile_rows <= H;
+    for (int m0 = 0; m0 < cur.M; m0 += MT) {
+      const int mc = min(MT, cur.M - m0);
+      if (m0 != cur.a_m0) {
+        cur.a_m0 = m0;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const uint8_t* hbase =
-              reinterpret_cast<const uint8_t*>(h + (size_t)(row0 + m0 + min(m, mc - 1)) * I);
+              reinterpret_cast<const uint8_t*>(h + (size_t)(cur.row0 + m0 + min(m, mc - 1)) * I);
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
             const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
@@ -418,6 +458,12 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
               hb[m][b][i] = __builtin_bit_cast(float4, ld16(hbase, kb * 128 + i * 16));
           }
         }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int b = 0; b < BPL; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) opaque(hb[m][b][i]);
       }
       float acc[S][MT];
 #pragma unroll
@@ -426,10 +472,10 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
         for (int m = 0; m < MT; ++m) acc[s][m] = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
+        const int n = n0 + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
-          float scale = e8m0_to_float(sc[s][b]);
+          float scale = e8m0_to_float(sc[d][s][b]);
           if (!(full && k_exact) && !(n < H && q + lpr * b < NB)) scale = 0.0f;
           if (MT == 1 || mc == MT) {
             float4 hs[MT][8];
@@ -437,14 +483,14 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
             for (int m = 0; m < MT; ++m)
 #pragma unroll
               for (int i = 0; i < 8; ++i) hs[m][i] = hb[m][b][i];
-            dot_block_f32<MT>(w[s][b], scale, hs, acc[s]);
+            dot_block_f32<MT>(w[d][s][b], scale, hs, acc[s]);
           } else {
             float4 hs[1][8];
             float a1[1];
 #pragma unroll
             for (int i = 0; i < 8; ++i) hs[0][i] = hb[0][b][i];
             a1[0] = acc[s][0];
-            dot_block_f32<1>(w[s][b], scale, hs, a1);
+            dot_block_f32<1>(w[d][s][b], scale, hs, a1);
             acc[s][0] = a1[0];
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -452,14 +498,24 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
       }
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = tile * tile_rows + (wave * S + s) * rpw + sub;
+        const int n = n0 + (wave * S + s) * rpw + sub;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m >= mc) break;
           const float v = segment_sum(acc[s][m], lpr);
-          if (q == lpr - 1 && n < H) y[(size_t)(row0 + m0 + m) * H + n] = v;
+          if (q == lpr - 1 && n < H) y[(size_t)(cur.row0 + m0 + m) * H + n] = v;
         }
       }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d) prefetch(d);
+  for (int base = ir.begin; base < ir.end; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (base + d < ir.end) consume(d, base + d);
+      prefetch(d);
     }
   }
 }
@@ -472,8 +528,9 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
   const dim3 grid(sp.gu_grid), block(256);
   const int lpr = sp.gu.lpr, tiles = sp.gu_tiles;
 #define MOE_GU(BPL, MT)                                                                        \
-  small_gateup_kernel<BPL, MT, gateup_slots(BPL), MODE><<<grid, block, 0, stream>>>(            \
-      r, list, list_count, H, I, tiles, wq, ws, lpr, clamp, h, g_ws)
+  small_gateup_kernel<BPL, MT, gateup_slots(BPL), gateup_ring(BPL), MODE><<<grid, block, 0, stream>>>( \
+      r.x, r.counts, r.offsets, r.sorted_pair, r.k, list, list_count, H, I, tiles, wq, ws, lpr, clamp, h,  \
+      g_ws)
 #define MOE_GU_MT(BPL) \
   if (sp.mt_gu == 2)   \
     MOE_GU(BPL, 2);    \
@@ -550,8 +607,8 @@ hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t
   const dim3 grid(sp.dn_grid), block(256);
   const int lpr = sp.dn.lpr, tiles = sp.dn_tiles;
 #define MOE_DN(BPL, MT)                                                                       \
-  small_down_kernel<BPL, MT, down_slots(BPL)><<<grid, block, 0, stream>>>(r, list, list_count, H, \
-                                                                        I, tiles, w2_q, w2_s, lpr, h, y)
+  small_down_kernel<BPL, MT, down_slots(BPL), down_ring(BPL)><<<grid, block, 0, stream>>>(          \
+      r.counts, r.offsets, list, list_count, H, I, tiles, w2_q, w2_s, lpr, h, y)
   switch (sp.dn.bpl) {
     case 1:
       if (sp.mt_dn == 2) MOE_DN(1, 2); else MOE_DN(1, 1);
