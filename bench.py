@@ -143,60 +143,77 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.copy_bytes} bytes done")
 
-    # eager: per-step HIP events around the gate_up, down and combine stages, recorded on the stream
-    # the kernels run on
+    # eager: per-step HIP events on the stream the kernels run on: around the whole layer (recorded
+    # here) and around the gate_up, down and combine stages (recorded by the library)
     stages = (moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
-          for _ in range(args.steps)]
-    for per_step in ev:  # create the underlying events
-        for a, b in per_step:
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev_layer = [(mk(), mk()) for _ in range(args.steps)]
+    ev_stage = [[(mk(), mk()) for _ in stages] for _ in range(args.steps)]
+    for i in range(args.steps):  # create the underlying events
+        for a, b in [ev_layer[i], *ev_stage[i]]:
             a.record(stream)
             b.record(stream)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     with torch.cuda.stream(stream):
         for i in range(args.steps):
-            for st, (a, b) in zip(stages, ev[i]):
+            for st, (a, b) in zip(stages, ev_stage[i]):
                 moe.set_stage_events(st, a, b)
+            ev_layer[i][0].record(stream)
             step(i)
+            ev_layer[i][1].record(stream)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t_start
     for st in stages:
         moe.set_stage_events(st, None, None)
-    stage_us = [[ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e3 for i in range(args.steps)] for j in range(len(stages))]
+    el = lambda a, b: a.elapsed_time(b) * 1e3  # noqa: E731  (µs)
+    layer_us = [el(*ev_layer[i]) for i in range(args.steps)]
+    route_group_us = [el(ev_layer[i][0], ev_stage[i][0][0]) for i in range(args.steps)]
+    ffn_us = [el(ev_stage[i][0][0], ev_stage[i][2][1]) for i in range(args.steps)]
+    stage_us = [[el(*ev_stage[i][j]) for i in range(args.steps)] for j in range(len(stages))]
     gateup_mean_s = statistics.fmean(stage_us[0]) / 1e6
-    down_mean_us = statistics.fmean(stage_us[1])
-    combine_mean_us = statistics.fmean(stage_us[2])
-    log(f"eager: {eager_s / args.steps * 1e6:.1f} us/layer, gate_up stage {gateup_mean_s * 1e6:.1f} us, "
-        f"down stage {down_mean_us:.1f} us, combine {combine_mean_us:.1f} us")
+    med = statistics.median
+    log(f"eager: {eager_s / args.steps * 1e6:.1f} us/layer wall, device median {med(layer_us):.1f} us "
+        f"(route+group {med(route_group_us):.1f}, gate_up {med(stage_us[0]):.1f}, down {med(stage_us[1]):.1f}, "
+        f"combine {med(stage_us[2]):.1f})")
 
-    # graph: one captured layer per replica, replayed in rotation
+    # graph: L consecutive layers captured in one hipGraph (layer j on replica j mod R), replayed
+    # `reps` times with each replay timed; K = reps * L layers in all
+    reps = next(r for r in (5, 4, 2, 1) if args.steps % r == 0 and args.steps // r >= 2) if args.steps >= 2 else 1
+    L = args.steps // reps
     graph_s = None
+    graph_layer_us = []
     try:
-        graphs = []
-        for rr in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                layer.forward(x, logits, replicas[rr], stream=stream)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % R].replay()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for j in range(L):
+                layer.forward(x, logits, replicas[j % R], stream=stream)
+        g.replay()  # warm-up replay
         torch.cuda.synchronize()
+        ev_g = [(mk(), mk()) for _ in range(reps)]
         t_start = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % R].replay()
+        with torch.cuda.stream(stream):
+            for r_ in range(reps):
+                ev_g[r_][0].record(stream)
+                g.replay()
+                ev_g[r_][1].record(stream)
         torch.cuda.synchronize()
         graph_s = time.perf_counter() - t_start
-        log(f"graph: {graph_s / args.steps * 1e6:.1f} us/layer")
+        graph_layer_us = [el(*ev_g[r_]) / L for r_ in range(reps)]
+        log(f"graph ({L} layers per graph, {reps} replays): median {med(graph_layer_us):.1f} us/layer, "
+            f"range {min(graph_layer_us):.1f}-{max(graph_layer_us):.1f}")
+        del g
     except Exception as exc:  # capture unsupported: report eager
         log(f"graph capture failed: {exc!r}")
 
     use_graph = args.mode == "graph" and graph_s is not None
     total_s = graph_s if use_graph else eager_s
-    us_layer = total_s / args.steps * 1e6
+    us_layer = med(graph_layer_us) if use_graph else med(layer_us)
     gbps = weight_bytes / (us_layer * 1e-6) / 1e9
+    ffn_med = med(ffn_us)
 
-    large = int(T > 8 or args.flags & moe.FORCE_LARGE_M)
+    plan = moe.ffn_plan(T, H, I, E, k, args.flags)
+    large = plan["launch_large"]
     mfma_bound = cfg.name == "m1024"
     if mfma_bound:
         achieved = gateup_flops / gateup_mean_s / 1e12
@@ -207,7 +224,9 @@ def main():
         traffic = committed_traffic(cfg.name, kernel_source_hash())
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
-    roofline["kernel"] = "gate_up stage (" + ("MFMA" if large else "weight-streaming") + " kernel)"
+    roofline["kernel"] = "gate_up stage (" + (
+        "weight-streaming + MFMA kernels" if large and plan["launch_small"] else "MFMA kernel" if large
+        else "weight-streaming kernel") + ")"
     roofline["bytes_per_launch" if not mfma_bound else "flops_per_launch"] = (
         gateup_bytes if not mfma_bound else gateup_flops)
     roofline["avg_launch_us"] = round(gateup_mean_s * 1e6, 2)
@@ -238,7 +257,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total_s / args.steps * 1e3, 5),
+        "ms_per_step": round(us_layer / 1e3, 5),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -247,15 +266,24 @@ def main():
         "config": {"workload": f"{cfg.name}: T={T} H={H} I={I} E={E} top-{k} "
                                f"{'sigmoid' if cfg.score_fn else 'softmax'} renorm"
                                + (f", clamp {cfg.clamp}" if cfg.clamp else ""),
-                   "timing": "hipGraph replay" if use_graph else "eager",
+                   "timing": (f"hipGraph of {L} layers, median of {reps} replays" if use_graph
+                              else "eager, median step"),
                    "flags": args.flags, "weight_replicas": R, "parallelism": "none (1 GPU)"},
         "weight_stream_GBps": round(gbps, 1),
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "ffn_only_us": round(ffn_med, 2),
+        "weight_stream_GBps_ffn_only": round(weight_bytes / (ffn_med * 1e-6) / 1e9, 1),
+        "stage_us_eager_median": {"route+group": round(med(route_group_us), 2), "gate_up": round(med(stage_us[0]), 2),
+                                  "down": round(med(stage_us[1]), 2), "combine": round(med(stage_us[2]), 2)},
         "active_experts": n_active,
         "weight_bytes_per_layer": weight_bytes,
         "tflops": round(flops / (us_layer * 1e-6) / 1e12, 2),
-        "us_per_layer_eager": round(eager_s / args.steps * 1e6, 2),
-        "us_per_layer_graph": round(graph_s / args.steps * 1e6, 2) if graph_s else None,
+        "us_per_layer_eager": {"median": round(med(layer_us), 2),
+                               "p10": round(statistics.quantiles(layer_us, n=10)[0], 2) if len(layer_us) > 1 else None,
+                               "p90": round(statistics.quantiles(layer_us, n=10)[-1], 2) if len(layer_us) > 1 else None,
+                               "host_wall": round(eager_s / args.steps * 1e6, 2)},
+        "us_per_layer_graph": ({"median": round(med(graph_layer_us), 2), "min": round(min(graph_layer_us), 2),
+                                "max": round(max(graph_layer_us), 2)} if graph_layer_us else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_sha": kernel_source_hash(),

@@ -16,11 +16,11 @@
 //   - gate row i and up row I+i are handled by the same lanes, so SwiGLU (with the optional clamp) is
 //     applied in registers and only h is written (gate_up fusion as in vllm.cpp PR #52; clamp-SwiGLU
 //     epilogue as the routed clamp-SwiGLU row of the Post-Portfolio Device Attribution table).
-// Scheduling: the work is a list of items (expert, tile of rows). The grid is persistent (as many
-// workgroups per CU as the register budget allows waves per SIMD); each workgroup takes a contiguous
-// range of items. A wave issues all loads of an item before consuming them, and the other resident
-// waves hide its latency. A contiguous range stays mostly within one expert, so the activations are
-// reloaded only when the expert changes.
+// Scheduling: the work is a list of items (expert, tile of rows), each one wave's share. The grid
+// is persistent with one workgroup per CU, holding as many waves as the register budget allows;
+// each workgroup owns an equal contiguous range of items and its waves take them one at a time
+// from a counter in LDS. Each wave keeps the loads of its next items in flight while it decodes
+// the current one.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,8 +42,8 @@ RowSplit choose_row_split(int K) {
 
 namespace {
 
-// Row slots per wave and item (gate_up slot = a gate row and its up row): about 8 block loads per
-// lane per item, so that 3-4 waves fit per SIMD.
+// Row slots per item (one wave's share; gate_up slot = a gate row and its up row): with the ring of
+// two items, about 8 block loads per lane in flight, so that 3-4 waves fit per SIMD.
 constexpr int gateup_slots(int bpl) { return bpl >= 2 ? 1 : 2; }
 constexpr int down_slots(int bpl) { return bpl >= 4 ? 1 : 4 / bpl; }
 // Items in flight per wave (ring depth).
@@ -53,11 +53,12 @@ constexpr int down_ring(int bpl) { return 2; }
 __device__ __forceinline__ int ilog2(int v) { return 31 - __clz(v); }
 
 // Waves per SIMD each variant's registers allow without spilling (4 waves x 128 VGPRs, 3 x 168,
-// 2 x 256, 1 x 512), read off the compiler's resource usage for these tile shapes.
-constexpr int gu_waves(int bpl, int mt, int) {
-  return bpl <= 2 ? (mt == 1 ? 5 : 4) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
+// 2 x 256, 1 x 512), read off the compiler's resource usage for these tile shapes; the workgroup
+// (one per CU) has four times as many waves.
+constexpr int gu_waves(int bpl, int mt) {
+  return bpl == 1 ? 4 : bpl == 2 ? (mt == 1 ? 4 : 3) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
 }
-constexpr int dn_waves(int bpl, int mt, int) {
+constexpr int dn_waves(int bpl, int mt) {
   return bpl == 1 ? (mt == 1 ? 4 : 3) : bpl == 2 ? (mt == 1 ? 3 : 2) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
 }
 
@@ -147,15 +148,68 @@ struct ItemRange {
   int begin, end;  // items [begin, end) of this workgroup
 };
 
-__device__ __forceinline__ bool my_items(const int* count_ptr, int tiles, ItemRange& ir) {
-  const int total = *count_ptr * tiles;
-  const int per = (total + gridDim.x - 1) / gridDim.x;
-  ir.begin = blockIdx.x * per;
-  ir.end = min(total, ir.begin + per);
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Relative cost of one item of an expert with M rows when MT rows are decoded per pass: a fixed
+// part per pass (the weight stream and the decode) plus one part per row (the dot products).
+__device__ __forceinline__ int item_cost(int M, int MT) { return 3 * ((M + MT - 1) / MT) + M; }
+
+// The workgroup's items: contiguous ranges of the (expert, tile) list holding equal shares of the
+// total cost, so workgroups streaming experts with more rows get fewer items (`weighted`; without
+// it, when every expert has the same row count, equal item counts). Every wave computes
+// the range from the active list and the counts (uniform values, no LDS). A range boundary at cost
+// position p is the first item whose cost interval starts at or after p; every workgroup evaluates
+// it the same way, so the end of one range is the begin of the next.
+__device__ __forceinline__ bool my_items(const int32_t* list, const int* count_ptr,
+                                         const int32_t* counts, int tiles, int MT, int weighted,
+                                         ItemRange& ir) {
+  const int lane = threadIdx.x & 63;
+  const int n = uniform(*count_ptr);
+  if (n <= 0) return false;
+  const int G = gridDim.x, b = blockIdx.x;
+  if (!weighted) {  // every expert has the same row count: equal item counts, no count loads
+    ir.begin = (int)((long)b * n * tiles / G);
+    ir.end = (int)((long)(b + 1) * n * tiles / G);
+    return ir.begin < ir.end;
+  }
+  // total cost
+  long total = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    const int c = i < n ? item_cost(counts[list[i]], MT) : 0;
+    total += (long)uniform(__shfl(wave_inclusive_scan(c, lane), 63, 64));
+  }
+  total *= tiles;
+  const long p0 = total * b / G, p1 = total * (b + 1) / G;
+  // walk the slots with a running prefix; find the items at cost positions p0 and p1
+  int begin = n * tiles, end = n * tiles;
+  long run = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    const long c = i < n ? (long)item_cost(counts[list[i]], MT) : 0;
+    const int scan = wave_inclusive_scan((int)c, lane);
+    const long incl = run + (long)tiles * scan;  // prefix after slot i
+    const long excl = incl - (long)tiles * c;     // prefix before slot i
+    // item of slot i at position p: i*tiles + ceil((p - excl) / c), for excl <= p < incl
+    const bool has0 = i < n && p0 >= excl && p0 < incl;
+    const bool has1 = i < n && p1 >= excl && p1 < incl;
+    const uint64_t m0 = __ballot(has0), m1 = __ballot(has1);
+    if (m0) {
+      const int src = __ffsll((unsigned long long)m0) - 1;
+      const int v = i * tiles + (int)((p0 - excl + c - 1) / (c > 0 ? c : 1));
+      begin = min(begin, uniform(__shfl(v, src, 64)));
+    }
+    if (m1) {
+      const int src = __ffsll((unsigned long long)m1) - 1;
+      const int v = i * tiles + (int)((p1 - excl + c - 1) / (c > 0 ? c : 1));
+      end = min(end, uniform(__shfl(v, src, 64)));
+    }
+    run += (long)tiles * uniform(__shfl(scan, 63, 64));
+  }
+  ir.begin = begin;
+  ir.end = end;
   return ir.begin < ir.end;
 }
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // 16 bytes / 1 byte at a uniform base plus a 32-bit per-lane offset (lets the compiler use the
 // scalar-base addressing form, one VGPR per address)
@@ -164,26 +218,24 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* base, uint32_t off) {
 }
 __device__ __forceinline__ uint32_t ld8(const uint8_t* base, uint32_t off) { return base[off]; }
 
-// The item currently streamed: its expert and row tile, and the expert's weight bases.
-struct Item {
-  int slot, e, tile;
-  const uint8_t* q;
-  const uint8_t* s;
-};
-
 // ---------------------------------------------------------------------------------------------
 // Item pipeline shared by both kernels.
 //
-// A wave keeps the weight loads of the next D items in flight in a ring of register sets: it
-// consumes ring entry d (item i) and then refills it with item i + D, so the loads of D items are
-// always outstanding while it decodes. Entries past the end of the workgroup's range re-load its
-// last item (L2 hits spread over the channels; no branch around the loads). The activations of the
-// current expert and token chunk stay in registers and are reloaded only when the item changes
-// expert (or an expert has more rows than one chunk holds); a reload waits for its loads at once,
-// so the decode paths never wait on anything but the ring entry they consume.
+// One workgroup per CU; an item is one wave's share of work: S row slots of one expert. The
+// workgroup owns a static range of items (see my_items) and its waves take items
+// from that range one at a time through a counter in LDS, so every wave stays busy until the range
+// is drained (with several workgroups per CU the oldest-first issue order starves the youngest one,
+// which then finishes alone at a fraction of the bandwidth).
+//
+// A wave keeps the weight loads of its next D items in flight in a ring of register sets: it
+// consumes ring entry d and refills it with a newly taken item, so D items' loads are outstanding
+// while it decodes. Entries past the end of the range re-load the range's last item (L2 hits spread
+// over the channels; no branch around the loads) and are never consumed. The activations of the
+// current expert and token chunk stay in registers and are reloaded only when a wave's item
+// changes expert (or an expert has more rows than one chunk holds); a reload waits for its loads at
+// once, so the decode paths never wait on anything but the ring entry they consume.
 
 struct Prefetch {
-  int next;                  // next item to prefetch
   int slot;                  // expert slot whose bases are cached
   const uint8_t* q;          // that expert's code and scale bases
   const uint8_t* s;
@@ -194,29 +246,38 @@ struct Current {
   int slot, e, M, row0, a_m0;
 };
 
-// ---------------------------------------------------------------------------------------------
-// gate_up: an item is S (gate row, up row) slot pairs per wave.
+// Next item of the workgroup's range for this wave (uniform); >= ir.end once the range is drained.
+__device__ __forceinline__ int take_item(int* counter, const ItemRange& ir) {
+  int v = 0;
+  if ((threadIdx.x & 63) == 0) v = atomicAdd(counter, 1);
+  return ir.begin + uniform(__shfl(v, 0, 64));
+}
 
-template <int BPL, int MT, int S, int D, int MODE>
-__global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel(
+// ---------------------------------------------------------------------------------------------
+// gate_up: an item is S (gate row, up row) slot pairs.
+
+template <int BPL, int MT, int S, int D, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
-    int tiles, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s, int lpr,
-    float clamp, float* __restrict__ h_out, float* __restrict__ g_ws) {
+    int tiles, int weighted, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s,
+    int lpr, float clamp, float* __restrict__ h_out, float* __restrict__ g_ws) {
   constexpr bool kGate = MODE != kUpWithGate;
   constexpr bool kUp = MODE != kGateOnly;
+  __shared__ int counter;
   ItemRange ir;
-  if (!my_items(list_count, tiles, ir)) return;
+  if (!my_items(list, list_count, counts, tiles, MT, weighted, ir)) return;
+  if (threadIdx.x == 0) counter = 0;
+  __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int lg = ilog2(lpr);
   const int q = lane & (lpr - 1);
   const int sub = lane >> lg;
   const int rpw = 64 >> lg;
   const int NB = H >> 5;
-  const int tile_rows = 4 * S * rpw;
+  const int tile_rows = S * rpw;
   const uint32_t qrow = (uint32_t)(H >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)2 * I * qrow, sexp = (size_t)2 * I * srow;
   const uint32_t up_q = (uint32_t)I * qrow, up_s = (uint32_t)I * srow;  // up rows follow the gate rows
@@ -224,12 +285,14 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
 
   uint4 w[D][S][2][BPL];
   uint32_t sc[D][S][2][BPL];
-  Prefetch pf{ir.begin, -1, w13_q, w13_s};
+  int ring_item[D];
+  Prefetch pf{-1, w13_q, w13_s};
 
-  // loads of item pf.next into ring entry d; rows of a partial last tile are clamped (their
-  // results are never stored)
+  // take an item into ring entry d and issue its loads; rows of a partial last tile are clamped
+  // (their results are never stored)
   auto prefetch = [&](int d) {
-    const int it = min(pf.next, ir.end - 1);
+    ring_item[d] = take_item(&counter, ir);
+    const int it = min(ring_item[d], ir.end - 1);
     const int slot = uniform(it / tiles);
     const int tile = uniform(it - slot * tiles);
     if (slot != pf.slot) {
@@ -238,34 +301,32 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
       pf.q = w13_q + (size_t)e * qexp;
       pf.s = w13_s + (size_t)e * sexp;
     }
-    const uint8_t* bq = pf.q;
-    const uint8_t* bs = pf.s;
     const int n0 = tile * tile_rows;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const uint32_t rr = (uint32_t)min(n0 + (wave * S + s) * rpw + sub, I - 1);
+      const uint32_t rr = (uint32_t)min(n0 + s * rpw + sub, I - 1);
 #pragma unroll
       for (int b = 0; b < BPL; ++b) {
         const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
         const uint32_t oq = rr * qrow + kb * 16;
         const uint32_t os = rr * srow + kb;
         if (kGate) {
-          w[d][s][0][b] = ld16(bq, oq);
-          sc[d][s][0][b] = ld8(bs, os);
+          w[d][s][0][b] = ld16(pf.q, oq);
+          sc[d][s][0][b] = ld8(pf.s, os);
         }
         if (kUp) {
-          w[d][s][1][b] = ld16(bq, oq + up_q);
-          sc[d][s][1][b] = ld8(bs, os + up_s);
+          w[d][s][1][b] = ld16(pf.q, oq + up_q);
+          sc[d][s][1][b] = ld8(pf.s, os + up_s);
         }
       }
     }
-    ++pf.next;
   };
 
   Current cur{-1, -1, 0, 0, -1};
   uint4 xb[MT][BPL][4];
 
-  auto consume = [&](int d, int item) {
+  auto consume = [&](int d) {
+    const int item = ring_item[d];
     const int slot = uniform(item / tiles);
     const int tile = uniform(item - slot * tiles);
     if (slot != cur.slot) {  // new expert
@@ -308,7 +369,7 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
           for (int m = 0; m < MT; ++m) acc[s][gu][m] = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = n0 + (wave * S + s) * rpw + sub;
+        const int n = n0 + s * rpw + sub;
 #pragma unroll
         for (int gu = 0; gu < 2; ++gu) {
           if ((gu == 0 && !kGate) || (gu == 1 && !kUp)) continue;
@@ -338,7 +399,7 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
       }
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = n0 + (wave * S + s) * rpw + sub;
+        const int n = n0 + s * rpw + sub;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m >= mc) break;
@@ -364,45 +425,57 @@ __global__ __launch_bounds__(256, gu_waves(BPL, MT, S)) void small_gateup_kernel
 
 #pragma unroll
   for (int d = 0; d < D; ++d) prefetch(d);
-  for (int base = ir.begin; base < ir.end; base += D) {
+  // items are taken in increasing order, so the first entry past the range ends the wave's work
+  bool more = true;
+  while (more) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (base + d < ir.end) consume(d, base + d);
-      prefetch(d);
+      if (more) {
+        if (ring_item[d] >= ir.end) {
+          more = false;
+        } else {
+          consume(d);
+          prefetch(d);
+        }
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// down: an item is S rows of W2 per wave; activations h in fp32.
+// down: an item is S rows of W2; activations h in fp32.
 
-template <int BPL, int MT, int S, int D>
-__global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
+template <int BPL, int MT, int S, int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
-    int tiles, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s, int lpr,
-    const float* __restrict__ h, float* __restrict__ y) {
+    int tiles, int weighted, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s,
+    int lpr, const float* __restrict__ h, float* __restrict__ y) {
+  __shared__ int counter;
   ItemRange ir;
-  if (!my_items(list_count, tiles, ir)) return;
+  if (!my_items(list, list_count, counts, tiles, MT, weighted, ir)) return;
+  if (threadIdx.x == 0) counter = 0;
+  __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int lg = ilog2(lpr);
   const int q = lane & (lpr - 1);
   const int sub = lane >> lg;
   const int rpw = 64 >> lg;
   const int NB = I >> 5;
-  const int tile_rows = 4 * S * rpw;
+  const int tile_rows = S * rpw;
   const uint32_t qrow = (uint32_t)(I >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)H * qrow, sexp = (size_t)H * srow;
   const bool k_exact = (NB % lpr) == 0;
 
   uint4 w[D][S][BPL];
   uint32_t sc[D][S][BPL];
-  Prefetch pf{ir.begin, -1, w2_q, w2_s};
+  int ring_item[D];
+  Prefetch pf{-1, w2_q, w2_s};
 
   auto prefetch = [&](int d) {
-    const int it = min(pf.next, ir.end - 1);
+    ring_item[d] = take_item(&counter, ir);
+    const int it = min(ring_item[d], ir.end - 1);
     const int slot = uniform(it / tiles);
     const int tile = uniform(it - slot * tiles);
     if (slot != pf.slot) {
@@ -411,26 +484,24 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
       pf.q = w2_q + (size_t)e * qexp;
       pf.s = w2_s + (size_t)e * sexp;
     }
-    const uint8_t* bq = pf.q;
-    const uint8_t* bs = pf.s;
     const int n0 = tile * tile_rows;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const uint32_t rr = (uint32_t)min(n0 + (wave * S + s) * rpw + sub, H - 1);
+      const uint32_t rr = (uint32_t)min(n0 + s * rpw + sub, H - 1);
 #pragma unroll
       for (int b = 0; b < BPL; ++b) {
         const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
-        w[d][s][b] = ld16(bq, rr * qrow + kb * 16);
-        sc[d][s][b] = ld8(bs, rr * srow + kb);
+        w[d][s][b] = ld16(pf.q, rr * qrow + kb * 16);
+        sc[d][s][b] = ld8(pf.s, rr * srow + kb);
       }
     }
-    ++pf.next;
   };
 
   Current cur{-1, -1, 0, 0, -1};
   float4 hb[MT][BPL][8];
 
-  auto consume = [&](int d, int item) {
+  auto consume = [&](int d) {
+    const int item = ring_item[d];
     const int slot = uniform(item / tiles);
     const int tile = uniform(item - slot * tiles);
     if (slot != cur.slot) {
@@ -472,7 +543,7 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
         for (int m = 0; m < MT; ++m) acc[s][m] = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = n0 + (wave * S + s) * rpw + sub;
+        const int n = n0 + s * rpw + sub;
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
           float scale = e8m0_to_float(sc[d][s][b]);
@@ -498,7 +569,7 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
       }
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = n0 + (wave * S + s) * rpw + sub;
+        const int n = n0 + s * rpw + sub;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m >= mc) break;
@@ -511,11 +582,18 @@ __global__ __launch_bounds__(256, dn_waves(BPL, MT, S)) void small_down_kernel(
 
 #pragma unroll
   for (int d = 0; d < D; ++d) prefetch(d);
-  for (int base = ir.begin; base < ir.end; base += D) {
+  bool more = true;
+  while (more) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (base + d < ir.end) consume(d, base + d);
-      prefetch(d);
+      if (more) {
+        if (ring_item[d] >= ir.end) {
+          more = false;
+        } else {
+          consume(d);
+          prefetch(d);
+        }
+      }
     }
   }
 }
@@ -525,12 +603,13 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
                            const int32_t* list_count, int H, int I, const uint8_t* wq,
                            const uint8_t* ws, float clamp, float* h, float* g_ws,
                            hipStream_t stream) {
-  const dim3 grid(sp.gu_grid), block(256);
+  const dim3 grid(sp.gu_grid);
   const int lpr = sp.gu.lpr, tiles = sp.gu_tiles;
-#define MOE_GU(BPL, MT)                                                                        \
-  small_gateup_kernel<BPL, MT, gateup_slots(BPL), gateup_ring(BPL), MODE><<<grid, block, 0, stream>>>( \
-      r.x, r.counts, r.offsets, r.sorted_pair, r.k, list, list_count, H, I, tiles, wq, ws, lpr, clamp, h,  \
-      g_ws)
+#define MOE_GU(BPL, MT)                                                                          \
+  small_gateup_kernel<BPL, MT, gateup_slots(BPL), gateup_ring(BPL), 4 * gu_waves(BPL, MT), MODE> \
+      <<<grid, 256 * gu_waves(BPL, MT), 0, stream>>>(r.x, r.counts, r.offsets, r.sorted_pair, r.k,   \
+                                                     list, list_count, H, I, tiles, sp.weighted, wq, \
+                                                     ws, lpr, clamp, h, g_ws)
 #define MOE_GU_MT(BPL) \
   if (sp.mt_gu == 2)   \
     MOE_GU(BPL, 2);    \
@@ -552,9 +631,6 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
   return hipGetLastError();
 }
 
-int gu_waves_rt(int bpl, int mt) { return gu_waves(bpl, mt, gateup_slots(bpl)); }
-int dn_waves_rt(int bpl, int mt) { return dn_waves(bpl, mt, down_slots(bpl)); }
-
 }  // namespace
 
 SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
@@ -562,21 +638,23 @@ SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
   sp.gu = choose_row_split(H);
   sp.dn = choose_row_split(I);
   const int rpw_gu = 64 / sp.gu.lpr, rpw_dn = 64 / sp.dn.lpr;
-  sp.gu_tile = 4 * gateup_slots(sp.gu.bpl) * rpw_gu;
-  sp.dn_tile = 4 * down_slots(sp.dn.bpl) * rpw_dn;
+  sp.gu_tile = gateup_slots(sp.gu.bpl) * rpw_gu;
+  sp.dn_tile = down_slots(sp.dn.bpl) * rpw_dn;
   sp.gu_tiles = (I + sp.gu_tile - 1) / sp.gu_tile;
   sp.dn_tiles = (H + sp.dn_tile - 1) / sp.dn_tile;
   const long P = (long)T * k;
   sp.slots = (int)(P < E ? P : E);
   sp.mt_gu = (T >= 2 && sp.gu.bpl <= 2) ? 2 : 1;
   sp.mt_dn = (T >= 2 && sp.dn.bpl <= 2) ? 2 : 1;
-  // persistent grid: one workgroup (4 waves) per CU per wave/SIMD of occupancy, never more than
-  // there can be items
-  const long gu_cap = (long)gu_waves_rt(sp.gu.bpl, sp.mt_gu) * num_cus;
-  const long dn_cap = (long)dn_waves_rt(sp.dn.bpl, sp.mt_dn) * num_cus;
+  // with T <= 2 every expert has one or two rows and costs about the same per item
+  sp.weighted = T > 2;
+  // one workgroup per CU (its waves share the CU's range of items), never more than there can
+  // be items
   const long gu_items = (long)sp.slots * sp.gu_tiles, dn_items = (long)sp.slots * sp.dn_tiles;
-  sp.gu_grid = (int)(gu_items < gu_cap ? gu_items : gu_cap);
-  sp.dn_grid = (int)(dn_items < dn_cap ? dn_items : dn_cap);
+  sp.gu_grid = (int)(gu_items < num_cus ? gu_items : num_cus);
+  sp.dn_grid = (int)(dn_items < num_cus ? dn_items : num_cus);
+  sp.gu_block = 256 * gu_waves(sp.gu.bpl, sp.mt_gu);
+  sp.dn_block = 256 * dn_waves(sp.dn.bpl, sp.mt_dn);
   return sp;
 }
 
@@ -604,11 +682,12 @@ hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t
                              const int32_t* list_count, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const float* h, float* y, hipStream_t stream) {
   if (sp.dn_grid <= 0) return hipSuccess;
-  const dim3 grid(sp.dn_grid), block(256);
+  const dim3 grid(sp.dn_grid);
   const int lpr = sp.dn.lpr, tiles = sp.dn_tiles;
-#define MOE_DN(BPL, MT)                                                                       \
-  small_down_kernel<BPL, MT, down_slots(BPL), down_ring(BPL)><<<grid, block, 0, stream>>>(          \
-      r.counts, r.offsets, list, list_count, H, I, tiles, w2_q, w2_s, lpr, h, y)
+#define MOE_DN(BPL, MT)                                                                        \
+  small_down_kernel<BPL, MT, down_slots(BPL), down_ring(BPL), 4 * dn_waves(BPL, MT)>           \
+      <<<grid, 256 * dn_waves(BPL, MT), 0, stream>>>(r.counts, r.offsets, list, list_count, H, I, \
+                                                     tiles, sp.weighted, w2_q, w2_s, lpr, h, y)
   switch (sp.dn.bpl) {
     case 1:
       if (sp.mt_dn == 2) MOE_DN(1, 2); else MOE_DN(1, 1);

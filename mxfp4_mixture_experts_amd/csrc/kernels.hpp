@@ -41,11 +41,13 @@ enum SmallGateUpMode { kGateUpFused = 0, kGateOnly = 1, kUpWithGate = 2 };
 
 struct SmallPlan {
   RowSplit gu, dn;
-  int gu_tile, dn_tile;    // rows per item (gate rows for gate_up, output rows for down)
+  int gu_tile, dn_tile;    // rows per item, one wave's share (gate rows for gate_up, output rows for down)
   int gu_tiles, dn_tiles;  // items per expert
-  int gu_grid, dn_grid;    // persistent workgroups
+  int gu_grid, dn_grid;    // persistent workgroups (one per CU)
+  int gu_block, dn_block;  // threads per workgroup
   int slots;               // bound on the number of experts in the list (min(E, P))
   int mt_gu, mt_dn;        // tokens per pass
+  int weighted;            // workgroup ranges weighted by the experts' row counts
 };
 
 SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus);
