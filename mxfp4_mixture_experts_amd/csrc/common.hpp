@@ -9,6 +9,7 @@ namespace moe {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -43,7 +44,19 @@ __device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, sel);
 }
 
+// Two E2M1 codes (byte `sel` of `w`) as fp16 values, unscaled (E2M1 values are exact in fp16).
+template <int sel>
+__device__ __forceinline__ f16x2_t fp4x2_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, sel);
+}
+
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+__device__ __forceinline__ f16x2_t as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2_t, v); }
+
+// acc + a.lo*b.lo + a.hi*b.hi in fp32 (products of two fp16 are exact in fp32).
+__device__ __forceinline__ float dot2_f16(f16x2_t a, f16x2_t b, float acc) {
+  return __builtin_amdgcn_fdot2(a, b, acc, false);
+}
 
 // acc + a.lo*b.lo + a.hi*b.hi in fp32 (products of two bf16 are exact in fp32).
 __device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float acc) {

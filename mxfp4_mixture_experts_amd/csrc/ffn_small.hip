@@ -9,9 +9,13 @@
 //     load covers up to 1 KB of consecutive bytes of a row) plus the block's E8M0 scale byte;
 //   - a row of K elements is split over `lpr` lanes (in-wave split-K), each owning fixed blocks, so
 //     the lane's slice of the activations stays in registers for every row of an expert;
-//   - the codes are decoded in registers with the gfx950 scaled FP4 conversion (two codes and the
-//     scale per instruction) and consumed by bf16 dot2 (gate/up; bf16 products are exact in fp32) or
-//     fp32 FMA (down, whose activations h are fp32);
+//   - the codes are decoded in registers with the gfx950 FP4 conversion (two codes per instruction)
+//     and consumed by dot2 instructions with fp32 accumulation: bf16 dot2 against x (gate/up, codes
+//     decoded with their scale; bf16 products are exact in fp32), fp16 dot2 against h (down, codes
+//     decoded unscaled, the block's scale applied to the block's sum). h is kept in fp32 in memory;
+//     each lane turns its 32-value h block into fp16 with a power-of-two scale that puts the block's
+//     largest magnitude in [2^14, 2^15), so no value overflows and each keeps fp16's 11-bit
+//     precision (relative to the block maximum);
 //   - partial sums are reduced across the row's lanes with DPP adds, deterministically;
 //   - gate row i and up row I+i are handled by the same lanes, so SwiGLU (with the optional clamp) is
 //     applied in registers and only h is written (gate_up fusion as in vllm.cpp PR #52; clamp-SwiGLU
@@ -59,7 +63,7 @@ constexpr int gu_waves(int bpl, int mt) {
   return bpl == 1 ? 4 : bpl == 2 ? (mt == 1 ? 4 : 3) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
 }
 constexpr int dn_waves(int bpl, int mt) {
-  return bpl == 1 ? (mt == 1 ? 4 : 3) : bpl == 2 ? (mt == 1 ? 3 : 2) : bpl == 3 ? 3 : bpl <= 5 ? 2 : 1;
+  return bpl == 1 ? 4 : bpl == 2 ? (mt == 1 ? 4 : 2) : bpl == 3 ? 4 : bpl <= 6 ? 2 : 1;
 }
 
 // The packed block is passed through an empty asm so the compiler cannot hoist its decode out of
@@ -95,34 +99,57 @@ __device__ __forceinline__ void dot_block_bf16(uint4 w, float scale, const uint4
   }
 }
 
-// acc[m] += <decoded block, h block of token m> for MTC tokens (down: fp32 FMA).
+// acc[m] += bs[m] * <codes of the block, h block of token m> for MTC tokens (down). The codes are
+// decoded unscaled to fp16 and dotted with the token's fp16 h block by v_dot2_f32_f16 (fp32
+// accumulation); bs[m] carries the block's E8M0 scale times the inverse of the h block's
+// power-of-two scale.
 template <int MTC>
-__device__ __forceinline__ void dot_block_f32(uint4 w, float scale, const float4 (&hb)[MTC][8],
-                                              float (&acc)[MTC]) {
+__device__ __forceinline__ void dot_block_f16s(uint4 w, const float (&bs)[MTC],
+                                               const uint32_t (&hh)[MTC][16], float (&acc)[MTC]) {
   opaque(w);
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float part[MTC];
+#pragma unroll
+  for (int m = 0; m < MTC; ++m) part[m] = 0.0f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const f32x2_t p0 = fp4x2_to_f32x2<0>(wd[d], scale);
-    const f32x2_t p1 = fp4x2_to_f32x2<1>(wd[d], scale);
-    const f32x2_t p2 = fp4x2_to_f32x2<2>(wd[d], scale);
-    const f32x2_t p3 = fp4x2_to_f32x2<3>(wd[d], scale);
+    const f16x2_t p0 = fp4x2_to_f16x2<0>(wd[d]);
+    const f16x2_t p1 = fp4x2_to_f16x2<1>(wd[d]);
+    const f16x2_t p2 = fp4x2_to_f16x2<2>(wd[d]);
+    const f16x2_t p3 = fp4x2_to_f16x2<3>(wd[d]);
 #pragma unroll
     for (int m = 0; m < MTC; ++m) {
-      const float4 h0 = hb[m][2 * d];
-      const float4 h1 = hb[m][2 * d + 1];
-      float a = acc[m];
-      a = fmaf(p0[0], h0.x, a);
-      a = fmaf(p0[1], h0.y, a);
-      a = fmaf(p1[0], h0.z, a);
-      a = fmaf(p1[1], h0.w, a);
-      a = fmaf(p2[0], h1.x, a);
-      a = fmaf(p2[1], h1.y, a);
-      a = fmaf(p3[0], h1.z, a);
-      a = fmaf(p3[1], h1.w, a);
-      acc[m] = a;
+      float a = part[m];
+      a = dot2_f16(p0, as_f16x2(hh[m][4 * d + 0]), a);
+      a = dot2_f16(p1, as_f16x2(hh[m][4 * d + 1]), a);
+      a = dot2_f16(p2, as_f16x2(hh[m][4 * d + 2]), a);
+      a = dot2_f16(p3, as_f16x2(hh[m][4 * d + 3]), a);
+      part[m] = a;
     }
   }
+#pragma unroll
+  for (int m = 0; m < MTC; ++m) acc[m] = fmaf(part[m], bs[m], acc[m]);
+}
+
+// One lane's 32-value h block (fp32) as 16 packed fp16 pairs, scaled by a power of two that puts
+// its largest magnitude in [2^14, 2^15) (so nothing overflows fp16 and every value keeps fp16's
+// 11-bit precision relative to the block maximum); returns the inverse scale.
+__device__ __forceinline__ float h_block_to_f16(const float4 (&v)[8], uint32_t (&hh)[16]) {
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    mx = fmaxf(fmaxf(fmaxf(mx, fabsf(v[i].x)), fmaxf(fabsf(v[i].y), fabsf(v[i].z))), fabsf(v[i].w));
+  const int eb = (int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF);  // biased exponent
+  const int f = min(max(268 - eb, 1), 253);  // scale 2^(f - 127): mx * scale < 2^15
+  const float sc = __builtin_bit_cast(float, (uint32_t)f << 23);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f16x2_t a = f16x2_t{(_Float16)(v[i].x * sc), (_Float16)(v[i].y * sc)};
+    const f16x2_t b = f16x2_t{(_Float16)(v[i].z * sc), (_Float16)(v[i].w * sc)};
+    hh[2 * i] = __builtin_bit_cast(uint32_t, a);
+    hh[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
+  }
+  return __builtin_bit_cast(float, (uint32_t)(254 - f) << 23);
 }
 
 // v plus a DPP lane permutation of v (lanes outside row_mask add 0).
@@ -498,7 +525,8 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
   };
 
   Current cur{-1, -1, 0, 0, -1};
-  float4 hb[MT][BPL][8];
+  uint32_t hh[MT][BPL][16];  // h blocks as scaled fp16 pairs
+  float hinv[MT][BPL];       // their inverse power-of-two scales
 
   auto consume = [&](int d) {
     const int item = ring_item[d];
@@ -524,9 +552,10 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
             const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
+            float4 v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-              hb[m][b][i] = __builtin_bit_cast(float4, ld16(hbase, kb * 128 + i * 16));
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(float4, ld16(hbase, kb * 128 + i * 16));
+            hinv[m][b] = h_block_to_f16(v, hh[m][b]);
           }
         }
 #pragma unroll
@@ -534,7 +563,11 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
 #pragma unroll
           for (int b = 0; b < BPL; ++b)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) opaque(hb[m][b][i]);
+            for (int i = 0; i < 16; i += 4) {
+              uint4 t = make_uint4(hh[m][b][i], hh[m][b][i + 1], hh[m][b][i + 2], hh[m][b][i + 3]);
+              opaque(t);
+              hh[m][b][i] = t.x, hh[m][b][i + 1] = t.y, hh[m][b][i + 2] = t.z, hh[m][b][i + 3] = t.w;
+            }
       }
       float acc[S][MT];
 #pragma unroll
@@ -549,19 +582,23 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
           float scale = e8m0_to_float(sc[d][s][b]);
           if (!(full && k_exact) && !(n < H && q + lpr * b < NB)) scale = 0.0f;
           if (MT == 1 || mc == MT) {
-            float4 hs[MT][8];
+            uint32_t hs[MT][16];
+            float bs[MT];
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+            for (int m = 0; m < MT; ++m) {
+              bs[m] = scale * hinv[m][b];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) hs[m][i] = hb[m][b][i];
-            dot_block_f32<MT>(w[d][s][b], scale, hs, acc[s]);
+              for (int i = 0; i < 16; ++i) hs[m][i] = hh[m][b][i];
+            }
+            dot_block_f16s<MT>(w[d][s][b], bs, hs, acc[s]);
           } else {
-            float4 hs[1][8];
+            uint32_t hs[1][16];
+            float bs[1] = {scale * hinv[0][b]};
             float a1[1];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) hs[0][i] = hb[0][b][i];
+            for (int i = 0; i < 16; ++i) hs[0][i] = hh[0][b][i];
             a1[0] = acc[s][0];
-            dot_block_f32<1>(w[d][s][b], scale, hs, a1);
+            dot_block_f16s<1>(w[d][s][b], bs, hs, a1);
             acc[s][0] = a1[0];
           }
           __builtin_amdgcn_sched_barrier(0);
