@@ -9,6 +9,8 @@
  *
  *     moe_route_topk  ->  moe_group_tokens  ->  moe_mxfp4_ffn
  *
+ * (moe_route_group runs the first two as one call, in a single launch for small batches.)
+ *
  * Conventions shared by every call:
  *   - Pointers marked [dev] are device pointers (hipMalloc'd or equivalent) on the current device;
  *     [host] pointers are host memory. The caller owns and allocates every buffer; the library
@@ -122,6 +124,19 @@ int moe_route_topk(const float* logits, int T, int E, int k, int score_fn, int r
 int moe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                      int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
                      int32_t* n_active, void* stream);
+
+/*
+ * moe_route_group — moe_route_topk followed by moe_group_tokens, with the same arguments, limits and
+ * outputs (bitwise identical: the same device code runs). For small batches (T <= 64 and
+ * T*k <= 1024, the decode regime) both steps run in one single-workgroup launch that keeps the ids in
+ * LDS between them; larger batches enqueue the two separate kernels. topk_ids and topk_w are still
+ * written in full. The fusion follows the pages' accounting of launch and dispatch overhead at
+ * decode (vllm.cpp PR #52 node-trace diff; "MTP1 Post-Portfolio Eager-Cycle Profile").
+ */
+int moe_route_group(const float* logits, int T, int E, int k, int score_fn, int renorm,
+                    int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                    int32_t* sorted_pair, int32_t* pair_pos, int32_t* active, int32_t* n_active,
+                    void* stream);
 
 /*
  * moe_mxfp4_ffn_workspace_size — bytes of device workspace moe_mxfp4_ffn needs for these sizes and

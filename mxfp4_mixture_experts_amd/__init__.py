@@ -66,6 +66,8 @@ def load_library(path: str | None = None):
     lib.moe_route_topk.restype = i
     lib.moe_group_tokens.argtypes = [V, i, i, i, V, V, V, V, V, V, V]
     lib.moe_group_tokens.restype = i
+    lib.moe_route_group.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V]
+    lib.moe_route_group.restype = i
     lib.moe_mxfp4_ffn_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.moe_mxfp4_ffn_workspace_size.restype = ctypes.c_size_t
     lib.moe_mxfp4_ffn.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_float,
@@ -179,6 +181,24 @@ def group_tokens(ids: torch.Tensor, E: int, out: Grouping | None = None, stream=
     return g
 
 
+def route_group(logits: torch.Tensor, k: int, score_fn: int = SCORE_SOFTMAX, renorm: bool = True,
+                ids: torch.Tensor | None = None, weights: torch.Tensor | None = None,
+                out: Grouping | None = None, stream=None):
+    """route_topk then group_tokens in one call (one launch for small batches)."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    g = out if out is not None else Grouping.empty(T, k, E, logits.device)
+    _check(load_library().moe_route_group(_ptr(logits), T, E, k, score_fn, int(bool(renorm)), _ptr(ids),
+                                          _ptr(weights), _ptr(g.counts), _ptr(g.offsets),
+                                          _ptr(g.sorted_pair), _ptr(g.pair_pos), _ptr(g.active),
+                                          _ptr(g.n_active), _stream(stream)), "moe_route_group")
+    return ids, weights, g
+
+
 @dataclass
 class Mxfp4Weights:
     """Expert weights in the library's MXFP4 layout (device tensors, uint8)."""
@@ -236,8 +256,8 @@ def mxfp4_ffn(x: torch.Tensor, w: Mxfp4Weights, topk_w: torch.Tensor, grp: Group
 class MoELayer:
     """One routed MXFP4 MoE layer with every buffer preallocated for up to ``max_tokens`` tokens.
 
-    ``forward`` enqueues route -> group -> ffn on the current stream and allocates nothing, so it can
-    be captured into a HIP graph (torch.cuda.CUDAGraph).
+    ``forward`` enqueues route + group (one call) -> ffn on the current stream and allocates nothing,
+    so it can be captured into a HIP graph (torch.cuda.CUDAGraph).
     """
 
     def __init__(self, weights: Mxfp4Weights, k: int, max_tokens: int, score_fn: int = SCORE_SOFTMAX,
@@ -265,6 +285,5 @@ class MoELayer:
             raise MoeError(f"{T} tokens exceed the layer's capacity {self.T}")
         w = weights if weights is not None else self.w
         ids, tw = self.ids[:T], self.topk_w[:T]
-        route_topk(logits, self.k, self.score_fn, self.renorm, ids, tw, stream)
-        group_tokens(ids, w.E, self.grp, stream)
+        route_group(logits, self.k, self.score_fn, self.renorm, ids, tw, self.grp, stream)
         return mxfp4_ffn(x, w, tw, self.grp, self.clamp, self.flags, self.out[:T], self.workspace, stream)

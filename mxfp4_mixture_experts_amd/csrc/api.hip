@@ -161,6 +161,30 @@ MOE_API int moe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32
   return MOE_OK;
 }
 
+MOE_API int moe_route_group(const float* logits, int T, int E, int k, int score_fn, int renorm,
+                            int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
+                            int32_t* n_active, void* stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E ||
+      (long)T * k > MOE_MAX_PAIRS)
+    return MOE_ERR_SHAPE;
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_pair || !pair_pos)) return MOE_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  if (T > 0 && moe::route_group_fusable(T, k))
+    return moe::launch_route_group(logits, T, E, k, score_fn, renorm, topk_ids, topk_w, counts, offsets,
+                                   sorted_pair, pair_pos, active, n_active, s) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_LAUNCH;
+  if (T > 0 && moe::launch_route_topk(logits, T, E, k, score_fn, renorm, topk_ids, topk_w, s) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  if (moe::launch_group_tokens(topk_ids, T * k, E, counts, offsets, sorted_pair, pair_pos, active,
+                               n_active, s) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}
+
 MOE_API size_t moe_mxfp4_ffn_workspace_size(int T, int H, int I, int E, int k, int flags) {
   if (!ffn_sizes_ok(T, H, I, E, k) || (flags & ~kKnownFlags)) return 0;
   return ws_layout((long)T * k, H, I, E, k, flags).total;

@@ -1,22 +1,11 @@
-// Token-to-expert grouping: expert histogram, exclusive prefix scan and a stable permutation of the
-// P = T*k routed pairs by expert ("Direct M=2 route remap" row of the Post-Portfolio Device
-// Attribution table, "MTP1 Post-Portfolio Eager-Cycle Profile").
-//
-// One workgroup of up to 16 waves. Each wave owns a contiguous range of whole 64-pair chunks. Within
-// a chunk, lanes holding the same expert are found with ten ballots over the id bits; the lowest
-// such lane updates the wave's own per-expert counter in LDS, so nothing is atomic and the result is
-// deterministic. A per-expert scan over the waves (in wave order) plus a scan over the experts gives
-// each pair's row: offsets[e] + (pairs of e in earlier waves) + (earlier chunks of this wave) + (rank
-// among equal lanes of its chunk). Rows within an expert therefore follow ascending p.
+// Token-to-expert grouping kernel (the algorithm is in group_dev.hpp).
 #include "common.hpp"
+#include "group_dev.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
-
-constexpr int kGroupMaxWaves = 16;
-constexpr int kGroupMaxExperts = 512;
 
 __global__ __launch_bounds__(1024) void group_tokens_kernel(const int32_t* __restrict__ ids, int P,
                                                             int E, int32_t* __restrict__ counts,
@@ -25,87 +14,8 @@ __global__ __launch_bounds__(1024) void group_tokens_kernel(const int32_t* __res
                                                             int32_t* __restrict__ pair_pos,
                                                             int32_t* __restrict__ active,
                                                             int32_t* __restrict__ n_active) {
-  __shared__ int hist[kGroupMaxWaves * kGroupMaxExperts];  // per-wave counters, then running rows
-  __shared__ int total[kGroupMaxExperts];
-  __shared__ int base[kGroupMaxExperts];
-
-  const int nw = blockDim.x >> 6;
-  const int w = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-
-  for (int i = threadIdx.x; i < nw * E; i += blockDim.x) hist[i] = 0;
-  __syncthreads();
-
-  const int chunks = (P + 63) >> 6;
-  const int per_wave = (chunks + nw - 1) / nw;
-  const int c_begin = w * per_wave;
-  const int c_end = min(chunks, c_begin + per_wave);
-  int* my_hist = hist + w * E;
-
-  // 1. per-wave histogram
-  for (int c = c_begin; c < c_end; ++c) {
-    const int p = (c << 6) + lane;
-    const bool valid = p < P;
-    const int e = valid ? ids[p] : 0;
-    const uint64_t peers = match_key(e, valid);
-    if (valid && lane == __ffsll((unsigned long long)peers) - 1) my_hist[e] += __popcll(peers);
-  }
-  __syncthreads();
-
-  // 2. per expert: exclusive prefix over waves, and the expert's total
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int v = 0; v < nw; ++v) {
-      const int c = hist[v * E + e];
-      hist[v * E + e] = run;
-      run += c;
-    }
-    total[e] = run;
-  }
-  __syncthreads();
-
-  // 3. exclusive scan over experts, counts/offsets, compacted active list (wave 0)
-  if (w == 0) {
-    int carry = 0, acarry = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + lane;
-      const int c = e < E ? total[e] : 0;
-      const int incl = wave_inclusive_scan(c, lane);
-      if (e < E) {
-        base[e] = carry + incl - c;
-        counts[e] = c;
-        offsets[e] = carry + incl - c;
-      }
-      carry += __shfl(incl, 63, 64);
-      const bool act = e < E && c > 0;
-      const uint64_t am = __ballot(act);
-      if (act) active[acarry + __popcll(am & lanemask_lt(lane))] = e;
-      acarry += __popcll(am);
-    }
-    if (lane == 0) {
-      offsets[E] = carry;
-      *n_active = acarry;
-    }
-    for (int i = acarry + lane; i < E; i += 64) active[i] = -1;
-  }
-  __syncthreads();
-
-  // 4. stable placement
-  for (int c = c_begin; c < c_end; ++c) {
-    const int p = (c << 6) + lane;
-    const bool valid = p < P;
-    const int e = valid ? ids[p] : 0;
-    const uint64_t peers = match_key(e, valid);
-    if (valid) {
-      const int pos = base[e] + my_hist[e] + __popcll(peers & lanemask_lt(lane));
-      sorted_pair[pos] = p;
-      pair_pos[p] = pos;
-    }
-    // every lane of this wave has read my_hist[e] above before the leader advances it
-    __builtin_amdgcn_wave_barrier();
-    if (valid && lane == __ffsll((unsigned long long)peers) - 1) my_hist[e] += __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
-  }
+  __shared__ group_dev::Shared sh;
+  group_dev::group_pairs(ids, P, E, counts, offsets, sorted_pair, pair_pos, active, n_active, sh);
 }
 
 }  // namespace
@@ -114,7 +24,7 @@ hipError_t launch_group_tokens(const int32_t* ids, int P, int E, int32_t* counts
                                int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
                                int32_t* n_active, hipStream_t stream) {
   const int chunks = (P + 63) / 64;
-  int waves = chunks < 1 ? 1 : (chunks > kGroupMaxWaves ? kGroupMaxWaves : chunks);
+  int waves = chunks < 1 ? 1 : (chunks > group_dev::kMaxWaves ? group_dev::kMaxWaves : chunks);
   group_tokens_kernel<<<1, waves * 64, 0, stream>>>(ids, P, E, counts, offsets, sorted_pair, pair_pos,
                                                     active, n_active);
   return hipGetLastError();

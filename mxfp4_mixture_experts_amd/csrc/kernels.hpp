@@ -14,6 +14,13 @@ hipError_t launch_group_tokens(const int32_t* ids, int P, int E, int32_t* counts
                                int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
                                int32_t* n_active, hipStream_t stream);
 
+// Router and grouping in one single-workgroup launch (small batches: route_group_fusable).
+bool route_group_fusable(int T, int k);
+hipError_t launch_route_group(const float* logits, int T, int E, int k, int score_fn, int renorm,
+                              int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
+                              int32_t* n_active, hipStream_t stream);
+
 // Grouping results and activations every FFN kernel reads.
 struct Routed {
   const uint16_t* x;         // bf16 [T, H]

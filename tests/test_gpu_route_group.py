@@ -1,4 +1,5 @@
-"""GPU parity of the router (moe_route_topk) and the grouping (moe_group_tokens) against the oracle:
+"""GPU parity of the router (moe_route_topk), the grouping (moe_group_tokens) and their fused call
+(moe_route_group) against the oracle:
 ids, counts, offsets, permutation and active list bit-exact; routing weights within the fp32 bound."""
 import numpy as np
 import pytest
@@ -103,3 +104,32 @@ def test_group_skewed(orc):
 
 def test_group_empty(orc):
     check_group(orc, np.zeros((0, 4), np.int32), 16, "empty")
+
+
+@pytest.mark.parametrize("T,E,k,score_fn,renorm", [(1, 128, 8, 0, True), (8, 256, 8, 0, True), (2, 64, 1, 1, False),
+                                                   (17, 300, 5, 0, False), (64, 512, 16, 1, True),
+                                                   (65, 256, 8, 0, True), (200, 64, 6, 1, True),
+                                                   (0, 32, 4, 0, True)])
+def test_route_group_matches_separate_calls(orc, T, E, k, score_fn, renorm):
+    """moe_route_group (one launch for T <= 64, the two kernels above) equals route_topk followed by
+    group_tokens bit for bit, and the oracle on ids and grouping."""
+    print(f"route_group T={T} E={E} k={k} fn={score_fn} renorm={renorm}", flush=True)
+    rng = np.random.default_rng(T * 1000 + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    lg = dev(logits) if T else torch.empty((0, E), dtype=torch.float32, device="cuda")
+    ids_f, w_f, g_f = moe.route_group(lg, k, score_fn, renorm)
+    ids_s, w_s = moe.route_topk(lg, k, score_fn, renorm)
+    g_s = moe.group_tokens(ids_s, E)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids_f.cpu().numpy(), ids_s.cpu().numpy())
+    np.testing.assert_array_equal(w_f.cpu().numpy().view(np.uint32), w_s.cpu().numpy().view(np.uint32))
+    P = T * k
+    for name in ("counts", "offsets", "active", "n_active"):
+        np.testing.assert_array_equal(getattr(g_f, name).cpu().numpy(), getattr(g_s, name).cpu().numpy())
+    for name in ("sorted_pair", "pair_pos"):
+        np.testing.assert_array_equal(getattr(g_f, name)[:P].cpu().numpy(), getattr(g_s, name)[:P].cpu().numpy())
+    if T:
+        oids, _ = orc.route_topk(logits, k, score_fn, renorm)
+        np.testing.assert_array_equal(ids_f.cpu().numpy(), oids)
+        ref = orc.group_tokens(oids, E)
+        np.testing.assert_array_equal(g_f.sorted_pair[:P].cpu().numpy(), ref["sorted_pair"])
