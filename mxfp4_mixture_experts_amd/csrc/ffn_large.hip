@@ -3,8 +3,9 @@
 // Once an expert has tens of rows its GEMM is a real dense contraction, so it runs on the gfx950
 // matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation). The weights stay MXFP4 in HBM and are
 // decoded exactly to bf16 with the scaled FP4 conversion right before the MFMA:
-//   - a workgroup owns one (expert, tile of up to 64 rows) pair and a block of output columns; the
-//     four waves split the columns, every wave covers all rows of the tile;
+//   - a workgroup owns one (expert, tile of up to 64 rows) pair and a block of output columns; its
+//     eight waves (two per SIMD, so one wave's MFMAs cover the other's waits) split the columns,
+//     every wave covers all rows of the tile;
 //   - the activation tile (gathered x rows for gate_up, h rows for down) is staged in LDS, 128 K
 //     elements per step, and read by all four waves as MFMA A operands;
 //   - each lane loads one 32-element MX block (16 bytes + one scale byte) of one weight row per
@@ -78,15 +79,17 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
 // Ring depth (K-steps of loads in flight) by tile height: the fewer MFMAs a step holds, the more
 // steps must be in flight to cover the memory latency with one workgroup per CU.
 constexpr int ring_depth(bool gateup, int msub) {
-  return gateup ? (msub == 1 ? 6 : msub == 2 ? 5 : msub == 3 ? 4 : 3)
-                : (msub == 1 ? 5 : msub == 2 ? 4 : msub == 3 ? 3 : 2);
+  return gateup ? (msub <= 2 ? 3 : 2) : (msub == 1 ? 3 : msub <= 3 ? 2 : 1);
 }
+
+constexpr int kNW = 8;           // waves per workgroup (2 per SIMD)
+constexpr int kThreads = 64 * kNW;
 
 // One (expert, row tile) x column block, with MSUB blocks of 16 rows fixed at compile time so the
 // step is straight-line code (no per-row-block branches between MFMAs).
-// Staging: gate_up stages MSUB*16 rows x 128 bf16 of gathered x per K-step (one 16-byte chunk per
-// thread and 16-row block); down stages MSUB*16 rows x 128 fp32 of h (two chunks per thread and
-// block) and writes them to LDS as a bf16 hi tile and a bf16 lo tile.
+// Staging: gate_up stages MSUB*16 rows x 128 bf16 of gathered x per K-step (16-byte chunks, spread
+// over the workgroup's threads; rows past the tile repeat its last row); down stages MSUB*16 rows x
+// 128 fp32 of h and writes them to LDS as a bf16 hi tile and a bf16 lo tile.
 template <bool GATEUP, int MSUB, int CB>
 __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const uint8_t* __restrict__ qe,
                                            const uint8_t* __restrict__ se, int e, int m0, int xblk,
@@ -96,7 +99,8 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
   constexpr int D = ring_depth(GATEUP, MSUB);
   constexpr int kATiles = GATEUP ? 1 : 2;  // bf16 x, or bf16 hi + lo of h
   constexpr int kTileBytes = kTileM * kLdsRow;
-  constexpr int NA = GATEUP ? MSUB : 2 * MSUB;
+  // 16-byte chunks per thread and K-step: MSUB*16 rows of 16 (bf16 x) or 32 (fp32 h) chunks
+  constexpr int NA = GATEUP ? (MSUB * 256 + kThreads - 1) / kThreads : (MSUB * 512 + kThreads - 1) / kThreads;
 
   const int rows = min(kTileM, uniform(r.counts[e]) - m0);
   const int row0 = uniform(r.offsets[e]) + m0;
@@ -119,12 +123,12 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
   for (int cb = 0; cb < CB; ++cb) {
     int wrow;
     if (GATEUP) {
-      const int gc = xblk * (32 * CB) + wave * (8 * CB) + (cb % (CB / 2)) * 16 + j16;
+      const int gc = xblk * (kNW * 8 * CB) + wave * (8 * CB) + (cb % (CB / 2)) * 16 + j16;
       col[cb] = gc;
       cval[cb] = gc < I;
       wrow = (cb < CB / 2) ? min(gc, I - 1) : I + min(gc, I - 1);
     } else {
-      const int c = xblk * (64 * CB) + wave * (16 * CB) + cb * 16 + j16;
+      const int c = xblk * (kNW * 16 * CB) + wave * (16 * CB) + cb * 16 + j16;
       col[cb] = c;
       cval[cb] = c < H;
       wrow = min(c, H - 1);
@@ -138,7 +142,8 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
   const uint8_t* arow[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int lr = min(GATEUP ? (tid >> 4) + 16 * i : (tid >> 5) + 8 * i, rows - 1);
+    const int ch = tid + kThreads * i;
+    const int lr = min(GATEUP ? ch >> 4 : ch >> 5, rows - 1);
     if (GATEUP) {
       const int t = r.sorted_pair[row0 + lr] / r.k;
       arow[i] = reinterpret_cast<const uint8_t*>(r.x + (size_t)t * H);
@@ -187,12 +192,14 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       if (GATEUP) {
-        const int lr = (tid >> 4) + 16 * i, c16 = tid & 15;
+        const int ch = tid + kThreads * i;
+        const int lr = ch >> 4, c16 = ch & 15;
         uint4 v = ra[slot][i];
         if (k_tail && step * 128 + c16 * 8 >= K) v = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(lb + lr * kLdsRow + c16 * 16) = v;
       } else {
-        const int lr = (tid >> 5) + 8 * i, c4 = tid & 31;
+        const int ch = tid + kThreads * i;
+        const int lr = ch >> 5, c4 = ch & 31;
         float4 v = __builtin_bit_cast(float4, ra[slot][i]);
         if (k_tail && step * 128 + c4 * 4 >= K) v = make_float4(0.f, 0.f, 0.f, 0.f);
         const uint16_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
@@ -234,6 +241,9 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
           for (int at = 0; at < kATiles; ++at)
             acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[at][ms], bop, acc[ms][cb], 0, 0, 0);
       }
+      // keep the decode of the next operand group below these MFMAs (hoisting all of a step's
+      // decodes ahead would hold 16 more B operands live and spill at two waves per SIMD)
+      __builtin_amdgcn_sched_barrier(0);
     }
     // the slot's registers are consumed: refill it with step + D
     issue(slot, step + D);
@@ -282,7 +292,7 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
 // y = x, x + 8, ... and dispatches all nx column blocks of one tile back to back on it, so a tile's
 // activation rows are fetched into that XCD's L2 once and reused by every column block.
 template <bool GATEUP, int CB>
-__global__ __launch_bounds__(256, 1) void large_kernel(Routed r, int H, int I, int nx, int tile_slots,
+__global__ __launch_bounds__(kThreads, 1) void large_kernel(Routed r, int H, int I, int nx, int tile_slots,
                                                        const uint8_t* __restrict__ wq_all,
                                                        const uint8_t* __restrict__ ws_all,
                                                        const int32_t* __restrict__ tile_e,
@@ -326,8 +336,8 @@ constexpr int kDnCB = 4;  // down: 4 column blocks per wave
 LargePlan plan_large(int T, int H, int I, int E, int k, int small_m_max) {
   LargePlan lp;
   lp.tile_m = kTileM;
-  lp.gu_tile_n = 32 * kGuCB;
-  lp.dn_tile_n = 64 * kDnCB;
+  lp.gu_tile_n = kNW * 8 * kGuCB;
+  lp.dn_tile_n = kNW * 16 * kDnCB;
   lp.gu_grid_x = (I + lp.gu_tile_n - 1) / lp.gu_tile_n;
   lp.dn_grid_x = (H + lp.dn_tile_n - 1) / lp.dn_tile_n;
   lp.tile_slots = tile_slots_bound(T, E, k, small_m_max);
@@ -356,7 +366,7 @@ hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int 
                                const uint8_t* w13_q, const uint8_t* w13_s, const int32_t* tile_e,
                                const int32_t* tile_m0, float clamp, float* h, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
-  large_kernel<true, kGuCB><<<lp.gu_blocks, 256, 0, stream>>>(r, H, I, lp.gu_grid_x, lp.tile_slots, w13_q,
+  large_kernel<true, kGuCB><<<lp.gu_blocks, kThreads, 0, stream>>>(r, H, I, lp.gu_grid_x, lp.tile_slots, w13_q,
                                                                w13_s, tile_e, tile_m0, clamp, nullptr, h,
                                                                nullptr);
   return hipGetLastError();
@@ -366,7 +376,7 @@ hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I,
                              const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
                              const float* h, float* y, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
-  large_kernel<false, kDnCB><<<lp.dn_blocks, 256, 0, stream>>>(r, H, I, lp.dn_grid_x, lp.tile_slots, w2_q,
+  large_kernel<false, kDnCB><<<lp.dn_blocks, kThreads, 0, stream>>>(r, H, I, lp.dn_grid_x, lp.tile_slots, w2_q,
                                                                 w2_s, tile_e, tile_m0, 0.0f, h, nullptr,
                                                                 y);
   return hipGetLastError();
