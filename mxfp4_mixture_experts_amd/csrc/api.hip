@@ -43,7 +43,7 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
   size_t h_f32, g_f32, y, sched, total;
-  int tile_slots_max;
+  int tile_slots_max, dense_slots_max;
 };
 
 // Every region is sized for the worst case over routings and launch-table thresholds, so one
@@ -52,8 +52,11 @@ WsLayout ws_layout(long P, int H, int I, int E, int k, int flags) {
   WsLayout w;
   size_t off = 0;
   w.tile_slots_max = moe::tile_slots_bound((int)(P / k), E, k, 0);
-  w.sched = off;  // small_list[E], n_small[1], tile_e[slots], tile_m0[slots]
-  off = align_up(off + sizeof(int32_t) * ((size_t)E + 1 + 2 * (size_t)w.tile_slots_max));
+  w.dense_slots_max = moe::dense_slots_bound((int)(P / k), E, k, moe::kDenseMinRows);
+  // small_list[E], n_small[1], tile_e[slots], tile_m0[slots], dense_e[dslots], dense_m0[dslots]
+  w.sched = off;
+  off = align_up(off + sizeof(int32_t) * ((size_t)E + 1 + 2 * (size_t)w.tile_slots_max +
+                                          2 * (size_t)w.dense_slots_max));
   w.h_f32 = off;
   off = align_up(off + (size_t)P * I * sizeof(float));
   w.g_f32 = off;
@@ -95,9 +98,11 @@ void fill_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan)
   plan->large_gateup_grid = plan->launch_large ? lp.gu_blocks : 0;
   plan->large_down_grid = plan->launch_large ? lp.dn_blocks : 0;
   plan->combine_grid = T > 0 ? moe::combine_grid(T, H) : 0;
-  // the MFMA kernels need the schedule kernel's tile list first
+  // the MFMA kernels need the schedule kernel's tile lists first; the dense kernels run only when an
+  // expert can have kDenseMinRows rows (an expert has at most T)
+  const bool dense = plan->launch_large && T >= moe::kDenseMinRows;
   plan->n_launches = (plan->launch_small ? gu_launches + 1 : 0) + (plan->launch_large ? 3 : 0) +
-                     (T > 0 ? 1 : 0);
+                     (dense ? 2 : 0) + (T > 0 ? 1 : 0);
 }
 
 void record(int stage, bool start, hipStream_t stream) {
@@ -236,14 +241,19 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   int32_t* n_small = small_list + E;
   int32_t* tile_e = n_small + 1;
   int32_t* tile_m0 = tile_e + wl.tile_slots_max;
+  int32_t* dense_e = tile_m0 + wl.tile_slots_max;
+  int32_t* dense_m0 = dense_e + wl.dense_slots_max;
+  const bool dense = plan.launch_large && T >= moe::kDenseMinRows;
+  const int dense_min = dense ? moe::kDenseMinRows : INT_MAX;
+  const moe::DensePlan dp = moe::plan_dense(T, H, I, E, k, moe::kDenseMinRows);
   // without MFMA kernels every active expert is small: the grouping's active list is the work list
   const int32_t* list = plan.launch_large ? small_list : active;
   const int32_t* list_count = plan.launch_large ? n_small : n_active;
   bool ok = true;
 
   if (plan.launch_large)
-    ok &= moe::launch_schedule(r, E, thr, wl.tile_slots_max, small_list, n_small, tile_e, tile_m0, s) ==
-          hipSuccess;
+    ok &= moe::launch_schedule(r, E, thr, wl.tile_slots_max, dense_min, dp.slots, small_list, n_small,
+                               tile_e, tile_m0, dense_e, dense_m0, s) == hipSuccess;
 
   record(MOE_STAGE_GATE_UP, true, s);
   if (plan.launch_small) {
@@ -260,6 +270,9 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   if (plan.launch_large)
     ok &= moe::launch_large_gateup(lp, r, H, I, w13_q, w13_s, tile_e, tile_m0, clamp_limit, h_f32, s) ==
           hipSuccess;
+  if (dense)
+    ok &= moe::launch_dense_gateup(dp, r, H, I, w13_q, w13_s, dense_e, dense_m0, clamp_limit, h_f32, s) ==
+          hipSuccess;
   record(MOE_STAGE_GATE_UP, false, s);
 
   record(MOE_STAGE_DOWN, true, s);
@@ -267,6 +280,8 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
     ok &= moe::launch_small_down(sp, r, list, list_count, H, I, w2_q, w2_s, h_f32, y, s) == hipSuccess;
   if (plan.launch_large)
     ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, tile_e, tile_m0, h_f32, y, s) == hipSuccess;
+  if (dense)
+    ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_f32, y, s) == hipSuccess;
   record(MOE_STAGE_DOWN, false, s);
 
   record(MOE_STAGE_COMBINE, true, s);

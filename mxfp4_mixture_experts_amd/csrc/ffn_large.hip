@@ -29,6 +29,7 @@ namespace moe {
 namespace {
 
 constexpr int kTileM = 64;      // rows per tile (4 MFMA row blocks of 16)
+constexpr int kDenseRows = 256; // rows per tile of the dense kernels
 constexpr int kKStep = 128;     // K elements per step (4 MX blocks)
 constexpr int kLdsRow = 272;    // bytes per LDS activation row (256 + 16 padding)
 
@@ -39,28 +40,32 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* base, uint32_t off) {
 __device__ __forceinline__ uint32_t ld8(const uint8_t* base, uint32_t off) { return base[off]; }
 
 // One wave: split the active experts into those for the weight-streaming kernels (at most
-// small_m_max rows) and the row tiles of the others, in ascending expert order. Unused tail entries
-// are -1, so consumers need not read the counts.
+// small_m_max rows), the 64-row tiles of those for the row-tile kernels and the 256-row tiles of
+// those with at least dense_m_min rows for the dense kernels, in ascending expert order. Unused tail
+// entries are -1, so consumers need not read the counts.
 __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict__ counts,
                                                       const int32_t* __restrict__ active,
                                                       const int32_t* __restrict__ n_active, int E,
-                                                      int small_m_max, int tile_slots,
-                                                      int32_t* __restrict__ small_list,
+                                                      int small_m_max, int tile_slots, int dense_m_min,
+                                                      int dense_slots, int32_t* __restrict__ small_list,
                                                       int32_t* __restrict__ n_small,
                                                       int32_t* __restrict__ tile_e,
-                                                      int32_t* __restrict__ tile_m0) {
+                                                      int32_t* __restrict__ tile_m0,
+                                                      int32_t* __restrict__ dense_e,
+                                                      int32_t* __restrict__ dense_m0) {
   const int lane = threadIdx.x;
   const int na = *n_active;
-  int ns = 0, nt = 0;
+  int ns = 0, nt = 0, nd = 0;
   for (int i0 = 0; i0 < na; i0 += 64) {
     const int i = i0 + lane;
     const int e = i < na ? active[i] : -1;
     const int c = e >= 0 ? counts[e] : 0;
     const bool small = e >= 0 && c <= small_m_max;
+    const bool dense = e >= 0 && !small && c >= dense_m_min;
     const uint64_t sm = __ballot(small);
     if (small) small_list[ns + __popcll(sm & lanemask_lt(lane))] = e;
     ns += __popcll(sm);
-    const int tiles = (e >= 0 && !small) ? (c + kTileM - 1) / kTileM : 0;
+    const int tiles = (e >= 0 && !small && !dense) ? (c + kTileM - 1) / kTileM : 0;
     const int incl = wave_inclusive_scan(tiles, lane);
     for (int t = 0; t < tiles; ++t) {
       const int slot = nt + incl - tiles + t;
@@ -70,9 +75,20 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
       }
     }
     nt += __shfl(incl, 63, 64);
+    const int dtiles = dense ? (c + kDenseRows - 1) / kDenseRows : 0;
+    const int dincl = wave_inclusive_scan(dtiles, lane);
+    for (int t = 0; t < dtiles; ++t) {
+      const int slot = nd + dincl - dtiles + t;
+      if (slot < dense_slots) {
+        dense_e[slot] = e;
+        dense_m0[slot] = t * kDenseRows;
+      }
+    }
+    nd += __shfl(dincl, 63, 64);
   }
   for (int i = ns + lane; i < E; i += 64) small_list[i] = -1;
   for (int i = nt + lane; i < tile_slots; i += 64) tile_e[i] = -1;
+  for (int i = nd + lane; i < dense_slots; i += 64) dense_e[i] = -1;
   if (lane == 0) *n_small = ns;
 }
 
@@ -355,10 +371,12 @@ int tile_slots_bound(int T, int E, int k, int small_m_max) {
   return (int)((P + kTileM - 1) / kTileM + n_large);
 }
 
-hipError_t launch_schedule(const Routed& r, int E, int small_m_max, int tile_slots, int32_t* small_list,
-                           int32_t* n_small, int32_t* tile_e, int32_t* tile_m0, hipStream_t stream) {
+hipError_t launch_schedule(const Routed& r, int E, int small_m_max, int tile_slots, int dense_m_min,
+                           int dense_slots, int32_t* small_list, int32_t* n_small, int32_t* tile_e,
+                           int32_t* tile_m0, int32_t* dense_e, int32_t* dense_m0, hipStream_t stream) {
   schedule_kernel<<<1, 64, 0, stream>>>(r.counts, r.active, r.n_active, E, small_m_max, tile_slots,
-                                        small_list, n_small, tile_e, tile_m0);
+                                        dense_m_min, dense_slots, small_list, n_small, tile_e, tile_m0,
+                                        dense_e, dense_m0);
   return hipGetLastError();
 }
 

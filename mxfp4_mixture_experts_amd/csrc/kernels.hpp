@@ -84,9 +84,11 @@ int tile_slots_bound(int T, int E, int k, int small_m_max);
 LargePlan plan_large(int T, int H, int I, int E, int k, int small_m_max);
 
 // Splits the active experts by row count: small_list/n_small for the weight-streaming kernels,
-// tile_e/tile_m0 (tile_slots entries, -1 past the last tile) for the MFMA kernels.
-hipError_t launch_schedule(const Routed& r, int E, int small_m_max, int tile_slots, int32_t* small_list,
-                           int32_t* n_small, int32_t* tile_e, int32_t* tile_m0, hipStream_t stream);
+// tile_e/tile_m0 (tile_slots entries, -1 past the last tile) for the row-tile MFMA kernels and
+// dense_e/dense_m0 (dense_slots entries) for the dense kernels (experts with >= dense_m_min rows).
+hipError_t launch_schedule(const Routed& r, int E, int small_m_max, int tile_slots, int dense_m_min,
+                           int dense_slots, int32_t* small_list, int32_t* n_small, int32_t* tile_e,
+                           int32_t* tile_m0, int32_t* dense_e, int32_t* dense_m0, hipStream_t stream);
 
 hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int I,
                                const uint8_t* w13_q, const uint8_t* w13_s, const int32_t* tile_e,
@@ -94,6 +96,28 @@ hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int 
 
 hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
+                             const float* h, float* y, hipStream_t stream);
+
+// Dense bf16-MFMA kernels for experts with at least kDenseMinRows rows: 256-row tiles, both operands
+// staged in LDS, weights decoded once per workgroup.
+constexpr int kDenseMinRows = 256;
+
+struct DensePlan {
+  int tile_m;                // rows per tile
+  int gu_grid_x, dn_grid_x;  // column tiles per row tile
+  int slots;                 // upper bound on the number of (expert, row-tile) pairs
+  int gu_blocks, dn_blocks;  // one-dimensional grids (XCD-interleaved tile order)
+};
+
+int dense_slots_bound(int T, int E, int k, int dense_m_min);
+DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min);
+
+hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w13_q,
+                               const uint8_t* w13_s, const int32_t* dense_e, const int32_t* dense_m0,
+                               float clamp, float* h, hipStream_t stream);
+
+hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
+                             const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
                              const float* h, float* y, hipStream_t stream);
 
 // out[t] = bf16(sum_j topk_w[t, j] * y[pair_pos[t*k + j]])

@@ -71,6 +71,24 @@ CASES = [
 ]
 
 
+DENSE_CASES = [
+    # experts with >= 256 rows take the dense kernels (256-row tiles, operands staged in LDS)
+    (600, 160, 96, 3, 2, 0, 0.0, 21),     # ~400 rows per expert: a full and a partial row tile;
+                                          # 5 and 3 K-steps (odd: a padding step)
+    (520, 256, 128, 2, 1, 1, 7.0, 22),    # ~260 rows: a 4-row second tile; sigmoid, clamp
+    (512, 2048, 1024, 1, 1, 0, 0.0, 23),  # exactly two full tiles
+    (300, 544, 320, 2, 2, 0, 0.0, 24),    # one expert >= 256, one below (row-tile kernels), columns
+                                          # not a multiple of the column tiles
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "T%d_H%d_I%d_E%d_k%d" % c[:5])
+def test_dense_shapes(orc, case):
+    T, H, I, E, k, fn, clamp, seed = case
+    cfg, inp = moe_synth.small_case(T, H, I, E, k, seed, score_fn=fn, clamp=clamp)
+    check_full(orc, cfg, inp, ("default", "large", "unfused"))
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_H%d_I%d_E%d_k%d" % c[:5])
 def test_small_shapes(orc, case):
     T, H, I, E, k, fn, clamp, seed = case
