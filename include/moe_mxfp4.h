@@ -140,8 +140,8 @@ int moe_route_group(const float* logits, int T, int E, int k, int score_fn, int 
 
 /*
  * moe_mxfp4_ffn_workspace_size — bytes of device workspace moe_mxfp4_ffn needs for these sizes and
- * flags: the SwiGLU activations h (fp32 for the small-M kernels, bf16 for the MFMA kernels), the
- * per-pair down-projection outputs y (fp32, P x H) and, with MOE_UNFUSED_GATE_UP, the gate
+ * flags: the SwiGLU activations h (two bf16 planes, 4 bytes per element of P x I), the per-pair
+ * down-projection outputs y (fp32, P x H) and, with MOE_UNFUSED_GATE_UP, the gate
  * activations. The size covers the worst case over every routing of the P pairs, so a workspace
  * sized once for (T, H, I, E, k, flags) is valid for every call with those sizes (cf. the split-K
  * workspace contract of tokenspeed PR #661, "The workspace contract": partial rows must be reserved
@@ -161,9 +161,11 @@ size_t moe_mxfp4_ffn_workspace_size(int T, int H, int I, int E, int k, int flags
  *   h_i = g_i / (1 + exp(-g_i)) * u_i                                   (SwiGLU)
  *   y_p = h . W2[e]ᵀ                                                     (fp32 accumulation)
  * and out[t] = sum over j = 0..k-1, in that order, of topk_w[t, j] * y_(t,j), rounded once to
- * bfloat16 (nearest-even). Experts with no pairs read no weights. Small per-expert row counts run on
- * weight-streaming kernels (fp32 h); large ones on bf16 MFMA kernels (h rounded to bf16 as the MFMA
- * operand). Results are deterministic: repeated calls give bitwise-identical outputs.
+ * bfloat16 (nearest-even). Experts with no pairs read no weights. h is kept between the two GEMMs
+ * as hi = bf16(h) and lo = bf16(h - hi) (hi + lo equals h to about 2^-17 relative). Small per-expert
+ * row counts run on weight-streaming kernels (down: hi + lo rebuilt, then scaled fp16 per 32-value
+ * block); large ones on bf16 MFMA kernels (down: one MFMA on each plane). Results are
+ * deterministic: repeated calls give bitwise-identical outputs.
  *
  *   x_bf16                       [dev] u16[T, H]  bfloat16 activations, 16-byte aligned
  *   w13_q, w13_s, w2_q, w2_s     [dev] MXFP4 weights (layout above); w13_q and w2_q 16-byte aligned

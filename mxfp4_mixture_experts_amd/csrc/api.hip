@@ -42,7 +42,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
-  size_t h_f32, g_f32, y, sched, total;
+  size_t h, g_f32, y, sched, total;
   int tile_slots_max, dense_slots_max;
 };
 
@@ -57,8 +57,9 @@ WsLayout ws_layout(long P, int H, int I, int E, int k, int flags) {
   w.sched = off;
   off = align_up(off + sizeof(int32_t) * ((size_t)E + 1 + 2 * (size_t)w.tile_slots_max +
                                           2 * (size_t)w.dense_slots_max));
-  w.h_f32 = off;
-  off = align_up(off + (size_t)P * I * sizeof(float));
+  // h as two bf16 planes [P, I] (hi, then lo)
+  w.h = off;
+  off = align_up(off + (size_t)P * I * 2 * sizeof(uint16_t));
   w.g_f32 = off;
   if (flags & MOE_UNFUSED_GATE_UP) off = align_up(off + (size_t)P * I * sizeof(float));
   w.y = off;
@@ -230,7 +231,8 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   const int thr = plan.small_m_max;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  float* h_f32 = (float*)(ws + wl.h_f32);
+  uint16_t* h_hi = (uint16_t*)(ws + wl.h);
+  uint16_t* h_lo = h_hi + (size_t)T * k * I;
   float* g_f32 = (float*)(ws + wl.g_f32);
   float* y = (float*)(ws + wl.y);
 
@@ -259,29 +261,29 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   if (plan.launch_small) {
     if (flags & MOE_UNFUSED_GATE_UP) {
       ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
-                                     moe::kGateOnly, h_f32, g_f32, s) == hipSuccess;
+                                     moe::kGateOnly, h_hi, h_lo, g_f32, s) == hipSuccess;
       ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
-                                     moe::kUpWithGate, h_f32, g_f32, s) == hipSuccess;
+                                     moe::kUpWithGate, h_hi, h_lo, g_f32, s) == hipSuccess;
     } else {
       ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
-                                     moe::kGateUpFused, h_f32, g_f32, s) == hipSuccess;
+                                     moe::kGateUpFused, h_hi, h_lo, g_f32, s) == hipSuccess;
     }
   }
   if (plan.launch_large)
-    ok &= moe::launch_large_gateup(lp, r, H, I, w13_q, w13_s, tile_e, tile_m0, clamp_limit, h_f32, s) ==
+    ok &= moe::launch_large_gateup(lp, r, H, I, w13_q, w13_s, tile_e, tile_m0, clamp_limit, h_hi, h_lo, s) ==
           hipSuccess;
   if (dense)
-    ok &= moe::launch_dense_gateup(dp, r, H, I, w13_q, w13_s, dense_e, dense_m0, clamp_limit, h_f32, s) ==
+    ok &= moe::launch_dense_gateup(dp, r, H, I, w13_q, w13_s, dense_e, dense_m0, clamp_limit, h_hi, h_lo, s) ==
           hipSuccess;
   record(MOE_STAGE_GATE_UP, false, s);
 
   record(MOE_STAGE_DOWN, true, s);
   if (plan.launch_small)
-    ok &= moe::launch_small_down(sp, r, list, list_count, H, I, w2_q, w2_s, h_f32, y, s) == hipSuccess;
+    ok &= moe::launch_small_down(sp, r, list, list_count, H, I, w2_q, w2_s, h_hi, h_lo, y, s) == hipSuccess;
   if (plan.launch_large)
-    ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, tile_e, tile_m0, h_f32, y, s) == hipSuccess;
+    ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, tile_e, tile_m0, h_hi, h_lo, y, s) == hipSuccess;
   if (dense)
-    ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_f32, y, s) == hipSuccess;
+    ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, h_lo, y, s) == hipSuccess;
   record(MOE_STAGE_DOWN, false, s);
 
   record(MOE_STAGE_COMBINE, true, s);

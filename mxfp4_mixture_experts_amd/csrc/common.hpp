@@ -28,6 +28,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// h of a routed pair as two bfloat16 planes: hi = bf16(v), lo = bf16(v - hi). hi + lo is exact in
+// fp32 and equals v to about 2^-17 relative.
+__device__ __forceinline__ void store_h_planes(uint16_t* hi, uint16_t* lo, size_t o, float v) {
+  const uint16_t h = f32_to_bf16_rne(v);
+  hi[o] = h;
+  lo[o] = f32_to_bf16_rne(v - __builtin_bit_cast(float, (uint32_t)h << 16));
+}
+
+// The two bf16 halves of a dword as floats (element 0 in the low half).
+__device__ __forceinline__ float bf16_lo_f32(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }

@@ -8,7 +8,7 @@
 //     matching 128 up columns; down: 256 output columns); its eight waves (two per SIMD) each
 //     compute 64 rows x 128 weight rows with v_mfma_f32_16x16x32_bf16 (32 accumulator blocks);
 //   - per K-step every thread loads 16-byte chunks of the activation rows (gathered x rows for
-//     gate_up; h rows for down, split into exact bf16 hi and lo tiles) and one MX block of one
+//     gate_up; for down, h rows of both of its bf16 planes, hi and lo) and one MX block of one
 //     weight row (16 bytes of E2M1 codes + the E8M0 scale), decodes the block exactly to 32 bf16
 //     with the scaled FP4 conversion and writes both to LDS; the loads of the next K-steps are in
 //     flight in registers meanwhile;
@@ -47,9 +47,10 @@ struct DenseShape {
   static constexpr int kATileBytes = kDM * kRow;
   static constexpr int kBTileBytes = kDN * kRow;
   static constexpr int kStage = kATiles * kATileBytes + kBTileBytes;
-  // 16-byte global chunks per thread and step: activations (bf16 x: kBK*2 bytes per row; fp32 h:
-  // kBK*4 bytes per row) and weight blocks
-  static constexpr int kAChunks = kDM * kBK * (GATEUP ? 2 : 4) / 16 / kDThreads;
+  // 16-byte global chunks per activation row and step (bf16 x: kBK*2 bytes; h: kBK*2 bytes of each
+  // plane), per thread and step, and weight-block chunks per thread and step
+  static constexpr int kCpr = kATiles * kBK * 2 / 16;
+  static constexpr int kAChunks = kDM * kCpr / kDThreads;
   static constexpr int kBChunks = (kDN * kBlocks + kDThreads - 1) / kDThreads;
   static constexpr int kD = GATEUP ? 1 : 2;             // K-steps of loads in flight
 };
@@ -73,7 +74,8 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k, int H, int I,
     int nx, int dense_slots, const uint8_t* __restrict__ wq_all, const uint8_t* __restrict__ ws_all,
     const int32_t* __restrict__ dense_e, const int32_t* __restrict__ dense_m0, float clamp,
-    const float* __restrict__ h_in, float* __restrict__ h_out, float* __restrict__ y_out) {
+    const uint16_t* __restrict__ h_hi_in, const uint16_t* __restrict__ h_lo_in,
+    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, float* __restrict__ y_out) {
   using S = DenseShape<GATEUP>;
   constexpr int D = S::kD;
   constexpr int NA = S::kAChunks;
@@ -111,8 +113,10 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   const int wc = wave / (kDW / 2);  // column group: B-tile rows wc*128 .. +128
 
   // ---- staging assignments
-  // activations: chunk c = tid + kDThreads * i covers 16 bytes of row (c / cpr) at byte (c % cpr)*16
-  constexpr int kCpr = S::kBK * (GATEUP ? 2 : 4) / 16;  // chunks per activation row and step
+  // activations: chunk c = tid + kDThreads * i covers 8 elements of row (c / kCpr): for down, of
+  // plane (c % kCpr) / (kBK / 8), for gate_up of x
+  constexpr int kCpr = S::kCpr;
+  constexpr int kCpp = S::kBK / 8;  // chunks per row and plane
   const uint8_t* arow[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
@@ -122,7 +126,8 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
       const int t = sorted_pair[row0 + lr] / k;
       arow[i] = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
     } else {
-      arow[i] = reinterpret_cast<const uint8_t*>(h_in + (size_t)(row0 + lr) * I);
+      const uint16_t* plane = ((c % kCpr) / kCpp) ? h_lo_in : h_hi_in;
+      arow[i] = reinterpret_cast<const uint8_t*>(plane + (size_t)(row0 + lr) * I);
     }
   }
   // weights: chunk q = tid + kDThreads * j is block (q % kBlocks) of B-tile row (q / kBlocks)
@@ -153,9 +158,9 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int c = tid + kDThreads * i;
-      const int el = st * S::kBK + (c % kCpr) * (GATEUP ? 8 : 4);  // first element of the chunk
-      const int elc = min(el, K - (GATEUP ? 8 : 4));
-      ra[slot][i] = ld16(arow[i], (uint32_t)elc * (GATEUP ? 2 : 4));
+      const int el = st * S::kBK + (c % kCpp) * 8;  // first element of the chunk
+      const int elc = min(el, K - 8);
+      ra[slot][i] = ld16(arow[i], (uint32_t)elc * 2);
     }
   };
 
@@ -175,26 +180,10 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int c = tid + kDThreads * i;
-      const int lr = c / kCpr, cc = c % kCpr;
-      const int el = step * S::kBK + cc * (GATEUP ? 8 : 4);
-      if (GATEUP) {
-        uint4 v = ra[slot][i];
-        if (el >= K) v = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(st_a + lr * S::kRow + cc * 16) = v;
-      } else {
-        float4 v = __builtin_bit_cast(float4, ra[slot][i]);
-        if (el >= K) v = make_float4(0.f, 0.f, 0.f, 0.f);
-        const uint16_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
-        const uint16_t h2 = f32_to_bf16_rne(v.z), h3 = f32_to_bf16_rne(v.w);
-        auto up = [](uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); };
-        uint2 hi, lo;
-        hi.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        hi.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
-        lo.x = pack_bf16x2(v.x - up(h0), v.y - up(h1));
-        lo.y = pack_bf16x2(v.z - up(h2), v.w - up(h3));
-        *reinterpret_cast<uint2*>(st_a + lr * S::kRow + cc * 8) = hi;
-        *reinterpret_cast<uint2*>(st_a + S::kATileBytes + lr * S::kRow + cc * 8) = lo;
-      }
+      const int lr = c / kCpr, pl = (c % kCpr) / kCpp, cc = c % kCpp;
+      uint4 v = ra[slot][i];
+      if (step * S::kBK + cc * 8 >= K) v = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(st_a + pl * S::kATileBytes + lr * S::kRow + cc * 16) = v;
     }
     // weight blocks of this step -> 32 bf16 each in LDS (a zero scale past K)
 #pragma unroll
@@ -277,7 +266,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
             gv = clampf(gv, clamp);
             uv = clampf(uv, clamp);
           }
-          h_out[orow * I + col] = silu_mul(gv, uv);
+          store_h_planes(h_hi, h_lo, orow * I + col, silu_mul(gv, uv));
         }
       } else {
 #pragma unroll
@@ -314,7 +303,7 @@ DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min) {
 
 hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w13_q,
                                const uint8_t* w13_s, const int32_t* dense_e, const int32_t* dense_m0,
-                               float clamp, float* h, hipStream_t stream) {
+                               float clamp, uint16_t* h_hi, uint16_t* h_lo, hipStream_t stream) {
   if (dp.slots <= 0) return hipSuccess;
   constexpr int lds = 2 * DenseShape<true>::kStage;
   static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<true>),
@@ -323,13 +312,13 @@ hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int 
   (void)attr_set;
   dense_kernel<true><<<dp.gu_blocks, kDThreads, lds, stream>>>(
       r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.gu_grid_x, dp.slots, w13_q, w13_s, dense_e,
-      dense_m0, clamp, nullptr, h, nullptr);
+      dense_m0, clamp, nullptr, nullptr, h_hi, h_lo, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
-                             const float* h, float* y, hipStream_t stream) {
+                             const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream) {
   if (dp.slots <= 0) return hipSuccess;
   constexpr int lds = 2 * DenseShape<false>::kStage;
   static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<false>),
@@ -338,7 +327,7 @@ hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I,
   (void)attr_set;
   dense_kernel<false><<<dp.dn_blocks, kDThreads, lds, stream>>>(
       r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.dn_grid_x, dp.slots, w2_q, w2_s, dense_e,
-      dense_m0, 0.0f, h, nullptr, y);
+      dense_m0, 0.0f, h_hi, h_lo, nullptr, nullptr, y);
   return hipGetLastError();
 }
 

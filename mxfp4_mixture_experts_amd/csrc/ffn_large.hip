@@ -105,17 +105,18 @@ constexpr int kThreads = 64 * kNW;
 // step is straight-line code (no per-row-block branches between MFMAs).
 // Staging: gate_up stages MSUB*16 rows x 128 bf16 of gathered x per K-step (16-byte chunks, spread
 // over the workgroup's threads; rows past the tile repeat its last row); down stages MSUB*16 rows x
-// 128 fp32 of h and writes them to LDS as a bf16 hi tile and a bf16 lo tile.
+// 128 of both bf16 planes of h (hi, lo) into two LDS tiles.
 template <bool GATEUP, int MSUB, int CB>
 __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const uint8_t* __restrict__ qe,
                                            const uint8_t* __restrict__ se, int e, int m0, int xblk,
-                                           float clamp, const float* __restrict__ h_in,
-                                           float* __restrict__ h_out, float* __restrict__ y_out,
-                                           uint8_t* lds_a) {
+                                           float clamp, const uint16_t* __restrict__ h_hi_in,
+                                           const uint16_t* __restrict__ h_lo_in,
+                                           uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
+                                           float* __restrict__ y_out, uint8_t* lds_a) {
   constexpr int D = ring_depth(GATEUP, MSUB);
   constexpr int kATiles = GATEUP ? 1 : 2;  // bf16 x, or bf16 hi + lo of h
   constexpr int kTileBytes = kTileM * kLdsRow;
-  // 16-byte chunks per thread and K-step: MSUB*16 rows of 16 (bf16 x) or 32 (fp32 h) chunks
+  // 16-byte chunks per thread and K-step: MSUB*16 rows of 16 (bf16 x) or 2 x 16 (h planes) chunks
   constexpr int NA = GATEUP ? (MSUB * 256 + kThreads - 1) / kThreads : (MSUB * 512 + kThreads - 1) / kThreads;
 
   const int rows = min(kTileM, uniform(r.counts[e]) - m0);
@@ -164,7 +165,8 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
       const int t = r.sorted_pair[row0 + lr] / r.k;
       arow[i] = reinterpret_cast<const uint8_t*>(r.x + (size_t)t * H);
     } else {
-      arow[i] = reinterpret_cast<const uint8_t*>(h_in + (size_t)(row0 + lr) * I);
+      const uint16_t* plane = ((ch >> 4) & 1) ? h_lo_in : h_hi_in;
+      arow[i] = reinterpret_cast<const uint8_t*>(plane + (size_t)(row0 + lr) * I);
     }
   }
 
@@ -186,9 +188,8 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
     }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const uint32_t el = GATEUP ? (uint32_t)min(step * 128 + (tid & 15) * 8, K - 8)
-                                 : (uint32_t)min(step * 128 + (tid & 31) * 4, K - 4);
-      ra[slot][i] = ld16(arow[i], el * (GATEUP ? 2 : 4));
+      const uint32_t el = (uint32_t)min(step * 128 + (tid & 15) * 8, K - 8);
+      ra[slot][i] = ld16(arow[i], el * 2);
     }
   };
 
@@ -215,19 +216,10 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
         *reinterpret_cast<uint4*>(lb + lr * kLdsRow + c16 * 16) = v;
       } else {
         const int ch = tid + kThreads * i;
-        const int lr = ch >> 5, c4 = ch & 31;
-        float4 v = __builtin_bit_cast(float4, ra[slot][i]);
-        if (k_tail && step * 128 + c4 * 4 >= K) v = make_float4(0.f, 0.f, 0.f, 0.f);
-        const uint16_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
-        const uint16_t h2 = f32_to_bf16_rne(v.z), h3 = f32_to_bf16_rne(v.w);
-        auto up = [](uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); };
-        uint2 hi, lo;
-        hi.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        hi.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
-        lo.x = pack_bf16x2(v.x - up(h0), v.y - up(h1));
-        lo.y = pack_bf16x2(v.z - up(h2), v.w - up(h3));
-        *reinterpret_cast<uint2*>(lb + lr * kLdsRow + c4 * 8) = hi;
-        *reinterpret_cast<uint2*>(lb + kTileBytes + lr * kLdsRow + c4 * 8) = lo;
+        const int lr = ch >> 5, pl = (ch >> 4) & 1, c16 = ch & 15;
+        uint4 v = ra[slot][i];
+        if (k_tail && step * 128 + c16 * 8 >= K) v = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(lb + pl * kTileBytes + lr * kLdsRow + c16 * 16) = v;
       }
     }
     __syncthreads();
@@ -292,7 +284,7 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
             gv = clampf(gv, clamp);
             uv = clampf(uv, clamp);
           }
-          h_out[orow * I + col[cb]] = silu_mul(gv, uv);
+          store_h_planes(h_hi, h_lo, orow * I + col[cb], silu_mul(gv, uv));
         }
       } else {
 #pragma unroll
@@ -313,8 +305,11 @@ __global__ __launch_bounds__(kThreads, 1) void large_kernel(Routed r, int H, int
                                                        const uint8_t* __restrict__ ws_all,
                                                        const int32_t* __restrict__ tile_e,
                                                        const int32_t* __restrict__ tile_m0,
-                                                       float clamp, const float* __restrict__ h_in,
-                                                       float* __restrict__ h_out,
+                                                       float clamp,
+                                                       const uint16_t* __restrict__ h_hi_in,
+                                                       const uint16_t* __restrict__ h_lo_in,
+                                                       uint16_t* __restrict__ h_hi,
+                                                       uint16_t* __restrict__ h_lo,
                                                        float* __restrict__ y_out) {
   constexpr int kATiles = GATEUP ? 1 : 2;
   // two LDS buffers (double-buffered across K-steps), each kATiles tiles
@@ -336,12 +331,15 @@ __global__ __launch_bounds__(kThreads, 1) void large_kernel(Routed r, int H, int
   const size_t nrows_w = GATEUP ? (size_t)2 * I : (size_t)H;
   const uint8_t* qe = wq_all + (size_t)e * nrows_w * (size_t)(K >> 1);
   const uint8_t* se = ws_all + (size_t)e * nrows_w * (size_t)(K >> 5);
+#define MOE_TILE(MS) \
+  large_tile<GATEUP, MS, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_hi_in, h_lo_in, h_hi, h_lo, y_out, lds_a)
   switch (msub_n) {
-    case 1: large_tile<GATEUP, 1, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_in, h_out, y_out, lds_a); break;
-    case 2: large_tile<GATEUP, 2, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_in, h_out, y_out, lds_a); break;
-    case 3: large_tile<GATEUP, 3, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_in, h_out, y_out, lds_a); break;
-    default: large_tile<GATEUP, 4, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_in, h_out, y_out, lds_a); break;
+    case 1: MOE_TILE(1); break;
+    case 2: MOE_TILE(2); break;
+    case 3: MOE_TILE(3); break;
+    default: MOE_TILE(4); break;
   }
+#undef MOE_TILE
 }
 
 constexpr int kGuCB = 4;  // gate_up: 4 column blocks per wave (2 gate + 2 up)
@@ -382,21 +380,22 @@ hipError_t launch_schedule(const Routed& r, int E, int small_m_max, int tile_slo
 
 hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int I,
                                const uint8_t* w13_q, const uint8_t* w13_s, const int32_t* tile_e,
-                               const int32_t* tile_m0, float clamp, float* h, hipStream_t stream) {
+                               const int32_t* tile_m0, float clamp, uint16_t* h_hi, uint16_t* h_lo,
+                               hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
-  large_kernel<true, kGuCB><<<lp.gu_blocks, kThreads, 0, stream>>>(r, H, I, lp.gu_grid_x, lp.tile_slots, w13_q,
-                                                               w13_s, tile_e, tile_m0, clamp, nullptr, h,
-                                                               nullptr);
+  large_kernel<true, kGuCB><<<lp.gu_blocks, kThreads, 0, stream>>>(
+      r, H, I, lp.gu_grid_x, lp.tile_slots, w13_q, w13_s, tile_e, tile_m0, clamp, nullptr, nullptr, h_hi,
+      h_lo, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
-                             const float* h, float* y, hipStream_t stream) {
+                             const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
-  large_kernel<false, kDnCB><<<lp.dn_blocks, kThreads, 0, stream>>>(r, H, I, lp.dn_grid_x, lp.tile_slots, w2_q,
-                                                                w2_s, tile_e, tile_m0, 0.0f, h, nullptr,
-                                                                y);
+  large_kernel<false, kDnCB><<<lp.dn_blocks, kThreads, 0, stream>>>(
+      r, H, I, lp.dn_grid_x, lp.tile_slots, w2_q, w2_s, tile_e, tile_m0, 0.0f, h_hi, h_lo, nullptr, nullptr,
+      y);
   return hipGetLastError();
 }
 

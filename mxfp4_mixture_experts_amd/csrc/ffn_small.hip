@@ -131,23 +131,34 @@ __device__ __forceinline__ void dot_block_f16s(uint4 w, const float (&bs)[MTC],
   for (int m = 0; m < MTC; ++m) acc[m] = fmaf(part[m], bs[m], acc[m]);
 }
 
-// One lane's 32-value h block (fp32) as 16 packed fp16 pairs, scaled by a power of two that puts
-// its largest magnitude in [2^14, 2^15) (so nothing overflows fp16 and every value keeps fp16's
-// 11-bit precision relative to the block maximum); returns the inverse scale.
-__device__ __forceinline__ float h_block_to_f16(const float4 (&v)[8], uint32_t (&hh)[16]) {
-  float mx = 0.0f;
+// One lane's 32-value h block, given as its two bf16 planes (16 bytes x 4 of hi, of lo), as 16
+// packed fp16 pairs: value j is hi_j + lo_j (exact in fp32), scaled by a power of two that puts the
+// largest |hi_j| in [2^14, 2^15) (read from the bf16 exponent fields, so no fp32 copy of the block
+// stays live). |hi + lo| <= |hi| (1 + 2^-8), so nothing overflows fp16 and every value keeps fp16's
+// 11-bit precision relative to the block maximum. Returns the inverse scale.
+__device__ __forceinline__ float h_planes_to_f16(const uint4 (&hv)[4], const uint4 (&lv)[4],
+                                                 uint32_t (&hh)[16]) {
+  // largest exponent field among the low and among the high bf16 halves
+  uint32_t mx_lo = 0, mx_hi = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    mx = fmaxf(fmaxf(fmaxf(mx, fabsf(v[i].x)), fmaxf(fabsf(v[i].y), fabsf(v[i].z))), fabsf(v[i].w));
-  const int eb = (int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF);  // biased exponent
-  const int f = min(max(268 - eb, 1), 253);  // scale 2^(f - 127): mx * scale < 2^15
+  for (int i = 0; i < 4; ++i) {
+    mx_lo = max(max(mx_lo, max(hv[i].x & 0x7F80u, hv[i].y & 0x7F80u)), max(hv[i].z & 0x7F80u, hv[i].w & 0x7F80u));
+    mx_hi = max(max(mx_hi, max(hv[i].x & 0x7F800000u, hv[i].y & 0x7F800000u)),
+                max(hv[i].z & 0x7F800000u, hv[i].w & 0x7F800000u));
+  }
+  const int eb = max((int)(mx_lo >> 7), (int)(mx_hi >> 23));  // biased exponent of max |hi|
+  const int f = min(max(268 - eb, 1), 253);  // scale 2^(f - 127)
   const float sc = __builtin_bit_cast(float, (uint32_t)f << 23);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const f16x2_t a = f16x2_t{(_Float16)(v[i].x * sc), (_Float16)(v[i].y * sc)};
-    const f16x2_t b = f16x2_t{(_Float16)(v[i].z * sc), (_Float16)(v[i].w * sc)};
-    hh[2 * i] = __builtin_bit_cast(uint32_t, a);
-    hh[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+    const uint32_t b[4] = {lv[i].x, lv[i].y, lv[i].z, lv[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v0 = bf16_lo_f32(a[j]) + bf16_lo_f32(b[j]);
+      const float v1 = bf16_hi_f32(a[j]) + bf16_hi_f32(b[j]);
+      hh[4 * i + j] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)(v0 * sc), (_Float16)(v1 * sc)});
+    }
   }
   return __builtin_bit_cast(float, (uint32_t)(254 - f) << 23);
 }
@@ -289,7 +300,8 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
     int tiles, int weighted, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s,
-    int lpr, float clamp, float* __restrict__ h_out, float* __restrict__ g_ws) {
+    int lpr, float clamp, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
+    float* __restrict__ g_ws) {
   constexpr bool kGate = MODE != kUpWithGate;
   constexpr bool kUp = MODE != kGateOnly;
   __shared__ int counter;
@@ -442,7 +454,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
                 g = clampf(g, clamp);
                 u = clampf(u, clamp);
               }
-              h_out[o] = silu_mul(g, u);
+              store_h_planes(h_hi, h_lo, o, silu_mul(g, u));
             }
           }
         }
@@ -470,14 +482,15 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// down: an item is S rows of W2; activations h in fp32.
+// down: an item is S rows of W2; activations h rebuilt in fp32 from its two bf16 planes.
 
 template <int BPL, int MT, int S, int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
     int tiles, int weighted, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s,
-    int lpr, const float* __restrict__ h, float* __restrict__ y) {
+    int lpr, const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo,
+    float* __restrict__ y) {
   __shared__ int counter;
   ItemRange ir;
   if (!my_items(list, list_count, counts, tiles, MT, weighted, ir)) return;
@@ -547,15 +560,21 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
         cur.a_m0 = m0;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const uint8_t* hbase =
-              reinterpret_cast<const uint8_t*>(h + (size_t)(cur.row0 + m0 + min(m, mc - 1)) * I);
+          const size_t roff = (size_t)(cur.row0 + m0 + min(m, mc - 1)) * I;
+          const uint8_t* hib = reinterpret_cast<const uint8_t*>(h_hi + roff);
+          const uint8_t* lob = reinterpret_cast<const uint8_t*>(h_lo + roff);
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
             const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
-            float4 v[8];
+            uint4 hv[4], lv[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(float4, ld16(hbase, kb * 128 + i * 16));
-            hinv[m][b] = h_block_to_f16(v, hh[m][b]);
+            for (int i = 0; i < 4; ++i) {
+              hv[i] = ld16(hib, kb * 64 + i * 16);
+              lv[i] = ld16(lob, kb * 64 + i * 16);
+            }
+            hinv[m][b] = h_planes_to_f16(hv, lv, hh[m][b]);
+            // one block's planes in registers at a time
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
 #pragma unroll
@@ -638,15 +657,15 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
 template <int MODE>
 hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* list,
                            const int32_t* list_count, int H, int I, const uint8_t* wq,
-                           const uint8_t* ws, float clamp, float* h, float* g_ws,
-                           hipStream_t stream) {
+                           const uint8_t* ws, float clamp, uint16_t* h_hi, uint16_t* h_lo,
+                           float* g_ws, hipStream_t stream) {
   const dim3 grid(sp.gu_grid);
   const int lpr = sp.gu.lpr, tiles = sp.gu_tiles;
 #define MOE_GU(BPL, MT)                                                                          \
   small_gateup_kernel<BPL, MT, gateup_slots(BPL), gateup_ring(BPL), 4 * gu_waves(BPL, MT), MODE> \
       <<<grid, 256 * gu_waves(BPL, MT), 0, stream>>>(r.x, r.counts, r.offsets, r.sorted_pair, r.k,   \
                                                      list, list_count, H, I, tiles, sp.weighted, wq, \
-                                                     ws, lpr, clamp, h, g_ws)
+                                                     ws, lpr, clamp, h_hi, h_lo, g_ws)
 #define MOE_GU_MT(BPL) \
   if (sp.mt_gu == 2)   \
     MOE_GU(BPL, 2);    \
@@ -697,18 +716,18 @@ SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
 
 hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32_t* list,
                                const int32_t* list_count, int H, int I, const uint8_t* w13_q,
-                               const uint8_t* w13_s, float clamp, int mode, float* h, float* g_ws,
-                               hipStream_t stream) {
+                               const uint8_t* w13_s, float clamp, int mode, uint16_t* h_hi,
+                               uint16_t* h_lo, float* g_ws, hipStream_t stream) {
   if (sp.gu_grid <= 0) return hipSuccess;
   switch (mode) {
     case kGateUpFused:
-      return gateup_dispatch<kGateUpFused>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h, g_ws,
+      return gateup_dispatch<kGateUpFused>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h_hi, h_lo, g_ws,
                                            stream);
     case kGateOnly:
-      return gateup_dispatch<kGateOnly>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h, g_ws,
+      return gateup_dispatch<kGateOnly>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h_hi, h_lo, g_ws,
                                         stream);
     case kUpWithGate:
-      return gateup_dispatch<kUpWithGate>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h, g_ws,
+      return gateup_dispatch<kUpWithGate>(sp, r, list, list_count, H, I, w13_q, w13_s, clamp, h_hi, h_lo, g_ws,
                                           stream);
     default:
       return hipErrorInvalidValue;
@@ -717,14 +736,15 @@ hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32
 
 hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t* list,
                              const int32_t* list_count, int H, int I, const uint8_t* w2_q,
-                             const uint8_t* w2_s, const float* h, float* y, hipStream_t stream) {
+                             const uint8_t* w2_s, const uint16_t* h_hi, const uint16_t* h_lo, float* y,
+                             hipStream_t stream) {
   if (sp.dn_grid <= 0) return hipSuccess;
   const dim3 grid(sp.dn_grid);
   const int lpr = sp.dn.lpr, tiles = sp.dn_tiles;
 #define MOE_DN(BPL, MT)                                                                        \
   small_down_kernel<BPL, MT, down_slots(BPL), down_ring(BPL), 4 * dn_waves(BPL, MT)>           \
       <<<grid, 256 * dn_waves(BPL, MT), 0, stream>>>(r.counts, r.offsets, list, list_count, H, I, \
-                                                     tiles, sp.weighted, w2_q, w2_s, lpr, h, y)
+                                                     tiles, sp.weighted, w2_q, w2_s, lpr, h_hi, h_lo, y)
   switch (sp.dn.bpl) {
     case 1:
       if (sp.mt_dn == 2) MOE_DN(1, 2); else MOE_DN(1, 1);

@@ -42,6 +42,8 @@ struct RowSplit {
 
 RowSplit choose_row_split(int K);
 
+// h travels between the gate_up and down kernels as two bf16 planes [P, I] (rows in sorted order):
+// hi = bf16(h), lo = bf16(h - hi); the MFMA down kernels use them directly as operands.
 // Weight-streaming kernels for experts with at most `small_m_max` rows. They work through the
 // experts of `list` (the first *list_count entries; the active list, or the schedule's small list).
 enum SmallGateUpMode { kGateUpFused = 0, kGateOnly = 1, kUpWithGate = 2 };
@@ -61,12 +63,14 @@ SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus);
 
 hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32_t* list,
                                const int32_t* list_count, int H, int I, const uint8_t* w13_q,
-                               const uint8_t* w13_s, float clamp, int mode, float* h, float* g_ws,
+                               const uint8_t* w13_s, float clamp, int mode, uint16_t* h_hi,
+                               uint16_t* h_lo, float* g_ws,
                                hipStream_t stream);
 
 hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t* list,
                              const int32_t* list_count, int H, int I, const uint8_t* w2_q,
-                             const uint8_t* w2_s, const float* h, float* y, hipStream_t stream);
+                             const uint8_t* w2_s, const uint16_t* h_hi, const uint16_t* h_lo, float* y,
+                             hipStream_t stream);
 
 // bf16-MFMA kernels for experts with more than `small_m_max` rows: tiles of up to 64 rows of one
 // expert; the weight rows are decoded from MXFP4 to bf16 in registers, the activation tile is staged
@@ -92,11 +96,12 @@ hipError_t launch_schedule(const Routed& r, int E, int small_m_max, int tile_slo
 
 hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int I,
                                const uint8_t* w13_q, const uint8_t* w13_s, const int32_t* tile_e,
-                               const int32_t* tile_m0, float clamp, float* h, hipStream_t stream);
+                               const int32_t* tile_m0, float clamp, uint16_t* h_hi, uint16_t* h_lo,
+                               hipStream_t stream);
 
 hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
-                             const float* h, float* y, hipStream_t stream);
+                             const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream);
 
 // Dense bf16-MFMA kernels for experts with at least kDenseMinRows rows: 256-row tiles, both operands
 // staged in LDS, weights decoded once per workgroup.
@@ -114,11 +119,11 @@ DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min);
 
 hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w13_q,
                                const uint8_t* w13_s, const int32_t* dense_e, const int32_t* dense_m0,
-                               float clamp, float* h, hipStream_t stream);
+                               float clamp, uint16_t* h_hi, uint16_t* h_lo, hipStream_t stream);
 
 hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
-                             const float* h, float* y, hipStream_t stream);
+                             const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream);
 
 // out[t] = bf16(sum_j topk_w[t, j] * y[pair_pos[t*k + j]])
 hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* pair_pos, int T, int H,
