@@ -92,27 +92,36 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
   if (lane == 0) *n_small = ns;
 }
 
-// Ring depth (K-steps of loads in flight) by tile height: the fewer MFMAs a step holds, the more
-// steps must be in flight to cover the memory latency with one workgroup per CU.
-constexpr int ring_depth(bool gateup, int msub) {
-  return gateup ? (msub <= 2 ? 3 : 2) : (msub == 1 ? 3 : msub <= 3 ? 2 : 1);
-}
+// Ring depth, in super-steps of two K-steps, by tile height: the fewer MFMAs a step holds, the more
+// steps must be in flight to cover the memory latency with one workgroup per CU (as deep as the
+// register file allows at two waves per SIMD).
+constexpr int ring_depth(bool gateup, int msub) { return msub <= 2 ? 2 : 1; }
 
 constexpr int kNW = 8;           // waves per workgroup (2 per SIMD)
 constexpr int kThreads = 64 * kNW;
+
+// Per-wave LDS buffer of one super-step's weights: CB column blocks x 16 rows x 128 bytes of codes
+// (8 MX blocks), then CB x 16 rows x 8 scale bytes.
+template <int CB>
+constexpr int wave_buf_bytes() { return CB * 2048 + CB * 128; }
 
 // One (expert, row tile) x column block, with MSUB blocks of 16 rows fixed at compile time so the
 // step is straight-line code (no per-row-block branches between MFMAs).
 // Staging: gate_up stages MSUB*16 rows x 128 bf16 of gathered x per K-step (16-byte chunks, spread
 // over the workgroup's threads; rows past the tile repeat its last row); down stages MSUB*16 rows x
 // 128 of both bf16 planes of h (hi, lo) into two LDS tiles.
+// Weights: the 16 weight rows of a column block are loaded per super-step (two K-steps, 8 MX blocks)
+// as two 1 KB reads of 8 rows x 128 contiguous bytes (lane l: row 8h + l/8, block l%8), so every
+// load instruction covers 8 whole cache lines; at use the wave passes them through its own LDS
+// buffer into the MFMA lane layout (lane: row j16, block 4*step + g). Only the wave itself reads its
+// buffer, so this needs no barrier.
 template <bool GATEUP, int MSUB, int CB>
 __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const uint8_t* __restrict__ qe,
                                            const uint8_t* __restrict__ se, int e, int m0, int xblk,
                                            float clamp, const uint16_t* __restrict__ h_hi_in,
                                            const uint16_t* __restrict__ h_lo_in,
                                            uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
-                                           float* __restrict__ y_out, uint8_t* lds_a) {
+                                           float* __restrict__ y_out, uint8_t* lds_a, uint8_t* lds_w) {
   constexpr int D = ring_depth(GATEUP, MSUB);
   constexpr int kATiles = GATEUP ? 1 : 2;  // bf16 x, or bf16 hi + lo of h
   constexpr int kTileBytes = kTileM * kLdsRow;
@@ -131,27 +140,29 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
   const int j16 = lane & 15;  // MFMA column (weight row) / A row within a 16-block
   const int g = lane >> 4;    // K group: this lane's block within a step is 4*step + g
 
-  // weight rows of this wave's CB column blocks (gate_up: CB/2 gate blocks, then the matching up
-  // blocks), the per-lane part of their addresses, and whether the column exists
+  // weight row (within the expert) of row j (0..15) of column block cb (gate_up: CB/2 gate blocks,
+  // then the matching up blocks), and the column it gives; columns past the end are clamped
+  auto col_of = [&](int cb, int j) {
+    return GATEUP ? xblk * (kNW * 8 * CB) + wave * (8 * CB) + (cb % (CB / 2)) * 16 + j
+                  : xblk * (kNW * 16 * CB) + wave * (16 * CB) + cb * 16 + j;
+  };
+  auto wrow_of = [&](int cb, int j) {
+    const int c = col_of(cb, j);
+    return GATEUP ? ((cb < CB / 2) ? min(c, I - 1) : I + min(c, I - 1)) : min(c, H - 1);
+  };
   int col[CB];
   bool cval[CB];
-  uint32_t bq[CB], bs[CB];  // byte offset of the weight row's codes and scales
+  uint32_t cq[CB][2], cs[CB][2];  // offsets of the rows this lane loads (coalesced pattern)
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    int wrow;
-    if (GATEUP) {
-      const int gc = xblk * (kNW * 8 * CB) + wave * (8 * CB) + (cb % (CB / 2)) * 16 + j16;
-      col[cb] = gc;
-      cval[cb] = gc < I;
-      wrow = (cb < CB / 2) ? min(gc, I - 1) : I + min(gc, I - 1);
-    } else {
-      const int c = xblk * (kNW * 16 * CB) + wave * (16 * CB) + cb * 16 + j16;
-      col[cb] = c;
-      cval[cb] = c < H;
-      wrow = min(c, H - 1);
+    col[cb] = col_of(cb, j16);
+    cval[cb] = col[cb] < (GATEUP ? I : H);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t wrow = (uint32_t)wrow_of(cb, 8 * h + (lane >> 3));
+      cq[cb][h] = wrow * qrow;
+      cs[cb][h] = wrow * srow;
     }
-    bq[cb] = (uint32_t)wrow * qrow;
-    bs[cb] = (uint32_t)wrow * srow;
   }
 
   // activation rows this thread stages (rows past the tile repeat its last row: their results
@@ -171,26 +182,31 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
   }
 
   const int nsteps = (NB + 3) >> 2;
-  // ring of D K-steps of loads in flight: weight blocks, scale bytes, activation slices
-  uint4 rb[D][CB];
-  uint32_t rs[D][CB];
-  uint4 ra[D][NA];
+  const int nss = (nsteps + 1) >> 1;  // super-steps
+  // ring of D super-steps of loads in flight: weight blocks, scale bytes, activation slices
+  uint4 rb[D][CB][2];
+  uint32_t rs[D][CB][2];
+  uint4 ra[D][2][NA];
 
-  // issue every load of step `step` into ring slot `slot`. Block and element indices are clamped
+  // issue every load of super-step ss into ring slot `slot`. Block and element indices are clamped
   // into the row: a partial last step re-reads in-bounds data that is masked at use, and the steps
   // past the end re-read the last step (L2 hits spread over the channels; no branch around the loads).
-  auto issue = [&](int slot, int step) {
-    const uint32_t blk = (uint32_t)min(step * 4 + g, NB - 1);
+  auto issue = [&](int slot, int ss) {
+    const uint32_t blk = (uint32_t)min(ss * 8 + (lane & 7), NB - 1);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      rb[slot][cb] = ld16(qe, bq[cb] + blk * 16);
-      rs[slot][cb] = ld8(se, bs[cb] + blk);
-    }
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const uint32_t el = (uint32_t)min(step * 128 + (tid & 15) * 8, K - 8);
-      ra[slot][i] = ld16(arow[i], el * 2);
-    }
+      for (int h = 0; h < 2; ++h) {
+        rb[slot][cb][h] = ld16(qe, cq[cb][h] + blk * 16);
+        rs[slot][cb][h] = ld8(se, cs[cb][h] + blk);
+      }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const uint32_t el = (uint32_t)min((2 * ss + st) * 128 + (tid & 15) * 8, K - 8);
+        ra[slot][st][i] = ld16(arow[i], el * 2);
+      }
   };
 
   f32x4_t acc[MSUB][CB];
@@ -202,27 +218,42 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
 
-  auto step_body = [&](int slot, int step) {
+  // this wave's buffer: row r of column block cb at cb*2048 + r*128, its 16-byte chunk c at position
+  // c ^ (r % 8) (the 8 lanes writing a row, and the 8 lanes reading one chunk of 8 rows, hit
+  // distinct banks); scale bytes at CB*2048 + cb*128 + r*8 + block
+  uint8_t* wbuf = lds_w + wave * wave_buf_bytes<CB>();
+
+  auto step_body = [&](int slot, int step, int st) {
     uint8_t* lb = lds_a + (step & 1) * (kATiles * kTileBytes);
-    // the oldest ring slot: its activation slice goes to LDS (zero past K), visible after the barrier
+    // the step's activation slice goes to LDS (zero past K), visible after the barrier
     const bool k_tail = (step * 4 + 4) > NB;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       if (GATEUP) {
         const int ch = tid + kThreads * i;
         const int lr = ch >> 4, c16 = ch & 15;
-        uint4 v = ra[slot][i];
+        uint4 v = ra[slot][st][i];
         if (k_tail && step * 128 + c16 * 8 >= K) v = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(lb + lr * kLdsRow + c16 * 16) = v;
       } else {
         const int ch = tid + kThreads * i;
         const int lr = ch >> 5, pl = (ch >> 4) & 1, c16 = ch & 15;
-        uint4 v = ra[slot][i];
+        uint4 v = ra[slot][st][i];
         if (k_tail && step * 128 + c16 * 8 >= K) v = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(lb + pl * kTileBytes + lr * kLdsRow + c16 * 16) = v;
       }
     }
     __syncthreads();
+    // this lane's weight block of the step (row j16, block 4*st + g) from the wave's buffer
+    uint4 wb[CB];
+    float scale[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = 4 * st + g;
+      wb[cb] = *reinterpret_cast<const uint4*>(wbuf + cb * 2048 + j16 * 128 + ((c ^ (j16 & 7)) << 4));
+      const bool ok = cval[cb] && step * 4 + g < NB;
+      scale[cb] = ok ? e8m0_to_float(wbuf[CB * 2048 + cb * 128 + j16 * 8 + c]) : 0.0f;
+    }
     // decode the weight blocks straight into MFMA B operands (operand s = elements 8s..8s+7)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -235,13 +266,11 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
                                                             (ms * 16 + j16) * kLdsRow + g * 64 + s * 16);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const bool ok = cval[cb] && step * 4 + g < NB;
-        const float scale = ok ? e8m0_to_float(rs[slot][cb]) : 0.0f;
-        const uint32_t wd = s == 0 ? rb[slot][cb].x : s == 1 ? rb[slot][cb].y : s == 2 ? rb[slot][cb].z : rb[slot][cb].w;
-        const bf16x2_t p0 = fp4x2_to_bf16x2<0>(wd, scale);
-        const bf16x2_t p1 = fp4x2_to_bf16x2<1>(wd, scale);
-        const bf16x2_t p2 = fp4x2_to_bf16x2<2>(wd, scale);
-        const bf16x2_t p3 = fp4x2_to_bf16x2<3>(wd, scale);
+        const uint32_t wd = s == 0 ? wb[cb].x : s == 1 ? wb[cb].y : s == 2 ? wb[cb].z : wb[cb].w;
+        const bf16x2_t p0 = fp4x2_to_bf16x2<0>(wd, scale[cb]);
+        const bf16x2_t p1 = fp4x2_to_bf16x2<1>(wd, scale[cb]);
+        const bf16x2_t p2 = fp4x2_to_bf16x2<2>(wd, scale[cb]);
+        const bf16x2_t p3 = fp4x2_to_bf16x2<3>(wd, scale[cb]);
         const bf16x8_t bop = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 #pragma unroll
         for (int ms = 0; ms < MSUB; ++ms)
@@ -253,18 +282,33 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
       // decodes ahead would hold 16 more B operands live and spill at two waves per SIMD)
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the slot's registers are consumed: refill it with step + D
-    issue(slot, step + D);
   };
 
-  int step = 0;
-  for (; step + D <= nsteps; step += D) {
+  auto super_step = [&](int slot, int ss) {
+    // the super-step's weights -> this wave's buffer (the wave finished reading the previous
+    // super-step's; its LDS operations complete in order)
 #pragma unroll
-    for (int d = 0; d < D; ++d) step_body(d, step + d);
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rr = 8 * h + (lane >> 3), c = lane & 7;
+        *reinterpret_cast<uint4*>(wbuf + cb * 2048 + rr * 128 + ((c ^ (rr & 7)) << 4)) = rb[slot][cb][h];
+        wbuf[CB * 2048 + cb * 128 + rr * 8 + c] = (uint8_t)rs[slot][cb][h];
+      }
+    step_body(slot, 2 * ss, 0);
+    step_body(slot, 2 * ss + 1, 1);
+    // the slot's registers are consumed: refill it with super-step ss + D
+    issue(slot, ss + D);
+  };
+
+  // the super-step count is padded to a multiple of D (padding steps see zero activations and zero
+  // scales): a conditional tail would merge into the loop's control flow and make the compiler
+  // count the newest ring slot's loads as needed by the oldest one
+  const int nss_pad = (nss + D - 1) / D * D;
+  for (int ss = 0; ss < nss_pad; ss += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) super_step(d, ss + d);
   }
-#pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (step + d < nsteps) step_body(d, step + d);
 
   // epilogue: lane holds rows 4*g + i (i < 4) of each 16-row block, column j16 of each block
 #pragma unroll
@@ -314,6 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void large_kernel(Routed r, int H, int
   constexpr int kATiles = GATEUP ? 1 : 2;
   // two LDS buffers (double-buffered across K-steps), each kATiles tiles
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kATiles * kTileM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w[kNW * wave_buf_bytes<CB>()];
 
   const int b = blockIdx.x;
   const int j = b >> 3;
@@ -332,7 +377,8 @@ __global__ __launch_bounds__(kThreads, 1) void large_kernel(Routed r, int H, int
   const uint8_t* qe = wq_all + (size_t)e * nrows_w * (size_t)(K >> 1);
   const uint8_t* se = ws_all + (size_t)e * nrows_w * (size_t)(K >> 5);
 #define MOE_TILE(MS) \
-  large_tile<GATEUP, MS, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_hi_in, h_lo_in, h_hi, h_lo, y_out, lds_a)
+  large_tile<GATEUP, MS, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_hi_in, h_lo_in, h_hi, h_lo, y_out, lds_a, \
+                             lds_w)
   switch (msub_n) {
     case 1: MOE_TILE(1); break;
     case 2: MOE_TILE(2); break;
