@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
 // Ring depth, in super-steps of two K-steps, by tile height: the fewer MFMAs a step holds, the more
 // steps must be in flight to cover the memory latency with one workgroup per CU (as deep as the
 // register file allows at two waves per SIMD).
-constexpr int ring_depth(bool gateup, int msub) { return msub <= 2 ? 2 : 1; }
+constexpr int ring_depth(bool gateup, int msub) { return msub <= 3 ? 2 : 1; }
 
 constexpr int kNW = 8;           // waves per workgroup (2 per SIMD)
 constexpr int kThreads = 64 * kNW;
