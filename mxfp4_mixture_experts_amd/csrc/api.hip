@@ -42,7 +42,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
-  size_t h, g_f32, y, sched, total;
+  size_t h, rexp, g_f32, y, sched, total;
   int tile_slots_max, dense_slots_max;
 };
 
@@ -60,6 +60,9 @@ WsLayout ws_layout(long P, int H, int I, int E, int k, int flags) {
   // h as two bf16 planes [P, I] (hi, then lo)
   w.h = off;
   off = align_up(off + (size_t)P * I * 2 * sizeof(uint16_t));
+  // per h row, the biased exponent of the largest |hi| of each 64-column segment (dense kernels)
+  w.rexp = off;
+  off = align_up(off + (size_t)P * moe::dense_row_segments(I));
   w.g_f32 = off;
   if (flags & MOE_UNFUSED_GATE_UP) off = align_up(off + (size_t)P * I * sizeof(float));
   w.y = off;
@@ -233,6 +236,7 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   char* ws = (char*)workspace;
   uint16_t* h_hi = (uint16_t*)(ws + wl.h);
   uint16_t* h_lo = h_hi + (size_t)T * k * I;
+  uint8_t* rexp = (uint8_t*)(ws + wl.rexp);
   float* g_f32 = (float*)(ws + wl.g_f32);
   float* y = (float*)(ws + wl.y);
 
@@ -273,8 +277,8 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
     ok &= moe::launch_large_gateup(lp, r, H, I, w13_q, w13_s, tile_e, tile_m0, clamp_limit, h_hi, h_lo, s) ==
           hipSuccess;
   if (dense)
-    ok &= moe::launch_dense_gateup(dp, r, H, I, w13_q, w13_s, dense_e, dense_m0, clamp_limit, h_hi, h_lo, s) ==
-          hipSuccess;
+    ok &= moe::launch_dense_gateup(dp, r, H, I, w13_q, w13_s, dense_e, dense_m0, clamp_limit, h_hi, h_lo,
+                                   rexp, s) == hipSuccess;
   record(MOE_STAGE_GATE_UP, false, s);
 
   record(MOE_STAGE_DOWN, true, s);
@@ -283,7 +287,8 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   if (plan.launch_large)
     ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, tile_e, tile_m0, h_hi, h_lo, y, s) == hipSuccess;
   if (dense)
-    ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, h_lo, y, s) == hipSuccess;
+    ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, h_lo, rexp, y, s) ==
+          hipSuccess;
   record(MOE_STAGE_DOWN, false, s);
 
   record(MOE_STAGE_COMBINE, true, s);

@@ -10,6 +10,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -29,11 +30,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // h of a routed pair as two bfloat16 planes: hi = bf16(v), lo = bf16(v - hi). hi + lo is exact in
-// fp32 and equals v to about 2^-17 relative.
-__device__ __forceinline__ void store_h_planes(uint16_t* hi, uint16_t* lo, size_t o, float v) {
+// fp32 and equals v to about 2^-17 relative. Returns the hi bits.
+__device__ __forceinline__ uint16_t store_h_planes(uint16_t* hi, uint16_t* lo, size_t o, float v) {
   const uint16_t h = f32_to_bf16_rne(v);
   hi[o] = h;
   lo[o] = f32_to_bf16_rne(v - __builtin_bit_cast(float, (uint32_t)h << 16));
+  return h;
 }
 
 // The two bf16 halves of a dword as floats (element 0 in the low half).
@@ -60,6 +62,13 @@ __device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w, float scale) {
 template <int sel>
 __device__ __forceinline__ f16x2_t fp4x2_to_f16x2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, sel);
+}
+
+// Two E2M1 codes (byte `sel` of `w`) times `scale` -> two fp16 (nearest-even; the even element in
+// the low half). Exact while the results are fp16 normals or multiples of 2^-24 below 65504.
+template <int sel>
+__device__ __forceinline__ f16x2_t fp4x2_to_f16x2_scaled(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, sel);
 }
 
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }

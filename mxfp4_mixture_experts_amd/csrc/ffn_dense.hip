@@ -1,23 +1,35 @@
-// Dense bf16-MFMA MXFP4 expert GEMMs for experts with hundreds of routed rows (compute-bound).
+// Dense MFMA MXFP4 expert GEMMs for experts with hundreds of routed rows (compute-bound).
 //
-// With M in the hundreds per expert the expert GEMMs are compute-bound (the M=1024 MFMA target of
-// the layer), and what limits the row-tile kernels there is the FP4 decode: each wave decodes its
-// own weight columns, one conversion per MFMA. Here a workgroup stages both operands of a K-step in
-// LDS and the weights are decoded once per workgroup:
+// With M in the hundreds per expert the expert GEMMs are compute-bound, and what limits the row-tile
+// kernels there is the FP4 decode: each wave decodes its own weight columns, one conversion per
+// MFMA. Here a workgroup stages both operands of a K-step in LDS and the weights are decoded once per
+// workgroup:
 //   - a workgroup owns 256 rows of one expert x 256 weight rows (gate_up: 128 gate columns and the
 //     matching 128 up columns; down: 256 output columns); its eight waves (two per SIMD) each
-//     compute 64 rows x 128 weight rows with v_mfma_f32_16x16x32_bf16 (32 accumulator blocks);
-//   - per K-step every thread loads 16-byte chunks of the activation rows (gathered x rows for
-//     gate_up; for down, h rows of both of its bf16 planes, hi and lo) and one MX block of one
-//     weight row (16 bytes of E2M1 codes + the E8M0 scale), decodes the block exactly to 32 bf16
-//     with the scaled FP4 conversion and writes both to LDS; the loads of the next K-steps are in
-//     flight in registers meanwhile;
+//     compute 64 rows x 128 weight rows with 16x16x32 MFMAs (32 accumulator blocks);
+//   - per K-step of 64 every thread loads 16-byte chunks of the activation rows and one MX block of
+//     one weight row (16 bytes of E2M1 codes + the E8M0 scale), decodes the block exactly with the
+//     scaled FP4 conversion and writes both to LDS; the loads of the next K-step are in flight in
+//     registers meanwhile;
 //   - LDS rows are padded to 16 bytes past a multiple of 64 so the MFMA operand reads (16 rows x
 //     16 bytes per lane group) hit 64 distinct banks; two LDS buffers alternate, one barrier per
-//     K-step;
-//   - gate columns and the matching up columns land in the same lanes of a wave, so the
-//     clamp-SwiGLU epilogue runs in registers; down adds the hi and lo products (two MFMAs per A
-//     operand), as the row-tile kernels do.
+//     K-step.
+// gate_up multiplies bf16 x with bf16 weights (E2M1 x E8M0 is exact in bf16). Gate columns and the
+// matching up columns land in the same lanes of a wave, so the clamp-SwiGLU epilogue runs in
+// registers; it writes h as its two bf16 planes and, per row and 64-column segment, the biased
+// exponent of the largest |hi| (no atomics: each segment has one writer).
+// down runs one fp16 MFMA per operand pair instead of one bf16 MFMA per h plane:
+//   - each h row is rebuilt as hi + lo (exact in fp32) and scaled by a power of two chosen from the
+//     row's largest |hi| (the maximum of its segment exponents) so that its largest magnitude lands
+//     in [2^14, 2^15), then rounded to fp16: 11 significant bits per value, as in the weight-
+//     streaming down kernel, and no overflow since |hi + lo| <= |hi| (1 + 2^-8);
+//   - each weight column (output column) is decoded as code x 2^(s - c + 13) in fp16, with c the
+//     largest scale byte of that column: the largest block reaches at most 6 x 2^13, and every
+//     block whose scale byte is within 36 of the column's largest is exact;
+//   - the epilogue multiplies the fp32 sum by 2^((127 - f) + (c - 140)) with one ldexp, which
+//     undoes both scalings exactly (within fp32 range).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,21 +50,51 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* base, uint32_t off) {
 }
 __device__ __forceinline__ uint32_t ld8(const uint8_t* base, uint32_t off) { return base[off]; }
 
+__device__ __forceinline__ uint32_t max_byte4(uint32_t w) {
+  return max(max(w & 0xFFu, (w >> 8) & 0xFFu), max((w >> 16) & 0xFFu, w >> 24));
+}
+
+// Largest of n bytes at p: 16-byte loads when `vec` (p 16-byte aligned, n a multiple of 16).
+__device__ __forceinline__ uint32_t max_bytes(const uint8_t* p, int n, bool vec) {
+  uint32_t m = 0;
+  if (vec) {
+    for (int j = 0; j < n; j += 16) {
+      const uint4 v = ld16(p, (uint32_t)j);
+      m = max(m, max(max(max_byte4(v.x), max_byte4(v.y)), max(max_byte4(v.z), max_byte4(v.w))));
+    }
+  } else {
+    for (int j = 0; j < n; ++j) m = max(m, ld8(p, (uint32_t)j));
+  }
+  return m;
+}
+
+// v and its rotations within each 16-lane row: every lane ends with its row's maximum.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));  // row_ror:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));  // row_ror:1
+  return v;
+}
+
 template <bool GATEUP>
 struct DenseShape {
-  static constexpr int kBK = GATEUP ? 64 : 32;          // K elements per step (MX blocks x 32)
+  static constexpr int kBK = 64;                        // K elements per step (two MX blocks)
   static constexpr int kBlocks = kBK / 32;              // MX blocks per weight row and step
-  static constexpr int kATiles = GATEUP ? 1 : 2;        // x, or h hi + lo
-  static constexpr int kRow = kBK * 2 + 16;             // LDS bytes per row (bf16 + padding)
+  static constexpr int kPlanes = GATEUP ? 1 : 2;        // global planes per activation: x, or hi + lo
+  static constexpr int kRow = kBK * 2 + 16;             // LDS bytes per row (16-bit values + padding)
   static constexpr int kATileBytes = kDM * kRow;
   static constexpr int kBTileBytes = kDN * kRow;
-  static constexpr int kStage = kATiles * kATileBytes + kBTileBytes;
-  // 16-byte global chunks per activation row and step (bf16 x: kBK*2 bytes; h: kBK*2 bytes of each
-  // plane), per thread and step, and weight-block chunks per thread and step
-  static constexpr int kCpr = kATiles * kBK * 2 / 16;
+  static constexpr int kStage = kATileBytes + kBTileBytes;
+  // LDS bytes past the two stages: down keeps the row and column exponents there
+  static constexpr int kExtra = GATEUP ? 0 : (kDM + kDN) * 4;
+  static constexpr int kLds = 2 * kStage + kExtra;
+  // 16-byte LDS chunks per activation row and step, per thread and step (each chunk is one global
+  // 16-byte load per plane), and weight-block chunks per thread and step
+  static constexpr int kCpr = kBK * 2 / 16;
   static constexpr int kAChunks = kDM * kCpr / kDThreads;
   static constexpr int kBChunks = (kDN * kBlocks + kDThreads - 1) / kDThreads;
-  static constexpr int kD = GATEUP ? 1 : 2;             // K-steps of loads in flight
+  static constexpr int kD = 1;                          // K-steps of loads in flight
 };
 
 // Weight row (within the expert) streamed as LDS B-tile row n of column tile xblk.
@@ -75,11 +117,16 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     int nx, int dense_slots, const uint8_t* __restrict__ wq_all, const uint8_t* __restrict__ ws_all,
     const int32_t* __restrict__ dense_e, const int32_t* __restrict__ dense_m0, float clamp,
     const uint16_t* __restrict__ h_hi_in, const uint16_t* __restrict__ h_lo_in,
-    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, float* __restrict__ y_out) {
+    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, uint8_t* __restrict__ rexp, int nseg,
+    float* __restrict__ y_out) {
   using S = DenseShape<GATEUP>;
+  using op_t = typename std::conditional<GATEUP, bf16x8_t, f16x8_t>::type;
   constexpr int D = S::kD;
   constexpr int NA = S::kAChunks;
+  constexpr int NP = S::kPlanes;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  int* s_rowe = reinterpret_cast<int*>(lds + 2 * S::kStage);  // down: 127 - f per tile row
+  int* s_colc = s_rowe + kDM;                                  // down: c per B-tile row
 
   // XCD-interleaved tile order (workgroup b runs on XCD b % 8): XCD x gets row tiles x, x + 8, ...
   // with all their column tiles back to back
@@ -113,21 +160,20 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   const int wc = wave / (kDW / 2);  // column group: B-tile rows wc*128 .. +128
 
   // ---- staging assignments
-  // activations: chunk c = tid + kDThreads * i covers 8 elements of row (c / kCpr): for down, of
-  // plane (c % kCpr) / (kBK / 8), for gate_up of x
+  // activations: chunk c = tid + kDThreads * i covers elements 8 (c % kCpr) .. +8 of row c / kCpr
+  // (of x for gate_up; of both h planes for down)
   constexpr int kCpr = S::kCpr;
-  constexpr int kCpp = S::kBK / 8;  // chunks per row and plane
-  const uint8_t* arow[NA];
+  const uint8_t* arow[NA][NP];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int c = tid + kDThreads * i;
     const int lr = min(c / kCpr, rows - 1);
     if (GATEUP) {
       const int t = sorted_pair[row0 + lr] / k;
-      arow[i] = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
+      arow[i][0] = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
     } else {
-      const uint16_t* plane = ((c % kCpr) / kCpp) ? h_lo_in : h_hi_in;
-      arow[i] = reinterpret_cast<const uint8_t*>(plane + (size_t)(row0 + lr) * I);
+      arow[i][0] = reinterpret_cast<const uint8_t*>(h_hi_in + (size_t)(row0 + lr) * I);
+      arow[i][NP - 1] = reinterpret_cast<const uint8_t*>(h_lo_in + (size_t)(row0 + lr) * I);
     }
   }
   // weights: chunk q = tid + kDThreads * j is block (q % kBlocks) of B-tile row (q / kBlocks)
@@ -143,7 +189,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     bs[jw] = wrow * srow;
   }
 
-  uint4 ra[D][NA];
+  uint4 ra[D][NA][NP];
   uint4 rb[D][NBW];
   uint32_t rs[D][NBW];
 
@@ -158,9 +204,10 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int c = tid + kDThreads * i;
-      const int el = st * S::kBK + (c % kCpp) * 8;  // first element of the chunk
+      const int el = st * S::kBK + (c % kCpr) * 8;  // first element of the chunk
       const int elc = min(el, K - 8);
-      ra[slot][i] = ld16(arow[i], (uint32_t)elc * 2);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) ra[slot][i][p] = ld16(arow[i][p], (uint32_t)elc * 2);
     }
   };
 
@@ -173,34 +220,91 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
 
+  // down: the row scales of this tile (from the segment exponents gate_up wrote) and the column
+  // shifts of this column tile; each staging thread keeps the scales of its activation rows
+  float asc[NA];
+  int ccol[NBW];
+  if (!GATEUP) {
+    if (tid < kDM) {
+      const int lr = min(tid, rows - 1);
+      const uint8_t* p = rexp + (size_t)(row0 + lr) * nseg;
+      const int eb = (int)max_bytes(p, nseg, (nseg & 15) == 0);  // biased exponent of max |hi|
+      const int f = min(max(268 - eb, 1), 253);                  // row scale 2^(f - 127)
+      s_rowe[tid] = 127 - f;
+    }
+    const bool svec = (NB & 15) == 0 && (reinterpret_cast<uintptr_t>(se) & 15) == 0;
+#pragma unroll
+    for (int jw = 0; jw < NBW; ++jw) {
+      ccol[jw] = (int)max_bytes(se + bs[jw], NB, svec);
+      if (tid + kDThreads * jw < kDN * S::kBlocks) s_colc[bn[jw]] = ccol[jw];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int lr = (tid + kDThreads * i) / kCpr;
+      asc[i] = __builtin_bit_cast(float, (uint32_t)(127 - s_rowe[lr]) << 23);
+    }
+  }
+
   auto step_body = [&](int slot, int step) {
     uint8_t* st_a = lds + (step & 1) * S::kStage;
-    uint8_t* st_b = st_a + S::kATiles * S::kATileBytes;
-    // activations of this step -> LDS (zero past K)
+    uint8_t* st_b = st_a + S::kATileBytes;
+    // activations of this step -> LDS (zero past K); down: hi + lo, scaled, as fp16
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int c = tid + kDThreads * i;
-      const int lr = c / kCpr, pl = (c % kCpr) / kCpp, cc = c % kCpp;
-      uint4 v = ra[slot][i];
+      const int lr = c / kCpr, cc = c % kCpr;
+      uint4 v;
+      if (GATEUP) {
+        v = ra[slot][i][0];
+      } else {
+        const uint4 hv = ra[slot][i][0], lv = ra[slot][i][NP - 1];
+        const uint32_t a[4] = {hv.x, hv.y, hv.z, hv.w};
+        const uint32_t l[4] = {lv.x, lv.y, lv.z, lv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v0 = bf16_lo_f32(a[j]) + bf16_lo_f32(l[j]);
+          const float v1 = bf16_hi_f32(a[j]) + bf16_hi_f32(l[j]);
+          o[j] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)(v0 * asc[i]), (_Float16)(v1 * asc[i])});
+        }
+        v = make_uint4(o[0], o[1], o[2], o[3]);
+      }
       if (step * S::kBK + cc * 8 >= K) v = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(st_a + pl * S::kATileBytes + lr * S::kRow + cc * 16) = v;
+      *reinterpret_cast<uint4*>(st_a + lr * S::kRow + cc * 16) = v;
     }
-    // weight blocks of this step -> 32 bf16 each in LDS (a zero scale past K)
+    // weight blocks of this step -> 32 16-bit values each in LDS (a zero scale past K): bf16 with
+    // the block scale for gate_up, fp16 with the block scale relative to the column's for down
 #pragma unroll
     for (int jw = 0; jw < NBW; ++jw) {
       if (tid + kDThreads * jw >= kDN * S::kBlocks) break;  // a repeated chunk: written by its owner
       const bool ok = step * S::kBlocks + bblk < NB;
-      const float scale = ok ? e8m0_to_float(rs[slot][jw]) : 0.0f;
       const uint32_t wd[4] = {rb[slot][jw].x, rb[slot][jw].y, rb[slot][jw].z, rb[slot][jw].w};
       uint8_t* dst = st_b + bn[jw] * S::kRow + bblk * 64;
+      if (GATEUP) {
+        const float scale = ok ? e8m0_to_float(rs[slot][jw]) : 0.0f;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x2_t p0 = fp4x2_to_bf16x2<0>(wd[d], scale);
-        const bf16x2_t p1 = fp4x2_to_bf16x2<1>(wd[d], scale);
-        const bf16x2_t p2 = fp4x2_to_bf16x2<2>(wd[d], scale);
-        const bf16x2_t p3 = fp4x2_to_bf16x2<3>(wd[d], scale);
-        *reinterpret_cast<bf16x8_t*>(dst + d * 16) =
-            bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        for (int d = 0; d < 4; ++d) {
+          const bf16x2_t p0 = fp4x2_to_bf16x2<0>(wd[d], scale);
+          const bf16x2_t p1 = fp4x2_to_bf16x2<1>(wd[d], scale);
+          const bf16x2_t p2 = fp4x2_to_bf16x2<2>(wd[d], scale);
+          const bf16x2_t p3 = fp4x2_to_bf16x2<3>(wd[d], scale);
+          *reinterpret_cast<bf16x8_t*>(dst + d * 16) =
+              bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+      } else {
+        // 2^(s - c + 13); blocks 140 or more below the column's largest scale byte decode to zero
+        const int ex = (int)rs[slot][jw] + 140 - ccol[jw];
+        const float scale = ok ? __builtin_bit_cast(float, (uint32_t)max(ex, 0) << 23) : 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const f16x2_t p0 = fp4x2_to_f16x2_scaled<0>(wd[d], scale);
+          const f16x2_t p1 = fp4x2_to_f16x2_scaled<1>(wd[d], scale);
+          const f16x2_t p2 = fp4x2_to_f16x2_scaled<2>(wd[d], scale);
+          const f16x2_t p3 = fp4x2_to_f16x2_scaled<3>(wd[d], scale);
+          *reinterpret_cast<f16x8_t*>(dst + d * 16) =
+              f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
       }
     }
     __syncthreads();
@@ -210,29 +314,26 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     // column blocks (lane: row / column j16, K elements 8g .. 8g+7 of the slice)
 #pragma unroll
     for (int kk = 0; kk < S::kBlocks; ++kk) {
-      bf16x8_t bop[8];
+      op_t bop[8];
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb)
-        bop[cb] = *reinterpret_cast<const bf16x8_t*>(st_b + (wc * 128 + cb * 16 + j16) * S::kRow + kk * 64 +
-                                                     g * 16);
+        bop[cb] = *reinterpret_cast<const op_t*>(st_b + (wc * 128 + cb * 16 + j16) * S::kRow + kk * 64 + g * 16);
       // A operands one row block ahead; the barrier keeps the compiler from hoisting every read of
       // the step (which would not fit next to the 256 accumulator registers)
-      auto read_a = [&](int ms, bf16x8_t (&a)[S::kATiles]) {
-#pragma unroll
-        for (int at = 0; at < S::kATiles; ++at)
-          a[at] = *reinterpret_cast<const bf16x8_t*>(st_a + at * S::kATileBytes +
-                                                     (wr * kWM + ms * 16 + j16) * S::kRow + kk * 64 + g * 16);
+      auto read_a = [&](int ms) {
+        return *reinterpret_cast<const op_t*>(st_a + (wr * kWM + ms * 16 + j16) * S::kRow + kk * 64 + g * 16);
       };
-      bf16x8_t aop[2][S::kATiles];
-      read_a(0, aop[0]);
+      op_t aop[2];
+      aop[0] = read_a(0);
 #pragma unroll
       for (int ms = 0; ms < kMS; ++ms) {
-        if (ms < kMS - 1) read_a(ms + 1, aop[(ms + 1) & 1]);
+        if (ms < kMS - 1) aop[(ms + 1) & 1] = read_a(ms + 1);
 #pragma unroll
-        for (int at = 0; at < S::kATiles; ++at) {
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb)
-            acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[ms & 1][at], bop[cb], acc[ms][cb], 0, 0, 0);
+        for (int cb = 0; cb < 8; ++cb) {
+          if constexpr (GATEUP)
+            acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[ms & 1], bop[cb], acc[ms][cb], 0, 0, 0);
+          else
+            acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[ms & 1], bop[cb], acc[ms][cb], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -248,14 +349,16 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   }
 
   // epilogue: lane holds rows 4g+i of each 16-row block, column j16 of each column block
+  if (GATEUP) {
+    uint32_t mx[kMS][4];  // largest |hi| bit pattern of the row over the wave's 64 columns
 #pragma unroll
-  for (int ms = 0; ms < kMS; ++ms) {
+    for (int ms = 0; ms < kMS; ++ms) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lr = wr * kWM + ms * 16 + g * 4 + i;
-      if (lr >= rows) continue;
-      const size_t orow = (size_t)(row0 + lr);
-      if (GATEUP) {
+      for (int i = 0; i < 4; ++i) {
+        mx[ms][i] = 0;
+        const int lr = wr * kWM + ms * 16 + g * 4 + i;
+        if (lr >= rows) continue;
+        const size_t orow = (size_t)(row0 + lr);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const int col = xblk * 128 + wc * 64 + cb * 16 + j16;
@@ -266,13 +369,37 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
             gv = clampf(gv, clamp);
             uv = clampf(uv, clamp);
           }
-          store_h_planes(h_hi, h_lo, orow * I + col, silu_mul(gv, uv));
+          const uint16_t hb = store_h_planes(h_hi, h_lo, orow * I + col, silu_mul(gv, uv));
+          mx[ms][i] = max(mx[ms][i], (uint32_t)(hb & 0x7FFFu));
         }
-      } else {
+      }
+    }
+    // one byte per row and segment: the biased exponent of the segment's largest |hi|
+#pragma unroll
+    for (int ms = 0; ms < kMS; ++ms) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t m = row16_max(mx[ms][i]);
+        const int lr = wr * kWM + ms * 16 + g * 4 + i;
+        if (j16 == 0 && lr < rows) rexp[(size_t)(row0 + lr) * nseg + xblk * 2 + wc] = (uint8_t)(m >> 7);
+      }
+    }
+  } else {
+    int ecol[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) ecol[cb] = s_colc[wc * 128 + cb * 16 + j16] - 140;
+#pragma unroll
+    for (int ms = 0; ms < kMS; ++ms) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lr = wr * kWM + ms * 16 + g * 4 + i;
+        if (lr >= rows) continue;
+        const size_t orow = (size_t)(row0 + lr);
+        const int erow = s_rowe[lr];
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
           const int col = xblk * kDN + wc * 128 + cb * 16 + j16;
-          if (col < N) y_out[orow * H + col] = acc[ms][cb][i];
+          if (col < N) y_out[orow * H + col] = __builtin_amdgcn_ldexpf(acc[ms][cb][i], erow + ecol[cb]);
         }
       }
     }
@@ -289,6 +416,9 @@ int dense_slots_bound(int T, int E, int k, int dense_m_min) {
   return (int)((P + kDM - 1) / kDM + n_dense);
 }
 
+// gate_up column tiles are 128 h columns, two 64-column segments (one per wave column group)
+int dense_row_segments(int I) { return 2 * ((I + 127) / 128); }
+
 DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min) {
   DensePlan dp;
   dp.tile_m = kDM;
@@ -303,31 +433,33 @@ DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min) {
 
 hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w13_q,
                                const uint8_t* w13_s, const int32_t* dense_e, const int32_t* dense_m0,
-                               float clamp, uint16_t* h_hi, uint16_t* h_lo, hipStream_t stream) {
+                               float clamp, uint16_t* h_hi, uint16_t* h_lo, uint8_t* rexp,
+                               hipStream_t stream) {
   if (dp.slots <= 0) return hipSuccess;
-  constexpr int lds = 2 * DenseShape<true>::kStage;
+  constexpr int lds = DenseShape<true>::kLds;
   static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<true>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    lds) == hipSuccess;
   (void)attr_set;
   dense_kernel<true><<<dp.gu_blocks, kDThreads, lds, stream>>>(
       r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.gu_grid_x, dp.slots, w13_q, w13_s, dense_e,
-      dense_m0, clamp, nullptr, nullptr, h_hi, h_lo, nullptr);
+      dense_m0, clamp, nullptr, nullptr, h_hi, h_lo, rexp, dense_row_segments(I), nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
-                             const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream) {
+                             const uint16_t* h_hi, const uint16_t* h_lo, const uint8_t* rexp, float* y,
+                             hipStream_t stream) {
   if (dp.slots <= 0) return hipSuccess;
-  constexpr int lds = 2 * DenseShape<false>::kStage;
+  constexpr int lds = DenseShape<false>::kLds;
   static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<false>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    lds) == hipSuccess;
   (void)attr_set;
   dense_kernel<false><<<dp.dn_blocks, kDThreads, lds, stream>>>(
       r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.dn_grid_x, dp.slots, w2_q, w2_s, dense_e,
-      dense_m0, 0.0f, h_hi, h_lo, nullptr, nullptr, y);
+      dense_m0, 0.0f, h_hi, h_lo, nullptr, nullptr, const_cast<uint8_t*>(rexp), dense_row_segments(I), y);
   return hipGetLastError();
 }
 

@@ -103,8 +103,10 @@ hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I,
                              const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
                              const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream);
 
-// Dense bf16-MFMA kernels for experts with at least kDenseMinRows rows: 256-row tiles, both operands
-// staged in LDS, weights decoded once per workgroup.
+// Dense MFMA kernels for experts with at least kDenseMinRows rows: 256-row tiles, both operands
+// staged in LDS, weights decoded once per workgroup. gate_up also writes, per h row, one byte per
+// 64-column segment (dense_row_segments(I) of them): the biased exponent of the segment's largest
+// |hi|; down reads them to scale its rows into fp16.
 constexpr int kDenseMinRows = 256;
 
 struct DensePlan {
@@ -116,14 +118,17 @@ struct DensePlan {
 
 int dense_slots_bound(int T, int E, int k, int dense_m_min);
 DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min);
+int dense_row_segments(int I);
 
 hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w13_q,
                                const uint8_t* w13_s, const int32_t* dense_e, const int32_t* dense_m0,
-                               float clamp, uint16_t* h_hi, uint16_t* h_lo, hipStream_t stream);
+                               float clamp, uint16_t* h_hi, uint16_t* h_lo, uint8_t* rexp,
+                               hipStream_t stream);
 
 hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
-                             const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream);
+                             const uint16_t* h_hi, const uint16_t* h_lo, const uint8_t* rexp, float* y,
+                             hipStream_t stream);
 
 // out[t] = bf16(sum_j topk_w[t, j] * y[pair_pos[t*k + j]])
 hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* pair_pos, int T, int H,

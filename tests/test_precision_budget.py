@@ -9,7 +9,13 @@ accumulation) and applies the block's E8M0 scale and the inverse power of two to
 These tests re-run the layer in float64 with h passed through that format (and, for comparison,
 through a single bf16 rounding) and measure the output against the exact layer with the same
 metrics the GPU parity tests use: the fp16 block format keeps the error far below the parity bar,
-a plain bf16 h would not. The GPU parity tests check the kernels themselves.
+a plain bf16 h would not.
+
+The dense (MFMA) down kernel uses one fp16 MFMA per operand pair: each h row is rebuilt as hi + lo,
+scaled by one power of two per row chosen from the row's largest |hi|, and rounded to fp16; each
+weight column is decoded in fp16 as code x 2^(s - c + 13), c the column's largest scale byte, and
+the fp32 sum is multiplied back by 2^(127 - f + c - 140). The same kind of test covers that format.
+The GPU parity tests check the kernels themselves.
 """
 import numpy as np
 import pytest
@@ -39,7 +45,34 @@ def f16_block(h):
     return (scaled.astype(np.float16).astype(np.float64) / sc).reshape(h.shape)
 
 
-def layer(cfg, inp, h_format=None):
+def f16_row(h):
+    """h through the dense down kernel's format: hi + lo as above, one scale 2^(f-127) per row with
+    f = clamp(268 - biased_exponent(max|hi| over the row), 1, 253), fp16 (nearest even), unscaled."""
+    h32 = np.asarray(h, np.float64).astype(np.float32)
+    hi = rne_bf16(h32).astype(np.float32)
+    lo = rne_bf16((h32 - hi).astype(np.float32)).astype(np.float32)
+    v = hi + lo
+    mx = np.abs(hi).max(axis=1, keepdims=True).astype(np.float32)
+    eb = ((mx.view(np.uint32) >> 23) & 0xFF).astype(np.int64)
+    f = np.clip(268 - eb, 1, 253)
+    sc = np.ldexp(1.0, f - 127)
+    scaled = v * sc.astype(np.float32)
+    assert np.all(np.abs(scaled) < 2.0 ** 15 * (1 + 2.0 ** -8))
+    return scaled.astype(np.float16).astype(np.float64) / sc
+
+
+def w2_f16_columns(q, s):
+    """One expert's down weights [H, I] as the dense down kernel decodes them: per output column
+    c = its largest scale byte, each element code * 2^(s - c + 13) rounded to fp16 (a scale factor of
+    2^(s - c + 13) below 2^-126 is zero), times 2^(c - 140)."""
+    codes = dequant(q, np.full_like(s, 127))  # E2M1 values, unscaled
+    c = s.max(axis=1, keepdims=True).astype(np.int64)
+    ex = np.repeat(s.astype(np.int64), 32, axis=1) - c + 13
+    fac = np.where(ex >= -126, np.ldexp(1.0, np.maximum(ex, -126)), 0.0)
+    return (codes * fac).astype(np.float16).astype(np.float64) * np.ldexp(1.0, c - 140)
+
+
+def layer(cfg, inp, h_format=None, w2_format=None):
     T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
     logits = inp["logits"].astype(np.float64)
     ids = np.argsort(-inp["logits"], axis=1, kind="stable")[:, :k]
@@ -54,7 +87,7 @@ def layer(cfg, inp, h_format=None):
     for e in np.unique(ids):
         rows = np.argwhere(ids == e)
         w13 = dequant(inp["w13_q"][e], inp["w13_s"][e])
-        w2 = dequant(inp["w2_q"][e], inp["w2_s"][e])
+        w2 = (w2_format or dequant)(inp["w2_q"][e], inp["w2_s"][e])
         gu = x[rows[:, 0]] @ w13.T
         g, u = gu[:, :I], gu[:, I:]
         if cfg.clamp > 0:
@@ -82,6 +115,51 @@ def test_fp16_block_h_within_budget(shape):
     # an order of magnitude below the parity bar
     assert m["max_excess"] < BAR_EXCESS / 8, m
     assert m["l1"] < BAR_L1 / 2, m
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_fp16_row_h_and_column_weights_within_budget(shape):
+    T, H, I, E, k, seed = shape
+    cfg, inp = moe_synth.small_case(T, H, I, E, k, seed)
+    m = parity_metrics(to_bf16_bits(layer(cfg, inp, f16_row, w2_f16_columns)), layer(cfg, inp))
+    assert m["max_excess"] < BAR_EXCESS / 8, m
+    assert m["l1"] < BAR_L1 / 2, m
+
+
+def test_f16_column_weights_exact_within_36():
+    """Column decode: exact wherever a block's scale byte is within 36 of the column's largest
+    (every E2M1 value times 2^(s - c + 13) is then an fp16 normal or a multiple of 2^-24); blocks
+    further down lose bits but stay within 2^-37 of the column's largest block value."""
+    rng = np.random.default_rng(11)
+    q = rng.integers(0, 256, size=(6, 64), dtype=np.uint8)
+    s = np.full((6, 4), 124, np.uint8)
+    s[0] = [124, 88, 100, 124]          # spans of 36 and less: exact
+    s[1] = [124, 87, 60, 2]             # further: rounded or dropped
+    s[2] = [254, 218, 254, 230]
+    s[3] = [2, 2, 2, 2]
+    exact = dequant(q, s)
+    got = w2_f16_columns(q, s)
+    span = (s.max(axis=1, keepdims=True) - s).repeat(32, axis=1)
+    assert np.array_equal(got[span <= 36], exact[span <= 36])
+    colmax = np.ldexp(6.0, s.max(axis=1).astype(np.int64) - 127)[:, None]
+    assert np.all(np.abs(got - exact) <= colmax * 2.0 ** -37)
+
+
+def test_f16_row_format_edges():
+    """Zero rows, huge and tiny rows, a row mixing magnitudes: no overflow, exact zeros, error at
+    most 2^-11 of the row's largest magnitude (and 2^-11 relative for values within 2^-14 of it)."""
+    rng = np.random.default_rng(6)
+    h = rng.standard_normal((5, 96))
+    h[0] = 0.0
+    h[1] *= 1e30
+    h[2] *= 1e-30
+    h[3, :48] *= 1e-9
+    r = f16_row(h)
+    assert np.all(r[0] == 0.0)
+    rmax = np.abs(h).max(axis=1, keepdims=True)
+    assert np.all(np.abs(r - h) <= rmax * 2.0 ** -11)
+    big = np.abs(h) >= rmax * 2.0 ** -13
+    assert np.all(np.abs(r - h)[big] <= np.abs(h)[big] * 2.0 ** -11)
 
 
 def test_bf16_h_would_break_the_bar():
