@@ -221,6 +221,16 @@ int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_pla
 int moe_set_small_m_max(int small_m_max);
 
 /*
+ * Column tile of the dense (M >= 256 per expert) down GEMM (host only, process-wide): 256 or 224
+ * output columns per workgroup. By default (0) the library takes the width that finishes the
+ * expected ceil(T*k/256) x ceil(H/width) tiles in fewer, fuller rounds over the compute units (one
+ * workgroup per compute unit), the wider on a tie; a value set here forces that width (tests cover
+ * both). Returns the previous setting (0 for automatic), or MOE_ERR_SHAPE for any other value. Not
+ * synchronised with calls in flight on other host threads.
+ */
+int moe_set_dense_down_cols(int cols);
+
+/*
  * Stage timing hook (host only), for measuring one stage of moe_mxfp4_ffn with HIP events on the
  * stream its kernels run on. While set, every moe_mxfp4_ffn call records `start` before the first
  * kernel of `stage` and `stop` after its last kernel, on the call's stream. Pass NULL events to

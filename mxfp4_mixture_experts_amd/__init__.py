@@ -77,6 +77,8 @@ def load_library(path: str | None = None):
     lib.moe_mxfp4_ffn_plan.restype = i
     lib.moe_set_small_m_max.argtypes = [i]
     lib.moe_set_small_m_max.restype = i
+    lib.moe_set_dense_down_cols.argtypes = [i]
+    lib.moe_set_dense_down_cols.restype = i
     lib.moe_set_stage_events.argtypes = [i, V, V]
     lib.moe_set_stage_events.restype = i
     if path is None:
@@ -117,6 +119,15 @@ def ffn_plan(T: int, H: int, I: int, E: int, k: int, flags: int = 0) -> dict:
     plan = FfnPlan()
     _check(load_library().moe_mxfp4_ffn_plan(T, H, I, E, k, flags, ctypes.byref(plan)), "moe_mxfp4_ffn_plan")
     return plan.as_dict()
+
+
+def set_dense_down_cols(cols: int) -> int:
+    """Force the dense down GEMM's column tile (256 or 224; 0 restores the per-shape choice);
+    returns the previous setting."""
+    prev = load_library().moe_set_dense_down_cols(int(cols))
+    if prev < 0:
+        _check(prev, "moe_set_dense_down_cols")
+    return prev
 
 
 def set_small_m_max(v: int) -> int:

@@ -19,6 +19,7 @@ namespace {
 // tokens' activations in registers, and each further pair of tokens costs another decode pass and a
 // reload). A value set through moe_set_small_m_max overrides the table; -1 restores it.
 std::atomic<int> g_small_m_max{-1};
+std::atomic<int> g_dense_down_cols{0};  // 0: chosen per shape; 256 or 224: forced
 
 int table_small_m_max(int T) { return T <= 8 ? 8 : 2; }
 
@@ -133,6 +134,11 @@ MOE_API const char* moe_status_string(int status) {
 MOE_API int moe_set_small_m_max(int v) {
   if (v < -1) return MOE_ERR_SHAPE;
   return g_small_m_max.exchange(v);
+}
+
+MOE_API int moe_set_dense_down_cols(int cols) {
+  if (cols != 0 && cols != 256 && cols != 224) return MOE_ERR_SHAPE;
+  return g_dense_down_cols.exchange(cols);
 }
 
 MOE_API int moe_set_stage_events(int stage, void* start_event, void* stop_event) {
@@ -251,7 +257,7 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   int32_t* dense_m0 = dense_e + wl.dense_slots_max;
   const bool dense = plan.launch_large && T >= moe::kDenseMinRows;
   const int dense_min = dense ? moe::kDenseMinRows : INT_MAX;
-  const moe::DensePlan dp = moe::plan_dense(T, H, I, E, k, moe::kDenseMinRows);
+  const moe::DensePlan dp = moe::plan_dense(T, H, I, E, k, moe::kDenseMinRows, num_cus(), g_dense_down_cols.load() / 32);
   // without MFMA kernels every active expert is small: the grouping's active list is the work list
   const int32_t* list = plan.launch_large ? small_list : active;
   const int32_t* list_count = plan.launch_large ? n_small : n_active;

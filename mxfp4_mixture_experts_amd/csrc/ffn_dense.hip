@@ -5,12 +5,14 @@
 // MFMA. Here a workgroup stages both operands of a K-step in LDS and the weights are decoded once per
 // workgroup:
 //   - a workgroup owns 256 rows of one expert x 256 weight rows (gate_up: 128 gate columns and the
-//     matching 128 up columns; down: 256 output columns); its eight waves (two per SIMD) each
-//     compute 64 rows x 128 weight rows with 16x16x32 MFMAs (32 accumulator blocks);
+//     matching 128 up columns; down: 256 or 224 output columns, whichever fills the compute units
+//     in fewer, fuller rounds); its eight waves (two per SIMD) each compute 64 rows x 128 (or 112)
+//     weight rows with 16x16x32 MFMAs (32 or 28 accumulator blocks);
 //   - per K-step of 64 every thread loads 16-byte chunks of the activation rows and one MX block of
 //     one weight row (16 bytes of E2M1 codes + the E8M0 scale), decodes the block exactly with the
-//     scaled FP4 conversion and writes both to LDS; the loads of the next K-step are in flight in
-//     registers meanwhile;
+//     scaled FP4 conversion and writes both to LDS; the staging of step s + 1 is interleaved with
+//     the MFMAs of step s, and each chunk's loads for step s + 2 are issued as soon as its
+//     registers are free;
 //   - LDS rows are padded to 16 bytes past a multiple of 64 so the MFMA operand reads (16 rows x
 //     16 bytes per lane group) hit 64 distinct banks; two LDS buffers alternate, one barrier per
 //     K-step.
@@ -38,7 +40,6 @@ namespace moe {
 namespace {
 
 constexpr int kDM = 256;              // rows per tile
-constexpr int kDN = 256;              // weight rows per workgroup
 constexpr int kDW = 8;                // waves: 4 row groups x 2 column groups
 constexpr int kWM = kDM / (kDW / 2);  // rows per wave (64)
 constexpr int kMS = kWM / 16;         // MFMA row blocks per wave
@@ -77,40 +78,44 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   return v;
 }
 
-template <bool GATEUP>
+// NCB: 16-column MFMA blocks per wave; a workgroup covers kTN = 32 NCB weight rows (two wave
+// column groups of kNW = 16 NCB). gate_up always uses 8 (128 gate + 128 up rows); down uses 8 or 7,
+// whichever fills the GPU's compute units in fewer, fuller rounds for the output width.
+template <bool GATEUP, int NCB>
 struct DenseShape {
+  static constexpr int kNW = 16 * NCB;
+  static constexpr int kTN = 2 * kNW;
   static constexpr int kBK = 64;                        // K elements per step (two MX blocks)
   static constexpr int kBlocks = kBK / 32;              // MX blocks per weight row and step
   static constexpr int kPlanes = GATEUP ? 1 : 2;        // global planes per activation: x, or hi + lo
   static constexpr int kRow = kBK * 2 + 16;             // LDS bytes per row (16-bit values + padding)
   static constexpr int kATileBytes = kDM * kRow;
-  static constexpr int kBTileBytes = kDN * kRow;
+  static constexpr int kBTileBytes = kTN * kRow;
   static constexpr int kStage = kATileBytes + kBTileBytes;
   // LDS bytes past the two stages: down keeps the row and column exponents there
-  static constexpr int kExtra = GATEUP ? 0 : (kDM + kDN) * 4;
+  static constexpr int kExtra = GATEUP ? 0 : (kDM + kTN) * 4;
   static constexpr int kLds = 2 * kStage + kExtra;
   // 16-byte LDS chunks per activation row and step, per thread and step (each chunk is one global
   // 16-byte load per plane), and weight-block chunks per thread and step
   static constexpr int kCpr = kBK * 2 / 16;
   static constexpr int kAChunks = kDM * kCpr / kDThreads;
-  static constexpr int kBChunks = (kDN * kBlocks + kDThreads - 1) / kDThreads;
-  static constexpr int kD = 1;                          // K-steps of loads in flight
+  static constexpr int kBChunks = (kTN * kBlocks + kDThreads - 1) / kDThreads;
 };
 
 // Weight row (within the expert) streamed as LDS B-tile row n of column tile xblk.
 //   gate_up: n in [0,64) gate of wave column 0, [64,128) its up rows, [128,192) gate of column 1,
 //            [192,256) its up rows (so a wave's gate and up blocks share lanes);
-//   down: n is the output column offset.
-template <bool GATEUP>
+//   down: n is the output column offset (kTN columns per tile).
+template <bool GATEUP, int kTN>
 __device__ __forceinline__ int dense_weight_row(int xblk, int n, int I, int H) {
   if (GATEUP) {
     const int c = min(xblk * 128 + (n >> 7) * 64 + (n & 63), I - 1);
     return (n & 64) ? I + c : c;
   }
-  return min(xblk * kDN + n, H - 1);
+  return min(xblk * kTN + n, H - 1);
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int NCB>
 __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k, int H, int I,
@@ -119,9 +124,11 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     const uint16_t* __restrict__ h_hi_in, const uint16_t* __restrict__ h_lo_in,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, uint8_t* __restrict__ rexp, int nseg,
     float* __restrict__ y_out) {
-  using S = DenseShape<GATEUP>;
+  using S = DenseShape<GATEUP, NCB>;
+  static_assert(!GATEUP || NCB == 8, "gate_up pairs gate blocks 0..3 with up blocks 4..7");
+  static_assert(NCB >= 2 + kMS, "the next slice's A operands are read during passes 2 .. 1 + kMS");
+  constexpr int kNW = S::kNW, kTN = S::kTN;
   using op_t = typename std::conditional<GATEUP, bf16x8_t, f16x8_t>::type;
-  constexpr int D = S::kD;
   constexpr int NA = S::kAChunks;
   constexpr int NP = S::kPlanes;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   const int j16 = lane & 15;
   const int g = lane >> 4;
   const int wr = wave % (kDW / 2);  // row group: rows wr*kWM .. +kWM
-  const int wc = wave / (kDW / 2);  // column group: B-tile rows wc*128 .. +128
+  const int wc = wave / (kDW / 2);  // column group: B-tile rows wc*kNW .. +kNW
 
   // ---- staging assignments
   // activations: chunk c = tid + kDThreads * i covers elements 8 (c % kCpr) .. +8 of row c / kCpr
@@ -183,42 +190,44 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   uint32_t bq[NBW], bs[NBW];
 #pragma unroll
   for (int jw = 0; jw < NBW; ++jw) {
-    bn[jw] = ((tid + kDThreads * jw) / S::kBlocks) % kDN;
-    const uint32_t wrow = (uint32_t)dense_weight_row<GATEUP>(xblk, bn[jw], I, H);
+    bn[jw] = ((tid + kDThreads * jw) / S::kBlocks) % kTN;
+    const uint32_t wrow = (uint32_t)dense_weight_row<GATEUP, kTN>(xblk, bn[jw], I, H);
     bq[jw] = wrow * qrow;
     bs[jw] = wrow * srow;
   }
 
-  uint4 ra[D][NA][NP];
-  uint4 rb[D][NBW];
-  uint32_t rs[D][NBW];
+  // one register set of loads: activation chunk i and the weight block(s) of one K-step
+  uint4 ra[NA][NP];
+  uint4 rb[NBW];
+  uint32_t rs[NBW];
 
-  auto issue = [&](int slot, int step) {
-    const int st = min(step, nsteps - 1);  // steps past the end re-load the last one (never used)
+  // loads of K-step `step` (steps past the end re-load the last one, never used)
+  auto load_a = [&](int i, int step) {
+    const int st = min(step, nsteps - 1);
+    const int c = tid + kDThreads * i;
+    const int elc = min(st * S::kBK + (c % kCpr) * 8, K - 8);  // first element of the chunk
+#pragma unroll
+    for (int p = 0; p < NP; ++p) ra[i][p] = ld16(arow[i][p], (uint32_t)elc * 2);
+  };
+  auto load_b = [&](int step) {
+    const int st = min(step, nsteps - 1);
     const uint32_t blk = (uint32_t)min(st * S::kBlocks + bblk, NB - 1);
 #pragma unroll
     for (int jw = 0; jw < NBW; ++jw) {
-      rb[slot][jw] = ld16(qe, bq[jw] + blk * 16);
-      rs[slot][jw] = ld8(se, bs[jw] + blk);
-    }
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int c = tid + kDThreads * i;
-      const int el = st * S::kBK + (c % kCpr) * 8;  // first element of the chunk
-      const int elc = min(el, K - 8);
-#pragma unroll
-      for (int p = 0; p < NP; ++p) ra[slot][i][p] = ld16(arow[i][p], (uint32_t)elc * 2);
+      rb[jw] = ld16(qe, bq[jw] + blk * 16);
+      rs[jw] = ld8(se, bs[jw] + blk);
     }
   };
 
-  f32x4_t acc[kMS][8];
+  f32x4_t acc[kMS][NCB];
 #pragma unroll
   for (int ms = 0; ms < kMS; ++ms)
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) acc[ms][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) acc[ms][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int d = 0; d < D; ++d) issue(d, d);
+  for (int i = 0; i < NA; ++i) load_a(i, 0);
+  load_b(0);
 
   // down: the row scales of this tile (from the segment exponents gate_up wrote) and the column
   // shifts of this column tile; each staging thread keeps the scales of its activation rows
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
 #pragma unroll
     for (int jw = 0; jw < NBW; ++jw) {
       ccol[jw] = (int)max_bytes(se + bs[jw], NB, svec);
-      if (tid + kDThreads * jw < kDN * S::kBlocks) s_colc[bn[jw]] = ccol[jw];
+      if (tid + kDThreads * jw < kTN * S::kBlocks) s_colc[bn[jw]] = ccol[jw];
     }
     __syncthreads();
 #pragma unroll
@@ -246,43 +255,47 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     }
   }
 
-  auto step_body = [&](int slot, int step) {
+  // activation chunk i of K-step `step` -> LDS buffer step & 1 (zero past K); down: hi + lo,
+  // scaled, as fp16
+  auto stage_a = [&](int i, int step) {
     uint8_t* st_a = lds + (step & 1) * S::kStage;
-    uint8_t* st_b = st_a + S::kATileBytes;
-    // activations of this step -> LDS (zero past K); down: hi + lo, scaled, as fp16
+    const int c = tid + kDThreads * i;
+    const int lr = c / kCpr, cc = c % kCpr;
+    uint4 v;
+    if (GATEUP) {
+      v = ra[i][0];
+    } else {
+      const uint4 hv = ra[i][0], lv = ra[i][NP - 1];
+      const uint32_t a[4] = {hv.x, hv.y, hv.z, hv.w};
+      const uint32_t l[4] = {lv.x, lv.y, lv.z, lv.w};
+      uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int c = tid + kDThreads * i;
-      const int lr = c / kCpr, cc = c % kCpr;
-      uint4 v;
-      if (GATEUP) {
-        v = ra[slot][i][0];
-      } else {
-        const uint4 hv = ra[slot][i][0], lv = ra[slot][i][NP - 1];
-        const uint32_t a[4] = {hv.x, hv.y, hv.z, hv.w};
-        const uint32_t l[4] = {lv.x, lv.y, lv.z, lv.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v0 = bf16_lo_f32(a[j]) + bf16_lo_f32(l[j]);
-          const float v1 = bf16_hi_f32(a[j]) + bf16_hi_f32(l[j]);
-          o[j] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)(v0 * asc[i]), (_Float16)(v1 * asc[i])});
-        }
-        v = make_uint4(o[0], o[1], o[2], o[3]);
+      for (int j = 0; j < 4; ++j) {
+        const float v0 = bf16_lo_f32(a[j]) + bf16_lo_f32(l[j]);
+        const float v1 = bf16_hi_f32(a[j]) + bf16_hi_f32(l[j]);
+        o[j] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)(v0 * asc[i]), (_Float16)(v1 * asc[i])});
       }
-      if (step * S::kBK + cc * 8 >= K) v = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(st_a + lr * S::kRow + cc * 16) = v;
+      v = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    // weight blocks of this step -> 32 16-bit values each in LDS (a zero scale past K): bf16 with
-    // the block scale for gate_up, fp16 with the block scale relative to the column's for down
+    // a mask rather than a select: the compiler turns a select into a branch that zeroes the
+    // load's registers in place
+    const uint32_t keep = step * S::kBK + cc * 8 < K ? ~0u : 0u;
+    v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    *reinterpret_cast<uint4*>(st_a + lr * S::kRow + cc * 16) = v;
+  };
+  // weight blocks of K-step `step` -> 32 16-bit values each in LDS buffer step & 1 (a zero scale
+  // past K): bf16 with the block scale for gate_up, fp16 with the block scale relative to the
+  // column's for down
+  auto stage_b = [&](int step) {
+    uint8_t* st_b = lds + (step & 1) * S::kStage + S::kATileBytes;
 #pragma unroll
     for (int jw = 0; jw < NBW; ++jw) {
-      if (tid + kDThreads * jw >= kDN * S::kBlocks) break;  // a repeated chunk: written by its owner
+      if (tid + kDThreads * jw >= kTN * S::kBlocks) break;  // a repeated chunk: written by its owner
       const bool ok = step * S::kBlocks + bblk < NB;
-      const uint32_t wd[4] = {rb[slot][jw].x, rb[slot][jw].y, rb[slot][jw].z, rb[slot][jw].w};
+      const uint32_t wd[4] = {rb[jw].x, rb[jw].y, rb[jw].z, rb[jw].w};
       uint8_t* dst = st_b + bn[jw] * S::kRow + bblk * 64;
       if (GATEUP) {
-        const float scale = ok ? e8m0_to_float(rs[slot][jw]) : 0.0f;
+        const float scale = ok ? e8m0_to_float(rs[jw]) : 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const bf16x2_t p0 = fp4x2_to_bf16x2<0>(wd[d], scale);
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
         }
       } else {
         // 2^(s - c + 13); blocks 140 or more below the column's largest scale byte decode to zero
-        const int ex = (int)rs[slot][jw] + 140 - ccol[jw];
+        const int ex = (int)rs[jw] + 140 - ccol[jw];
         const float scale = ok ? __builtin_bit_cast(float, (uint32_t)max(ex, 0) << 23) : 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -307,45 +320,69 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
         }
       }
     }
-    __syncthreads();
-    // refill the slot with step + D while this step computes
-    issue(slot, step + D);
-    // MFMAs: per 32-wide K slice, A operands of the wave's 4 row blocks and B operands of its 8
-    // column blocks (lane: row / column j16, K elements 8g .. 8g+7 of the slice)
-#pragma unroll
-    for (int kk = 0; kk < S::kBlocks; ++kk) {
-      op_t bop[8];
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
-        bop[cb] = *reinterpret_cast<const op_t*>(st_b + (wc * 128 + cb * 16 + j16) * S::kRow + kk * 64 + g * 16);
-      // A operands one row block ahead; the barrier keeps the compiler from hoisting every read of
-      // the step (which would not fit next to the 256 accumulator registers)
-      auto read_a = [&](int ms) {
-        return *reinterpret_cast<const op_t*>(st_a + (wr * kWM + ms * 16 + j16) * S::kRow + kk * 64 + g * 16);
-      };
-      op_t aop[2];
-      aop[0] = read_a(0);
-#pragma unroll
-      for (int ms = 0; ms < kMS; ++ms) {
-        if (ms < kMS - 1) aop[(ms + 1) & 1] = read_a(ms + 1);
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          if constexpr (GATEUP)
-            acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[ms & 1], bop[cb], acc[ms][cb], 0, 0, 0);
-          else
-            acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[ms & 1], bop[cb], acc[ms][cb], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
   };
 
-  // the step count is padded to a multiple of D (padding steps see zero activations and zero
-  // scales), so the loop body has no conditional MFMA block and the accumulators stay in place
-  const int nsteps_pad = (nsteps + D - 1) / D * D;
-  for (int step = 0; step < nsteps_pad; step += D) {
+  // software pipeline: step 0 staged and step 1 in flight before the loop; during step s the MFMA
+  // groups read buffer s & 1 while, between them, the chunks of step s + 1 go to buffer (s + 1) & 1
+  // (last read in step s - 1, before the barrier that opened step s) and each chunk's registers are
+  // refilled at once with step s + 2, so every load has a whole step to arrive. One barrier per step.
 #pragma unroll
-    for (int d = 0; d < D; ++d) step_body(d, step + d);
+  for (int i = 0; i < NA; ++i) {
+    stage_a(i, 0);
+    load_a(i, 1);
+  }
+  stage_b(0);
+  load_b(1);
+  __syncthreads();
+
+  // operand reads from LDS (lane: row / column j16, K elements 8g .. 8g+7 of 32-wide slice kk)
+  auto read_a = [&](const uint8_t* st_a, int kk, int ms) {
+    return *reinterpret_cast<const op_t*>(st_a + (wr * kWM + ms * 16 + j16) * S::kRow + kk * 64 + g * 16);
+  };
+  auto read_b = [&](const uint8_t* st_b, int kk, int cb) {
+    return *reinterpret_cast<const op_t*>(st_b + (wc * kNW + cb * 16 + j16) * S::kRow + kk * 64 + g * 16);
+  };
+  constexpr int kQ = S::kBlocks * NCB;  // column-block passes per step (slice-major)
+
+  for (int step = 0; step < nsteps; ++step) {
+    const uint8_t* st_a = lds + (step & 1) * S::kStage;
+    const uint8_t* st_b = st_a + S::kATileBytes;
+    // Column-block-major passes: pass q = 8 kk + cb multiplies the slice's four A operands (held in
+    // registers) with one B operand. B operands stream through a three-entry register ring read two
+    // passes ahead, and the next slice's A operands are read during the current slice, so LDS reads
+    // are spread over the step instead of arriving in one burst per slice.
+    op_t acur[kMS], anxt[kMS], bring[3];
+#pragma unroll
+    for (int ms = 0; ms < kMS; ++ms) acur[ms] = read_a(st_a, 0, ms);
+    bring[0] = read_b(st_b, 0, 0);
+    bring[1] = read_b(st_b, 0, 1);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int kk = q / NCB, cb = q % NCB;
+      if (q + 2 < kQ) bring[(q + 2) % 3] = read_b(st_b, (q + 2) / NCB, (q + 2) % NCB);
+      if (kk + 1 < S::kBlocks && cb >= 2 && cb < 2 + kMS) anxt[cb - 2] = read_a(st_a, kk + 1, cb - 2);
+#pragma unroll
+      for (int ms = 0; ms < kMS; ++ms) {
+        if constexpr (GATEUP)
+          acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[ms], bring[q % 3], acc[ms][cb], 0, 0, 0);
+        else
+          acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[ms], bring[q % 3], acc[ms][cb], 0, 0, 0);
+      }
+      // one staging piece of the next step after every other pass
+      if ((q & 1) && (q >> 1) < NA) {
+        stage_a(q >> 1, step + 1);
+        load_a(q >> 1, step + 2);
+      } else if ((q & 1) && (q >> 1) == NA) {
+        stage_b(step + 1);
+        load_b(step + 2);
+      }
+      if (cb == NCB - 1) {
+#pragma unroll
+        for (int ms = 0; ms < kMS; ++ms) acur[ms] = anxt[ms];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
   }
 
   // epilogue: lane holds rows 4g+i of each 16-row block, column j16 of each column block
@@ -385,9 +422,9 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
       }
     }
   } else {
-    int ecol[8];
+    int ecol[NCB];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) ecol[cb] = s_colc[wc * 128 + cb * 16 + j16] - 140;
+    for (int cb = 0; cb < NCB; ++cb) ecol[cb] = s_colc[wc * kNW + cb * 16 + j16] - 140;
 #pragma unroll
     for (int ms = 0; ms < kMS; ++ms) {
 #pragma unroll
@@ -397,8 +434,8 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
         const size_t orow = (size_t)(row0 + lr);
         const int erow = s_rowe[lr];
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          const int col = xblk * kDN + wc * 128 + cb * 16 + j16;
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int col = xblk * kTN + wc * kNW + cb * 16 + j16;
           if (col < N) y_out[orow * H + col] = __builtin_amdgcn_ldexpf(acc[ms][cb][i], erow + ecol[cb]);
         }
       }
@@ -419,11 +456,27 @@ int dense_slots_bound(int T, int E, int k, int dense_m_min) {
 // gate_up column tiles are 128 h columns, two 64-column segments (one per wave column group)
 int dense_row_segments(int I) { return 2 * ((I + 127) / 128); }
 
-DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min) {
+DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min, int num_cus, int force_ncb) {
   DensePlan dp;
   dp.tile_m = kDM;
   dp.gu_grid_x = (I + 127) / 128;
-  dp.dn_grid_x = (H + kDN - 1) / kDN;
+  // down column tile: with one workgroup per compute unit (LDS), the layer takes
+  // ceil(tiles / CUs) rounds of work proportional to the tile width; expect ceil(P / 256) row tiles
+  // (every pair in a dense expert) and take the width with the smaller product (ties: the wider)
+  const long rt = ((long)T * k + kDM - 1) / kDM;
+  const int cus = num_cus > 0 ? num_cus : 1;
+  long best = -1;
+  for (int ncb = 8; ncb >= 7; --ncb) {
+    const int width = 32 * ncb;
+    const long tiles = rt * ((H + width - 1) / width);
+    const long cost = (tiles + cus - 1) / cus * width;
+    if (best < 0 || cost < best) {
+      best = cost;
+      dp.dn_ncb = ncb;
+    }
+  }
+  if (force_ncb == 7 || force_ncb == 8) dp.dn_ncb = force_ncb;
+  dp.dn_grid_x = (H + 32 * dp.dn_ncb - 1) / (32 * dp.dn_ncb);
   dp.slots = dense_slots_bound(T, E, k, dense_m_min);
   const int groups = (dp.slots + 7) / 8;
   dp.gu_blocks = 8 * dp.gu_grid_x * groups;
@@ -436,14 +489,30 @@ hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int 
                                float clamp, uint16_t* h_hi, uint16_t* h_lo, uint8_t* rexp,
                                hipStream_t stream) {
   if (dp.slots <= 0) return hipSuccess;
-  constexpr int lds = DenseShape<true>::kLds;
-  static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<true>),
+  constexpr int lds = DenseShape<true, 8>::kLds;
+  static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<true, 8>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    lds) == hipSuccess;
   (void)attr_set;
-  dense_kernel<true><<<dp.gu_blocks, kDThreads, lds, stream>>>(
+  dense_kernel<true, 8><<<dp.gu_blocks, kDThreads, lds, stream>>>(
       r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.gu_grid_x, dp.slots, w13_q, w13_s, dense_e,
       dense_m0, clamp, nullptr, nullptr, h_hi, h_lo, rexp, dense_row_segments(I), nullptr);
+  return hipGetLastError();
+}
+
+template <int NCB>
+hipError_t launch_dense_down_ncb(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
+                                 const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
+                                 const uint16_t* h_hi, const uint16_t* h_lo, const uint8_t* rexp, float* y,
+                                 hipStream_t stream) {
+  constexpr int lds = DenseShape<false, NCB>::kLds;
+  static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<false, NCB>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   lds) == hipSuccess;
+  (void)attr_set;
+  dense_kernel<false, NCB><<<dp.dn_blocks, kDThreads, lds, stream>>>(
+      r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.dn_grid_x, dp.slots, w2_q, w2_s, dense_e,
+      dense_m0, 0.0f, h_hi, h_lo, nullptr, nullptr, const_cast<uint8_t*>(rexp), dense_row_segments(I), y);
   return hipGetLastError();
 }
 
@@ -452,15 +521,9 @@ hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I,
                              const uint16_t* h_hi, const uint16_t* h_lo, const uint8_t* rexp, float* y,
                              hipStream_t stream) {
   if (dp.slots <= 0) return hipSuccess;
-  constexpr int lds = DenseShape<false>::kLds;
-  static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<false>),
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   lds) == hipSuccess;
-  (void)attr_set;
-  dense_kernel<false><<<dp.dn_blocks, kDThreads, lds, stream>>>(
-      r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.dn_grid_x, dp.slots, w2_q, w2_s, dense_e,
-      dense_m0, 0.0f, h_hi, h_lo, nullptr, nullptr, const_cast<uint8_t*>(rexp), dense_row_segments(I), y);
-  return hipGetLastError();
+  if (dp.dn_ncb == 7)
+    return launch_dense_down_ncb<7>(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, h_lo, rexp, y, stream);
+  return launch_dense_down_ncb<8>(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, h_lo, rexp, y, stream);
 }
 
 }  // namespace moe

@@ -112,12 +112,14 @@ constexpr int kDenseMinRows = 256;
 struct DensePlan {
   int tile_m;                // rows per tile
   int gu_grid_x, dn_grid_x;  // column tiles per row tile
+  int dn_ncb;                // down: 16-column MFMA blocks per wave (8: 256-column tiles, 7: 224)
   int slots;                 // upper bound on the number of (expert, row-tile) pairs
   int gu_blocks, dn_blocks;  // one-dimensional grids (XCD-interleaved tile order)
 };
 
 int dense_slots_bound(int T, int E, int k, int dense_m_min);
-DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min);
+// force_ncb: 7 or 8 forces the down column tile; 0 picks it from the shape
+DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min, int num_cus, int force_ncb = 0);
 int dense_row_segments(int I);
 
 hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w13_q,

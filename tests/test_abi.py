@@ -148,6 +148,20 @@ def test_launch_plan(lib):
         m.ffn_plan(8, 4096, 2048, 256, 8, 6)
 
 
+def test_dense_down_cols_setting(lib):
+    import mxfp4_mixture_experts_amd as m
+
+    for bad in (-1, 1, 128, 255, 512):
+        with pytest.raises(m.MoeError):
+            m.set_dense_down_cols(bad)
+    prev = m.set_dense_down_cols(224)
+    try:
+        assert prev == 0
+        assert m.set_dense_down_cols(256) == 224
+    finally:
+        assert m.set_dense_down_cols(prev) == 256
+
+
 def test_stage_events_validation(lib):
     assert lib.moe_set_stage_events(3, None, None) == -2
     assert lib.moe_set_stage_events(0, None, None) == 0

@@ -86,7 +86,18 @@ DENSE_CASES = [
 def test_dense_shapes(orc, case):
     T, H, I, E, k, fn, clamp, seed = case
     cfg, inp = moe_synth.small_case(T, H, I, E, k, seed, score_fn=fn, clamp=clamp)
-    check_full(orc, cfg, inp, ("default", "large", "unfused"))
+    outs = check_full(orc, cfg, inp, ("default", "large", "unfused"))
+    # both column tiles of the dense down GEMM: the tile decides which workgroup computes an output
+    # column, not its arithmetic, so the bits are the same
+    w = weights_to_device(inp)
+    for cols in (256, 224):
+        print(f"dense down with {cols}-column tiles", flush=True)
+        prev = moe.set_dense_down_cols(cols)
+        try:
+            g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w, renorm=cfg.renorm)
+        finally:
+            moe.set_dense_down_cols(prev)
+        np.testing.assert_array_equal(g["out_bf16"], outs["default"])
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_H%d_I%d_E%d_k%d" % c[:5])
