@@ -67,7 +67,7 @@ enum {
   MOE_UNFUSED_GATE_UP = 1,
   /* Force every active expert onto the weight-streaming small-M kernels, whatever its row count. */
   MOE_FORCE_SMALL_M = 2,
-  /* Force every active expert onto the LDS-dequantising bf16 MFMA kernels. */
+  /* Force every active expert onto the MFMA kernels (row-tile, or dense from 256 rows). */
   MOE_FORCE_LARGE_M = 4
 };
 
@@ -140,9 +140,9 @@ int moe_route_group(const float* logits, int T, int E, int k, int score_fn, int 
 
 /*
  * moe_mxfp4_ffn_workspace_size — bytes of device workspace moe_mxfp4_ffn needs for these sizes and
- * flags: the SwiGLU activations h (two bf16 planes, 4 bytes per element of P x I), the per-pair
- * down-projection outputs y (fp32, P x H) and, with MOE_UNFUSED_GATE_UP, the gate
- * activations. The size covers the worst case over every routing of the P pairs, so a workspace
+ * flags: the SwiGLU activations h (two bf16 planes, 4 bytes per element of P x I), one scale byte
+ * per pair row, the per-pair down-projection outputs y (fp32, P x H) and, with
+ * MOE_UNFUSED_GATE_UP, the gate activations. The size covers the worst case over every routing of the P pairs, so a workspace
  * sized once for (T, H, I, E, k, flags) is valid for every call with those sizes (cf. the split-K
  * workspace contract of tokenspeed PR #661, "The workspace contract": partial rows must be reserved
  * for the worst case, not the current M). Returns 0 for invalid sizes.
@@ -164,8 +164,10 @@ size_t moe_mxfp4_ffn_workspace_size(int T, int H, int I, int E, int k, int flags
  * bfloat16 (nearest-even). Experts with no pairs read no weights. h is kept between the two GEMMs
  * as hi = bf16(h) and lo = bf16(h - hi) (hi + lo equals h to about 2^-17 relative). Small per-expert
  * row counts run on weight-streaming kernels (down: hi + lo rebuilt, then scaled fp16 per 32-value
- * block); large ones on bf16 MFMA kernels (down: one MFMA on each plane). Results are
- * deterministic: repeated calls give bitwise-identical outputs.
+ * block); larger ones on MFMA kernels: below 256 rows bf16 (down: one MFMA on each plane), from
+ * 256 rows on the dense kernels (gate_up bf16; down on hi + lo rebuilt as fp16 scaled per row and
+ * weights decoded to fp16 relative to each output column's largest scale, one fp16 MFMA). Results
+ * are deterministic: repeated calls give bitwise-identical outputs.
  *
  *   x_bf16                       [dev] u16[T, H]  bfloat16 activations, 16-byte aligned
  *   w13_q, w13_s, w2_q, w2_s     [dev] MXFP4 weights (layout above); w13_q and w2_q 16-byte aligned

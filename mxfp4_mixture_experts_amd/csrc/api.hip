@@ -43,7 +43,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
-  size_t h, rexp, g_f32, y, sched, total;
+  size_t h, rowf, g_f32, y, sched, total;
   int tile_slots_max, dense_slots_max;
 };
 
@@ -61,9 +61,9 @@ WsLayout ws_layout(long P, int H, int I, int E, int k, int flags) {
   // h as two bf16 planes [P, I] (hi, then lo)
   w.h = off;
   off = align_up(off + (size_t)P * I * 2 * sizeof(uint16_t));
-  // per h row, the biased exponent of the largest |hi| of each 64-column segment (dense kernels)
-  w.rexp = off;
-  off = align_up(off + (size_t)P * moe::dense_row_segments(I));
+  // per h row of a dense expert, the exponent of its fp16 scale (one byte)
+  w.rowf = off;
+  off = align_up(off + (size_t)P);
   w.g_f32 = off;
   if (flags & MOE_UNFUSED_GATE_UP) off = align_up(off + (size_t)P * I * sizeof(float));
   w.y = off;
@@ -103,11 +103,12 @@ void fill_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan)
   plan->large_gateup_grid = plan->launch_large ? lp.gu_blocks : 0;
   plan->large_down_grid = plan->launch_large ? lp.dn_blocks : 0;
   plan->combine_grid = T > 0 ? moe::combine_grid(T, H) : 0;
-  // the MFMA kernels need the schedule kernel's tile lists first; the dense kernels run only when an
-  // expert can have kDenseMinRows rows (an expert has at most T)
+  // the MFMA kernels need the schedule kernel's tile lists first; the dense kernels (gate_up, the
+  // fp16 rewrite of their h rows, down) run only when an expert can have kDenseMinRows rows (an
+  // expert has at most T)
   const bool dense = plan->launch_large && T >= moe::kDenseMinRows;
   plan->n_launches = (plan->launch_small ? gu_launches + 1 : 0) + (plan->launch_large ? 3 : 0) +
-                     (dense ? 2 : 0) + (T > 0 ? 1 : 0);
+                     (dense ? 3 : 0) + (T > 0 ? 1 : 0);
 }
 
 void record(int stage, bool start, hipStream_t stream) {
@@ -242,7 +243,7 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   char* ws = (char*)workspace;
   uint16_t* h_hi = (uint16_t*)(ws + wl.h);
   uint16_t* h_lo = h_hi + (size_t)T * k * I;
-  uint8_t* rexp = (uint8_t*)(ws + wl.rexp);
+  uint8_t* rowf = (uint8_t*)(ws + wl.rowf);
   float* g_f32 = (float*)(ws + wl.g_f32);
   float* y = (float*)(ws + wl.y);
 
@@ -283,18 +284,19 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
     ok &= moe::launch_large_gateup(lp, r, H, I, w13_q, w13_s, tile_e, tile_m0, clamp_limit, h_hi, h_lo, s) ==
           hipSuccess;
   if (dense)
-    ok &= moe::launch_dense_gateup(dp, r, H, I, w13_q, w13_s, dense_e, dense_m0, clamp_limit, h_hi, h_lo,
-                                   rexp, s) == hipSuccess;
+    ok &= moe::launch_dense_gateup(dp, r, H, I, w13_q, w13_s, dense_e, dense_m0, clamp_limit, h_hi, h_lo, s) ==
+          hipSuccess;
   record(MOE_STAGE_GATE_UP, false, s);
 
   record(MOE_STAGE_DOWN, true, s);
+  if (dense)
+    ok &= moe::launch_dense_h16(dp, r, I, dense_e, dense_m0, h_hi, h_lo, rowf, s) == hipSuccess;
   if (plan.launch_small)
     ok &= moe::launch_small_down(sp, r, list, list_count, H, I, w2_q, w2_s, h_hi, h_lo, y, s) == hipSuccess;
   if (plan.launch_large)
     ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, tile_e, tile_m0, h_hi, h_lo, y, s) == hipSuccess;
   if (dense)
-    ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, h_lo, rexp, y, s) ==
-          hipSuccess;
+    ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, rowf, y, s) == hipSuccess;
   record(MOE_STAGE_DOWN, false, s);
 
   record(MOE_STAGE_COMBINE, true, s);

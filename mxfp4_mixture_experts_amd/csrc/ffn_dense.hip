@@ -18,18 +18,19 @@
 //     K-step.
 // gate_up multiplies bf16 x with bf16 weights (E2M1 x E8M0 is exact in bf16). Gate columns and the
 // matching up columns land in the same lanes of a wave, so the clamp-SwiGLU epilogue runs in
-// registers; it writes h as its two bf16 planes and, per row and 64-column segment, the biased
-// exponent of the largest |hi| (no atomics: each segment has one writer).
+// registers; it writes h as its two bf16 planes.
 // down runs one fp16 MFMA per operand pair instead of one bf16 MFMA per h plane:
-//   - each h row is rebuilt as hi + lo (exact in fp32) and scaled by a power of two chosen from the
-//     row's largest |hi| (the maximum of its segment exponents) so that its largest magnitude lands
-//     in [2^14, 2^15), then rounded to fp16: 11 significant bits per value, as in the weight-
-//     streaming down kernel, and no overflow since |hi + lo| <= |hi| (1 + 2^-8);
+//   - between the two GEMMs one wave per row rebuilds the row as hi + lo (exact in fp32), scales it
+//     by a power of two chosen from the row's largest |hi| so that its largest magnitude lands in
+//     [2^14, 2^15), rounds it to fp16 (11 significant bits per value, as in the weight-streaming
+//     down kernel; no overflow since |hi + lo| <= |hi| (1 + 2^-8)) and writes it over the hi plane,
+//     with the scale's exponent in one byte per row; the down workgroups then stage it unchanged;
 //   - each weight column (output column) is decoded as code x 2^(s - c + 13) in fp16, with c the
 //     largest scale byte of that column: the largest block reaches at most 6 x 2^13, and every
 //     block whose scale byte is within 36 of the column's largest is exact;
 //   - the epilogue multiplies the fp32 sum by 2^((127 - f) + (c - 140)) with one ldexp, which
 //     undoes both scalings exactly (within fp32 range).
+// Only the dense down GEMM reads the rows of dense experts, so their hi plane can be overwritten.
 #include <type_traits>
 
 #include "common.hpp"
@@ -69,25 +70,12 @@ __device__ __forceinline__ uint32_t max_bytes(const uint8_t* p, int n, bool vec)
   return m;
 }
 
-// v and its rotations within each 16-lane row: every lane ends with its row's maximum.
-__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));  // row_ror:2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));  // row_ror:1
-  return v;
-}
-
-// NCB: 16-column MFMA blocks per wave; a workgroup covers kTN = 32 NCB weight rows (two wave
-// column groups of kNW = 16 NCB). gate_up always uses 8 (128 gate + 128 up rows); down uses 8 or 7,
-// whichever fills the GPU's compute units in fewer, fuller rounds for the output width.
 template <bool GATEUP, int NCB>
 struct DenseShape {
   static constexpr int kNW = 16 * NCB;
   static constexpr int kTN = 2 * kNW;
   static constexpr int kBK = 64;                        // K elements per step (two MX blocks)
   static constexpr int kBlocks = kBK / 32;              // MX blocks per weight row and step
-  static constexpr int kPlanes = GATEUP ? 1 : 2;        // global planes per activation: x, or hi + lo
   static constexpr int kRow = kBK * 2 + 16;             // LDS bytes per row (16-bit values + padding)
   static constexpr int kATileBytes = kDM * kRow;
   static constexpr int kBTileBytes = kTN * kRow;
@@ -95,8 +83,8 @@ struct DenseShape {
   // LDS bytes past the two stages: down keeps the row and column exponents there
   static constexpr int kExtra = GATEUP ? 0 : (kDM + kTN) * 4;
   static constexpr int kLds = 2 * kStage + kExtra;
-  // 16-byte LDS chunks per activation row and step, per thread and step (each chunk is one global
-  // 16-byte load per plane), and weight-block chunks per thread and step
+  // 16-byte LDS chunks per activation row and step (each one global 16-byte load), per thread and
+  // step, and weight-block chunks per thread and step
   static constexpr int kCpr = kBK * 2 / 16;
   static constexpr int kAChunks = kDM * kCpr / kDThreads;
   static constexpr int kBChunks = (kTN * kBlocks + kDThreads - 1) / kDThreads;
@@ -121,8 +109,8 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k, int H, int I,
     int nx, int dense_slots, const uint8_t* __restrict__ wq_all, const uint8_t* __restrict__ ws_all,
     const int32_t* __restrict__ dense_e, const int32_t* __restrict__ dense_m0, float clamp,
-    const uint16_t* __restrict__ h_hi_in, const uint16_t* __restrict__ h_lo_in,
-    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, uint8_t* __restrict__ rexp, int nseg,
+    const uint16_t* __restrict__ h16_in, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
+    const uint8_t* __restrict__ rowf,
     float* __restrict__ y_out) {
   using S = DenseShape<GATEUP, NCB>;
   static_assert(!GATEUP || NCB == 8, "gate_up pairs gate blocks 0..3 with up blocks 4..7");
@@ -130,7 +118,6 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   constexpr int kNW = S::kNW, kTN = S::kTN;
   using op_t = typename std::conditional<GATEUP, bf16x8_t, f16x8_t>::type;
   constexpr int NA = S::kAChunks;
-  constexpr int NP = S::kPlanes;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int* s_rowe = reinterpret_cast<int*>(lds + 2 * S::kStage);  // down: 127 - f per tile row
   int* s_colc = s_rowe + kDM;                                  // down: c per B-tile row
@@ -168,19 +155,18 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
 
   // ---- staging assignments
   // activations: chunk c = tid + kDThreads * i covers elements 8 (c % kCpr) .. +8 of row c / kCpr
-  // (of x for gate_up; of both h planes for down)
+  // (of x for gate_up; of the fp16 h row for down)
   constexpr int kCpr = S::kCpr;
-  const uint8_t* arow[NA][NP];
+  const uint8_t* arow[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int c = tid + kDThreads * i;
     const int lr = min(c / kCpr, rows - 1);
     if (GATEUP) {
       const int t = sorted_pair[row0 + lr] / k;
-      arow[i][0] = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
+      arow[i] = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
     } else {
-      arow[i][0] = reinterpret_cast<const uint8_t*>(h_hi_in + (size_t)(row0 + lr) * I);
-      arow[i][NP - 1] = reinterpret_cast<const uint8_t*>(h_lo_in + (size_t)(row0 + lr) * I);
+      arow[i] = reinterpret_cast<const uint8_t*>(h16_in + (size_t)(row0 + lr) * I);
     }
   }
   // weights: chunk q = tid + kDThreads * j is block (q % kBlocks) of B-tile row (q / kBlocks)
@@ -197,7 +183,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   }
 
   // one register set of loads: activation chunk i and the weight block(s) of one K-step
-  uint4 ra[NA][NP];
+  uint4 ra[NA];
   uint4 rb[NBW];
   uint32_t rs[NBW];
 
@@ -206,8 +192,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     const int st = min(step, nsteps - 1);
     const int c = tid + kDThreads * i;
     const int elc = min(st * S::kBK + (c % kCpr) * 8, K - 8);  // first element of the chunk
-#pragma unroll
-    for (int p = 0; p < NP; ++p) ra[i][p] = ld16(arow[i][p], (uint32_t)elc * 2);
+    ra[i] = ld16(arow[i], (uint32_t)elc * 2);
   };
   auto load_b = [&](int step) {
     const int st = min(step, nsteps - 1);
@@ -229,18 +214,10 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   for (int i = 0; i < NA; ++i) load_a(i, 0);
   load_b(0);
 
-  // down: the row scales of this tile (from the segment exponents gate_up wrote) and the column
-  // shifts of this column tile; each staging thread keeps the scales of its activation rows
-  float asc[NA];
+  // down: the row scales of this tile and the column shifts of this column tile
   int ccol[NBW];
   if (!GATEUP) {
-    if (tid < kDM) {
-      const int lr = min(tid, rows - 1);
-      const uint8_t* p = rexp + (size_t)(row0 + lr) * nseg;
-      const int eb = (int)max_bytes(p, nseg, (nseg & 15) == 0);  // biased exponent of max |hi|
-      const int f = min(max(268 - eb, 1), 253);                  // row scale 2^(f - 127)
-      s_rowe[tid] = 127 - f;
-    }
+    if (tid < kDM) s_rowe[tid] = 127 - (int)rowf[row0 + min(tid, rows - 1)];  // row scale 2^(f - 127)
     const bool svec = (NB & 15) == 0 && (reinterpret_cast<uintptr_t>(se) & 15) == 0;
 #pragma unroll
     for (int jw = 0; jw < NBW; ++jw) {
@@ -248,35 +225,14 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
       if (tid + kDThreads * jw < kTN * S::kBlocks) s_colc[bn[jw]] = ccol[jw];
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int lr = (tid + kDThreads * i) / kCpr;
-      asc[i] = __builtin_bit_cast(float, (uint32_t)(127 - s_rowe[lr]) << 23);
-    }
   }
 
-  // activation chunk i of K-step `step` -> LDS buffer step & 1 (zero past K); down: hi + lo,
-  // scaled, as fp16
+  // activation chunk i of K-step `step` -> LDS buffer step & 1 (zero past K)
   auto stage_a = [&](int i, int step) {
     uint8_t* st_a = lds + (step & 1) * S::kStage;
     const int c = tid + kDThreads * i;
     const int lr = c / kCpr, cc = c % kCpr;
-    uint4 v;
-    if (GATEUP) {
-      v = ra[i][0];
-    } else {
-      const uint4 hv = ra[i][0], lv = ra[i][NP - 1];
-      const uint32_t a[4] = {hv.x, hv.y, hv.z, hv.w};
-      const uint32_t l[4] = {lv.x, lv.y, lv.z, lv.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v0 = bf16_lo_f32(a[j]) + bf16_lo_f32(l[j]);
-        const float v1 = bf16_hi_f32(a[j]) + bf16_hi_f32(l[j]);
-        o[j] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)(v0 * asc[i]), (_Float16)(v1 * asc[i])});
-      }
-      v = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+    uint4 v = ra[i];
     // a mask rather than a select: the compiler turns a select into a branch that zeroes the
     // load's registers in place
     const uint32_t keep = step * S::kBK + cc * 8 < K ? ~0u : 0u;
@@ -387,12 +343,10 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
 
   // epilogue: lane holds rows 4g+i of each 16-row block, column j16 of each column block
   if (GATEUP) {
-    uint32_t mx[kMS][4];  // largest |hi| bit pattern of the row over the wave's 64 columns
 #pragma unroll
     for (int ms = 0; ms < kMS; ++ms) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        mx[ms][i] = 0;
         const int lr = wr * kWM + ms * 16 + g * 4 + i;
         if (lr >= rows) continue;
         const size_t orow = (size_t)(row0 + lr);
@@ -406,19 +360,8 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
             gv = clampf(gv, clamp);
             uv = clampf(uv, clamp);
           }
-          const uint16_t hb = store_h_planes(h_hi, h_lo, orow * I + col, silu_mul(gv, uv));
-          mx[ms][i] = max(mx[ms][i], (uint32_t)(hb & 0x7FFFu));
+          store_h_planes(h_hi, h_lo, orow * I + col, silu_mul(gv, uv));
         }
-      }
-    }
-    // one byte per row and segment: the biased exponent of the segment's largest |hi|
-#pragma unroll
-    for (int ms = 0; ms < kMS; ++ms) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t m = row16_max(mx[ms][i]);
-        const int lr = wr * kWM + ms * 16 + g * 4 + i;
-        if (j16 == 0 && lr < rows) rexp[(size_t)(row0 + lr) * nseg + xblk * 2 + wc] = (uint8_t)(m >> 7);
       }
     }
   } else {
@@ -443,6 +386,81 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   }
 }
 
+// Rows of dense experts, between the two GEMMs: one wave per row rebuilds h as hi + lo, scales it by
+// 2^(f - 127) with f = clamp(268 - biased exponent of the row's largest |hi|, 1, 253) and writes it
+// as fp16 over the hi plane; rowf[row] = f. Both passes read the row in groups of four 16-byte
+// chunks per lane (the second finds the hi plane in L2).
+constexpr int kH16Waves = 4;  // rows per workgroup
+
+__global__ __launch_bounds__(64 * kH16Waves) void dense_h16_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int I, int dense_slots,
+    const int32_t* __restrict__ dense_e, const int32_t* __restrict__ dense_m0, uint16_t* h_hi,
+    const uint16_t* __restrict__ h_lo, uint8_t* __restrict__ rowf) {
+  constexpr int kSub = kDM / kH16Waves;  // workgroups per row tile
+  const int y = blockIdx.x / kSub;
+  if (y >= dense_slots) return;
+  const int te = dense_e[y];
+  if (te < 0) return;
+  const int e = uniform(te);
+  const int m0 = uniform(dense_m0[y]);
+  const int rows = min(kDM, uniform(counts[e]) - m0);
+  const int lr = (blockIdx.x % kSub) * kH16Waves + uniform((int)(threadIdx.x >> 6));
+  if (lr >= rows) return;
+  const size_t row = (size_t)(uniform(offsets[e]) + m0 + lr);
+  uint8_t* hi = reinterpret_cast<uint8_t*>(h_hi + row * I);
+  const uint8_t* lo = reinterpret_cast<const uint8_t*>(h_lo + row * I);
+  const int lane = threadIdx.x & 63;
+  const int nch = I >> 3;  // 16-byte chunks per row and plane
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+
+  // largest exponent field among the low and among the high bf16 halves of the hi plane
+  uint32_t mx_lo = 0, mx_hi = 0;
+  for (int c0 = 0; c0 < nch; c0 += 256) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 64 * u + lane;
+      v[u] = c < nch ? ld16(hi, (uint32_t)c * 16) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      mx_lo = max(mx_lo, max(max(v[u].x & 0x7F80u, v[u].y & 0x7F80u), max(v[u].z & 0x7F80u, v[u].w & 0x7F80u)));
+      mx_hi = max(mx_hi, max(max(v[u].x & 0x7F800000u, v[u].y & 0x7F800000u),
+                             max(v[u].z & 0x7F800000u, v[u].w & 0x7F800000u)));
+    }
+  }
+  int eb = max((int)(mx_lo >> 7), (int)(mx_hi >> 23));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) eb = max(eb, __shfl_xor(eb, off));
+  const int f = min(max(268 - eb, 1), 253);
+  const float sc = __builtin_bit_cast(float, (uint32_t)f << 23);
+
+  for (int c0 = 0; c0 < nch; c0 += 256) {
+    uint4 hv[4], lv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 64 * u + lane;
+      hv[u] = c < nch ? ld16(hi, (uint32_t)c * 16) : zero;
+      lv[u] = c < nch ? ld16(lo, (uint32_t)c * 16) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 64 * u + lane;
+      const uint32_t a[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+      const uint32_t l[4] = {lv[u].x, lv[u].y, lv[u].z, lv[u].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v0 = bf16_lo_f32(a[j]) + bf16_lo_f32(l[j]);
+        const float v1 = bf16_hi_f32(a[j]) + bf16_hi_f32(l[j]);
+        o[j] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)(v0 * sc), (_Float16)(v1 * sc)});
+      }
+      if (c < nch) *reinterpret_cast<uint4*>(hi + (size_t)c * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  if (lane == 0) rowf[row] = (uint8_t)f;
+}
+
 }  // namespace
 
 int dense_slots_bound(int T, int E, int k, int dense_m_min) {
@@ -452,9 +470,6 @@ int dense_slots_bound(int T, int E, int k, int dense_m_min) {
   if (n_dense > E) n_dense = E;
   return (int)((P + kDM - 1) / kDM + n_dense);
 }
-
-// gate_up column tiles are 128 h columns, two 64-column segments (one per wave column group)
-int dense_row_segments(int I) { return 2 * ((I + 127) / 128); }
 
 DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min, int num_cus, int force_ncb) {
   DensePlan dp;
@@ -486,8 +501,7 @@ DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min, int num
 
 hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w13_q,
                                const uint8_t* w13_s, const int32_t* dense_e, const int32_t* dense_m0,
-                               float clamp, uint16_t* h_hi, uint16_t* h_lo, uint8_t* rexp,
-                               hipStream_t stream) {
+                               float clamp, uint16_t* h_hi, uint16_t* h_lo, hipStream_t stream) {
   if (dp.slots <= 0) return hipSuccess;
   constexpr int lds = DenseShape<true, 8>::kLds;
   static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<true, 8>),
@@ -496,15 +510,23 @@ hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int 
   (void)attr_set;
   dense_kernel<true, 8><<<dp.gu_blocks, kDThreads, lds, stream>>>(
       r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.gu_grid_x, dp.slots, w13_q, w13_s, dense_e,
-      dense_m0, clamp, nullptr, nullptr, h_hi, h_lo, rexp, dense_row_segments(I), nullptr);
+      dense_m0, clamp, nullptr, h_hi, h_lo, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_h16(const DensePlan& dp, const Routed& r, int I, const int32_t* dense_e,
+                            const int32_t* dense_m0, uint16_t* h_hi, const uint16_t* h_lo, uint8_t* rowf,
+                            hipStream_t stream) {
+  if (dp.slots <= 0) return hipSuccess;
+  dense_h16_kernel<<<dp.slots * (kDM / kH16Waves), 64 * kH16Waves, 0, stream>>>(
+      r.counts, r.offsets, I, dp.slots, dense_e, dense_m0, h_hi, h_lo, rowf);
   return hipGetLastError();
 }
 
 template <int NCB>
 hipError_t launch_dense_down_ncb(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
                                  const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
-                                 const uint16_t* h_hi, const uint16_t* h_lo, const uint8_t* rexp, float* y,
-                                 hipStream_t stream) {
+                                 const uint16_t* h16, const uint8_t* rowf, float* y, hipStream_t stream) {
   constexpr int lds = DenseShape<false, NCB>::kLds;
   static const bool attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<false, NCB>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -512,18 +534,17 @@ hipError_t launch_dense_down_ncb(const DensePlan& dp, const Routed& r, int H, in
   (void)attr_set;
   dense_kernel<false, NCB><<<dp.dn_blocks, kDThreads, lds, stream>>>(
       r.x, r.counts, r.offsets, r.sorted_pair, r.k, H, I, dp.dn_grid_x, dp.slots, w2_q, w2_s, dense_e,
-      dense_m0, 0.0f, h_hi, h_lo, nullptr, nullptr, const_cast<uint8_t*>(rexp), dense_row_segments(I), y);
+      dense_m0, 0.0f, h16, nullptr, nullptr, rowf, y);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
-                             const uint16_t* h_hi, const uint16_t* h_lo, const uint8_t* rexp, float* y,
-                             hipStream_t stream) {
+                             const uint16_t* h16, const uint8_t* rowf, float* y, hipStream_t stream) {
   if (dp.slots <= 0) return hipSuccess;
   if (dp.dn_ncb == 7)
-    return launch_dense_down_ncb<7>(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, h_lo, rexp, y, stream);
-  return launch_dense_down_ncb<8>(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, h_lo, rexp, y, stream);
+    return launch_dense_down_ncb<7>(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h16, rowf, y, stream);
+  return launch_dense_down_ncb<8>(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h16, rowf, y, stream);
 }
 
 }  // namespace moe

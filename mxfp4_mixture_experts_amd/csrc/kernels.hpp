@@ -104,9 +104,9 @@ hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I,
                              const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream);
 
 // Dense MFMA kernels for experts with at least kDenseMinRows rows: 256-row tiles, both operands
-// staged in LDS, weights decoded once per workgroup. gate_up also writes, per h row, one byte per
-// 64-column segment (dense_row_segments(I) of them): the biased exponent of the segment's largest
-// |hi|; down reads them to scale its rows into fp16.
+// staged in LDS, weights decoded once per workgroup. Between the GEMMs, launch_dense_h16 rewrites
+// the hi plane of those rows as row-scaled fp16 (scale 2^(f - 127), f in rowf[row]), which the
+// down GEMM reads.
 constexpr int kDenseMinRows = 256;
 
 struct DensePlan {
@@ -120,17 +120,18 @@ struct DensePlan {
 int dense_slots_bound(int T, int E, int k, int dense_m_min);
 // force_ncb: 7 or 8 forces the down column tile; 0 picks it from the shape
 DensePlan plan_dense(int T, int H, int I, int E, int k, int dense_m_min, int num_cus, int force_ncb = 0);
-int dense_row_segments(int I);
 
 hipError_t launch_dense_gateup(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w13_q,
                                const uint8_t* w13_s, const int32_t* dense_e, const int32_t* dense_m0,
-                               float clamp, uint16_t* h_hi, uint16_t* h_lo, uint8_t* rexp,
-                               hipStream_t stream);
+                               float clamp, uint16_t* h_hi, uint16_t* h_lo, hipStream_t stream);
+
+hipError_t launch_dense_h16(const DensePlan& dp, const Routed& r, int I, const int32_t* dense_e,
+                            const int32_t* dense_m0, uint16_t* h_hi, const uint16_t* h_lo, uint8_t* rowf,
+                            hipStream_t stream);
 
 hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
-                             const uint16_t* h_hi, const uint16_t* h_lo, const uint8_t* rexp, float* y,
-                             hipStream_t stream);
+                             const uint16_t* h16, const uint8_t* rowf, float* y, hipStream_t stream);
 
 // out[t] = bf16(sum_j topk_w[t, j] * y[pair_pos[t*k + j]])
 hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* pair_pos, int T, int H,
