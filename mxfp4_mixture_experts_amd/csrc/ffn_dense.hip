@@ -227,17 +227,13 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     __syncthreads();
   }
 
-  // activation chunk i of K-step `step` -> LDS buffer step & 1 (zero past K)
+  // activation chunk i of K-step `step` -> LDS buffer step & 1. Past K (a last step of 32 when K is
+  // not a multiple of 64) the chunk repeats the row's last eight finite values: the weights there
+  // decode with a zero scale, so those products are exact zeros and no masking is needed.
   auto stage_a = [&](int i, int step) {
     uint8_t* st_a = lds + (step & 1) * S::kStage;
     const int c = tid + kDThreads * i;
-    const int lr = c / kCpr, cc = c % kCpr;
-    uint4 v = ra[i];
-    // a mask rather than a select: the compiler turns a select into a branch that zeroes the
-    // load's registers in place
-    const uint32_t keep = step * S::kBK + cc * 8 < K ? ~0u : 0u;
-    v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-    *reinterpret_cast<uint4*>(st_a + lr * S::kRow + cc * 16) = v;
+    *reinterpret_cast<uint4*>(st_a + (c / kCpr) * S::kRow + (c % kCpr) * 16) = ra[i];
   };
   // weight blocks of K-step `step` -> 32 16-bit values each in LDS buffer step & 1 (a zero scale
   // past K): bf16 with the block scale for gate_up, fp16 with the block scale relative to the
@@ -246,7 +242,8 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     uint8_t* st_b = lds + (step & 1) * S::kStage + S::kATileBytes;
 #pragma unroll
     for (int jw = 0; jw < NBW; ++jw) {
-      if (tid + kDThreads * jw >= kTN * S::kBlocks) break;  // a repeated chunk: written by its owner
+      // a repeated chunk (only when the tile has fewer blocks than threads): written by its owner
+      if (kTN * S::kBlocks < kDThreads * NBW && tid + kDThreads * jw >= kTN * S::kBlocks) break;
       const bool ok = step * S::kBlocks + bblk < NB;
       const uint32_t wd[4] = {rb[jw].x, rb[jw].y, rb[jw].z, rb[jw].w};
       uint8_t* dst = st_b + bn[jw] * S::kRow + bblk * 64;
