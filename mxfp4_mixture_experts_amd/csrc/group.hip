@@ -15,7 +15,7 @@ __global__ __launch_bounds__(1024) void group_tokens_kernel(const int32_t* __res
                                                             int32_t* __restrict__ active,
                                                             int32_t* __restrict__ n_active) {
   __shared__ group_dev::Shared sh;
-  group_dev::group_pairs(ids, P, E, counts, offsets, sorted_pair, pair_pos, active, n_active, sh);
+  group_dev::group_pairs<8>(ids, P, E, counts, offsets, sorted_pair, pair_pos, active, n_active, sh);
 }
 
 }  // namespace

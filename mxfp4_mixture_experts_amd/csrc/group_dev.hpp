@@ -8,7 +8,9 @@
 // such lane updates the wave's own per-expert counter in LDS, so nothing is atomic and the result is
 // deterministic. A per-expert scan over the waves (in wave order) plus a scan over the experts gives
 // each pair's row: offsets[e] + (pairs of e in earlier waves) + (earlier chunks of this wave) + (rank
-// among equal lanes of its chunk). Rows within an expert therefore follow ascending p.
+// among equal lanes of its chunk). Rows within an expert therefore follow ascending p. With the ids
+// in global memory (kIdGroup > 1) both passes load those of kIdGroup chunks at once, so a wave waits
+// for one memory round trip per group rather than per chunk; ids in LDS are read one chunk at a time.
 #pragma once
 
 #include "common.hpp"
@@ -26,8 +28,9 @@ struct Shared {
   int base[kMaxExperts];
 };
 
-// Group the P pairs of `ids` (global or LDS) with the whole workgroup (every thread calls it).
-template <typename IdPtr>
+// Group the P pairs of `ids` (global or LDS) with the whole workgroup (every thread calls it);
+// kIdGroup chunks' ids are loaded together.
+template <int kIdGroup, typename IdPtr>
 __device__ __forceinline__ void group_pairs(IdPtr ids, int P, int E, int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets,
                                             int32_t* __restrict__ sorted_pair,
@@ -50,13 +53,28 @@ __device__ __forceinline__ void group_pairs(IdPtr ids, int P, int E, int32_t* __
   const int c_end = min(chunks, c_begin + per_wave);
   int* my_hist = hist + w * E;
 
+  // ids of chunks c0 .. c0 + kIdGroup - 1 of this wave (0 past the wave's range or past P)
+  auto load_ids = [&](int c0, int (&ev)[kIdGroup]) {
+#pragma unroll
+    for (int j = 0; j < kIdGroup; ++j) {
+      const int p = ((c0 + j) << 6) + lane;
+      ev[j] = (c0 + j < c_end && p < P) ? ids[p] : 0;
+    }
+  };
+
   // 1. per-wave histogram
-  for (int c = c_begin; c < c_end; ++c) {
-    const int p = (c << 6) + lane;
-    const bool valid = p < P;
-    const int e = valid ? ids[p] : 0;
-    const uint64_t peers = match_key(e, valid);
-    if (valid && lane == __ffsll((unsigned long long)peers) - 1) my_hist[e] += __popcll(peers);
+  for (int c0 = c_begin; c0 < c_end; c0 += kIdGroup) {
+    int ev[kIdGroup];
+    load_ids(c0, ev);
+#pragma unroll
+    for (int j = 0; j < kIdGroup; ++j) {
+      const int c = c0 + j;
+      if (c >= c_end) break;  // uniform
+      const int p = (c << 6) + lane;
+      const bool valid = p < P;
+      const uint64_t peers = match_key(ev[j], valid);
+      if (valid && lane == __ffsll((unsigned long long)peers) - 1) my_hist[ev[j]] += __popcll(peers);
+    }
   }
   __syncthreads();
 
@@ -99,20 +117,27 @@ __device__ __forceinline__ void group_pairs(IdPtr ids, int P, int E, int32_t* __
   __syncthreads();
 
   // 4. stable placement
-  for (int c = c_begin; c < c_end; ++c) {
-    const int p = (c << 6) + lane;
-    const bool valid = p < P;
-    const int e = valid ? ids[p] : 0;
-    const uint64_t peers = match_key(e, valid);
-    if (valid) {
-      const int pos = base[e] + my_hist[e] + __popcll(peers & lanemask_lt(lane));
-      sorted_pair[pos] = p;
-      pair_pos[p] = pos;
+  for (int c0 = c_begin; c0 < c_end; c0 += kIdGroup) {
+    int ev[kIdGroup];
+    load_ids(c0, ev);
+#pragma unroll
+    for (int j = 0; j < kIdGroup; ++j) {
+      const int c = c0 + j;
+      if (c >= c_end) break;  // uniform
+      const int p = (c << 6) + lane;
+      const bool valid = p < P;
+      const int e = ev[j];
+      const uint64_t peers = match_key(e, valid);
+      if (valid) {
+        const int pos = base[e] + my_hist[e] + __popcll(peers & lanemask_lt(lane));
+        sorted_pair[pos] = p;
+        pair_pos[p] = pos;
+      }
+      // every lane of this wave has read my_hist[e] above before the leader advances it
+      __builtin_amdgcn_wave_barrier();
+      if (valid && lane == __ffsll((unsigned long long)peers) - 1) my_hist[e] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
     }
-    // every lane of this wave has read my_hist[e] above before the leader advances it
-    __builtin_amdgcn_wave_barrier();
-    if (valid && lane == __ffsll((unsigned long long)peers) - 1) my_hist[e] += __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
   }
 }
 

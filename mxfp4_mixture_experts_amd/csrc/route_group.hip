@@ -27,7 +27,7 @@ __global__ __launch_bounds__(1024) void route_group_kernel(
   for (int t = w; t < T; t += nw)
     route_dev::route_token<EPL>(logits, t, E, k, score_fn, renorm, ids, weights, ids_lds);
   __syncthreads();
-  group_dev::group_pairs(static_cast<const int32_t*>(ids_lds), T * k, E, counts, offsets, sorted_pair,
+  group_dev::group_pairs<1>(static_cast<const int32_t*>(ids_lds), T * k, E, counts, offsets, sorted_pair,
                          pair_pos, active, n_active, sh);
 }
 
