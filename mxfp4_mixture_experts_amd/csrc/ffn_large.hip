@@ -13,7 +13,8 @@
 //     The reduction order inside a step is a fixed permutation of K, applied identically to A and B,
 //     which is all a dot product needs;
 //   - gate columns i and up columns I+i of a wave land in the same lanes, so the clamp-SwiGLU
-//     epilogue runs in registers; h is written in fp32, like the weight-streaming kernels do;
+//     epilogue runs in registers; h is written as its two bf16 planes, like the weight-streaming
+//     kernels do;
 //   - the down GEMM feeds h to the bf16 MFMA as an exact-to-fp32 pair hi + lo (hi = bf16(h),
 //     lo = bf16(h - hi)), two MFMAs per operand: a single bf16 rounding of h alone can cost up to
 //     ~2% of the output's rms at small I or k (no averaging over many terms), while these medium-M

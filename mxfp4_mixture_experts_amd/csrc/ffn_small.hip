@@ -12,10 +12,11 @@
 //   - the codes are decoded in registers with the gfx950 FP4 conversion (two codes per instruction)
 //     and consumed by dot2 instructions with fp32 accumulation: bf16 dot2 against x (gate/up, codes
 //     decoded with their scale; bf16 products are exact in fp32), fp16 dot2 against h (down, codes
-//     decoded unscaled, the block's scale applied to the block's sum). h is kept in fp32 in memory;
-//     each lane turns its 32-value h block into fp16 with a power-of-two scale that puts the block's
-//     largest magnitude in [2^14, 2^15), so no value overflows and each keeps fp16's 11-bit
-//     precision (relative to the block maximum);
+//     decoded unscaled, the block's scale applied to the block's sum). h is kept in memory as two
+//     bf16 planes, hi = bf16(h) and lo = bf16(h - hi); each lane rebuilds its 32-value h block as
+//     hi + lo and turns it into fp16 with a power-of-two scale that puts the block's largest
+//     magnitude in [2^14, 2^15), so no value overflows and each keeps fp16's 11-bit precision
+//     (relative to the block maximum);
 //   - partial sums are reduced across the row's lanes with DPP adds, deterministically;
 //   - gate row i and up row I+i are handled by the same lanes, so SwiGLU (with the optional clamp) is
 //     applied in registers and only h is written (gate_up fusion as in vllm.cpp PR #52; clamp-SwiGLU
