@@ -127,9 +127,9 @@ int moe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* coun
 
 /*
  * moe_route_group — moe_route_topk followed by moe_group_tokens, with the same arguments, limits and
- * outputs (bitwise identical: the same device code runs). For small batches (T <= 64 and
+ * outputs (bitwise identical: the same device code runs). For small batches (T <= 16 and
  * T*k <= 1024, the decode regime) both steps run in one single-workgroup launch that keeps the ids in
- * LDS between them; larger batches enqueue the two separate kernels. topk_ids and topk_w are still
+ * LDS between them (a wave per token); larger batches enqueue the two separate kernels. topk_ids and topk_w are still
  * written in full. The fusion follows the pages' accounting of launch and dispatch overhead at
  * decode (vllm.cpp PR #52 node-trace diff; "MTP1 Post-Portfolio Eager-Cycle Profile").
  */

@@ -107,11 +107,12 @@ def test_group_empty(orc):
 
 
 @pytest.mark.parametrize("T,E,k,score_fn,renorm", [(1, 128, 8, 0, True), (8, 256, 8, 0, True), (2, 64, 1, 1, False),
-                                                   (17, 300, 5, 0, False), (64, 512, 16, 1, True),
+                                                   (16, 512, 16, 1, True), (17, 300, 5, 0, False),
+                                                   (64, 512, 16, 1, True),
                                                    (65, 256, 8, 0, True), (200, 64, 6, 1, True),
                                                    (0, 32, 4, 0, True)])
 def test_route_group_matches_separate_calls(orc, T, E, k, score_fn, renorm):
-    """moe_route_group (one launch for T <= 64, the two kernels above) equals route_topk followed by
+    """moe_route_group (one launch for T <= 16, the two kernels above) equals route_topk followed by
     group_tokens bit for bit, and the oracle on ids and grouping."""
     print(f"route_group T={T} E={E} k={k} fn={score_fn} renorm={renorm}", flush=True)
     rng = np.random.default_rng(T * 1000 + E + k)
