@@ -212,6 +212,35 @@ def main():
     except Exception as exc:  # capture unsupported: report eager
         log(f"graph capture failed: {exc!r}")
 
+    # warm weights, labelled: the same replica every step (what of it fits the 256 MB Infinity Cache
+    # stays there), eager, layer events only
+    n_warm = min(args.steps, 50)
+    ev_warm = [(mk(), mk()) for _ in range(n_warm)]
+    with torch.cuda.stream(stream):
+        step(0)
+        for a, b in ev_warm:
+            a.record(stream)
+            step(0)
+            b.record(stream)
+    torch.cuda.synchronize()
+    warm_us = [el(a, b) for a, b in ev_warm]
+
+    # attainable read bandwidth on this machine: a plain device reduction of 2 GiB in rows of 4096 floats
+    # (one output per row; best of 5). A single whole-buffer sum reaches only about two thirds of it.
+    probe = torch.zeros((1 << 31) // 4, dtype=torch.float32, device="cuda")
+    probe_s = []
+    for _ in range(5):
+        a, b = mk(), mk()
+        a.record(stream)
+        with torch.cuda.stream(stream):
+            probe.view(-1, 4096).sum(dim=1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        probe_s.append(a.elapsed_time(b) / 1e3)
+    read_probe_gbps = probe.numel() * 4 / min(probe_s) / 1e9
+    del probe
+    log(f"warm weights: median {med(warm_us):.1f} us/layer eager; read probe {read_probe_gbps:.0f} GB/s")
+
     use_graph = args.mode == "graph" and graph_s is not None
     total_s = graph_s if use_graph else eager_s
     us_layer = med(graph_layer_us) if use_graph else med(layer_us)
@@ -281,6 +310,10 @@ def main():
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "ffn_only_us": round(ffn_med, 2),
         "weight_stream_GBps_ffn_only": round(weight_bytes / (ffn_med * 1e-6) / 1e9, 1),
+        "read_probe_GBps": round(read_probe_gbps, 1),
+        "pct_read_probe": round(100 * gbps / read_probe_gbps, 1),
+        "us_per_layer_warm_eager": {"median": round(med(warm_us), 2), "steps": n_warm,
+                                    "note": "one weight replica reused every step (not the metric)"},
         "stage_us_eager_median": {"route+group": round(med(route_group_us), 2), "gate_up": round(med(stage_us[0]), 2),
                                   "down": round(med(stage_us[1]), 2), "combine": round(med(stage_us[2]), 2)},
         "active_experts": n_active,
