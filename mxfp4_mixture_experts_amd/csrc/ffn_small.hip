@@ -195,8 +195,8 @@ __device__ __forceinline__ int item_cost(int M, int MT) { return 3 * ((M + MT - 
 
 // The workgroup's items: contiguous ranges of the (expert, tile) list holding equal shares of the
 // total cost, so workgroups streaming experts with more rows get fewer items (`weighted`; without
-// it, when every expert has the same row count, equal item counts). Every wave computes
-// the range from the active list and the counts (uniform values, no LDS). A range boundary at cost
+// it, when every expert has the same row count, equal item counts). One wave computes the range
+// from the active list and the counts (uniform values). A range boundary at cost
 // position p is the first item whose cost interval starts at or after p; every workgroup evaluates
 // it the same way, so the end of one range is the begin of the next.
 __device__ __forceinline__ bool my_items(const int32_t* list, const int* count_ptr,
@@ -247,6 +247,26 @@ __device__ __forceinline__ bool my_items(const int32_t* list, const int* count_p
   }
   ir.begin = begin;
   ir.end = end;
+  return ir.begin < ir.end;
+}
+
+// The workgroup's range, computed by its first wave alone and passed to the others through LDS
+// (every wave of the GPU loading the same few lines of the list and the counts at once would queue
+// on those lines). Returns false, in every wave, for an empty range.
+__device__ __forceinline__ bool my_items_wg(const int32_t* list, const int* count_ptr,
+                                            const int32_t* counts, int tiles, int MT, int weighted,
+                                            int* shared_range, ItemRange& ir) {
+  if (threadIdx.x < 64) {
+    ItemRange r{0, 0};
+    if (!my_items(list, count_ptr, counts, tiles, MT, weighted, r)) r = ItemRange{0, 0};
+    if (threadIdx.x == 0) {
+      shared_range[0] = r.begin;
+      shared_range[1] = r.end;
+    }
+  }
+  __syncthreads();
+  ir.begin = shared_range[0];
+  ir.end = shared_range[1];
   return ir.begin < ir.end;
 }
 
@@ -306,10 +326,10 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
   constexpr bool kGate = MODE != kUpWithGate;
   constexpr bool kUp = MODE != kGateOnly;
   __shared__ int counter;
+  __shared__ int range[2];
   ItemRange ir;
-  if (!my_items(list, list_count, counts, tiles, MT, weighted, ir)) return;
   if (threadIdx.x == 0) counter = 0;
-  __syncthreads();
+  if (!my_items_wg(list, list_count, counts, tiles, MT, weighted, range, ir)) return;
 
   const int lane = threadIdx.x & 63;
   const int lg = ilog2(lpr);
@@ -493,10 +513,10 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     int lpr, const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo,
     float* __restrict__ y) {
   __shared__ int counter;
+  __shared__ int range[2];
   ItemRange ir;
-  if (!my_items(list, list_count, counts, tiles, MT, weighted, ir)) return;
   if (threadIdx.x == 0) counter = 0;
-  __syncthreads();
+  if (!my_items_wg(list, list_count, counts, tiles, MT, weighted, range, ir)) return;
 
   const int lane = threadIdx.x & 63;
   const int lg = ilog2(lpr);
