@@ -100,6 +100,49 @@ def test_dense_shapes(orc, case):
         np.testing.assert_array_equal(g["out_bf16"], outs["default"])
 
 
+def crafted_case(T, H, I, rows, seed):
+    """k = 1, expert e receives exactly rows[e] tokens (logits one-hot on the chosen expert)."""
+    E = len(rows)
+    assert sum(rows) == T
+    cfg, inp = moe_synth.small_case(T, H, I, E, 1, seed)
+    owner = np.repeat(np.arange(E), rows)
+    logits = np.zeros((T, E), np.float32)
+    logits[np.arange(T), owner] = 1.0
+    inp["logits"] = logits
+    return cfg, inp
+
+
+DENSE_EDGES = [
+    # T, H, I, rows per expert: one row past a full tile; a 256-row dense expert next to a 255-row
+    # row-tile expert; an output width that is a multiple of neither down column tile (480)
+    (257, 96, 64, (257,), 31),
+    (511, 160, 96, (256, 255), 32),
+    (300, 480, 160, (300,), 33),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_EDGES, ids=lambda c: "T%d_H%d_I%d_rows%s" % (c[0], c[1], c[2], "-".join(map(str, c[3]))))
+def test_dense_edges(orc, case):
+    T, H, I, rows, seed = case
+    cfg, inp = crafted_case(T, H, I, rows, seed)
+    ref = oracle_full(orc, inp, cfg)
+    np.testing.assert_array_equal(ref["counts"], np.array(rows))
+    w = weights_to_device(inp)
+    outs = []
+    for cols in (0, 256, 224):
+        print(f"dense edge T={T} H={H} I={I} rows={rows} down cols={cols or 'auto'}", flush=True)
+        prev = moe.set_dense_down_cols(cols)
+        try:
+            g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w, renorm=cfg.renorm)
+        finally:
+            moe.set_dense_down_cols(prev)
+        np.testing.assert_array_equal(g["sorted_pair"], ref["sorted_pair"])
+        assert_output_parity(g["out_bf16"], ref["out_ref"], f"dense edge {rows} cols={cols}")
+        outs.append(g["out_bf16"])
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_H%d_I%d_E%d_k%d" % c[:5])
 def test_small_shapes(orc, case):
     T, H, I, E, k, fn, clamp, seed = case
