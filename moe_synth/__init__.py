@@ -125,6 +125,13 @@ def make_weights(E: int, H: int, I: int, seed: int, scale_lo: int = 120, scale_h
     )
 
 
+def make_router_weights(E: int, H: int, seed: int) -> np.ndarray:
+    """Router weights W_router[E, H] as bfloat16 bits, N(0, 1/H) from their own seed, so that with
+    N(0, 1) activations the logits are about N(0, 1), like the logits the configs draw directly."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return f32_to_bf16_bits((rng.standard_normal(size=(E, H), dtype=np.float32) / np.float32(np.sqrt(H))))
+
+
 def small_case(T: int, H: int, I: int, E: int, k: int, seed: int, logits: str = "normal",
                score_fn: int = SCORE_SOFTMAX, clamp: float = 0.0) -> tuple[Config, dict]:
     """A random small workload with explicit shape (ragged shapes, edge cases)."""

@@ -71,6 +71,8 @@ class OracleLib:
         lib.oracle_mxfp4_ffn.argtypes = [P, i, i, i, i, i, P, P, P, P, P, P, ctypes.c_double, i,
                                          P, P, P]
         lib.oracle_mxfp4_ffn.restype = i
+        lib.oracle_router_logits.argtypes = [P, P, i, i, i, i, P]
+        lib.oracle_router_logits.restype = i
         lib.oracle_num_threads.argtypes = [i]
         lib.oracle_num_threads.restype = i
         self.lib = lib
@@ -106,6 +108,19 @@ class OracleLib:
         if rc != 0:
             raise ValueError(f"oracle_route_topk failed with {rc}")
         return ids, w
+
+    def router_logits(self, x_bf16: np.ndarray, w_bf16: np.ndarray, nthreads: int = 0) -> np.ndarray:
+        """float64[T,E] = x . w^T for bfloat16 bit arrays x[T,H] and w[E,H]."""
+        x = _c(x_bf16, np.uint16)
+        w = _c(w_bf16, np.uint16)
+        T, H = x.shape
+        E = w.shape[0]
+        assert w.shape[1] == H
+        out = np.zeros((T, E), np.float64)
+        rc = self.lib.oracle_router_logits(_ptr(x), _ptr(w), T, H, E, int(nthreads), _ptr(out))
+        if rc != 0:
+            raise ValueError(f"oracle_router_logits failed with {rc}")
+        return out
 
     def group_tokens(self, topk_ids: np.ndarray, E: int) -> dict:
         ids = _c(topk_ids, np.int32)
@@ -214,6 +229,10 @@ def route_topk(logits, k, score_fn=SCORE_SOFTMAX, renorm=True):
 
 def group_tokens(topk_ids, E):
     return default().group_tokens(topk_ids, E)
+
+
+def router_logits(x_bf16, w_bf16, nthreads=0):
+    return default().router_logits(x_bf16, w_bf16, nthreads)
 
 
 def mxfp4_ffn(x_bf16, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, clamp_limit=0.0, nthreads=0,

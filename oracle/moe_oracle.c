@@ -13,6 +13,9 @@
  *     32 E2M1 elements sharing one E8M0 scale. The pages name MXFP4 as the weight format of the routed
  *     expert GEMMs (vllm.cpp PR #52 title and body; b70-optimization-lab "MTP1 Post-Portfolio
  *     Eager-Cycle Profile", Purpose And Identity: "MXFP4 N64 policy") without defining it.
+ *   - Router logits: the token's hidden state projected onto one vector per expert. The pages time
+ *     only the router's select/normalize kernel (next item) and do not define the projection; the
+ *     plainest reading is a dense bf16 matrix W_router[E, H], logits = x . W_router^T.
  *   - Routing: per token, score the experts, select the top k, normalise the selected weights
  *     ("Native router select/normalize" row of the Post-Portfolio Device Attribution table).
  *   - Grouping: the pairs (token, slot) are remapped into per-expert order ("Direct M=2 route remap"
@@ -266,6 +269,32 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
   }
   if (own_y) free(y);
   return bad ? -2 : 0;
+}
+
+/* ---- router logits ------------------------------------------------------------------------ */
+
+/* logits[t][e] = sum over h of x[t][h] * w[e][h] for bfloat16 x[T, H] and w[E, H], in fp64 with h
+ * ascending (a product of two bfloat16 values is exact in fp64). Tokens are independent, so the
+ * thread count changes no result. */
+int oracle_router_logits(const uint16_t* x_bf16, const uint16_t* w_bf16, int T, int H, int E,
+                         int nthreads, double* logits) {
+  if (T < 0 || H < 1 || E < 1 || (T > 0 && (!x_bf16 || !w_bf16 || !logits))) return -2;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+#else
+  (void)nthreads;
+#endif
+  for (long t = 0; t < T; ++t) {
+    const uint16_t* xr = x_bf16 + t * (long)H;
+    for (long e = 0; e < E; ++e) {
+      const uint16_t* wr = w_bf16 + e * (long)H;
+      double acc = 0.0;
+      for (long h = 0; h < H; ++h) acc += oracle_bf16_to_double(xr[h]) * oracle_bf16_to_double(wr[h]);
+      logits[t * (long)E + e] = acc;
+    }
+  }
+  return 0;
 }
 
 int oracle_num_threads(int nthreads) {

@@ -41,6 +41,10 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
                      double clamp_limit, int nthreads, double* y_pairs, double* out_ref,
                      uint16_t* out_bf16);
 
+/* Router logits f64[T,E] = x . w^T for bfloat16 x[T,H] and w[E,H] (fp64, h ascending). */
+int oracle_router_logits(const uint16_t* x_bf16, const uint16_t* w_bf16, int T, int H, int E,
+                         int nthreads, double* logits);
+
 int oracle_num_threads(int nthreads);
 
 #ifdef __cplusplus
