@@ -241,6 +241,40 @@ def main():
     del probe
     log(f"warm weights: median {med(warm_us):.1f} us/layer eager; read probe {read_probe_gbps:.0f} GB/s")
 
+    # the router projection + top-k at this workload's sizes (the step before routing; not part of
+    # `value`): bf16 W_router[E, H], one hipGraph of 50 calls, best of 5 replays
+    w_router = dev(moe_synth.make_router_weights(E, H, 20261203 + 99).view(np.int16)).view(torch.bfloat16)
+    ws_router = torch.empty(moe.router_gemm_topk_workspace_size(T, H, E), dtype=torch.uint8, device="cuda")
+    r_ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    n_router = 50
+    with torch.cuda.stream(stream):
+        moe.router_gemm_topk(x, w_router, k, cfg.score_fn, cfg.renorm, want_logits=False,
+                             workspace=ws_router, stream=stream)
+    torch.cuda.synchronize()
+    router_us = None
+    try:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for _ in range(n_router):
+                moe.router_gemm_topk(x, w_router, k, cfg.score_fn, cfg.renorm, want_logits=False,
+                                     workspace=ws_router, stream=stream)
+        best = None
+        for _ in range(5):
+            a, b = mk(), mk()
+            a.record(stream)
+            gr.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            v = a.elapsed_time(b) * 1e3 / n_router
+            best = v if best is None else min(best, v)
+        router_us = best
+        del gr
+    except Exception as exc:  # capture unsupported: skip the router line
+        log(f"router graph capture failed: {exc!r}")
+    del r_ids
+    if router_us is not None:
+        log(f"router gemm+top-k: {router_us:.2f} us per call")
+
     use_graph = args.mode == "graph" and graph_s is not None
     total_s = graph_s if use_graph else eager_s
     us_layer = med(graph_layer_us) if use_graph else med(layer_us)
@@ -314,6 +348,12 @@ def main():
         "pct_read_probe": round(100 * gbps / read_probe_gbps, 1),
         "us_per_layer_warm_eager": {"median": round(med(warm_us), 2), "steps": n_warm,
                                     "note": "one weight replica reused every step (not the metric)"},
+        "router_gemm_topk": (None if router_us is None else {
+            "us": round(router_us, 2),
+            "weight_GBps": round(E * H * 2 / (router_us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * E * H * 2 / (router_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
+            "tflops": round(2 * T * E * H / (router_us * 1e-6) / 1e12, 2),
+            "note": "logits = x . W_router^T (bf16 [E, H]) and top-k, graph of 50 calls; not part of value"}),
         "stage_us_eager_median": {"route+group": round(med(route_group_us), 2), "gate_up": round(med(stage_us[0]), 2),
                                   "down": round(med(stage_us[1]), 2), "combine": round(med(stage_us[2]), 2)},
         "active_experts": n_active,

@@ -102,6 +102,31 @@ int moe_route_topk(const float* logits, int T, int E, int k, int score_fn, int r
                    int32_t* topk_ids, float* topk_w, void* stream);
 
 /*
+ * moe_router_gemm_topk — the router's projection and its top-k in one call:
+ *   logits[t, e] = sum over h of x[t, h] * w_router[e, h]   (bfloat16 operands, fp32 accumulation)
+ * followed by exactly the selection and weights of moe_route_topk on those logits (the same device
+ * code). The pages time only the router's select/normalize kernel ("Native router select/normalize"
+ * row, Post-Portfolio Device Attribution table, "MTP1 Post-Portfolio Eager-Cycle Profile") and leave
+ * the projection before it undefined; here it is a dense bfloat16 matrix.
+ * The projection runs on the matrix cores with K split into up to 16 slices (chosen from T, H and E
+ * only); the slices' partial logits go to the workspace and are summed in slice order, so results
+ * are deterministic for given sizes. Two kernels are enqueued.
+ *
+ *   x_bf16         [dev] u16[T, H]  bfloat16 activations, 16-byte aligned
+ *   w_router_bf16  [dev] u16[E, H]  bfloat16 router weights (one row per expert), 16-byte aligned
+ *   logits         [dev] f32[T, E]  (written) or NULL
+ *   topk_ids, topk_w               as moe_route_topk (written)
+ *   workspace, ws_bytes            [dev] at least moe_router_gemm_topk_workspace_size(T, H, E) bytes,
+ *                                  256-byte aligned; contents on entry do not matter
+ * Limits: T >= 0 (T == 0 enqueues nothing), 32 <= H <= MOE_MAX_HIDDEN, H % 32 == 0,
+ * 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK), T*k <= MOE_MAX_PAIRS, score_fn in {0, 1}.
+ */
+size_t moe_router_gemm_topk_workspace_size(int T, int H, int E);  /* host; 0 for invalid sizes */
+int moe_router_gemm_topk(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int E,
+                         int k, int score_fn, int renorm, float* logits, int32_t* topk_ids,
+                         float* topk_w, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * moe_group_tokens — token-to-expert grouping (expert histogram, exclusive prefix scan and a stable
  * permutation of the pairs by expert).
  * ("Direct M=2 route remap" row, Post-Portfolio Device Attribution table, "MTP1 Post-Portfolio

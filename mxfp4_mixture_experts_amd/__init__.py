@@ -64,6 +64,10 @@ def load_library(path: str | None = None):
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_route_topk.argtypes = [V, i, i, i, i, i, V, V, V]
     lib.moe_route_topk.restype = i
+    lib.moe_router_gemm_topk_workspace_size.argtypes = [i, i, i]
+    lib.moe_router_gemm_topk_workspace_size.restype = ctypes.c_size_t
+    lib.moe_router_gemm_topk.argtypes = [V, V, i, i, i, i, i, i, V, V, V, V, ctypes.c_size_t, V]
+    lib.moe_router_gemm_topk.restype = i
     lib.moe_group_tokens.argtypes = [V, i, i, i, V, V, V, V, V, V, V]
     lib.moe_group_tokens.restype = i
     lib.moe_route_group.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V]
@@ -164,6 +168,37 @@ def route_topk(logits: torch.Tensor, k: int, score_fn: int = SCORE_SOFTMAX, reno
     _check(load_library().moe_route_topk(_ptr(logits), T, E, k, score_fn, int(bool(renorm)),
                                          _ptr(ids), _ptr(weights), _stream(stream)), "moe_route_topk")
     return ids, weights
+
+
+def router_gemm_topk_workspace_size(T: int, H: int, E: int) -> int:
+    n = load_library().moe_router_gemm_topk_workspace_size(T, H, E)
+    if n == 0:
+        raise MoeError("invalid sizes for moe_router_gemm_topk_workspace_size")
+    return n
+
+
+def router_gemm_topk(x: torch.Tensor, w_router: torch.Tensor, k: int, score_fn: int = SCORE_SOFTMAX,
+                     renorm: bool = True, want_logits: bool = True, workspace: torch.Tensor | None = None,
+                     stream=None):
+    """logits = x . w_router^T (bf16, fp32 accumulation) and their top-k; returns
+    (topk_ids, topk_w, logits or None)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_router, torch.bfloat16, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise MoeError("w_router must be [E, H] with the H of x")
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    weights = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    need = router_gemm_topk_workspace_size(T, H, E)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(load_library().moe_router_gemm_topk(_ptr(x), _ptr(w_router), T, H, E, int(k), int(score_fn),
+                                               int(bool(renorm)), _ptr(logits), _ptr(ids), _ptr(weights),
+                                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                               _stream(stream)), "moe_router_gemm_topk")
+    return ids, weights, logits
 
 
 @dataclass

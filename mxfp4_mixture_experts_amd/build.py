@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libmoe_mxfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "route.hip", "group.hip", "route_group.hip", "ffn_small.hip", "ffn_large.hip",
-           "ffn_dense.hip", "combine.hip"]
+           "ffn_dense.hip", "combine.hip", "router.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -163,6 +163,30 @@ MOE_API int moe_route_topk(const float* logits, int T, int E, int k, int score_f
   return MOE_OK;
 }
 
+MOE_API size_t moe_router_gemm_topk_workspace_size(int T, int H, int E) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || H < 32 || H > MOE_MAX_HIDDEN || H % 32) return 0;
+  const size_t b = moe::router_workspace_bytes(T, H, E);
+  return b > 0 ? b : 256;
+}
+
+MOE_API int moe_router_gemm_topk(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int E,
+                                 int k, int score_fn, int renorm, float* logits, int32_t* topk_ids,
+                                 float* topk_w, void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E ||
+      (long)T * k > MOE_MAX_PAIRS || H < 32 || H > MOE_MAX_HIDDEN || H % 32)
+    return MOE_ERR_SHAPE;
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !w_router_bf16 || !topk_ids || !topk_w || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w_router_bf16, 16) || !aligned(workspace, 256))
+    return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < moe_router_gemm_topk_workspace_size(T, H, E)) return MOE_ERR_WORKSPACE;
+  if (moe::launch_router_gemm_topk(x_bf16, w_router_bf16, T, H, E, k, score_fn, renorm, (float*)workspace,
+                                   logits, topk_ids, topk_w, (hipStream_t)stream) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}
+
 MOE_API int moe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                              int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                              int32_t* active, int32_t* n_active, void* stream) {

@@ -7,6 +7,20 @@
 
 namespace moe {
 
+// Router GEMM (bf16 MFMA, K split into `splits` slices whose partial logits go to the workspace)
+// followed by the router's select/normalize on the in-order sum of the partials.
+struct RouterPlan {
+  int tiles_t;          // 64-token tiles
+  int splits;           // K slices
+  int steps_per_split;  // 32-wide K steps per slice
+  int blocks;           // workgroups of the GEMM
+};
+RouterPlan plan_router(int T, int H, int E);
+size_t router_workspace_bytes(int T, int H, int E);
+hipError_t launch_router_gemm_topk(const uint16_t* x, const uint16_t* w, int T, int H, int E, int k,
+                                   int score_fn, int renorm, float* part, float* logits, int32_t* ids,
+                                   float* weights, hipStream_t stream);
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int score_fn, int renorm,
                              int32_t* ids, float* weights, hipStream_t stream);
 

@@ -45,24 +45,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
   return (uint32_t)__builtin_amdgcn_readlane((int)k, 63);
 }
 
-// Route token t (one wave): ids[t*k + j] and weights[t*k + j] for j < k; the ids also go to
-// ids_copy[t*k + j] when it is not null (the fused kernel's LDS copy). Each of the k rounds takes
-// the wave maximum of the keys, then the lowest expert index holding it (expert e lives in lane
-// e % 64, slot e / 64, so the first slot with a match and its lowest lane give the lowest index).
+// Route token t (one wave) from its logits, held as v[i] = logit of expert lane + 64 i (0 past E):
+// ids[t*k + j] and weights[t*k + j] for j < k; the ids also go to ids_copy[t*k + j] when it is not
+// null (the fused kernel's LDS copy). Each of the k rounds takes the wave maximum of the keys, then
+// the lowest expert index holding it (expert e lives in lane e % 64, slot e / 64, so the first slot
+// with a match and its lowest lane give the lowest index).
 template <int EPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
-                                            int score_fn, int renorm, int32_t* __restrict__ ids,
-                                            float* __restrict__ weights, int32_t* ids_copy) {
+__device__ __forceinline__ void route_values(const float (&v)[EPL], int t, int E, int k, int score_fn,
+                                             int renorm, int32_t* __restrict__ ids,
+                                             float* __restrict__ weights, int32_t* ids_copy) {
   const int lane = threadIdx.x & 63;
-  const float* row = logits + (size_t)t * E;
-  float v[EPL];
   uint32_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : 0.0f;
-    key[i] = e < E ? order_key(v[i]) : 0u;
-  }
+  for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? order_key(v[i]) : 0u;
 
   float my_v = 0.0f;  // lane j < k keeps the logit and id of rank j
   int my_e = -1;
@@ -116,6 +111,22 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     weights[(size_t)t * k + lane] = w;
     if (ids_copy) ids_copy[t * k + lane] = my_e;
   }
+}
+
+// Route token t (one wave) from row t of logits f32[T, E] (see route_values).
+template <int EPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int score_fn, int renorm, int32_t* __restrict__ ids,
+                                            float* __restrict__ weights, int32_t* ids_copy) {
+  const int lane = threadIdx.x & 63;
+  const float* row = logits + (size_t)t * E;
+  float v[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : 0.0f;
+  }
+  route_values<EPL>(v, t, E, k, score_fn, renorm, ids, weights, ids_copy);
 }
 
 }  // namespace route_dev

@@ -166,3 +166,25 @@ def test_dense_down_cols_setting(lib):
 def test_stage_events_validation(lib):
     assert lib.moe_set_stage_events(3, None, None) == -2
     assert lib.moe_set_stage_events(0, None, None) == 0
+
+
+def test_router_gemm_validation(lib):
+    lib.moe_router_gemm_topk_workspace_size.restype = ctypes.c_size_t
+    assert lib.moe_router_gemm_topk_workspace_size(8, 4096, 256) >= 8 * 256 * 4
+    assert lib.moe_router_gemm_topk_workspace_size(8, 4016, 256) == 0  # H % 32
+    assert lib.moe_router_gemm_topk_workspace_size(8, 4096, 513) == 0  # E > MOE_MAX_EXPERTS
+    need = lib.moe_router_gemm_topk_workspace_size(8, 4096, 256)
+    sz = ctypes.c_size_t
+    call = lambda **kw: lib.moe_router_gemm_topk(  # noqa: E731
+        kw.get("x", DUMMY), kw.get("w", DUMMY), kw.get("T", 8), kw.get("H", 4096), kw.get("E", 256),
+        kw.get("k", 8), kw.get("fn", 0), 1, None, kw.get("ids", DUMMY), DUMMY, kw.get("ws", DUMMY),
+        sz(kw.get("ws_bytes", need)), None)
+    assert call(H=96 + 16) == -2            # H % 32
+    assert call(k=9, E=8) == -2             # k > E
+    assert call(fn=3) == -3                 # unknown score function
+    assert call(T=0) == 0                   # nothing to do, nothing launched
+    assert call(x=None) == -1
+    assert call(ids=None) == -1
+    assert call(x=V(0x1008)) == -3          # x not 16-byte aligned
+    assert call(ws=V(0x1010)) == -3         # workspace not 256-byte aligned
+    assert call(ws_bytes=need - 1) == -4

@@ -1,0 +1,88 @@
+"""GPU parity of the router GEMM + top-k (moe_router_gemm_topk) against the oracle.
+
+The logits are compared with the fp64 oracle logits within the fp32 accumulation bound. The
+selection is checked where it is unique whatever the rounding: the ids must equal the oracle's top-k
+of the GPU's own logits bit for bit (selection is exact given the logits), the weights must be within
+the routing-weight bound, and both must equal moe_route_topk on those logits bitwise (the same device
+code). Sizes span ragged token, expert and hidden counts, every expert-count path of the selection
+kernel, one to sixteen K slices, and the decode and high-concurrency router shapes."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from _gpu import weight_rtol
+from _util import bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("mxfp4_mixture_experts_amd")
+
+CASES = [
+    # T, H, E, k, score_fn, renorm, seed
+    (1, 64, 8, 2, 0, True, 1),
+    (8, 4096, 256, 8, 0, True, 2),      # decode M=8 router
+    (5, 96, 65, 3, 1, False, 3),
+    (70, 544, 130, 6, 0, False, 4),
+    (257, 1024, 512, 16, 1, True, 5),
+    (33, 7168, 300, 8, 1, True, 6),
+    (1024, 7168, 256, 8, 1, True, 7),   # high-concurrency router
+    (64, 32, 1, 1, 0, True, 8),         # one K step, one expert
+]
+
+
+def bf16_tensor(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_H%d_E%d_k%d" % c[:4])
+def test_router_gemm_topk(orc, case):
+    T, H, E, k, fn, renorm, seed = case
+    print(f"router gemm T={T} H={H} E={E} k={k} fn={fn} renorm={renorm}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = moe_synth.f32_to_bf16_bits(rng.standard_normal(size=(T, H), dtype=np.float32))
+    w = moe_synth.make_router_weights(E, H, seed + 100)
+    xg, wg = bf16_tensor(x), bf16_tensor(w)
+    ids, tw, logits = moe.router_gemm_topk(xg, wg, k, fn, renorm)
+    ids2, tw2, logits2 = moe.router_gemm_topk(xg, wg, k, fn, renorm)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+
+    # logits against fp64: each of the H products is exact in fp32; allow one rounding per product
+    # and per slice addition, relative to the sum of the absolute products
+    ref = orc.router_logits(x, w)
+    mag = np.abs(bf16_to_f64(x)) @ np.abs(bf16_to_f64(w)).T
+    bound = (H + 64) * 2.0 ** -24 * mag + 1e-30
+    err = np.abs(lg.astype(np.float64) - ref)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    print(f"  max |logit err| {err.max():.3g} (bound {bound.max():.3g})", flush=True)
+
+    # selection: the oracle's top-k of the GPU logits, exactly; weights within the fp32 bound
+    oids, ow = orc.route_topk(lg, k, fn, renorm)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    n_terms = k if (renorm or fn == 1) else E
+    np.testing.assert_allclose(tw.cpu().numpy(), ow, rtol=weight_rtol(n_terms), atol=0)
+
+    # the same device code as moe_route_topk, and deterministic
+    rids, rw = moe.route_topk(logits, k, fn, renorm)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), rids.cpu().numpy())
+    np.testing.assert_array_equal(tw.cpu().numpy().view(np.uint32), rw.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(lg.view(np.uint32), logits2.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids2.cpu().numpy())
+
+
+def test_router_gemm_without_logits_and_empty():
+    rng = np.random.Generator(np.random.PCG64(9))
+    T, H, E, k = 8, 256, 32, 4
+    x = bf16_tensor(moe_synth.f32_to_bf16_bits(rng.standard_normal(size=(T, H), dtype=np.float32)))
+    w = bf16_tensor(moe_synth.make_router_weights(E, H, 10))
+    ids_a, w_a, lg = moe.router_gemm_topk(x, w, k)
+    ids_b, w_b, none = moe.router_gemm_topk(x, w, k, want_logits=False)
+    torch.cuda.synchronize()
+    assert none is None
+    np.testing.assert_array_equal(ids_a.cpu().numpy(), ids_b.cpu().numpy())
+    np.testing.assert_array_equal(w_a.cpu().numpy().view(np.uint32), w_b.cpu().numpy().view(np.uint32))
+    ids0, w0, lg0 = moe.router_gemm_topk(x[:0], w, k)
+    torch.cuda.synchronize()
+    assert ids0.shape == (0, k) and lg0.shape == (0, E)
