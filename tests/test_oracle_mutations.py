@@ -41,9 +41,12 @@ MUTANTS = {
     "unstable_group": ("sorted_pair[r] = (int32_t)p;", "sorted_pair[r] = (int32_t)(P - 1 - p);"),
     "bf16_truncate": ("double r = ldexp(nearbyint(ldexp(a, -q)), q);", "double r = ldexp(floor(ldexp(a, -q)), q);"),
     "x_decode_shift": ("uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+    "router_last_term_dropped": ("for (long h = 0; h < H; ++h) acc +=", "for (long h = 0; h < H - 1; ++h) acc +="),
+    "router_k_reversed": ("oracle_bf16_to_double(wr[h]);", "oracle_bf16_to_double(wr[H - 1 - h]);"),
 }
 
-PIN_MODULES = ["test_oracle_formats.py", "test_oracle_route.py", "test_oracle_group.py", "test_oracle_ffn.py"]
+PIN_MODULES = ["test_oracle_formats.py", "test_oracle_route.py", "test_oracle_group.py", "test_oracle_ffn.py",
+               "test_oracle_router.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
