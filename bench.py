@@ -44,6 +44,8 @@ def parse():
                     help="which timing is reported as value (both are measured)")
     ap.add_argument("--flags", type=int, default=0, help="moe_mxfp4_ffn flags (1 = unfused gate/up)")
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough for cold weights)")
+    ap.add_argument("--small-m-max", type=int, default=-1,
+                    help="launch-table threshold override (moe_set_small_m_max; -1 = the library's table)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -104,6 +106,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     moe.load_library()
+    if args.small_m_max >= 0:
+        moe.set_small_m_max(args.small_m_max)
     cfg = moe_synth.CONFIGS[args.config]
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     t0 = time.time()
@@ -339,7 +343,8 @@ def main():
                                + (f", clamp {cfg.clamp}" if cfg.clamp else ""),
                    "timing": (f"hipGraph of {L} layers, median of {reps} replays" if use_graph
                               else "eager, median step"),
-                   "flags": args.flags, "weight_replicas": R, "parallelism": "none (1 GPU)"},
+                   "flags": args.flags, "weight_replicas": R, "parallelism": "none (1 GPU)",
+                   "small_m_max": plan["small_m_max"]},
         "weight_stream_GBps": round(gbps, 1),
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "ffn_only_us": round(ffn_med, 2),
