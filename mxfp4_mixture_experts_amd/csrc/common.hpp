@@ -8,7 +8,6 @@ namespace moe {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -51,11 +50,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int sel>
 __device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t w, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, sel);
-}
-
-template <int sel>
-__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w, float scale) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, sel);
 }
 
 // Two E2M1 codes (byte `sel` of `w`) as fp16 values, unscaled (E2M1 values are exact in fp16).
