@@ -141,5 +141,55 @@ __device__ __forceinline__ void group_pairs(IdPtr ids, int P, int E, int32_t* __
   }
 }
 
+// The same grouping for at most 64 pairs, by one wave alone (lane p holds pair p): the other waves
+// of the workgroup may have exited. Each expert's count is written to LDS by the lowest lane
+// holding it, one wave-wide scan over the experts gives counts, offsets and the active list (and
+// turns the LDS counts into base rows), and each pair's row is its expert's base plus the number of
+// lower lanes holding the same expert — the definition above, so the outputs are the same.
+template <typename IdPtr>
+__device__ __forceinline__ void group_pairs_one_wave(IdPtr ids, int P, int E, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_pair,
+                                                     int32_t* __restrict__ pair_pos,
+                                                     int32_t* __restrict__ active,
+                                                     int32_t* __restrict__ n_active, Shared& sh) {
+  const int lane = threadIdx.x & 63;
+  int* cnt = sh.total;  // per expert: count, then base row
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  const bool valid = lane < P;
+  const int my_e = valid ? ids[lane] : 0;
+  const uint64_t peers = match_key(my_e, valid);
+  const int rank = __popcll(peers & lanemask_lt(lane));
+  // LDS accesses of one wave complete in order: the zeroing above lands before these counts
+  if (valid && rank == 0) cnt[my_e] = __popcll(peers);
+
+  int carry = 0, acarry = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int c = e < E ? cnt[e] : 0;
+    const int incl = wave_inclusive_scan(c, lane);
+    if (e < E) {
+      counts[e] = c;
+      offsets[e] = carry + incl - c;
+      cnt[e] = carry + incl - c;
+    }
+    carry += __shfl(incl, 63, 64);
+    const bool act = e < E && c > 0;
+    const uint64_t am = __ballot(act);
+    if (act) active[acarry + __popcll(am & lanemask_lt(lane))] = e;
+    acarry += __popcll(am);
+  }
+  if (lane == 0) {
+    offsets[E] = carry;
+    *n_active = acarry;
+  }
+  for (int i = acarry + lane; i < E; i += 64) active[i] = -1;
+  if (valid) {
+    const int pos = cnt[my_e] + rank;
+    sorted_pair[pos] = lane;
+    pair_pos[lane] = pos;
+  }
+}
+
 }  // namespace group_dev
 }  // namespace moe

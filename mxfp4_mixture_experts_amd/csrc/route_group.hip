@@ -1,5 +1,6 @@
 // Router top-k fused with the token grouping, for small batches (decode): one workgroup routes every
-// token (a wave per token), keeps the chosen ids in LDS and, after one barrier, groups them. The two
+// token (a wave per token), keeps the chosen ids in LDS and, after one barrier, groups them (at most
+// 64 pairs: the first wave alone, one pair per lane). The two
 // steps then cost one launch and no round trip of the ids through memory; the outputs are the same
 // as those of the two separate kernels (same device code, see route_dev.hpp and group_dev.hpp).
 #include "common.hpp"
@@ -30,6 +31,12 @@ __global__ __launch_bounds__(1024) void route_group_kernel(
   for (int t = w; t < T; t += nw)
     route_dev::route_token<EPL>(logits, t, E, k, score_fn, renorm, ids, weights, ids_lds);
   __syncthreads();
+  if (T * k <= 64) {  // one pair per lane of the first wave; the other waves are done
+    if (w == 0)
+      group_dev::group_pairs_one_wave(static_cast<const int32_t*>(ids_lds), T * k, E, counts, offsets,
+                                      sorted_pair, pair_pos, active, n_active, sh);
+    return;
+  }
   group_dev::group_pairs<1>(static_cast<const int32_t*>(ids_lds), T * k, E, counts, offsets, sorted_pair,
                          pair_pos, active, n_active, sh);
 }
