@@ -358,7 +358,8 @@ def main():
             "weight_GBps": round(E * H * 2 / (router_us * 1e-6) / 1e9, 1),
             "pct_hbm_peak": round(100 * E * H * 2 / (router_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
             "tflops": round(2 * T * E * H / (router_us * 1e-6) / 1e12, 2),
-            "note": "logits = x . W_router^T (bf16 [E, H]) and top-k, graph of 50 calls; not part of value"}),
+            "note": ("logits = x . W_router^T (bf16 [E, H]) and top-k, graph of 50 calls on the same operands "
+                     "(warm: they stay in the Infinity Cache); not part of value")}),
         "stage_us_eager_median": {"route+group": round(med(route_group_us), 2), "gate_up": round(med(stage_us[0]), 2),
                                   "down": round(med(stage_us[1]), 2), "combine": round(med(stage_us[2]), 2)},
         "active_experts": n_active,
