@@ -10,7 +10,8 @@ namespace moe {
 // Router GEMM (bf16 MFMA, K split into `splits` slices whose partial logits go to the workspace)
 // followed by the router's select/normalize on the in-order sum of the partials.
 struct RouterPlan {
-  int tiles_t;          // 64-token tiles
+  int nb;               // 16-token blocks per workgroup tile (1, 2 or 4)
+  int tiles_t;          // token tiles of 16 * nb tokens
   int splits;           // K slices
   int steps_per_split;  // 32-wide K steps per slice
   int blocks;           // workgroups of the GEMM

@@ -4,16 +4,18 @@
 // The pages time the router only as its select/normalize kernel ("Native router select/normalize"
 // row of the Post-Portfolio Device Attribution table, "MTP1 Post-Portfolio Eager-Cycle Profile") and
 // leave the projection before it undefined; here it is a dense bf16 matrix W_router[E, H].
-//   - The projection runs on the matrix cores (v_mfma_f32_16x16x32_bf16). A workgroup owns 64 tokens
-//     x 64 experts and one slice of K; each of its four waves computes 16 tokens x 64 experts and
-//     loads its operands straight into the MFMA lane layout (lane: row / expert j16, K elements
-//     8g .. 8g+7 of a 32-wide step), with no LDS: the tile is small and the weight rows are streamed
-//     once per token tile.
-//   - At decode there are only one or two 64 x 64 tiles per expert group, so K is split into up to 16
-//     slices to spread the weight stream over the GPU; each slice writes its partial logits to the
-//     workspace.
-//   - One wave per token then sums its partial logits in slice order (deterministic, no atomics),
-//     optionally writes the logits, and runs the same selection code as the router kernel.
+//   - The projection runs on the matrix cores (v_mfma_f32_16x16x32_bf16). Up to 32 tokens, a workgroup
+//     owns 16 NB tokens (NB = 1 or 2 16-token blocks) x 64 experts and one slice of K; each of its four
+//     waves computes 16 experts for the NB blocks and loads its operands straight into the MFMA lane
+//     layout (lane: token / expert j16, K elements 8g .. 8g+7 of a 32-wide step), with no LDS: the
+//     activations are a few rows and each wave streams its own expert rows. Above 32 tokens a
+//     workgroup owns 64 tokens x 64 experts and stages both operands through LDS in whole lines.
+//   - There are few tiles (4 at decode with 256 experts, 64 at T = 1024), so K is split into
+//     up to 16 slices to give the GPU about 512 workgroups; each slice writes its partial logits
+//     to the workspace.
+//   - One wave per token then loads all its partial logits at once, sums them in slice order
+//     (deterministic, no atomics), optionally writes the logits, and runs the same selection code as
+//     the router kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_dev.hpp"
@@ -22,15 +24,20 @@ namespace moe {
 
 namespace {
 
-constexpr int kRouterTile = 64;      // tokens and experts per workgroup tile
+constexpr int kRouterTile = 64;      // experts per workgroup tile (16 per wave)
 constexpr int kRouterMaxSplits = 16;  // K slices at most
-constexpr int kRouterTargetBlocks = 256;
+constexpr int kRouterTargetBlocks = 512;  // about two workgroups per CU; more slices add partial-sum traffic
 
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
 }
 
-// part[split][t][e] = sum over K-steps [split * steps_per_split, ...) of x[t][.] . w[e][.]
+// part[split][t][e] = sum over K-steps [split * steps_per_split, ...) of x[t][.] . w[e][.]. Wave w of
+// the workgroup owns experts e0 + 16 w .. +16 and NB 16-token blocks of the tile (NB = 1 at decode:
+// all four waves still stream their own expert rows; T <= 32 only). The operands of U steps are loaded before any
+// of their MFMAs, so a wave has U * (NB + 1) loads in flight; steps past the slice re-read its last
+// step and multiply by a zeroed weight operand, which leaves the accumulator unchanged.
+template <int NB, int U>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ w, int T, int H,
                                                           int E, int tiles_t, int splits,
@@ -42,39 +49,155 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j16 = lane & 15, g = lane >> 4;
-  const int t0 = tt * kRouterTile + wave * 16;
-  if (t0 >= T) return;  // no token of this wave
-  const int e0 = te * kRouterTile;
+  const int t0 = tt * (16 * NB);
+  const int eb = te * kRouterTile + wave * 16;  // the wave's 16 experts
+  if (eb >= E) return;
   const int steps = H >> 5;
   const int s0 = split * steps_per_split;
   const int s1 = min(s0 + steps_per_split, steps);
 
   // operand rows; rows past T or E repeat the last one (their results are not stored)
-  const uint16_t* xa = x + (size_t)min(t0 + j16, T - 1) * H + g * 8;
-  const uint16_t* wb[4];
+  const uint16_t* xa[NB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) wb[cb] = w + (size_t)min(e0 + cb * 16 + j16, E - 1) * H + g * 8;
+  for (int tb = 0; tb < NB; ++tb) xa[tb] = x + (size_t)min(t0 + tb * 16 + j16, T - 1) * H + g * 8;
+  const uint16_t* wb = w + (size_t)min(eb + j16, E - 1) * H + g * 8;
 
-  f32x4_t acc[4];
+  f32x4_t acc[NB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int st = s0; st < s1; ++st) {
-    const bf16x8_t a = ld_bf16x8(xa + st * 32);
+  for (int tb = 0; tb < NB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int st = s0; st < s1; st += U) {
+    uint4 bw[U];
+    bf16x8_t ax[U][NB];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ld_bf16x8(wb[cb] + st * 32), acc[cb], 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int s = min(st + u, s1 - 1) * 32;
+      bw[u] = *reinterpret_cast<const uint4*>(wb + s);
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) ax[u][tb] = ld_bf16x8(xa[tb] + s);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t keep = st + u < s1 ? 0xffffffffu : 0u;
+      const uint4 m{bw[u].x & keep, bw[u].y & keep, bw[u].z & keep, bw[u].w & keep};
+      const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, m);
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u][tb], bop, acc[tb], 0, 0, 0);
+    }
   }
 
-  // lane holds tokens t0 + 4g + i and expert e0 + 16 cb + j16
+  // lane holds tokens t0 + 16 tb + 4g + i and expert eb + j16
+  const int e = eb + j16;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int e = e0 + cb * 16 + j16;
+  for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * g + i;
-      if (t < T && e < E) part[((size_t)split * T + t) * E + e] = acc[cb][i];
+      const int t = t0 + tb * 16 + 4 * g + i;
+      if (t < T && e < E) part[((size_t)split * T + t) * E + e] = acc[tb][i];
     }
+}
+
+// T > 32: a workgroup owns 64 tokens x 64 experts and stages both operands through LDS, so every
+// global load reads whole 128-byte lines and each operand element is fetched once per workgroup
+// (loaded straight into the lane layout, 16 lanes read 64 bytes of each of 16 rows and the four
+// waves would each re-read the tile's activations). A chunk is four K steps (256 bytes of every row);
+// thread tid loads 16 bytes at column tid % 16 of rows tid / 16 + 16 i, i = 0..3, of both operands,
+// the next chunk's loads are in flight while the waves multiply the current one, and wave (wr, wc)
+// computes tokens 32 wr .. +32 x experts 32 wc .. +32 (four MFMAs per step). Steps past the slice
+// re-read its last step and are stored as zeros, so they add nothing.
+constexpr int kChunkSteps = 4;
+constexpr int kLdsRowBytes = kChunkSteps * 64 + 16;  // padded: rows 4 banks apart
+
+__global__ __launch_bounds__(256) void router_gemm_lds_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ w, int T, int H,
+                                                              int E, int tiles_t, int splits,
+                                                              int steps_per_split, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kRouterTile * kLdsRowBytes];  // x rows, then w rows
+  const int b = blockIdx.x;
+  const int split = b % splits;
+  const int tile = b / splits;
+  const int tt = tile % tiles_t, te = tile / tiles_t;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = tt * kRouterTile, e0 = te * kRouterTile;
+  const int steps = H >> 5;
+  const int s0 = split * steps_per_split;
+  const int s1 = min(s0 + steps_per_split, steps);
+  const int nchunks = (s1 - s0 + kChunkSteps - 1) / kChunkSteps;
+
+  // staging: rows past T or E repeat the last one (their results are not stored)
+  const int c16 = tid & 15, r0 = tid >> 4, cstep = c16 >> 2;
+  const uint16_t* xs[4];
+  const uint16_t* wsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xs[i] = x + (size_t)min(t0 + r0 + 16 * i, T - 1) * H + (c16 & 3) * 8;
+    wsrc[i] = w + (size_t)min(e0 + r0 + 16 * i, E - 1) * H + (c16 & 3) * 8;
+  }
+  uint4 rx[4], rw[4];
+  uint32_t keep = 0;
+  auto load = [&](int st) {  // the chunk whose first step is st
+    const int s = st + cstep;
+    keep = s < s1 ? 0xffffffffu : 0u;
+    const int off = min(s, s1 - 1) * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rx[i] = *reinterpret_cast<const uint4*>(xs[i] + off);
+      rw[i] = *reinterpret_cast<const uint4*>(wsrc[i] + off);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 vx{rx[i].x & keep, rx[i].y & keep, rx[i].z & keep, rx[i].w & keep};
+      const uint4 vw{rw[i].x & keep, rw[i].y & keep, rw[i].z & keep, rw[i].w & keep};
+      *reinterpret_cast<uint4*>(lds + (r0 + 16 * i) * kLdsRowBytes + c16 * 16) = vx;
+      *reinterpret_cast<uint4*>(lds + (kRouterTile + r0 + 16 * i) * kLdsRowBytes + c16 * 16) = vw;
+    }
+  };
+
+  const int wr = wave >> 1, wc = wave & 1;
+  const int j16 = lane & 15, g = lane >> 4;
+  const uint8_t* la = lds + (wr * 32 + j16) * kLdsRowBytes + g * 16;
+  const uint8_t* lb = lds + (kRouterTile + wc * 32 + j16) * kLdsRowBytes + g * 16;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  load(s0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    store();
+    __syncthreads();
+    if (ch + 1 < nchunks) load(s0 + (ch + 1) * kChunkSteps);
+#pragma unroll
+    for (int u = 0; u < kChunkSteps; ++u) {
+      bf16x8_t av[2], bv[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) av[a] = *reinterpret_cast<const bf16x8_t*>(la + a * 16 * kLdsRowBytes + u * 64);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) bv[c] = *reinterpret_cast<const bf16x8_t*>(lb + c * 16 * kLdsRowBytes + u * 64);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], bv[c], acc[a][c], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // lane holds tokens t0 + 32 wr + 16 a + 4g + i and expert e0 + 32 wc + 16 c + j16
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int e = e0 + wc * 32 + c * 16 + j16;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + wr * 32 + a * 16 + 4 * g + i;
+        if (t < T && e < E) part[((size_t)split * T + t) * E + e] = acc[a][c][i];
+      }
   }
 }
 
@@ -89,18 +212,26 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   const size_t slice = (size_t)T * E;
+  // every partial in flight at once (slices past the last re-read it: loads under a branch would be
+  // waited for one by one), then summed in slice order; absent slices are skipped, not added as
+  // zeros, so the sum's bits do not depend on the bound
+  float pv[EPL][kRouterMaxSplits];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    const float* p = part + (size_t)t * E + e;
+#pragma unroll
+    for (int sp = 0; sp < kRouterMaxSplits; ++sp) pv[i][sp] = p[min(sp, splits - 1) * slice];
+  }
   float v[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    float s = 0.0f;
-    if (e < E) {
-      const float* p = part + (size_t)t * E + e;
-      s = p[0];
-#pragma unroll 4
-      for (int sp = 1; sp < splits; ++sp) s += p[sp * slice];
-      if (logits) logits[(size_t)t * E + e] = s;
-    }
+    float s = pv[i][0];
+#pragma unroll
+    for (int sp = 1; sp < kRouterMaxSplits; ++sp) s = sp < splits ? s + pv[i][sp] : s;
+    if (e >= E) s = 0.0f;
+    else if (logits) logits[(size_t)t * E + e] = s;
     v[i] = s;
   }
   route_dev::route_values<EPL>(v, t, E, k, score_fn, renorm, ids, weights, nullptr);
@@ -110,7 +241,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
 
 RouterPlan plan_router(int T, int H, int E) {
   RouterPlan rp;
-  rp.tiles_t = (T + kRouterTile - 1) / kRouterTile;
+  rp.nb = T <= 16 ? 1 : (T <= 32 ? 2 : 4);  // 4: the LDS-staged kernel
+  rp.tiles_t = (T + 16 * rp.nb - 1) / (16 * rp.nb);
   const int tiles = rp.tiles_t * ((E + kRouterTile - 1) / kRouterTile);
   const int steps = H / 32;
   int splits = (kRouterTargetBlocks + tiles - 1) / (tiles > 0 ? tiles : 1);
@@ -130,8 +262,17 @@ hipError_t launch_router_gemm_topk(const uint16_t* x, const uint16_t* w, int T, 
                                    int score_fn, int renorm, float* part, float* logits, int32_t* ids,
                                    float* weights, hipStream_t stream) {
   const RouterPlan rp = plan_router(T, H, E);
-  router_gemm_kernel<<<rp.blocks, 256, 0, stream>>>(x, w, T, H, E, rp.tiles_t, rp.splits, rp.steps_per_split,
-                                                    part);
+#define MOE_RGEMM(NB, U)                                                                                 \
+  router_gemm_kernel<NB, U><<<rp.blocks, 256, 0, stream>>>(x, w, T, H, E, rp.tiles_t, rp.splits,         \
+                                                           rp.steps_per_split, part)
+  if (rp.nb == 1)
+    MOE_RGEMM(1, 8);
+  else if (rp.nb == 2)
+    MOE_RGEMM(2, 8);
+  else
+    router_gemm_lds_kernel<<<rp.blocks, 256, 0, stream>>>(x, w, T, H, E, rp.tiles_t, rp.splits,
+                                                          rp.steps_per_split, part);
+#undef MOE_RGEMM
   const dim3 grid((T + 3) / 4), block(256);
 #define MOE_RS(EPL)                                                                                    \
   router_select_kernel<EPL><<<grid, block, 0, stream>>>(part, rp.splits, T, E, k, score_fn, renorm, logits, \

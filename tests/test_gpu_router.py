@@ -5,7 +5,9 @@ selection is checked where it is unique whatever the rounding: the ids must equa
 of the GPU's own logits bit for bit (selection is exact given the logits), the weights must be within
 the routing-weight bound, and both must equal moe_route_topk on those logits bitwise (the same device
 code). Sizes span ragged token, expert and hidden counts, every expert-count path of the selection
-kernel, one to sixteen K slices, and the decode and high-concurrency router shapes."""
+kernel, both GEMM kernels (operands in registers up to 32 tokens, staged through LDS above; K
+chunks cut by the slice end), one to sixteen K slices, and the decode and high-concurrency router
+shapes."""
 import numpy as np
 import pytest
 import torch
@@ -28,6 +30,8 @@ CASES = [
     (33, 7168, 300, 8, 1, True, 6),
     (1024, 7168, 256, 8, 1, True, 7),   # high-concurrency router
     (64, 32, 1, 1, 0, True, 8),         # one K step, one expert
+    (24, 2080, 200, 4, 0, True, 11),    # two 16-token blocks per tile
+    (32, 160, 64, 2, 1, False, 12),     # the largest batch without LDS staging
 ]
 
 
