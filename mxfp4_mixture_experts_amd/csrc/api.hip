@@ -316,7 +316,8 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   if (dense)
     ok &= moe::launch_dense_h16(dp, r, I, dense_e, dense_m0, h_hi, h_lo, rowf, s) == hipSuccess;
   if (plan.launch_small)
-    ok &= moe::launch_small_down(sp, r, list, list_count, H, I, w2_q, w2_s, h_hi, h_lo, y, s) == hipSuccess;
+    ok &= moe::launch_small_down(sp, r, list, list_count, !plan.launch_large, H, I, w2_q, w2_s, h_hi, h_lo, y,
+                                 s) == hipSuccess;
   if (plan.launch_large)
     ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, tile_e, tile_m0, h_hi, h_lo, y, s) == hipSuccess;
   if (dense)

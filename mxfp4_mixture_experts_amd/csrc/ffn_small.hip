@@ -26,6 +26,8 @@
 // each workgroup owns an equal contiguous range of items and its waves take them one at a time
 // from a counter in LDS. Each wave keeps the loads of its next items in flight while it decodes
 // the current one.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -504,8 +506,16 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
 
 // ---------------------------------------------------------------------------------------------
 // down: an item is S rows of W2; activations h rebuilt in fp32 from its two bf16 planes.
+//
+// STAGED: the h rows of the experts in a workgroup's range form one contiguous block of the sorted
+// rows when the list is the whole active list (ascending, and no expert between two listed ones has
+// rows). The workgroup copies both planes of that block to LDS once, right after issuing its first
+// weight loads, and its waves read their h blocks from there with LDS loads, which a wave waits for
+// without waiting for its weight loads in flight; otherwise a wave fetches its rows from L2 at every
+// change of expert and, the loads being in order, drains its weight ring there. The host enables it
+// only when a bound on the rows of any range fits the LDS it allocates (down_stage_rows).
 
-template <int BPL, int MT, int S, int D, int NW>
+template <int BPL, int MT, int S, int D, int NW, bool STAGED>
 __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
@@ -514,6 +524,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     float* __restrict__ y) {
   __shared__ int counter;
   __shared__ int range[2];
+  extern __shared__ __attribute__((aligned(16))) uint8_t h_stage[];  // STAGED: hi plane, then lo plane
   ItemRange ir;
   if (threadIdx.x == 0) counter = 0;
   if (!my_items_wg(list, list_count, counts, tiles, MT, weighted, range, ir)) return;
@@ -527,6 +538,16 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
   const int tile_rows = S * rpw;
   const uint32_t qrow = (uint32_t)(I >> 1), srow = (uint32_t)NB;
   const size_t qexp = (size_t)H * qrow, sexp = (size_t)H * srow;
+
+  // STAGED: the range's h rows [row_lo, row_hi)
+  int row_lo = 0;
+  uint32_t stage_plane = 0;  // bytes per plane
+  if constexpr (STAGED) {
+    const int e_last = uniform(list[(ir.end - 1) / tiles]);
+    row_lo = uniform(offsets[uniform(list[ir.begin / tiles])]);
+    const int row_hi = uniform(offsets[e_last]) + uniform(counts[e_last]);
+    stage_plane = (uint32_t)(row_hi - row_lo) * (uint32_t)I * 2;
+  }
   const bool k_exact = (NB % lpr) == 0;
 
   uint4 w[D][S][BPL];
@@ -581,17 +602,23 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
         cur.a_m0 = m0;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const size_t roff = (size_t)(cur.row0 + m0 + min(m, mc - 1)) * I;
-          const uint8_t* hib = reinterpret_cast<const uint8_t*>(h_hi + roff);
-          const uint8_t* lob = reinterpret_cast<const uint8_t*>(h_lo + roff);
+          const int row = cur.row0 + m0 + min(m, mc - 1);
+          const uint8_t* hib = reinterpret_cast<const uint8_t*>(h_hi + (size_t)row * I);
+          const uint8_t* lob = reinterpret_cast<const uint8_t*>(h_lo + (size_t)row * I);
+          const uint32_t soff = (uint32_t)(row - row_lo) * (uint32_t)I * 2;
 #pragma unroll
           for (int b = 0; b < BPL; ++b) {
             const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
             uint4 hv[4], lv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              hv[i] = ld16(hib, kb * 64 + i * 16);
-              lv[i] = ld16(lob, kb * 64 + i * 16);
+              if constexpr (STAGED) {
+                hv[i] = *reinterpret_cast<const uint4*>(h_stage + soff + kb * 64 + i * 16);
+                lv[i] = *reinterpret_cast<const uint4*>(h_stage + stage_plane + soff + kb * 64 + i * 16);
+              } else {
+                hv[i] = ld16(hib, kb * 64 + i * 16);
+                lv[i] = ld16(lob, kb * 64 + i * 16);
+              }
             }
             hinv[m][b] = h_planes_to_f16(hv, lv, hh[m][b]);
             // one block's planes in registers at a time
@@ -659,6 +686,18 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
 
 #pragma unroll
   for (int d = 0; d < D; ++d) prefetch(d);
+  if constexpr (STAGED) {  // after the first weight loads, so both round trips overlap
+    const uint32_t n16 = stage_plane >> 4;
+    const uint4* src_hi = reinterpret_cast<const uint4*>(h_hi + (size_t)row_lo * I);
+    const uint4* src_lo = reinterpret_cast<const uint4*>(h_lo + (size_t)row_lo * I);
+    uint4* dst = reinterpret_cast<uint4*>(h_stage);
+    for (uint32_t i = threadIdx.x; i < n16; i += blockDim.x) {
+      const uint4 a = src_hi[i], c = src_lo[i];
+      dst[i] = a;
+      dst[n16 + i] = c;
+    }
+    __syncthreads();
+  }
   bool more = true;
   while (more) {
 #pragma unroll
@@ -721,6 +760,8 @@ SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
   sp.dn_tiles = (H + sp.dn_tile - 1) / sp.dn_tile;
   const long P = (long)T * k;
   sp.slots = (int)(P < E ? P : E);
+  sp.T = T;
+  sp.P = (int)P;
   sp.mt_gu = (T >= 2 && sp.gu.bpl <= 2) ? 2 : 1;
   sp.mt_dn = (T >= 2 && sp.dn.bpl <= 2) ? 2 : 1;
   // with T <= 2 every expert has one or two rows and costs about the same per item
@@ -755,17 +796,63 @@ hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32
   }
 }
 
+// Bound on the h rows of one down workgroup's range when the list is the whole active list (every
+// expert has at most T rows). Weighted ranges hold cost total/G, and an expert inside a range costs
+// at least (rows + 3) per item over its items, so the experts wholly inside hold at most 4P/G + 1
+// rows (the total cost is at most 4 per row); two more experts can overlap its ends. Equal-count
+// ranges span at most ceil(P/G) + 2 experts.
+int down_stage_rows(const SmallPlan& sp) {
+  const long G = sp.dn_grid > 0 ? sp.dn_grid : 1;
+  const long P = sp.P, T = sp.T;
+  const long rows = sp.weighted ? 4 * P / G + 1 + 2 * T : ((P + G - 1) / G + 2) * T;
+  return (int)(rows < P ? rows : P);
+}
+
+// LDS a workgroup can hold on the current device (at most kStageMaxBytes)
+constexpr size_t kStageMaxBytes = 150 * 1024;
+size_t stage_limit() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) {
+    (void)hipGetLastError();
+    return 65536;
+  }
+  const size_t lim = (size_t)v - 1024;  // the kernel's own LDS variables
+  return lim < kStageMaxBytes ? lim : kStageMaxBytes;
+}
+
 hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t* list,
-                             const int32_t* list_count, int H, int I, const uint8_t* w2_q,
-                             const uint8_t* w2_s, const uint16_t* h_hi, const uint16_t* h_lo, float* y,
-                             hipStream_t stream) {
+                             const int32_t* list_count, bool list_is_active, int H, int I,
+                             const uint8_t* w2_q, const uint8_t* w2_s, const uint16_t* h_hi,
+                             const uint16_t* h_lo, float* y, hipStream_t stream) {
   if (sp.dn_grid <= 0) return hipSuccess;
   const dim3 grid(sp.dn_grid);
   const int lpr = sp.dn.lpr, tiles = sp.dn_tiles;
-#define MOE_DN(BPL, MT)                                                                        \
-  small_down_kernel<BPL, MT, down_slots(BPL), down_ring(BPL), 4 * dn_waves(BPL, MT)>           \
-      <<<grid, 256 * dn_waves(BPL, MT), 0, stream>>>(r.counts, r.offsets, list, list_count, H, I, \
-                                                     tiles, sp.weighted, w2_q, w2_s, lpr, h_hi, h_lo, y)
+  const size_t stage_bytes = (size_t)down_stage_rows(sp) * I * 4;
+  const bool staged = list_is_active && stage_bytes <= stage_limit();
+#define MOE_DN_K(BPL, MT, ST)                                                                          \
+  {                                                                                                   \
+    auto kern = small_down_kernel<BPL, MT, down_slots(BPL), down_ring(BPL), 4 * dn_waves(BPL, MT), ST>; \
+    const size_t lds = ST ? stage_bytes : 0;                                                          \
+    static std::atomic<bool> lds_attr_set{false};                                                     \
+    if (lds > 65536 && !lds_attr_set.load()) {                                                        \
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                                    \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageMaxBytes) !=     \
+          hipSuccess)                                                                                 \
+        return hipErrorInvalidValue;                                                                  \
+      lds_attr_set.store(true);                                                                       \
+    }                                                                                                 \
+    kern<<<grid, 256 * dn_waves(BPL, MT), lds, stream>>>(r.counts, r.offsets, list, list_count, H, I,   \
+                                                         tiles, sp.weighted, w2_q, w2_s, lpr, h_hi,    \
+                                                         h_lo, y);                                     \
+  }
+#define MOE_DN(BPL, MT)        \
+  do {                         \
+    if (staged)                \
+      MOE_DN_K(BPL, MT, true)  \
+    else                       \
+      MOE_DN_K(BPL, MT, false) \
+  } while (0)
   switch (sp.dn.bpl) {
     case 1:
       if (sp.mt_dn == 2) MOE_DN(1, 2); else MOE_DN(1, 1);
@@ -782,6 +869,7 @@ hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t
     default: return hipErrorInvalidValue;
   }
 #undef MOE_DN
+#undef MOE_DN_K
   return hipGetLastError();
 }
 

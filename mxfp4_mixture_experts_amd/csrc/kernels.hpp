@@ -70,6 +70,7 @@ struct SmallPlan {
   int gu_grid, dn_grid;    // persistent workgroups (one per CU)
   int gu_block, dn_block;  // threads per workgroup
   int slots;               // bound on the number of experts in the list (min(E, P))
+  int T, P;                // tokens, routed pairs
   int mt_gu, mt_dn;        // tokens per pass
   int weighted;            // workgroup ranges weighted by the experts' row counts
 };
@@ -83,7 +84,7 @@ hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32
                                hipStream_t stream);
 
 hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t* list,
-                             const int32_t* list_count, int H, int I, const uint8_t* w2_q,
+                             const int32_t* list_count, bool list_is_active, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const uint16_t* h_hi, const uint16_t* h_lo, float* y,
                              hipStream_t stream);
 
