@@ -100,13 +100,17 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 // T > 32: a workgroup owns 64 tokens x 64 experts and stages both operands through LDS, so every
 // global load reads whole 128-byte lines and each operand element is fetched once per workgroup
 // (loaded straight into the lane layout, 16 lanes read 64 bytes of each of 16 rows and the four
-// waves would each re-read the tile's activations). A chunk is four K steps (256 bytes of every row);
-// thread tid loads 16 bytes at column tid % 16 of rows tid / 16 + 16 i, i = 0..3, of both operands,
-// the next chunk's loads are in flight while the waves multiply the current one, and wave (wr, wc)
+// waves would each re-read the tile's activations). A chunk is kChunkSteps K steps (64 bytes of every
+// row per step); thread tid loads 16 bytes at column tid % kRowThreads of rows tid / kRowThreads +
+// kRowsPerPass i of both operands, the next chunk's loads are in flight while the waves multiply the
+// current one, and wave (wr, wc)
 // computes tokens 32 wr .. +32 x experts 32 wc .. +32 (four MFMAs per step). Steps past the slice
 // re-read its last step and are stored as zeros, so they add nothing.
 constexpr int kChunkSteps = 4;
 constexpr int kLdsRowBytes = kChunkSteps * 64 + 16;  // padded: rows 4 banks apart
+constexpr int kRowThreads = kChunkSteps * 4;         // threads loading one row's chunk, 16 bytes each
+constexpr int kRowsPerPass = 256 / kRowThreads;
+constexpr int kStageRows = kRouterTile / kRowsPerPass;  // rows of each operand per thread
 
 __global__ __launch_bounds__(256) void router_gemm_lds_kernel(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ w, int T, int H,
@@ -126,33 +130,33 @@ __global__ __launch_bounds__(256) void router_gemm_lds_kernel(const uint16_t* __
   const int nchunks = (s1 - s0 + kChunkSteps - 1) / kChunkSteps;
 
   // staging: rows past T or E repeat the last one (their results are not stored)
-  const int c16 = tid & 15, r0 = tid >> 4, cstep = c16 >> 2;
-  const uint16_t* xs[4];
-  const uint16_t* wsrc[4];
+  const int c16 = tid % kRowThreads, r0 = tid / kRowThreads, cstep = c16 >> 2;
+  const uint16_t* xs[kStageRows];
+  const uint16_t* wsrc[kStageRows];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    xs[i] = x + (size_t)min(t0 + r0 + 16 * i, T - 1) * H + (c16 & 3) * 8;
-    wsrc[i] = w + (size_t)min(e0 + r0 + 16 * i, E - 1) * H + (c16 & 3) * 8;
+  for (int i = 0; i < kStageRows; ++i) {
+    xs[i] = x + (size_t)min(t0 + r0 + kRowsPerPass * i, T - 1) * H + (c16 & 3) * 8;
+    wsrc[i] = w + (size_t)min(e0 + r0 + kRowsPerPass * i, E - 1) * H + (c16 & 3) * 8;
   }
-  uint4 rx[4], rw[4];
+  uint4 rx[kStageRows], rw[kStageRows];
   uint32_t keep = 0;
   auto load = [&](int st) {  // the chunk whose first step is st
     const int s = st + cstep;
     keep = s < s1 ? 0xffffffffu : 0u;
     const int off = min(s, s1 - 1) * 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kStageRows; ++i) {
       rx[i] = *reinterpret_cast<const uint4*>(xs[i] + off);
       rw[i] = *reinterpret_cast<const uint4*>(wsrc[i] + off);
     }
   };
   auto store = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kStageRows; ++i) {
       const uint4 vx{rx[i].x & keep, rx[i].y & keep, rx[i].z & keep, rx[i].w & keep};
       const uint4 vw{rw[i].x & keep, rw[i].y & keep, rw[i].z & keep, rw[i].w & keep};
-      *reinterpret_cast<uint4*>(lds + (r0 + 16 * i) * kLdsRowBytes + c16 * 16) = vx;
-      *reinterpret_cast<uint4*>(lds + (kRouterTile + r0 + 16 * i) * kLdsRowBytes + c16 * 16) = vw;
+      *reinterpret_cast<uint4*>(lds + (r0 + kRowsPerPass * i) * kLdsRowBytes + c16 * 16) = vx;
+      *reinterpret_cast<uint4*>(lds + (kRouterTile + r0 + kRowsPerPass * i) * kLdsRowBytes + c16 * 16) = vw;
     }
   };
 
