@@ -22,6 +22,8 @@
 // Tile schedule: a one-wave kernel lists the (expert, row-tile) pairs of experts above small_m_max
 // (and the remaining experts for the weight-streaming kernels) on the device, so the grids come from
 // host bounds only and no launch needs a host synchronisation.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -102,9 +104,10 @@ constexpr int kNW = 8;           // waves per workgroup (2 per SIMD)
 constexpr int kThreads = 64 * kNW;
 
 // Per-wave LDS buffer of one super-step's weights: CB column blocks x 16 rows x 128 bytes of codes
-// (8 MX blocks), then CB x 16 rows x 8 scale bytes.
-template <int CB>
-constexpr int wave_buf_bytes() { return CB * 2048 + CB * 128; }
+// (8 MX blocks), then the scale bytes: CB x 16 rows x 8 (one super-step), or with WIN, CB x 16 rows x
+// 32 (a window of four super-steps).
+template <int CB, bool WIN>
+constexpr int wave_buf_bytes() { return CB * 2048 + CB * (WIN ? 512 : 128); }
 
 // One (expert, row tile) x column block, with MSUB blocks of 16 rows fixed at compile time so the
 // step is straight-line code (no per-row-block branches between MFMAs).
@@ -116,7 +119,14 @@ constexpr int wave_buf_bytes() { return CB * 2048 + CB * 128; }
 // load instruction covers 8 whole cache lines; at use the wave passes them through its own LDS
 // buffer into the MFMA lane layout (lane: row j16, block 4*step + g). Only the wave itself reads its
 // buffer, so this needs no barrier.
-template <bool GATEUP, int MSUB, int CB>
+// Scale bytes: without WIN a lane loads the one byte it writes to the buffer, per super-step, so each
+// 32-byte sector of a row's scales is requested four times, a super-step apart, and the L2 serves
+// few of those repeats (under the weight stream the counters showed the gate_up launch fetching 42%
+// more than its weights and scales, and pointing every scale load at one sector took high_c4's
+// gate_up from 1100 to 920 us). With WIN (K % 256 == 0) a lane loads 8 bytes of one row, and the
+// wave the 32-byte windows of its 16 rows for four super-steps at once: every sector is fetched by
+// one load.
+template <bool GATEUP, int MSUB, int CB, bool WIN>
 __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const uint8_t* __restrict__ qe,
                                            const uint8_t* __restrict__ se, int e, int m0, int xblk,
                                            float clamp, const uint16_t* __restrict__ h_hi_in,
@@ -154,6 +164,7 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
   int col[CB];
   bool cval[CB];
   uint32_t cq[CB][2], cs[CB][2];  // offsets of the rows this lane loads (coalesced pattern)
+  uint32_t cw[CB];                // WIN: scale-row offset of row lane / 4 of each column block
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     col[cb] = col_of(cb, j16);
@@ -164,6 +175,7 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
       cq[cb][h] = wrow * qrow;
       cs[cb][h] = wrow * srow;
     }
+    cw[cb] = (uint32_t)wrow_of(cb, lane >> 2) * srow;
   }
 
   // activation rows this thread stages (rows past the tile repeat its last row: their results
@@ -187,6 +199,7 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
   // ring of D super-steps of loads in flight: weight blocks, scale bytes, activation slices
   uint4 rb[D][CB][2];
   uint32_t rs[D][CB][2];
+  uint2 sw[CB];  // WIN: the next window's scale bytes
   uint4 ra[D][2][NA];
 
   // issue every load of super-step ss into ring slot `slot`. Block and element indices are clamped
@@ -199,7 +212,7 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         rb[slot][cb][h] = ld16(qe, cq[cb][h] + blk * 16);
-        rs[slot][cb][h] = ld8(se, cs[cb][h] + blk);
+        if constexpr (!WIN) rs[slot][cb][h] = ld8(se, cs[cb][h] + blk);
       }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -210,19 +223,28 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
       }
   };
 
+  // WIN: scale bytes of super-steps ss .. ss + 3 (blocks 8 ss .. 8 ss + 31; clamped into the row,
+  // blocks past K are masked at use)
+  auto issue_window = [&](int ss) {
+    const uint32_t blk = (uint32_t)min(ss * 8 + (lane & 3) * 8, NB - 8);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) sw[cb] = *reinterpret_cast<const uint2*>(se + cw[cb] + blk);
+  };
+
   f32x4_t acc[MSUB][CB];
 #pragma unroll
   for (int ms = 0; ms < MSUB; ++ms)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[ms][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  if constexpr (WIN) issue_window(0);
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
 
   // this wave's buffer: row r of column block cb at cb*2048 + r*128, its 16-byte chunk c at position
   // c ^ (r % 8) (the 8 lanes writing a row, and the 8 lanes reading one chunk of 8 rows, hit
   // distinct banks); scale bytes at CB*2048 + cb*128 + r*8 + block
-  uint8_t* wbuf = lds_w + wave * wave_buf_bytes<CB>();
+  uint8_t* wbuf = lds_w + wave * wave_buf_bytes<CB, WIN>();
 
   auto step_body = [&](int slot, int step, int st) {
     uint8_t* lb = lds_a + (step & 1) * (kATiles * kTileBytes);
@@ -253,7 +275,9 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
       const int c = 4 * st + g;
       wb[cb] = *reinterpret_cast<const uint4*>(wbuf + cb * 2048 + j16 * 128 + ((c ^ (j16 & 7)) << 4));
       const bool ok = cval[cb] && step * 4 + g < NB;
-      scale[cb] = ok ? e8m0_to_float(wbuf[CB * 2048 + cb * 128 + j16 * 8 + c]) : 0.0f;
+      const int so = WIN ? CB * 2048 + cb * 512 + j16 * 32 + ((step >> 1) & 3) * 8 + c
+                         : CB * 2048 + cb * 128 + j16 * 8 + c;
+      scale[cb] = ok ? e8m0_to_float(wbuf[so]) : 0.0f;
     }
     // decode the weight blocks straight into MFMA B operands (operand s = elements 8s..8s+7)
 #pragma unroll
@@ -285,7 +309,8 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
     }
   };
 
-  auto super_step = [&](int slot, int ss) {
+  // WINDOW_START: ss is the first super-step of a scale window (known at compile time below)
+  auto super_step = [&](int slot, int ss, auto window_start, auto window_issue) {
     // the super-step's weights -> this wave's buffer (the wave finished reading the previous
     // super-step's; its LDS operations complete in order)
 #pragma unroll
@@ -294,21 +319,32 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
       for (int h = 0; h < 2; ++h) {
         const int rr = 8 * h + (lane >> 3), c = lane & 7;
         *reinterpret_cast<uint4*>(wbuf + cb * 2048 + rr * 128 + ((c ^ (rr & 7)) << 4)) = rb[slot][cb][h];
-        wbuf[CB * 2048 + cb * 128 + rr * 8 + c] = (uint8_t)rs[slot][cb][h];
+        if constexpr (!WIN) wbuf[CB * 2048 + cb * 128 + rr * 8 + c] = (uint8_t)rs[slot][cb][h];
       }
+    if constexpr (WIN && decltype(window_start)::value) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        *reinterpret_cast<uint2*>(wbuf + CB * 2048 + cb * 512 + (lane >> 2) * 32 + (lane & 3) * 8) = sw[cb];
+    }
     step_body(slot, 2 * ss, 0);
     step_body(slot, 2 * ss + 1, 1);
-    // the slot's registers are consumed: refill it with super-step ss + D
+    // the slot's registers are consumed: refill it with super-step ss + D (and, when that starts a
+    // window, load the window)
+    if constexpr (WIN && decltype(window_issue)::value) issue_window(ss + D);
     issue(slot, ss + D);
   };
 
-  // the super-step count is padded to a multiple of D (padding steps see zero activations and zero
-  // scales): a conditional tail would merge into the loop's control flow and make the compiler
-  // count the newest ring slot's loads as needed by the oldest one
-  const int nss_pad = (nss + D - 1) / D * D;
-  for (int ss = 0; ss < nss_pad; ss += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) super_step(d, ss + d);
+  // the super-step count is padded to a multiple of 4 (of D, and of the scale window; padding steps
+  // see zero activations and zero scales): a conditional tail would merge into the loop's control
+  // flow and make the compiler count the newest ring slot's loads as needed by the oldest one
+  const int nss_pad = (nss + 3) / 4 * 4;
+  using T0 = std::integral_constant<bool, true>;
+  using F0 = std::integral_constant<bool, false>;
+  for (int ss = 0; ss < nss_pad; ss += 4) {
+    super_step(0, ss, T0{}, std::integral_constant<bool, D == 4>{});
+    super_step(1 % D, ss + 1, F0{}, std::integral_constant<bool, 1 + D == 4>{});
+    super_step(2 % D, ss + 2, F0{}, std::integral_constant<bool, 2 + D == 4>{});
+    super_step(3 % D, ss + 3, F0{}, std::integral_constant<bool, 3 + D == 4>{});
   }
 
   // epilogue: lane holds rows 4*g + i (i < 4) of each 16-row block, column j16 of each block
@@ -344,7 +380,7 @@ __device__ __forceinline__ void large_tile(const Routed& r, int H, int I, const 
 // 8 XCDs in turn, so workgroup b runs on XCD b % 8; the mapping below gives XCD x the row tiles
 // y = x, x + 8, ... and dispatches all nx column blocks of one tile back to back on it, so a tile's
 // activation rows are fetched into that XCD's L2 once and reused by every column block.
-template <bool GATEUP, int CB>
+template <bool GATEUP, int CB, bool WIN>
 __global__ __launch_bounds__(kThreads, 1) void large_kernel(Routed r, int H, int I, int nx, int tile_slots,
                                                        const uint8_t* __restrict__ wq_all,
                                                        const uint8_t* __restrict__ ws_all,
@@ -359,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void large_kernel(Routed r, int H, int
   constexpr int kATiles = GATEUP ? 1 : 2;
   // two LDS buffers (double-buffered across K-steps), each kATiles tiles
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kATiles * kTileM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_w[kNW * wave_buf_bytes<CB>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w[kNW * wave_buf_bytes<CB, WIN>()];
 
   const int b = blockIdx.x;
   const int j = b >> 3;
@@ -378,8 +414,8 @@ __global__ __launch_bounds__(kThreads, 1) void large_kernel(Routed r, int H, int
   const uint8_t* qe = wq_all + (size_t)e * nrows_w * (size_t)(K >> 1);
   const uint8_t* se = ws_all + (size_t)e * nrows_w * (size_t)(K >> 5);
 #define MOE_TILE(MS) \
-  large_tile<GATEUP, MS, CB>(r, H, I, qe, se, e, m0, xblk, clamp, h_hi_in, h_lo_in, h_hi, h_lo, y_out, lds_a, \
-                             lds_w)
+  large_tile<GATEUP, MS, CB, WIN>(r, H, I, qe, se, e, m0, xblk, clamp, h_hi_in, h_lo_in, h_hi, h_lo, y_out, \
+                                  lds_a, lds_w)
   switch (msub_n) {
     case 1: MOE_TILE(1); break;
     case 2: MOE_TILE(2); break;
@@ -430,9 +466,14 @@ hipError_t launch_large_gateup(const LargePlan& lp, const Routed& r, int H, int 
                                const int32_t* tile_m0, float clamp, uint16_t* h_hi, uint16_t* h_lo,
                                hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
-  large_kernel<true, kGuCB><<<lp.gu_blocks, kThreads, 0, stream>>>(
-      r, H, I, lp.gu_grid_x, lp.tile_slots, w13_q, w13_s, tile_e, tile_m0, clamp, nullptr, nullptr, h_hi,
-      h_lo, nullptr);
+  if (H % 256 == 0)
+    large_kernel<true, kGuCB, true><<<lp.gu_blocks, kThreads, 0, stream>>>(
+        r, H, I, lp.gu_grid_x, lp.tile_slots, w13_q, w13_s, tile_e, tile_m0, clamp, nullptr, nullptr, h_hi,
+        h_lo, nullptr);
+  else
+    large_kernel<true, kGuCB, false><<<lp.gu_blocks, kThreads, 0, stream>>>(
+        r, H, I, lp.gu_grid_x, lp.tile_slots, w13_q, w13_s, tile_e, tile_m0, clamp, nullptr, nullptr, h_hi,
+        h_lo, nullptr);
   return hipGetLastError();
 }
 
@@ -440,9 +481,14 @@ hipError_t launch_large_down(const LargePlan& lp, const Routed& r, int H, int I,
                              const uint8_t* w2_s, const int32_t* tile_e, const int32_t* tile_m0,
                              const uint16_t* h_hi, const uint16_t* h_lo, float* y, hipStream_t stream) {
   if (lp.tile_slots <= 0) return hipSuccess;
-  large_kernel<false, kDnCB><<<lp.dn_blocks, kThreads, 0, stream>>>(
-      r, H, I, lp.dn_grid_x, lp.tile_slots, w2_q, w2_s, tile_e, tile_m0, 0.0f, h_hi, h_lo, nullptr, nullptr,
-      y);
+  if (I % 256 == 0)
+    large_kernel<false, kDnCB, true><<<lp.dn_blocks, kThreads, 0, stream>>>(
+        r, H, I, lp.dn_grid_x, lp.tile_slots, w2_q, w2_s, tile_e, tile_m0, 0.0f, h_hi, h_lo, nullptr, nullptr,
+        y);
+  else
+    large_kernel<false, kDnCB, false><<<lp.dn_blocks, kThreads, 0, stream>>>(
+        r, H, I, lp.dn_grid_x, lp.tile_slots, w2_q, w2_s, tile_e, tile_m0, 0.0f, h_hi, h_lo, nullptr, nullptr,
+        y);
   return hipGetLastError();
 }
 
