@@ -33,10 +33,11 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
 }
 
 // part[split][t][e] = sum over K-steps [split * steps_per_split, ...) of x[t][.] . w[e][.]. Wave w of
-// the workgroup owns experts e0 + 16 w .. +16 and NB 16-token blocks of the tile (NB = 1 at decode:
-// all four waves still stream their own expert rows; T <= 32 only). The operands of U steps are loaded before any
-// of their MFMAs, so a wave has U * (NB + 1) loads in flight; steps past the slice re-read its last
-// step and multiply by a zeroed weight operand, which leaves the accumulator unchanged.
+// the workgroup owns experts e0 + 16 w .. +16 and NB 16-token blocks of the tile (T <= 32 only; NB = 1
+// at decode, where all four waves still stream their own expert rows). The operands of U steps are
+// loaded before any of their MFMAs, so a wave has U * (NB + 1) loads in flight; steps past the slice
+// re-read its last step and multiply by a zeroed weight operand, which leaves the accumulator
+// unchanged (for finite activations).
 template <int NB, int U>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ w, int T, int H,
