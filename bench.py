@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--flags", type=int, default=0, help="moe_mxfp4_ffn flags (1 = unfused gate/up)")
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough for cold weights)")
     ap.add_argument("--small-m-max", type=int, default=-1,
-                    help="launch-table threshold override (moe_set_small_m_max; -1 = the library's table)")
+                    help="launch-table threshold override (moe_ffn_options.small_m_max; -1 = the library's table)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -106,8 +106,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     moe.load_library()
-    if args.small_m_max >= 0:
-        moe.set_small_m_max(args.small_m_max)
+    base_opts = moe.ffn_options(small_m_max=args.small_m_max)
     cfg = moe_synth.CONFIGS[args.config]
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     t0 = time.time()
@@ -132,8 +131,8 @@ def main():
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
 
-    def step(i):
-        layer.forward(x, logits, replicas[i % R], stream=stream)
+    def step(i, opts=None):
+        layer.forward(x, logits, replicas[i % R], stream=stream, options=opts or base_opts)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -164,18 +163,17 @@ def main():
             a.record(stream)
             b.record(stream)
     torch.cuda.synchronize()
+    step_opts = [moe.ffn_options(small_m_max=args.small_m_max,
+                                 stage_events={st: ev for st, ev in zip(stages, ev_stage[i])})
+                 for i in range(args.steps)]
     t_start = time.perf_counter()
     with torch.cuda.stream(stream):
         for i in range(args.steps):
-            for st, (a, b) in zip(stages, ev_stage[i]):
-                moe.set_stage_events(st, a, b)
             ev_layer[i][0].record(stream)
-            step(i)
+            step(i, step_opts[i])
             ev_layer[i][1].record(stream)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t_start
-    for st in stages:
-        moe.set_stage_events(st, None, None)
     el = lambda a, b: a.elapsed_time(b) * 1e3  # noqa: E731  (µs)
     layer_us = [el(*ev_layer[i]) for i in range(args.steps)]
     route_group_us = [el(ev_layer[i][0], ev_stage[i][0][0]) for i in range(args.steps)]
@@ -197,7 +195,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for j in range(L):
-                layer.forward(x, logits, replicas[j % R], stream=stream)
+                layer.forward(x, logits, replicas[j % R], stream=stream, options=base_opts)
         g.replay()  # warm-up replay
         torch.cuda.synchronize()
         ev_g = [(mk(), mk()) for _ in range(reps)]
@@ -300,7 +298,7 @@ def main():
     gbps = weight_bytes / (us_layer * 1e-6) / 1e9
     ffn_med = med(ffn_us)
 
-    plan = moe.ffn_plan(T, H, I, E, k, args.flags)
+    plan = moe.ffn_plan(T, H, I, E, k, args.flags, base_opts)
     large = plan["launch_large"]
     mfma_bound = cfg.name == "m1024"
     if mfma_bound:

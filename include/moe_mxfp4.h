@@ -32,8 +32,13 @@
  *   w13_s u8[E, 2I, H/32]
  *   w2_q  u8[E, H, I/2]   down projection
  *   w2_s  u8[E, H, I/32]
- * The GPU decodes exactly for scale bytes 2..254 (every decoded value is then a normal binary32);
- * bytes 0, 1 and 255 (NaN) are outside the device contract.
+ * The GPU decodes every element exactly for scale bytes 2..252: each decoded value, at most
+ * 6 * 2^(s-127), is then a normal binary32 (at 253 and 254 the largest codes overflow binary32).
+ * Bytes 0, 1, 253, 254 and 255 (NaN) are outside the device contract. One kernel rounds weights on
+ * purpose: the down GEMM of experts with at least 256 rows decodes each element to fp16 relative
+ * to the largest scale byte c of its output row, exactly while the element's scale byte s is at
+ * least c - 36; below that it is rounded to a multiple of 2^(c-164) (nearest-even), an absolute
+ * error of at most 2^(c-165), below 2^-40 of the largest value the row can hold (6 * 2^(c-127)).
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -45,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 typedef enum {
@@ -144,11 +149,19 @@ int moe_router_gemm_topk(const uint16_t* x_bf16, const uint16_t* w_router_bf16, 
  * Every output is an integer and is deterministic. Limits: T >= 0, 1 <= k <= MOE_MAX_TOPK,
  * 1 <= E <= MOE_MAX_EXPERTS, T*k <= MOE_MAX_PAIRS. With T == 0 the counts, offsets, active and
  * n_active outputs are still written (all zero / -1). sorted_pair and pair_pos may be NULL only when
- * T == 0.
+ * T == 0. Ids need not be distinct within a token (an expert then holds several of its pairs).
+ *
+ * Workspace: moe_group_tokens_workspace_size(T, k, E) returns the device bytes a call needs for
+ * these sizes, or (size_t)-1 for invalid sizes. The grouping runs in one workgroup whose
+ * histograms and scans live in LDS, so the size is 0 for every valid shape and `workspace` may be
+ * NULL; a caller that passes a buffer keeps working if a later version needs one (the size is a
+ * function of T, k and E only, the worst case over every routing, as tokenspeed PR #661 "The
+ * workspace contract" requires). ws_bytes below the query's result returns MOE_ERR_WORKSPACE.
  */
+size_t moe_group_tokens_workspace_size(int T, int k, int E);  /* host */
 int moe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                      int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
-                     int32_t* n_active, void* stream);
+                     int32_t* n_active, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * moe_route_group — moe_route_topk followed by moe_group_tokens, with the same arguments, limits and
@@ -198,7 +211,10 @@ size_t moe_mxfp4_ffn_workspace_size(int T, int H, int I, int E, int k, int flags
  *   w13_q, w13_s, w2_q, w2_s     [dev] MXFP4 weights (layout above); w13_q and w2_q 16-byte aligned
  *   topk_w                       [dev] f32[T, k]  routing weights (from moe_route_topk)
  *   counts, offsets, sorted_pair, pair_pos, active, n_active
- *                                [dev] the outputs of moe_group_tokens for the same ids
+ *                                [dev] the outputs of moe_group_tokens for the same ids (which
+ *                                need not be distinct within a token); the ids themselves are not
+ *                                an argument, since the grouping carries everything the kernels
+ *                                read of them (rows per expert, pair of each row, row of each pair)
  *   clamp_limit                  <= 0 disables the clamp
  *   flags                        MOE_UNFUSED_GATE_UP | MOE_FORCE_SMALL_M | MOE_FORCE_LARGE_M
  *                                (the two FORCE flags are mutually exclusive)
@@ -217,12 +233,54 @@ int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k, con
                   void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * Launch plan of moe_mxfp4_ffn (host only, no GPU needed): which kernels one call enqueues, for
- * tests and for reading the launch table. Per-expert row counts live on the device, so the plan is
- * decided from host-known bounds: with T <= small_m_max every expert has at most T rows and only the
- * weight-streaming kernels run; otherwise both kernel families are launched and each expert is
- * handled by the family its row count selects (the launch table keyed by token count of tokenspeed
- * PR #661, "What the sweep found").
+ * Per-call options of moe_mxfp4_ffn_ex and moe_mxfp4_ffn_plan (host struct, read during the call
+ * only; the library keeps no copy and no process-wide setting, so concurrent callers never see
+ * each other's choices). moe_ffn_options_init fills the defaults that moe_mxfp4_ffn uses.
+ *   small_m_max       launch-table threshold: experts with at most this many rows run on the
+ *                     weight-streaming kernels, the others on the MFMA kernels. -1 (default) follows
+ *                     the table keyed by token count (tokenspeed PR #661, "What the sweep found"):
+ *                     8 for T <= 8 (every expert streams), 2 above. Values below -1 are rejected
+ *                     (MOE_ERR_SHAPE). The FORCE flags take precedence.
+ *   dense_down_cols   column tile of the dense (>= 256 rows per expert) down GEMM: 0 (default)
+ *                     picks 256 or 224 output columns per workgroup, whichever finishes the expected
+ *                     ceil(T*k/256) x ceil(H/width) tiles in fewer, fuller rounds over the compute
+ *                     units; 256 or 224 forces that width; anything else is MOE_ERR_SHAPE. The width
+ *                     decides which workgroup computes an output column, not its arithmetic: results
+ *                     are bitwise the same.
+ *   stage_start/stop  hipEvent_t handles (caller-owned) or NULL: when set, the call records
+ *                     stage_start[s] before the first kernel of stage s and stage_stop[s] after its
+ *                     last kernel, on the call's stream (stages MOE_STAGE_*), so one stage can be
+ *                     timed on the stream its kernels run on.
+ */
+enum { MOE_STAGE_GATE_UP = 0, MOE_STAGE_DOWN = 1, MOE_STAGE_COMBINE = 2, MOE_NUM_STAGES = 3 };
+typedef struct {
+  int small_m_max;
+  int dense_down_cols;
+  void* stage_start[MOE_NUM_STAGES];
+  void* stage_stop[MOE_NUM_STAGES];
+} moe_ffn_options;
+
+void moe_ffn_options_init(moe_ffn_options* opts /*[host]*/);
+
+/*
+ * moe_mxfp4_ffn_ex — moe_mxfp4_ffn with per-call options (NULL = the defaults of
+ * moe_ffn_options_init); same arguments, limits, results and errors otherwise.
+ */
+int moe_mxfp4_ffn_ex(const uint16_t* x_bf16, int T, int H, int I, int E, int k, const uint8_t* w13_q,
+                     const uint8_t* w13_s, const uint8_t* w2_q, const uint8_t* w2_s,
+                     const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                     const int32_t* sorted_pair, const int32_t* pair_pos, const int32_t* active,
+                     const int32_t* n_active, float clamp_limit, int flags, uint16_t* out_bf16,
+                     void* workspace, size_t ws_bytes, const moe_ffn_options* opts /*[host]*/,
+                     void* stream);
+
+/*
+ * Launch plan of moe_mxfp4_ffn_ex (host only, no GPU needed): which kernels one call with these
+ * sizes, flags and options enqueues, for tests and for reading the launch table. Per-expert row
+ * counts live on the device, so the plan is decided from host-known bounds: with T <= small_m_max
+ * every expert has at most T rows and only the weight-streaming kernels run; otherwise both kernel
+ * families are launched and each expert is handled by the family its row count selects.
+ * opts may be NULL (defaults).
  */
 typedef struct {
   int small_m_max;       /* experts with at most this many rows use the weight-streaming kernels */
@@ -236,36 +294,8 @@ typedef struct {
   int n_launches;        /* kernels enqueued by one call */
 } moe_ffn_plan;
 
-int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan /*[host]*/);
-
-/*
- * Launch-table threshold (host only, process-wide): experts with at most `small_m_max` rows run on
- * the weight-streaming kernels, the rest on the MFMA kernels. By default (-1) the threshold follows
- * the token count: 8 for T <= 8 (every expert streams), 2 above. Returns the previous setting (-1
- * for the default table), or MOE_ERR_SHAPE for a value below -1. Not synchronised with calls in
- * flight on other host threads.
- */
-int moe_set_small_m_max(int small_m_max);
-
-/*
- * Column tile of the dense (M >= 256 per expert) down GEMM (host only, process-wide): 256 or 224
- * output columns per workgroup. By default (0) the library takes the width that finishes the
- * expected ceil(T*k/256) x ceil(H/width) tiles in fewer, fuller rounds over the compute units (one
- * workgroup per compute unit), the wider on a tie; a value set here forces that width (tests cover
- * both). Returns the previous setting (0 for automatic), or MOE_ERR_SHAPE for any other value. Not
- * synchronised with calls in flight on other host threads.
- */
-int moe_set_dense_down_cols(int cols);
-
-/*
- * Stage timing hook (host only), for measuring one stage of moe_mxfp4_ffn with HIP events on the
- * stream its kernels run on. While set, every moe_mxfp4_ffn call records `start` before the first
- * kernel of `stage` and `stop` after its last kernel, on the call's stream. Pass NULL events to
- * clear. The events are hipEvent_t handles created by the caller; the library does not own them.
- * Returns MOE_ERR_SHAPE for an unknown stage.
- */
-enum { MOE_STAGE_GATE_UP = 0, MOE_STAGE_DOWN = 1, MOE_STAGE_COMBINE = 2, MOE_NUM_STAGES = 3 };
-int moe_set_stage_events(int stage, void* start_event, void* stop_event);
+int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags,
+                       const moe_ffn_options* opts /*[host]*/, moe_ffn_plan* plan /*[host]*/);
 
 /* Human-readable name of a status code (host, static storage). */
 const char* moe_status_string(int status);

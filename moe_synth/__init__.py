@@ -133,11 +133,71 @@ def make_router_weights(E: int, H: int, seed: int) -> np.ndarray:
 
 
 def small_case(T: int, H: int, I: int, E: int, k: int, seed: int, logits: str = "normal",
-               score_fn: int = SCORE_SOFTMAX, clamp: float = 0.0) -> tuple[Config, dict]:
-    """A random small workload with explicit shape (ragged shapes, edge cases)."""
+               score_fn: int = SCORE_SOFTMAX, clamp: float = 0.0, scale_lo: int = 120,
+               scale_hi: int = 124) -> tuple[Config, dict]:
+    """A random small workload with explicit shape (ragged shapes, edge cases); scale bytes uniform
+    in [scale_lo, scale_hi]."""
     cfg = Config(f"case_T{T}_H{H}_I{I}_E{E}_k{k}_s{seed}", T, H, I, E, k, score_fn=score_fn,
                  clamp=clamp, logits=logits)
-    return cfg, make_inputs(cfg, seed=seed)
+    return cfg, make_inputs(cfg, seed=seed, scale_lo=scale_lo, scale_hi=scale_hi)
+
+
+def lower_one_block_per_row(s: np.ndarray, below: int, seed: int) -> np.ndarray:
+    """Scale bytes [E, N, K/32] (K/32 >= 2) with one block of every row (a seeded choice) set `below`
+    steps under the largest byte of the row's other blocks (at least 2), the rest unchanged."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    s = s.copy()
+    E, N, nb = s.shape
+    assert nb >= 2
+    pick = rng.integers(0, nb, size=(E, N))
+    others = s.astype(np.int64)
+    np.put_along_axis(others, pick[..., None], -1, axis=2)
+    low = np.maximum(others.max(axis=2) - below, 2).astype(np.uint8)
+    np.put_along_axis(s, pick[..., None], low[..., None], axis=2)
+    return s
+
+
+def extreme_scale_case(T: int, H: int, I: int, E: int, k: int, seed: int, lam=(0, 20, -20, 100),
+                       score_fn: int = SCORE_SOFTMAX) -> tuple[Config, dict]:
+    """Weights whose E8M0 scale bytes reach both ends of the range the device decodes exactly (2 and
+    252), with activations that offset them so that no product or sum leaves the binary32 range.
+
+      - every fourth H-block of x holds values +-(1 + U[0,1)) * 2^-125 (normal bfloat16); the gate rows'
+        scale bytes in those blocks are 252 (products of ordinary size), elsewhere x ~ N(0,1) and the
+        gate scale bytes are 127 + U{-2..2}, with byte 2 in every fifth block (products ~2^-125);
+      - the up rows of I-block j carry an offset lam[j % len(lam)]: scale byte 127 + d - lam (kept in
+        [2, 252]), d = 125 on the 2^-125 x blocks and 0 elsewhere, so u (and h) of those rows is about
+        2^-lam;
+      - the down rows' scale bytes in I-block j are 127 + lam[j % len(lam)] + U{-2..2}, which brings each
+        block's products back to ordinary size, except: byte 252 in every third I-block whose lam is the
+        largest (products ~2^(125 - lam): those blocks dominate the output) and byte 2 in every seventh
+        block.
+    Codes are uniform bytes, logits N(0,1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cfg = Config(f"extreme_T{T}_H{H}_I{I}_E{E}_k{k}_s{seed}", T, H, I, E, k, score_fn=score_fn)
+    nbh, nbi = H // 32, I // 32
+    logits = rng.standard_normal(size=(T, E), dtype=np.float32)
+    d = np.where(np.arange(nbh) % 4 == 1, 125, 0)  # x exponent offset per H-block
+    mag = (1.0 + rng.random(size=(T, H))) * np.where(rng.random(size=(T, H)) < 0.5, -1.0, 1.0)
+    x = np.where(np.repeat(d, 32)[None, :] == 125, mag * 2.0 ** -125,
+                 rng.standard_normal(size=(T, H))).astype(np.float32)
+    lam_i = np.array([lam[j % len(lam)] for j in range(nbi)])  # per I-block of h
+    jit = lambda shape: rng.integers(-2, 3, size=shape)  # noqa: E731
+    gate_s = np.where(d[None, None, :] == 125, 252, 127 + jit((E, I, nbh)))
+    gate_s = np.where((np.arange(nbh) % 5 == 3)[None, None, :] & (d[None, None, :] == 0), 2, gate_s)
+    up_lam = np.repeat(lam_i, 32)[:I]  # per up row
+    up_s = np.broadcast_to(np.clip(127 + d[None, None, :] - up_lam[None, :, None], 2, 252), (E, I, nbh))
+    w2_s = 127 + lam_i[None, None, :] + jit((E, H, nbi))
+    w2_s = np.where(((np.arange(nbi) % 3 == 0) & (lam_i == max(lam)))[None, None, :], 252, w2_s)
+    w2_s = np.where((np.arange(nbi) % 7 == 5)[None, None, :], 2, w2_s)
+    w13_s = np.concatenate([gate_s, up_s], axis=1)
+    assert w13_s.min() >= 2 and w13_s.max() <= 252 and w2_s.min() >= 2 and w2_s.max() <= 252
+    out = dict(logits=logits, x=f32_to_bf16_bits(x),
+               w13_q=rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8),
+               w13_s=w13_s.astype(np.uint8),
+               w2_q=rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8),
+               w2_s=w2_s.astype(np.uint8))
+    return cfg, out
 
 
 def active_weight_bytes(counts: np.ndarray, H: int, I: int) -> int:

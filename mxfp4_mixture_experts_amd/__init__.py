@@ -38,6 +38,28 @@ class MoeError(RuntimeError):
     pass
 
 
+NUM_STAGES = 3
+
+
+class FfnOptions(ctypes.Structure):
+    """moe_ffn_options: per-call launch-table threshold, dense down column tile and stage events."""
+    _fields_ = [("small_m_max", ctypes.c_int), ("dense_down_cols", ctypes.c_int),
+                ("stage_start", ctypes.c_void_p * NUM_STAGES), ("stage_stop", ctypes.c_void_p * NUM_STAGES)]
+
+
+def ffn_options(small_m_max: int = -1, dense_down_cols: int = 0, stage_events: dict | None = None) -> FfnOptions:
+    """Options for one mxfp4_ffn call. stage_events maps a STAGE_* constant to a (start, stop) pair of
+    torch.cuda.Event objects recorded around that stage on the call's stream."""
+    o = FfnOptions()
+    load_library().moe_ffn_options_init(ctypes.byref(o))
+    o.small_m_max = int(small_m_max)
+    o.dense_down_cols = int(dense_down_cols)
+    for st, (a, b) in (stage_events or {}).items():
+        o.stage_start[st] = a.cuda_event if a is not None else None
+        o.stage_stop[st] = b.cuda_event if b is not None else None
+    return o
+
+
 class FfnPlan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int) for name in (
         "small_m_max", "launch_small", "launch_large", "small_gateup_grid", "small_down_grid",
@@ -68,7 +90,9 @@ def load_library(path: str | None = None):
     lib.moe_router_gemm_topk_workspace_size.restype = ctypes.c_size_t
     lib.moe_router_gemm_topk.argtypes = [V, V, i, i, i, i, i, i, V, V, V, V, ctypes.c_size_t, V]
     lib.moe_router_gemm_topk.restype = i
-    lib.moe_group_tokens.argtypes = [V, i, i, i, V, V, V, V, V, V, V]
+    lib.moe_group_tokens_workspace_size.argtypes = [i, i, i]
+    lib.moe_group_tokens_workspace_size.restype = ctypes.c_size_t
+    lib.moe_group_tokens.argtypes = [V, i, i, i, V, V, V, V, V, V, V, ctypes.c_size_t, V]
     lib.moe_group_tokens.restype = i
     lib.moe_route_group.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V]
     lib.moe_route_group.restype = i
@@ -77,14 +101,13 @@ def load_library(path: str | None = None):
     lib.moe_mxfp4_ffn.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_float,
                                   i, V, V, ctypes.c_size_t, V]
     lib.moe_mxfp4_ffn.restype = i
-    lib.moe_mxfp4_ffn_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(FfnPlan)]
+    lib.moe_mxfp4_ffn_ex.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_float,
+                                     i, V, V, ctypes.c_size_t, ctypes.POINTER(FfnOptions), V]
+    lib.moe_mxfp4_ffn_ex.restype = i
+    lib.moe_ffn_options_init.argtypes = [ctypes.POINTER(FfnOptions)]
+    lib.moe_ffn_options_init.restype = None
+    lib.moe_mxfp4_ffn_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(FfnOptions), ctypes.POINTER(FfnPlan)]
     lib.moe_mxfp4_ffn_plan.restype = i
-    lib.moe_set_small_m_max.argtypes = [i]
-    lib.moe_set_small_m_max.restype = i
-    lib.moe_set_dense_down_cols.argtypes = [i]
-    lib.moe_set_dense_down_cols.restype = i
-    lib.moe_set_stage_events.argtypes = [i, V, V]
-    lib.moe_set_stage_events.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -119,35 +142,12 @@ def abi_version() -> int:
     return load_library().moe_abi_version()
 
 
-def ffn_plan(T: int, H: int, I: int, E: int, k: int, flags: int = 0) -> dict:
+def ffn_plan(T: int, H: int, I: int, E: int, k: int, flags: int = 0, options: FfnOptions | None = None) -> dict:
     plan = FfnPlan()
-    _check(load_library().moe_mxfp4_ffn_plan(T, H, I, E, k, flags, ctypes.byref(plan)), "moe_mxfp4_ffn_plan")
+    _check(load_library().moe_mxfp4_ffn_plan(T, H, I, E, k, flags,
+                                             ctypes.byref(options) if options is not None else None,
+                                             ctypes.byref(plan)), "moe_mxfp4_ffn_plan")
     return plan.as_dict()
-
-
-def set_dense_down_cols(cols: int) -> int:
-    """Force the dense down GEMM's column tile (256 or 224; 0 restores the per-shape choice);
-    returns the previous setting."""
-    prev = load_library().moe_set_dense_down_cols(int(cols))
-    if prev < 0:
-        _check(prev, "moe_set_dense_down_cols")
-    return prev
-
-
-def set_small_m_max(v: int) -> int:
-    """Override the launch-table threshold (-1 restores the token-count table); returns the
-    previous setting."""
-    prev = load_library().moe_set_small_m_max(int(v))
-    if prev < -1:
-        _check(prev, "moe_set_small_m_max")
-    return prev
-
-
-def set_stage_events(stage: int, start, stop):
-    """Record HIP events around one stage of every later mxfp4_ffn call (None clears)."""
-    s = ctypes.c_void_p(start.cuda_event) if start is not None else None
-    e = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
-    _check(load_library().moe_set_stage_events(stage, s, e), "moe_set_stage_events")
 
 
 def ffn_workspace_size(T: int, H: int, I: int, E: int, k: int, flags: int = 0) -> int:
@@ -160,11 +160,17 @@ def ffn_workspace_size(T: int, H: int, I: int, E: int, k: int, flags: int = 0) -
 def route_topk(logits: torch.Tensor, k: int, score_fn: int = SCORE_SOFTMAX, renorm: bool = True,
                ids: torch.Tensor | None = None, weights: torch.Tensor | None = None, stream=None):
     _dev(logits, torch.float32, "logits")
+    if logits.dim() != 2:
+        raise MoeError("logits must be [T, E]")
     T, E = logits.shape
     if ids is None:
         ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     if weights is None:
         weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    if ids.shape != (T, k) or weights.shape != (T, k):
+        raise MoeError(f"ids and weights must be [{T}, {k}]")
+    _dev(ids, torch.int32, "topk_ids")
+    _dev(weights, torch.float32, "topk_w")
     _check(load_library().moe_route_topk(_ptr(logits), T, E, k, score_fn, int(bool(renorm)),
                                          _ptr(ids), _ptr(weights), _stream(stream)), "moe_route_topk")
     return ids, weights
@@ -216,14 +222,41 @@ class Grouping:
         z = lambda n: torch.empty(n, dtype=torch.int32, device=device)  # noqa: E731
         return Grouping(z(E), z(E + 1), z(P), z(P), z(E), z(1))
 
+    def check(self, T: int, k: int, E: int):
+        """Raise unless every buffer is a contiguous int32 device tensor large enough for T*k pairs
+        over E experts."""
+        P = T * k
+        for name, need in (("counts", E), ("offsets", E + 1), ("sorted_pair", P), ("pair_pos", P),
+                           ("active", E), ("n_active", 1)):
+            t = _dev(getattr(self, name), torch.int32, f"grouping.{name}")
+            if t.numel() < need:
+                raise MoeError(f"grouping.{name} holds {t.numel()} entries, needs {need} "
+                               f"(T={T}, k={k}, E={E})")
 
-def group_tokens(ids: torch.Tensor, E: int, out: Grouping | None = None, stream=None) -> Grouping:
+
+def group_workspace_size(T: int, k: int, E: int) -> int:
+    n = load_library().moe_group_tokens_workspace_size(T, k, E)
+    if n == ctypes.c_size_t(-1).value:
+        raise MoeError("invalid sizes for moe_group_tokens_workspace_size")
+    return n
+
+
+def group_tokens(ids: torch.Tensor, E: int, out: Grouping | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> Grouping:
     _dev(ids, torch.int32, "topk_ids")
+    if ids.dim() != 2:
+        raise MoeError("topk_ids must be [T, k]")
     T, k = ids.shape
     g = out if out is not None else Grouping.empty(T, k, E, ids.device)
+    g.check(T, k, E)
+    need = group_workspace_size(T, k, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=ids.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load_library().moe_group_tokens(_ptr(ids), T, k, E, _ptr(g.counts), _ptr(g.offsets),
                                            _ptr(g.sorted_pair), _ptr(g.pair_pos), _ptr(g.active),
-                                           _ptr(g.n_active), _stream(stream)), "moe_group_tokens")
+                                           _ptr(g.n_active), _ptr(workspace), ws_bytes, _stream(stream)),
+           "moe_group_tokens")
     return g
 
 
@@ -237,7 +270,12 @@ def route_group(logits: torch.Tensor, k: int, score_fn: int = SCORE_SOFTMAX, ren
         ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     if weights is None:
         weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    if ids.shape != (T, k) or weights.shape != (T, k):
+        raise MoeError(f"ids and weights must be [{T}, {k}]")
+    _dev(ids, torch.int32, "topk_ids")
+    _dev(weights, torch.float32, "topk_w")
     g = out if out is not None else Grouping.empty(T, k, E, logits.device)
+    g.check(T, k, E)
     _check(load_library().moe_route_group(_ptr(logits), T, E, k, score_fn, int(bool(renorm)), _ptr(ids),
                                           _ptr(weights), _ptr(g.counts), _ptr(g.offsets),
                                           _ptr(g.sorted_pair), _ptr(g.pair_pos), _ptr(g.active),
@@ -276,26 +314,59 @@ class Mxfp4Weights:
                 raise MoeError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
 
 
+def _as_bf16(x: torch.Tensor, name: str = "x") -> torch.Tensor:
+    """x as a contiguous 2-D bf16 device tensor (a uint16/int16 tensor of bf16 bit patterns is
+    viewed as bf16)."""
+    if not x.is_cuda or x.dim() != 2:
+        raise MoeError(f"{name} must be a 2-D device tensor")
+    if x.dtype in (torch.int16, torch.uint16):
+        x = x.view(torch.bfloat16)
+    return _dev(x, torch.bfloat16, name)
+
+
+def ffn_check(x: torch.Tensor, w: Mxfp4Weights, topk_w: torch.Tensor, grp: Grouping,
+              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, flags: int = 0):
+    """Shape, dtype and size checks of one mxfp4_ffn call (host only, before any launch)."""
+    x = _as_bf16(x)
+    T, H = x.shape
+    w.validate()
+    if H != w.H:
+        raise MoeError(f"x has hidden size {H}, the weights {w.H}")
+    _dev(topk_w, torch.float32, "topk_w")
+    if topk_w.dim() != 2 or topk_w.shape[0] != T:
+        raise MoeError(f"topk_w must be [T={T}, k], got {tuple(topk_w.shape)}")
+    k = topk_w.shape[1]
+    grp.check(T, k, w.E)
+    if out is not None:
+        _dev(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (T, H):
+            raise MoeError(f"out must be [{T}, {H}], got {tuple(out.shape)}")
+    if workspace is not None:
+        _dev(workspace, torch.uint8, "workspace")
+        need = ffn_workspace_size(T, H, w.I, w.E, k, flags)
+        if workspace.numel() < need:
+            raise MoeError(f"workspace holds {workspace.numel()} bytes, needs {need}")
+    return x, T, H, k
+
+
 def mxfp4_ffn(x: torch.Tensor, w: Mxfp4Weights, topk_w: torch.Tensor, grp: Grouping,
               clamp_limit: float = 0.0, flags: int = 0, out: torch.Tensor | None = None,
-              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+              workspace: torch.Tensor | None = None, options: FfnOptions | None = None,
+              stream=None) -> torch.Tensor:
     """x: bf16 [T, H] (torch.bfloat16 or its uint16/int16 bit pattern); returns bf16 [T, H]."""
-    if not x.is_cuda or x.dim() != 2:
-        raise MoeError("x must be a 2-D device tensor")
-    T, H = x.shape
-    k = topk_w.shape[1] if topk_w.dim() == 2 else 1
+    x, T, H, k = ffn_check(x, w, topk_w, grp, out, workspace, flags)
     E, I = w.E, w.I
-    _dev(topk_w, torch.float32, "topk_w")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     need = ffn_workspace_size(T, H, I, E, k, flags)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    _check(load_library().moe_mxfp4_ffn(
+    _check(load_library().moe_mxfp4_ffn_ex(
         _ptr(x), T, H, I, E, k, _ptr(w.w13_q), _ptr(w.w13_s), _ptr(w.w2_q), _ptr(w.w2_s),
         _ptr(topk_w), _ptr(grp.counts), _ptr(grp.offsets), _ptr(grp.sorted_pair), _ptr(grp.pair_pos),
         _ptr(grp.active), _ptr(grp.n_active), float(clamp_limit), int(flags), _ptr(out),
-        _ptr(workspace), workspace.numel(), _stream(stream)), "moe_mxfp4_ffn")
+        _ptr(workspace), workspace.numel(), ctypes.byref(options) if options is not None else None,
+        _stream(stream)), "moe_mxfp4_ffn_ex")
     return out
 
 
@@ -325,11 +396,20 @@ class MoELayer:
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, weights: Mxfp4Weights | None = None,
-                stream=None) -> torch.Tensor:
+                stream=None, options: FfnOptions | None = None) -> torch.Tensor:
+        x = _as_bf16(x)
         T = x.shape[0]
         if T > self.T:
             raise MoeError(f"{T} tokens exceed the layer's capacity {self.T}")
         w = weights if weights is not None else self.w
+        if (w.E, w.H, w.I) != (self.w.E, self.w.H, self.w.I):
+            raise MoeError("weights differ in shape from the layer's")
+        _dev(logits, torch.float32, "logits")
+        if tuple(logits.shape) != (T, w.E):
+            raise MoeError(f"logits must be [{T}, {w.E}], got {tuple(logits.shape)}")
+        if x.shape[1] != w.H:
+            raise MoeError(f"x has hidden size {x.shape[1]}, the layer {w.H}")
         ids, tw = self.ids[:T], self.topk_w[:T]
         route_group(logits, self.k, self.score_fn, self.renorm, ids, tw, self.grp, stream)
-        return mxfp4_ffn(x, w, tw, self.grp, self.clamp, self.flags, self.out[:T], self.workspace, stream)
+        return mxfp4_ffn(x, w, tw, self.grp, self.clamp, self.flags, self.out[:T], self.workspace, options,
+                         stream)

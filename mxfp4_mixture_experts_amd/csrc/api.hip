@@ -2,7 +2,6 @@
 // stream-ordered launches. Nothing here allocates, synchronises or reads device memory.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <climits>
 
 #include "kernels.hpp"
@@ -17,14 +16,8 @@ namespace {
 // T <= 8 every expert stays on the streaming kernels (no schedule or MFMA launches at decode); above
 // that, experts with more than 2 rows go to the MFMA kernels (the streaming kernels hold two
 // tokens' activations in registers, and each further pair of tokens costs another decode pass and a
-// reload). A value set through moe_set_small_m_max overrides the table; -1 restores it.
-std::atomic<int> g_small_m_max{-1};
-std::atomic<int> g_dense_down_cols{0};  // 0: chosen per shape; 256 or 224: forced
-
+// reload). A call's options may override the threshold.
 int table_small_m_max(int T) { return T <= 8 ? 8 : 2; }
-
-std::atomic<void*> g_stage_start[MOE_NUM_STAGES];
-std::atomic<void*> g_stage_stop[MOE_NUM_STAGES];
 
 constexpr size_t kAlign = 256;
 
@@ -82,15 +75,25 @@ bool ffn_sizes_ok(int T, int H, int I, int E, int k) {
 
 constexpr int kKnownFlags = MOE_UNFUSED_GATE_UP | MOE_FORCE_SMALL_M | MOE_FORCE_LARGE_M;
 
-int effective_small_m_max(int T, int flags) {
+int effective_small_m_max(int T, int flags, const moe_ffn_options& o) {
   if (flags & MOE_FORCE_SMALL_M) return INT_MAX;
   if (flags & MOE_FORCE_LARGE_M) return 0;
-  const int v = g_small_m_max.load();
-  return v >= 0 ? v : table_small_m_max(T);
+  return o.small_m_max >= 0 ? o.small_m_max : table_small_m_max(T);
 }
 
-void fill_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan) {
-  const int thr = effective_small_m_max(T, flags);
+// The caller's options (validated), or the defaults.
+int read_options(const moe_ffn_options* in, moe_ffn_options& o) {
+  moe_ffn_options_init(&o);
+  if (!in) return MOE_OK;
+  if (in->small_m_max < -1) return MOE_ERR_SHAPE;
+  if (in->dense_down_cols != 0 && in->dense_down_cols != 256 && in->dense_down_cols != 224)
+    return MOE_ERR_SHAPE;
+  o = *in;
+  return MOE_OK;
+}
+
+void fill_plan(int T, int H, int I, int E, int k, int flags, const moe_ffn_options& o, moe_ffn_plan* plan) {
+  const int thr = effective_small_m_max(T, flags, o);
   const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k, num_cus());
   const moe::LargePlan lp = moe::plan_large(T, H, I, E, k, thr == INT_MAX ? INT_MAX - 1 : thr);
   plan->small_m_max = thr;
@@ -111,8 +114,8 @@ void fill_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan)
                      (dense ? 3 : 0) + (T > 0 ? 1 : 0);
 }
 
-void record(int stage, bool start, hipStream_t stream) {
-  void* ev = start ? g_stage_start[stage].load() : g_stage_stop[stage].load();
+void record(const moe_ffn_options& o, int stage, bool start, hipStream_t stream) {
+  void* ev = start ? o.stage_start[stage] : o.stage_stop[stage];
   if (ev) (void)hipEventRecord((hipEvent_t)ev, stream);
 }
 
@@ -132,21 +135,11 @@ MOE_API const char* moe_status_string(int status) {
   }
 }
 
-MOE_API int moe_set_small_m_max(int v) {
-  if (v < -1) return MOE_ERR_SHAPE;
-  return g_small_m_max.exchange(v);
-}
-
-MOE_API int moe_set_dense_down_cols(int cols) {
-  if (cols != 0 && cols != 256 && cols != 224) return MOE_ERR_SHAPE;
-  return g_dense_down_cols.exchange(cols);
-}
-
-MOE_API int moe_set_stage_events(int stage, void* start_event, void* stop_event) {
-  if (stage < 0 || stage >= MOE_NUM_STAGES) return MOE_ERR_SHAPE;
-  g_stage_start[stage].store(start_event);
-  g_stage_stop[stage].store(stop_event);
-  return MOE_OK;
+MOE_API void moe_ffn_options_init(moe_ffn_options* o) {
+  if (!o) return;
+  o->small_m_max = -1;
+  o->dense_down_cols = 0;
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) o->stage_start[i] = o->stage_stop[i] = nullptr;
 }
 
 MOE_API int moe_route_topk(const float* logits, int T, int E, int k, int score_fn, int renorm,
@@ -187,12 +180,22 @@ MOE_API int moe_router_gemm_topk(const uint16_t* x_bf16, const uint16_t* w_route
   return MOE_OK;
 }
 
+// The grouping is one workgroup with its histograms and scans in LDS: no device workspace.
+MOE_API size_t moe_group_tokens_workspace_size(int T, int k, int E) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || (long)T * k > MOE_MAX_PAIRS)
+    return (size_t)-1;
+  return 0;
+}
+
 MOE_API int moe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                              int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                             int32_t* active, int32_t* n_active, void* stream) {
+                             int32_t* active, int32_t* n_active, void* workspace, size_t ws_bytes,
+                             void* stream) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK ||
       (long)T * k > MOE_MAX_PAIRS)
     return MOE_ERR_SHAPE;
+  (void)workspace;
+  if (ws_bytes < moe_group_tokens_workspace_size(T, k, E)) return MOE_ERR_WORKSPACE;
   if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
   if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return MOE_ERR_NULL;
   if (moe::launch_group_tokens(topk_ids, T * k, E, counts, offsets, sorted_pair, pair_pos, active,
@@ -230,25 +233,34 @@ MOE_API size_t moe_mxfp4_ffn_workspace_size(int T, int H, int I, int E, int k, i
   return ws_layout((long)T * k, H, I, E, k, flags).total;
 }
 
-MOE_API int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags, moe_ffn_plan* plan) {
+MOE_API int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags, const moe_ffn_options* opts,
+                               moe_ffn_plan* plan) {
   if (!plan) return MOE_ERR_NULL;
   if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
   if ((flags & ~kKnownFlags) || ((flags & MOE_FORCE_SMALL_M) && (flags & MOE_FORCE_LARGE_M)))
     return MOE_ERR_UNSUPPORTED;
-  fill_plan(T, H, I, E, k, flags, plan);
+  moe_ffn_options o;
+  const int st = read_options(opts, o);
+  if (st != MOE_OK) return st;
+  fill_plan(T, H, I, E, k, flags, o, plan);
   return MOE_OK;
 }
 
-MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
-                          const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
-                          const uint8_t* w2_s, const float* topk_w, const int32_t* counts,
-                          const int32_t* offsets, const int32_t* sorted_pair,
-                          const int32_t* pair_pos, const int32_t* active, const int32_t* n_active,
-                          float clamp_limit, int flags, uint16_t* out_bf16, void* workspace,
-                          size_t ws_bytes, void* stream) {
+MOE_API int moe_mxfp4_ffn_ex(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                             const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                             const uint8_t* w2_s, const float* topk_w, const int32_t* counts,
+                             const int32_t* offsets, const int32_t* sorted_pair,
+                             const int32_t* pair_pos, const int32_t* active, const int32_t* n_active,
+                             float clamp_limit, int flags, uint16_t* out_bf16, void* workspace,
+                             size_t ws_bytes, const moe_ffn_options* opts, void* stream) {
   if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
   if ((flags & ~kKnownFlags) || ((flags & MOE_FORCE_SMALL_M) && (flags & MOE_FORCE_LARGE_M)))
     return MOE_ERR_UNSUPPORTED;
+  moe_ffn_options o;
+  {
+    const int st = read_options(opts, o);
+    if (st != MOE_OK) return st;
+  }
   if (T == 0) return MOE_OK;
   if (!x_bf16 || !w13_q || !w13_s || !w2_q || !w2_s || !topk_w || !counts || !offsets ||
       !sorted_pair || !pair_pos || !active || !n_active || !out_bf16 || !workspace)
@@ -261,7 +273,7 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
 
   moe_ffn_plan plan;
-  fill_plan(T, H, I, E, k, flags, &plan);
+  fill_plan(T, H, I, E, k, flags, o, &plan);
   const int thr = plan.small_m_max;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -282,7 +294,7 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   int32_t* dense_m0 = dense_e + wl.dense_slots_max;
   const bool dense = plan.launch_large && T >= moe::kDenseMinRows;
   const int dense_min = dense ? moe::kDenseMinRows : INT_MAX;
-  const moe::DensePlan dp = moe::plan_dense(T, H, I, E, k, moe::kDenseMinRows, num_cus(), g_dense_down_cols.load() / 32);
+  const moe::DensePlan dp = moe::plan_dense(T, H, I, E, k, moe::kDenseMinRows, num_cus(), o.dense_down_cols / 32);
   // without MFMA kernels every active expert is small: the grouping's active list is the work list
   const int32_t* list = plan.launch_large ? small_list : active;
   const int32_t* list_count = plan.launch_large ? n_small : n_active;
@@ -292,7 +304,7 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
     ok &= moe::launch_schedule(r, E, thr, wl.tile_slots_max, dense_min, dp.slots, small_list, n_small,
                                tile_e, tile_m0, dense_e, dense_m0, s) == hipSuccess;
 
-  record(MOE_STAGE_GATE_UP, true, s);
+  record(o, MOE_STAGE_GATE_UP, true, s);
   if (plan.launch_small) {
     if (flags & MOE_UNFUSED_GATE_UP) {
       ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
@@ -310,9 +322,9 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   if (dense)
     ok &= moe::launch_dense_gateup(dp, r, H, I, w13_q, w13_s, dense_e, dense_m0, clamp_limit, h_hi, h_lo, s) ==
           hipSuccess;
-  record(MOE_STAGE_GATE_UP, false, s);
+  record(o, MOE_STAGE_GATE_UP, false, s);
 
-  record(MOE_STAGE_DOWN, true, s);
+  record(o, MOE_STAGE_DOWN, true, s);
   if (dense)
     ok &= moe::launch_dense_h16(dp, r, I, dense_e, dense_m0, h_hi, h_lo, rowf, s) == hipSuccess;
   if (plan.launch_small)
@@ -322,10 +334,22 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
     ok &= moe::launch_large_down(lp, r, H, I, w2_q, w2_s, tile_e, tile_m0, h_hi, h_lo, y, s) == hipSuccess;
   if (dense)
     ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, rowf, y, s) == hipSuccess;
-  record(MOE_STAGE_DOWN, false, s);
+  record(o, MOE_STAGE_DOWN, false, s);
 
-  record(MOE_STAGE_COMBINE, true, s);
+  record(o, MOE_STAGE_COMBINE, true, s);
   ok &= moe::launch_combine(y, topk_w, pair_pos, T, H, k, out_bf16, nullptr, s) == hipSuccess;
-  record(MOE_STAGE_COMBINE, false, s);
+  record(o, MOE_STAGE_COMBINE, false, s);
   return ok ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                          const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                          const uint8_t* w2_s, const float* topk_w, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* sorted_pair,
+                          const int32_t* pair_pos, const int32_t* active, const int32_t* n_active,
+                          float clamp_limit, int flags, uint16_t* out_bf16, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  return moe_mxfp4_ffn_ex(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, topk_w, counts, offsets,
+                          sorted_pair, pair_pos, active, n_active, clamp_limit, flags, out_bf16,
+                          workspace, ws_bytes, nullptr, stream);
 }

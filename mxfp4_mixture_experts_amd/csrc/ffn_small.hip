@@ -796,17 +796,12 @@ hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32
   }
 }
 
-// Bound on the h rows of one down workgroup's range when the list is the whole active list (every
-// expert has at most T rows). Weighted ranges hold cost total/G, and an expert inside a range costs
-// at least (rows + 3) per item over its items, so the experts wholly inside hold at most 4P/G + 1
-// rows (the total cost is at most 4 per row); two more experts can overlap its ends. Equal-count
-// ranges span at most ceil(P/G) + 2 experts.
-int down_stage_rows(const SmallPlan& sp) {
-  const long G = sp.dn_grid > 0 ? sp.dn_grid : 1;
-  const long P = sp.P, T = sp.T;
-  const long rows = sp.weighted ? 4 * P / G + 1 + 2 * T : ((P + G - 1) / G + 2) * T;
-  return (int)(rows < P ? rows : P);
-}
+// Bound on the h rows of one down workgroup's range when the list is the whole active list. The
+// grouping does not require a token's ids to be distinct, so one expert can hold every one of the
+// P rows; a range of consecutive experts spans at most all of them. The bound is therefore P: the
+// staged kernel runs only when all of h fits the LDS (decode at one or two tokens), whatever the
+// routing.
+int down_stage_rows(const SmallPlan& sp) { return sp.P; }
 
 // LDS a workgroup can hold on the current device (at most kStageMaxBytes)
 constexpr size_t kStageMaxBytes = 150 * 1024;

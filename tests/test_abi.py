@@ -28,10 +28,21 @@ def lib():
     return m.load_library()
 
 
-def test_header_declares_the_three_calls():
+# The boundary's entry points as the hot-path scope lists them (route, group with its workspace
+# query, the FFN with its workspace query, status strings and the version).
+BOUNDARY = ("moe_route_topk", "moe_group_tokens_workspace_size", "moe_group_tokens",
+            "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_status_string", "moe_abi_version")
+
+
+def test_header_declares_the_boundary_calls():
     fns = declared_functions()
-    for name in ("moe_route_topk", "moe_group_tokens", "moe_mxfp4_ffn", "moe_mxfp4_ffn_workspace_size"):
+    for name in BOUNDARY:
         assert name in fns
+
+
+def test_no_process_wide_setters():
+    """Tuning and timing choices are per-call options, not mutable library state."""
+    assert not [f for f in declared_functions() if f.startswith("moe_set_")]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -44,7 +55,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.moe_status_string(code)
     assert b"unknown" in lib.moe_status_string(42)
@@ -69,18 +80,33 @@ def test_route_validation(lib):
 
 def test_group_validation(lib):
     s = None
-    assert lib.moe_group_tokens(DUMMY, 4, 2, 0, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, s) == -2
-    assert lib.moe_group_tokens(DUMMY, 4, 0, 8, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, s) == -2
-    assert lib.moe_group_tokens(DUMMY, 4, 2, 8, None, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, s) == -1
-    assert lib.moe_group_tokens(DUMMY, 4, 2, 8, DUMMY, DUMMY, None, DUMMY, DUMMY, DUMMY, s) == -1
-    assert lib.moe_group_tokens(None, 4, 2, 8, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, s) == -1
-    assert lib.moe_group_tokens(DUMMY, 1 << 20, 8, 8, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, s) == -2
+    sz = ctypes.c_size_t
+    lib.moe_group_tokens_workspace_size.restype = ctypes.c_size_t
+    assert lib.moe_group_tokens_workspace_size(8, 8, 256) == 0
+    assert lib.moe_group_tokens_workspace_size(0, 8, 256) == 0
+    invalid = ctypes.c_size_t(-1).value
+    assert lib.moe_group_tokens_workspace_size(4, 2, 0) == invalid
+    assert lib.moe_group_tokens_workspace_size(1 << 20, 8, 8) == invalid
+
+    def call(ids=DUMMY, T=4, k=2, E=8, counts=DUMMY, sp=DUMMY, ws=None, ws_bytes=0):
+        return lib.moe_group_tokens(ids, T, k, E, counts, DUMMY, sp, DUMMY, DUMMY, DUMMY, ws, sz(ws_bytes), s)
+
+    assert call(E=0) == -2
+    assert call(k=0) == -2
+    assert call(counts=None) == -1
+    assert call(sp=None) == -1
+    assert call(ids=None) == -1
+    assert call(T=1 << 20, k=8) == -2
 
 
-def ffn(lib, T=8, H=4096, I=2048, E=256, k=8, x=DUMMY, ws=V(0x10000), ws_bytes=1 << 40, flags=0, out=DUMMY):
+def ffn(lib, T=8, H=4096, I=2048, E=256, k=8, x=DUMMY, ws=V(0x10000), ws_bytes=1 << 40, flags=0, out=DUMMY,
+        opts=None):
     d = DUMMY
-    return lib.moe_mxfp4_ffn(x, T, H, I, E, k, d, d, d, d, d, d, d, d, d, d, d, ctypes.c_float(0.0),
-                             flags, out, ws, ws_bytes, None)
+    if opts is None:
+        return lib.moe_mxfp4_ffn(x, T, H, I, E, k, d, d, d, d, d, d, d, d, d, d, d, ctypes.c_float(0.0),
+                                 flags, out, ws, ws_bytes, None)
+    return lib.moe_mxfp4_ffn_ex(x, T, H, I, E, k, d, d, d, d, d, d, d, d, d, d, d, ctypes.c_float(0.0),
+                                flags, out, ws, ws_bytes, ctypes.byref(opts), None)
 
 
 def test_ffn_shape_validation(lib):
@@ -138,34 +164,26 @@ def test_launch_plan(lib):
     assert p["n_launches"] == 0
     assert m.ffn_plan(8, 4096, 2048, 256, 8)["small_m_max"] == 8
     assert m.ffn_plan(256, 4096, 2048, 256, 8)["small_m_max"] == 2
-    prev = m.set_small_m_max(2)
-    try:
-        assert prev == -1
-        assert m.ffn_plan(8, 4096, 2048, 256, 8)["launch_large"] == 1
-    finally:
-        m.set_small_m_max(prev)
-    assert m.ffn_plan(8, 4096, 2048, 256, 8)["launch_large"] == 0
+    assert m.ffn_plan(8, 4096, 2048, 256, 8, options=m.ffn_options(small_m_max=2))["launch_large"] == 1
+    assert m.ffn_plan(8, 4096, 2048, 256, 8)["launch_large"] == 0  # nothing persists between calls
     with pytest.raises(m.MoeError):
         m.ffn_plan(8, 4096, 2048, 256, 8, 6)
+    with pytest.raises(m.MoeError):
+        m.ffn_plan(8, 4096, 2048, 256, 8, options=m.ffn_options(small_m_max=-2))
 
 
-def test_dense_down_cols_setting(lib):
+def test_ffn_options_validation(lib):
     import mxfp4_mixture_experts_amd as m
 
+    o = m.FfnOptions()
+    lib.moe_ffn_options_init(ctypes.byref(o))
+    assert o.small_m_max == -1 and o.dense_down_cols == 0
+    assert all(v is None for v in o.stage_start) and all(v is None for v in o.stage_stop)
     for bad in (-1, 1, 128, 255, 512):
-        with pytest.raises(m.MoeError):
-            m.set_dense_down_cols(bad)
-    prev = m.set_dense_down_cols(224)
-    try:
-        assert prev == 0
-        assert m.set_dense_down_cols(256) == 224
-    finally:
-        assert m.set_dense_down_cols(prev) == 256
-
-
-def test_stage_events_validation(lib):
-    assert lib.moe_set_stage_events(3, None, None) == -2
-    assert lib.moe_set_stage_events(0, None, None) == 0
+        assert ffn(lib, opts=m.ffn_options(dense_down_cols=bad)) == -2
+    assert ffn(lib, opts=m.ffn_options(small_m_max=-5)) == -2
+    # valid options pass validation (the call then fails on its NULL output only)
+    assert ffn(lib, out=None, opts=m.ffn_options(dense_down_cols=224, small_m_max=0)) == -1
 
 
 def test_router_gemm_validation(lib):

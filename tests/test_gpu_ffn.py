@@ -92,11 +92,8 @@ def test_dense_shapes(orc, case):
     w = weights_to_device(inp)
     for cols in (256, 224):
         print(f"dense down with {cols}-column tiles", flush=True)
-        prev = moe.set_dense_down_cols(cols)
-        try:
-            g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w, renorm=cfg.renorm)
-        finally:
-            moe.set_dense_down_cols(prev)
+        g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w, renorm=cfg.renorm,
+                      options=moe.ffn_options(dense_down_cols=cols))
         np.testing.assert_array_equal(g["out_bf16"], outs["default"])
 
 
@@ -131,11 +128,8 @@ def test_dense_edges(orc, case):
     outs = []
     for cols in (0, 256, 224):
         print(f"dense edge T={T} H={H} I={I} rows={rows} down cols={cols or 'auto'}", flush=True)
-        prev = moe.set_dense_down_cols(cols)
-        try:
-            g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w, renorm=cfg.renorm)
-        finally:
-            moe.set_dense_down_cols(prev)
+        g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w, renorm=cfg.renorm,
+                      options=moe.ffn_options(dense_down_cols=cols))
         np.testing.assert_array_equal(g["sorted_pair"], ref["sorted_pair"])
         assert_output_parity(g["out_bf16"], ref["out_ref"], f"dense edge {rows} cols={cols}")
         outs.append(g["out_bf16"])
@@ -155,22 +149,26 @@ def test_threshold_sweep_same_result(orc):
     cfg, inp = moe_synth.small_case(48, 512, 256, 8, 3, 21)
     ref = oracle_full(orc, inp, cfg)
     w = weights_to_device(inp)
-    prev = moe.set_small_m_max(-1)
-    try:
-        for thr in (0, 1, 2, 4, 8, 16, 32, 1000):
-            moe.set_small_m_max(thr)
-            print(f"threshold {thr}", flush=True)
-            g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w)
-            assert_output_parity(g["out_bf16"], ref["out_ref"], f"thr={thr}")
-    finally:
-        moe.set_small_m_max(prev)
+    for thr in (0, 1, 2, 4, 8, 16, 32, 1000):
+        print(f"threshold {thr}", flush=True)
+        g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w, options=moe.ffn_options(small_m_max=thr))
+        assert_output_parity(g["out_bf16"], ref["out_ref"], f"thr={thr}")
 
 
-def sample_tokens(ref_ids, counts, T, n=6):
-    """Tokens to check at full size: first, last, and tokens routed to the most and least loaded
-    active experts (so both kernel families are covered)."""
+def sample_tokens(ref_ids, grp, T, k, n=20):
+    """Tokens to check at full size: first, last, tokens routed to the most and least loaded active
+    experts, and the tokens at the row-tile edges (rows 0, 63, 64, 127, 128, 255, 256, 511, 512,
+    767, 768 and the last) of the most loaded expert, so every 64-row MFMA tile boundary and every
+    256-row dense tile of it is reached (with one token per row of every expert, as at m1024, of
+    every expert); the rest seeded at random."""
+    counts, offsets, sorted_pair = grp["counts"], grp["offsets"], grp["sorted_pair"]
     loads = counts[ref_ids].max(axis=1)
     picks = {0, T - 1, int(np.argmax(loads)), int(np.argmin(loads))}
+    e = int(np.argmax(counts))
+    M = int(counts[e])
+    for r in (0, 63, 64, 127, 128, 255, 256, 511, 512, 767, 768, M - 1):
+        if 0 <= r < M:
+            picks.add(int(sorted_pair[offsets[e] + r]) // k)
     rng = np.random.default_rng(T)
     while len(picks) < n:
         picks.add(int(rng.integers(0, T)))
@@ -183,7 +181,7 @@ def test_large_configs_sampled(orc, name):
     inp = moe_synth.make_inputs(cfg)
     ids, wts = orc.route_topk(inp["logits"], cfg.k, cfg.score_fn, cfg.renorm)
     grp = orc.group_tokens(ids, cfg.E)
-    toks = sample_tokens(ids, grp["counts"], cfg.T)
+    toks = sample_tokens(ids, grp, cfg.T, cfg.k)
     ref = orc.mxfp4_ffn(inp["x"][toks], inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"], ids[toks],
                         wts[toks], cfg.clamp)
     w = weights_to_device(inp)
@@ -193,7 +191,33 @@ def test_large_configs_sampled(orc, name):
         np.testing.assert_array_equal(g["topk_ids"], ids)
         np.testing.assert_array_equal(g["counts"], grp["counts"])
         np.testing.assert_array_equal(g["sorted_pair"], grp["sorted_pair"])
-        assert_output_parity(g["out_bf16"][toks], ref["out_ref"], f"{name}/{fname}")
+        assert_output_parity(g["out_bf16"][toks], ref["out_ref"], f"{name}/{fname} ({len(toks)} tokens)")
+
+
+DUP_IDS = [
+    # T, H, I, E, k, ids of every token: repeated ids put several pairs of one token in one expert
+    (8, 4096, 2048, 8, 8, [0] * 8),                   # one expert with all 64 rows
+    (2, 4096, 2048, 8, 8, [0] * 8),                   # 16 rows: all of h fits the LDS (staged down)
+    (8, 1024, 512, 8, 8, [0, 0, 0, 1, 1, 2, 4, 0]),   # mixed multiplicities
+    (300, 256, 128, 3, 2, [1, 1]),                     # 600 rows in one expert: dense kernels
+]
+
+
+@pytest.mark.parametrize("case", DUP_IDS, ids=lambda c: "T%d_H%d_I%d_E%d_k%d" % c[:5])
+def test_duplicate_ids(orc, case):
+    """The grouping accepts ids repeated within a token; every kernel family handles the expert
+    that then holds more rows than there are tokens."""
+    T, H, I, E, k, row = case
+    cfg, inp = moe_synth.small_case(T, H, I, E, k, 50 + T)
+    ids = np.tile(np.array(row, np.int32), (T, 1))
+    wts = np.full((T, k), 1.0 / k)
+    ref = orc.mxfp4_ffn(inp["x"], inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"], ids, wts)
+    w = weights_to_device(inp)
+    for fname in ("default", "small", "large"):
+        print(f"duplicate ids T={T} H={H} I={I} E={E} k={k} flags={fname}", flush=True)
+        g = run_layer(inp, k, 0, 0.0, FLAG_SETS[fname], w=w, ids=ids)
+        np.testing.assert_array_equal(g["counts"], np.bincount(ids.ravel(), minlength=E))
+        assert_output_parity(g["out_bf16"], ref["out_ref"], f"dup ids T{T} I{I} {row}/{fname}")
 
 
 def test_empty_batch():
@@ -206,3 +230,36 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert out.shape == (0, 32)
     assert int(grp.n_active.item()) == 0 and int(grp.counts.sum().item()) == 0
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The binding checks shapes, dtypes and buffer sizes before any launch (MoeError)."""
+    cfg, inp = moe_synth.small_case(4, 256, 128, 8, 2, 77)
+    w = weights_to_device(inp)
+    x = x_to_device(inp["x"])
+    logits = dev(inp["logits"])
+    layer = moe.MoELayer(w, 2, 4)
+    ids, tw = moe.route_topk(logits, 2)
+    grp = moe.group_tokens(ids, 8)
+    bad = [
+        lambda: layer.forward(x, dev(np.zeros((4, 9), np.float32))),       # logits wider than E
+        lambda: layer.forward(x, dev(np.zeros((5, 8), np.float32))),       # more logits rows than tokens
+        lambda: layer.forward(x[:, :128], logits),                          # hidden size
+        lambda: layer.forward(torch.zeros((5, 256), dtype=torch.bfloat16, device="cuda"),
+                              dev(np.zeros((5, 8), np.float32))),          # above capacity
+        lambda: moe.mxfp4_ffn(x[:, :224], w, tw, grp),                      # x width != H
+        lambda: moe.mxfp4_ffn(x.float(), w, tw, grp),                       # x dtype
+        lambda: moe.mxfp4_ffn(x.t().contiguous().t(), w, tw, grp),          # x not contiguous
+        lambda: moe.mxfp4_ffn(x, w, tw[:3], grp),                           # topk_w rows != T
+        lambda: moe.mxfp4_ffn(x, w, tw, moe.Grouping.empty(4, 2, 4, "cuda")),  # grouping for E=4
+        lambda: moe.mxfp4_ffn(x, w, tw, moe.Grouping.empty(2, 2, 8, "cuda")),  # grouping for P=4
+        lambda: moe.mxfp4_ffn(x, w, tw, grp, workspace=torch.empty(16, dtype=torch.uint8, device="cuda")),
+        lambda: moe.mxfp4_ffn(x, w, tw, grp, out=torch.empty((4, 128), dtype=torch.bfloat16, device="cuda")),
+        lambda: moe.group_tokens(ids, 8, out=moe.Grouping.empty(4, 2, 4, "cuda")),
+        lambda: moe.route_topk(logits, 2, ids=torch.empty((4, 3), dtype=torch.int32, device="cuda")),
+    ]
+    for i, f in enumerate(bad):
+        print(f"binding check #{i}", flush=True)
+        with pytest.raises(moe.MoeError):
+            f()
+    torch.cuda.synchronize()
