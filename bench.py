@@ -5,9 +5,11 @@ on one batch of seeded synthetic input resident in HBM. The default workload is 
 T=8 tokens, H=4096, I=2048, E=256 experts, top-8 softmax routing (the c8 decode shape the vllm.cpp
 PR #52 node-trace diff measures). Weights are random MXFP4 of that shape, rotated over enough
 device replicas that every step streams them cold from HBM (no step finds its weights in the 256 MB
-last-level cache). Prints one JSON line.
+last-level cache). Prints one JSON line: the headline workload's numbers, then the same layer
+measurement for the other workloads (one token, two tokens, decode M=8 with the unfused gate/up,
+and per-expert M=1024 on the matrix cores) under "other_workloads".
 
-  python bench.py [--steps K] [--warmup W] [--config decode_m8] [--mode graph|eager]
+  python bench.py [--steps K] [--warmup W] [--config decode_m8] [--mode graph|eager] [--no-others]
 """
 from __future__ import annotations
 
@@ -29,6 +31,10 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 LLC_BYTES = 256 << 20           # MI355X Infinity Cache
 METRIC = "µs/MoE layer + weight-stream GB/s (% HBM peak) at M=8 decode, 1 GPU"
 
+# (name, workload, ffn flags) measured after the headline, fewer steps each, no CPU baseline
+OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0), ("decode_m2", "decode_m2", 0),
+                   ("decode_m8_unfused", "decode_m8", 1), ("m1024", "m1024", 0))
+
 
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -48,6 +54,8 @@ def parse():
                     help="launch-table threshold override (moe_ffn_options.small_m_max; -1 = the library's table)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-others", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--other-steps", type=int, default=50, help="timed steps of each other workload")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain device copy of this many bytes (counter calibration)")
     return ap.parse_args()
@@ -87,118 +95,114 @@ def committed_traffic(config: str, src_hash: str):
         return None
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path (the layer would shard by "
-              "experts or by the intermediate dimension, with one all-to-all or all-reduce per layer); "
-              "run it with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def quantile(v, q):
+    """q-th decile (1..9) of v, or None for a single value."""
+    return round(statistics.quantiles(v, n=10)[q - 1], 2) if len(v) > 1 else None
 
-    import numpy as np
-    import torch
 
-    import moe_synth
-    import mxfp4_mixture_experts_amd as moe
+class Env:
+    """torch, the library and the timing stream, shared by every measurement."""
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    moe.load_library()
-    base_opts = moe.ffn_options(small_m_max=args.small_m_max)
-    cfg = moe_synth.CONFIGS[args.config]
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import moe_synth
+        import mxfp4_mixture_experts_amd as moe
+
+        self.np, self.torch, self.moe_synth, self.moe = np, torch, moe_synth, moe
+        self.args = args
+        self.stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def dev(self, a):
+        return self.torch.from_numpy(self.np.ascontiguousarray(a)).cuda()
+
+
+def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_max: int = -1,
+                  replicas_override: int = 0, warm: bool = False) -> dict:
+    """Eager (per-stage HIP events) and graph (L layers per hipGraph, timed replays) timings of one
+    layer workload with cold weights; optionally the warm-weight eager time."""
+    np, torch, moe, moe_synth = env.np, env.torch, env.moe, env.moe_synth
+    stream = env.stream
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     t0 = time.time()
     inp = moe_synth.make_inputs(cfg)
-    log(f"generated {cfg.name} inputs in {time.time() - t0:.1f}s")
-
+    log(f"{cfg.name} flags={flags}: inputs in {time.time() - t0:.1f}s")
     per_expert = 3 * H * I // 2 + 3 * H * I // 32
     replica_bytes = E * per_expert
-    R = args.replicas or max(2, math.ceil((2 << 30) / replica_bytes), math.ceil(8 * LLC_BYTES / replica_bytes))
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
-    host = [inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"]]
-    first = moe.Mxfp4Weights(*(dev(a) for a in host))
+    R = replicas_override or max(2, math.ceil((2 << 30) / replica_bytes), math.ceil(8 * LLC_BYTES / replica_bytes))
+    first = moe.Mxfp4Weights(*(env.dev(inp[a]) for a in ("w13_q", "w13_s", "w2_q", "w2_s")))
     replicas = [first] + [moe.Mxfp4Weights(*(t.clone() for t in (first.w13_q, first.w13_s, first.w2_q, first.w2_s)))
                           for _ in range(R - 1)]
-    del host
-    x = dev(inp["x"].view(np.int16)).view(torch.bfloat16)
-    logits = dev(inp["logits"])
-    layer = moe.MoELayer(first, k, T, cfg.score_fn, cfg.renorm, cfg.clamp, args.flags)
+    x = env.dev(inp["x"].view(np.int16)).view(torch.bfloat16)
+    logits = env.dev(inp["logits"])
+    layer = moe.MoELayer(first, k, T, cfg.score_fn, cfg.renorm, cfg.clamp, flags)
+    base_opts = moe.ffn_options(small_m_max=small_m_max)
     torch.cuda.synchronize()
-    log(f"{R} weight replicas of {replica_bytes / 1e9:.2f} GB on device")
-
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
+    log(f"{cfg.name}: {R} weight replicas of {replica_bytes / 1e9:.2f} GB on device")
 
     def step(i, opts=None):
         layer.forward(x, logits, replicas[i % R], stream=stream, options=opts or base_opts)
 
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
+        for i in range(warmup):
             step(i)
     torch.cuda.synchronize()
     counts = layer.grp.counts.cpu().numpy()
     n_active = int(np.count_nonzero(counts))
-    weight_bytes = n_active * per_expert
-    gateup_bytes = n_active * 2 * I * (H // 2 + H // 32)
-    flops = 2 * T * k * 3 * H * I
-    gateup_flops = 2 * T * k * 2 * I * H
-
-    if args.copy_bytes:
-        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {args.copy_bytes} bytes done")
+    res = dict(cfg=cfg, flags=flags, R=R, inp=inp, n_active=n_active, weight_bytes=n_active * per_expert,
+               gateup_bytes=n_active * 2 * I * (H // 2 + H // 32), flops=2 * T * k * 3 * H * I,
+               gateup_flops=2 * T * k * 2 * I * H,
+               plan=moe.ffn_plan(T, H, I, E, k, flags, base_opts), steps=steps)
 
     # eager: per-step HIP events on the stream the kernels run on: around the whole layer (recorded
     # here) and around the gate_up, down and combine stages (recorded by the library)
     stages = (moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE)
-    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev_layer = [(mk(), mk()) for _ in range(args.steps)]
-    ev_stage = [[(mk(), mk()) for _ in stages] for _ in range(args.steps)]
-    for i in range(args.steps):  # create the underlying events
+    ev_layer = [(env.event(), env.event()) for _ in range(steps)]
+    ev_stage = [[(env.event(), env.event()) for _ in stages] for _ in range(steps)]
+    for i in range(steps):  # create the underlying events
         for a, b in [ev_layer[i], *ev_stage[i]]:
             a.record(stream)
             b.record(stream)
+    step_opts = [moe.ffn_options(small_m_max=small_m_max, stage_events={st: ev for st, ev in zip(stages, ev_stage[i])})
+                 for i in range(steps)]
     torch.cuda.synchronize()
-    step_opts = [moe.ffn_options(small_m_max=args.small_m_max,
-                                 stage_events={st: ev for st, ev in zip(stages, ev_stage[i])})
-                 for i in range(args.steps)]
     t_start = time.perf_counter()
     with torch.cuda.stream(stream):
-        for i in range(args.steps):
+        for i in range(steps):
             ev_layer[i][0].record(stream)
             step(i, step_opts[i])
             ev_layer[i][1].record(stream)
     torch.cuda.synchronize()
-    eager_s = time.perf_counter() - t_start
+    res["eager_s"] = time.perf_counter() - t_start
     el = lambda a, b: a.elapsed_time(b) * 1e3  # noqa: E731  (µs)
-    layer_us = [el(*ev_layer[i]) for i in range(args.steps)]
-    route_group_us = [el(ev_layer[i][0], ev_stage[i][0][0]) for i in range(args.steps)]
-    ffn_us = [el(ev_stage[i][0][0], ev_stage[i][2][1]) for i in range(args.steps)]
-    stage_us = [[el(*ev_stage[i][j]) for i in range(args.steps)] for j in range(len(stages))]
-    gateup_mean_s = statistics.fmean(stage_us[0]) / 1e6
+    res["layer_us"] = [el(*ev_layer[i]) for i in range(steps)]
+    res["route_group_us"] = [el(ev_layer[i][0], ev_stage[i][0][0]) for i in range(steps)]
+    res["ffn_us"] = [el(ev_stage[i][0][0], ev_stage[i][2][1]) for i in range(steps)]
+    res["stage_us"] = [[el(*ev_stage[i][j]) for i in range(steps)] for j in range(len(stages))]
     med = statistics.median
-    log(f"eager: {eager_s / args.steps * 1e6:.1f} us/layer wall, device median {med(layer_us):.1f} us "
-        f"(route+group {med(route_group_us):.1f}, gate_up {med(stage_us[0]):.1f}, down {med(stage_us[1]):.1f}, "
-        f"combine {med(stage_us[2]):.1f})")
+    log(f"{cfg.name} eager: {res['eager_s'] / steps * 1e6:.1f} us/layer wall, device median {med(res['layer_us']):.1f} us "
+        f"(route+group {med(res['route_group_us']):.1f}, gate_up {med(res['stage_us'][0]):.1f}, "
+        f"down {med(res['stage_us'][1]):.1f}, combine {med(res['stage_us'][2]):.1f})")
 
     # graph: L consecutive layers captured in one hipGraph (layer j on replica j mod R), replayed
     # `reps` times with each replay timed; K = reps * L layers in all
-    reps = next(r for r in (5, 4, 2, 1) if args.steps % r == 0 and args.steps // r >= 2) if args.steps >= 2 else 1
-    L = args.steps // reps
-    graph_s = None
-    graph_layer_us = []
+    reps = next(r for r in (5, 4, 2, 1) if steps % r == 0 and steps // r >= 2) if steps >= 2 else 1
+    L = steps // reps
+    res.update(graph_s=None, graph_layer_us=[], L=L, reps=reps)
     try:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for j in range(L):
                 layer.forward(x, logits, replicas[j % R], stream=stream, options=base_opts)
-        g.replay()  # warm-up replay
+        with torch.cuda.stream(stream):
+            g.replay()  # warm-up replay
         torch.cuda.synchronize()
-        ev_g = [(mk(), mk()) for _ in range(reps)]
+        ev_g = [(env.event(), env.event()) for _ in range(reps)]
         t_start = time.perf_counter()
         with torch.cuda.stream(stream):
             for r_ in range(reps):
@@ -206,50 +210,136 @@ def main():
                 g.replay()
                 ev_g[r_][1].record(stream)
         torch.cuda.synchronize()
-        graph_s = time.perf_counter() - t_start
-        graph_layer_us = [el(*ev_g[r_]) / L for r_ in range(reps)]
-        log(f"graph ({L} layers per graph, {reps} replays): median {med(graph_layer_us):.1f} us/layer, "
-            f"range {min(graph_layer_us):.1f}-{max(graph_layer_us):.1f}")
+        res["graph_s"] = time.perf_counter() - t_start
+        res["graph_layer_us"] = [el(*ev_g[r_]) / L for r_ in range(reps)]
+        log(f"{cfg.name} graph ({L} layers per graph, {reps} replays): median {med(res['graph_layer_us']):.1f} "
+            f"us/layer, range {min(res['graph_layer_us']):.1f}-{max(res['graph_layer_us']):.1f}")
         del g
     except Exception as exc:  # capture unsupported: report eager
         log(f"graph capture failed: {exc!r}")
 
-    # warm weights, labelled: the same replica every step (what of it fits the 256 MB Infinity Cache
-    # stays there), eager, layer events only
-    n_warm = min(args.steps, 50)
-    ev_warm = [(mk(), mk()) for _ in range(n_warm)]
-    with torch.cuda.stream(stream):
-        step(0)
-        for a, b in ev_warm:
-            a.record(stream)
+    if warm:
+        # warm weights, labelled: the same replica every step (what of it fits the 256 MB Infinity
+        # Cache stays there), eager, layer events only
+        n_warm = min(steps, 50)
+        ev_warm = [(env.event(), env.event()) for _ in range(n_warm)]
+        with torch.cuda.stream(stream):
             step(0)
-            b.record(stream)
+            for a, b in ev_warm:
+                a.record(stream)
+                step(0)
+                b.record(stream)
+        torch.cuda.synchronize()
+        res["warm_us"] = [el(a, b) for a, b in ev_warm]
+    res["x"] = x
+    del replicas, layer, first
     torch.cuda.synchronize()
-    warm_us = [el(a, b) for a, b in ev_warm]
+    torch.cuda.empty_cache()
+    return res
 
-    # attainable read bandwidth on this machine: a plain device reduction of 2 GiB in rows of 4096 floats
-    # (one output per row; best of 5). A single whole-buffer sum reaches only about two thirds of it.
+
+def roofline_of(res: dict) -> dict:
+    """Roofline of the gate_up stage (the dominant kernel: two thirds of the bytes and flops):
+    algorithmic weight bytes (HBM-bound decode) or flops (per-expert M = 1024) per launch over its
+    mean event-timed duration on the stream it runs on."""
+    cfg, plan = res["cfg"], res["plan"]
+    gateup_mean_s = statistics.fmean(res["stage_us"][0]) / 1e6
+    large = plan["launch_large"]
+    mfma_bound = cfg.name == "m1024"
+    if mfma_bound:
+        achieved = res["gateup_flops"] / gateup_mean_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = res["gateup_bytes"] / gateup_mean_s / 1e9
+        # the counters were taken on the fused weight-streaming kernel; with MFMA kernels in the stage
+        # too the measurement must match every source
+        traffic = None if res["flags"] else committed_traffic(
+            cfg.name, kernel_source_hash(None if large else STREAMING_SOURCES))
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    roofline["kernel"] = "gate_up stage (" + (
+        "weight-streaming + MFMA kernels" if large and plan["launch_small"] else
+        "dense MFMA kernel" if large else "weight-streaming kernel" +
+        (", gate and up passes" if res["flags"] & 1 else "")) + ")"
+    roofline["bytes_per_launch" if not mfma_bound else "flops_per_launch"] = (
+        res["gateup_bytes"] if not mfma_bound else res["gateup_flops"])
+    roofline["avg_launch_us"] = round(gateup_mean_s * 1e6, 2)
+    return roofline
+
+
+def workload_name(cfg) -> str:
+    return (f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} top-{cfg.k} "
+            f"{'sigmoid' if cfg.score_fn else 'softmax'} renorm" + (f", clamp {cfg.clamp}" if cfg.clamp else ""))
+
+
+def summary(res: dict, use_graph: bool) -> dict:
+    """The per-workload numbers every measured workload reports."""
+    med = statistics.median
+    use_graph = use_graph and bool(res["graph_layer_us"])
+    us_layer = med(res["graph_layer_us"]) if use_graph else med(res["layer_us"])
+    gbps = res["weight_bytes"] / (us_layer * 1e-6) / 1e9
+    tflops = res["flops"] / (us_layer * 1e-6) / 1e12
+    stage = res["stage_us"]
+    return {
+        "us_per_layer": round(us_layer, 2),
+        "timing": (f"hipGraph of {res['L']} layers, median of {res['reps']} replays" if use_graph
+                   else "eager, median step"),
+        "weight_stream_GBps": round(gbps, 1),
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "tflops": round(tflops, 2),
+        "pct_bf16_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 1),
+        "ffn_only_us": round(med(res["ffn_us"]), 2),
+        "stage_us_eager_median": {"route+group": round(med(res["route_group_us"]), 2),
+                                  "gate_up": round(med(stage[0]), 2), "down": round(med(stage[1]), 2),
+                                  "combine": round(med(stage[2]), 2)},
+        "us_per_layer_eager": {"median": round(med(res["layer_us"]), 2), "p10": quantile(res["layer_us"], 1),
+                               "p90": quantile(res["layer_us"], 9),
+                               "host_wall": round(res["eager_s"] / res["steps"] * 1e6, 2)},
+        "us_per_layer_graph": ({"median": round(med(res["graph_layer_us"]), 2),
+                                "min": round(min(res["graph_layer_us"]), 2),
+                                "max": round(max(res["graph_layer_us"]), 2)} if res["graph_layer_us"] else None),
+        "active_experts": res["n_active"],
+        "weight_bytes_per_layer": res["weight_bytes"],
+        "flops_per_layer": res["flops"],
+        "roofline": roofline_of(res),
+        "config": {"workload": workload_name(res["cfg"]), "flags": res["flags"], "weight_replicas": res["R"],
+                   "small_m_max": res["plan"]["small_m_max"]},
+    }
+
+
+def read_probe_gbps(env: Env) -> float:
+    """Attainable read bandwidth on this machine: a plain device reduction of 2 GiB in rows of 4096
+    floats (one output per row; best of 5). A single whole-buffer sum reaches only about two thirds
+    of it."""
+    torch = env.torch
     probe = torch.zeros((1 << 31) // 4, dtype=torch.float32, device="cuda")
     probe_s = []
     for _ in range(5):
-        a, b = mk(), mk()
-        a.record(stream)
-        with torch.cuda.stream(stream):
+        a, b = env.event(), env.event()
+        a.record(env.stream)
+        with torch.cuda.stream(env.stream):
             probe.view(-1, 4096).sum(dim=1)
-        b.record(stream)
+        b.record(env.stream)
         torch.cuda.synchronize()
         probe_s.append(a.elapsed_time(b) / 1e3)
-    read_probe_gbps = probe.numel() * 4 / min(probe_s) / 1e9
+    v = probe.numel() * 4 / min(probe_s) / 1e9
     del probe
-    log(f"warm weights: median {med(warm_us):.1f} us/layer eager; read probe {read_probe_gbps:.0f} GB/s")
+    torch.cuda.empty_cache()
+    return v
 
-    # the router projection + top-k at this workload's sizes (the step before routing; not part of
-    # `value`): bf16 W_router[E, H]; one hipGraph over enough copies of (W_router, x) that every call
-    # reads cold operands (four times the Infinity Cache in total: at twice it, a cyclic sweep still
-    # found some of its operands there), best of 5 replays
+
+def router_timing(env: Env, cfg, x) -> dict | None:
+    """The router projection + top-k at this workload's sizes (the step before routing; not part of
+    `value`): bf16 W_router[E, H]; one hipGraph over enough copies of (W_router, x) that every call
+    reads cold operands (four times the Infinity Cache in total: at twice it, a cyclic sweep still
+    found some of its operands there), best of 5 replays."""
+    np, torch, moe, moe_synth = env.np, env.torch, env.moe, env.moe_synth
+    stream = env.stream
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
     router_bytes = E * H * 2 + T * H * 2
     n_router = max(8, min(1024, math.ceil(4 * LLC_BYTES / router_bytes)))
-    w_router0 = dev(moe_synth.make_router_weights(E, H, 20261203 + 99).view(np.int16)).view(torch.bfloat16)
+    w_router0 = env.dev(moe_synth.make_router_weights(E, H, 20261203 + 99).view(np.int16)).view(torch.bfloat16)
     r_ops = [(w_router0.clone(), x.clone()) for _ in range(n_router)]
     del w_router0
     ws_router = torch.empty(moe.router_gemm_topk_workspace_size(T, H, E), dtype=torch.uint8, device="cuda")
@@ -258,7 +348,7 @@ def main():
                              workspace=ws_router, stream=stream)
     torch.cuda.synchronize()
 
-    def router_graph_us(ops):
+    def graph_us(ops):
         """Per-call time of one hipGraph of calls over `ops`, best of 5 replays on `stream`."""
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=stream):
@@ -270,7 +360,7 @@ def main():
         torch.cuda.synchronize()
         best = None
         for _ in range(5):
-            a, b = mk(), mk()
+            a, b = env.event(), env.event()
             with torch.cuda.stream(stream):
                 a.record(stream)
                 gr.replay()
@@ -281,66 +371,101 @@ def main():
         del gr
         return best
 
-    router_us = router_warm_us = None
     try:
-        router_us = router_graph_us(r_ops)
-        router_warm_us = router_graph_us([r_ops[0]] * 50)
+        us = graph_us(r_ops)
+        us_warm = graph_us([r_ops[0]] * 50)
     except Exception as exc:  # capture unsupported: skip the router line
         log(f"router graph capture failed: {exc!r}")
-    del r_ops
-    if router_us is not None:
-        log(f"router gemm+top-k: {router_us:.2f} us per call cold ({n_router} operand copies), "
-            f"{router_warm_us:.2f} us warm")
+        return None
+    finally:
+        del r_ops
+        torch.cuda.empty_cache()
+    log(f"router gemm+top-k: {us:.2f} us per call cold ({n_router} operand copies), {us_warm:.2f} us warm")
+    return {
+        "us": round(us, 2),
+        "operand_GBps": round(router_bytes / (us * 1e-6) / 1e9, 1),
+        "pct_hbm_peak": round(100 * router_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
+        "tflops": round(2 * T * E * H / (us * 1e-6) / 1e12, 2),
+        "us_warm": round(us_warm, 2),
+        "note": (f"logits = x . W_router^T (bf16 [E, H]) and top-k; us: one graph over {n_router} copies of "
+                 "(W_router, x), so every call reads cold operands (GB/s counts W_router and x once); "
+                 "us_warm: 50 calls on one copy; not part of value")}
 
-    use_graph = args.mode == "graph" and graph_s is not None
-    total_s = graph_s if use_graph else eager_s
-    us_layer = med(graph_layer_us) if use_graph else med(layer_us)
-    gbps = weight_bytes / (us_layer * 1e-6) / 1e9
-    ffn_med = med(ffn_us)
 
-    plan = moe.ffn_plan(T, H, I, E, k, args.flags, base_opts)
-    large = plan["launch_large"]
-    mfma_bound = cfg.name == "m1024"
-    if mfma_bound:
-        achieved = gateup_flops / gateup_mean_s / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
-    else:
-        achieved = gateup_bytes / gateup_mean_s / 1e9
-        # the counters were taken on the weight-streaming kernel; with MFMA kernels in the stage too
-        # the measurement must match every source
-        traffic = committed_traffic(cfg.name, kernel_source_hash(None if large else STREAMING_SOURCES))
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
-    roofline["kernel"] = "gate_up stage (" + (
-        "weight-streaming + MFMA kernels" if large and plan["launch_small"] else "MFMA kernel" if large
-        else "weight-streaming kernel") + ")"
-    roofline["bytes_per_launch" if not mfma_bound else "flops_per_launch"] = (
-        gateup_bytes if not mfma_bound else gateup_flops)
-    roofline["avg_launch_us"] = round(gateup_mean_s * 1e6, 2)
+def cpu_baseline(args, cfg, inp) -> dict:
+    """The oracle, as it stands, on the host cores: a bounded sample of the workload's tokens,
+    scaled to the whole layer."""
+    import oracle
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
+    host_cores = os.cpu_count() or 1
+    threads = min(16, host_cores)
+    times = []
+    sample_tokens = cfg.T if cfg.T <= 8 else 1
+    for rep in range(args.cpu_reps):
+        t_c = time.perf_counter()
+        oracle.moe_layer(inp["logits"][:sample_tokens], inp["x"][:sample_tokens], inp["w13_q"], inp["w13_s"],
+                         inp["w2_q"], inp["w2_s"], cfg.k, cfg.score_fn, cfg.renorm, cfg.clamp, threads)
+        times.append(time.perf_counter() - t_c)
+        log(f"oracle rep {rep}: {times[-1]:.2f}s")
+    per_layer_us = statistics.median(times) * 1e6 * (cfg.T / sample_tokens)
+    used = oracle.num_threads(threads)
+    return {"value": round(per_layer_us, 1), "unit": "µs/layer", "cores": used, "kind": "oracle",
+            "threads_used": used, "host_cores": host_cores,
+            "sample": (f"{sample_tokens} of {cfg.T} tokens of one {cfg.name} layer (route+group+ffn+combine, "
+                       f"fp64, {used} OpenMP threads on a host reporting {host_cores} cores), median of "
+                       f"{args.cpu_reps}, scaled to the whole layer")}
 
-        threads = min(16, os.cpu_count() or 1)
-        times = []
-        sample_tokens = T if cfg.T <= 8 else 1
-        for rep in range(args.cpu_reps):
-            t_c = time.perf_counter()
-            oracle.moe_layer(inp["logits"][:sample_tokens], inp["x"][:sample_tokens], inp["w13_q"], inp["w13_s"],
-                             inp["w2_q"], inp["w2_s"], k, cfg.score_fn, cfg.renorm, cfg.clamp, threads)
-            times.append(time.perf_counter() - t_c)
-            log(f"oracle rep {rep}: {times[-1]:.2f}s")
-        per_layer_us = statistics.median(times) * 1e6 * (T / sample_tokens)
-        cpu = {"value": round(per_layer_us, 1), "unit": "µs/layer", "cores": oracle.num_threads(threads),
-               "kind": "oracle",
-               "sample": (f"{sample_tokens} of {T} tokens of one {cfg.name} layer (route+group+ffn+combine, "
-                          f"fp64), median of {args.cpu_reps}, scaled to the whole layer")}
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path (the layer would shard by "
+              "experts or by the intermediate dimension, with one all-to-all or all-reduce per layer); "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    env = Env(args)
+    env.moe.load_library()
+    cfg = env.moe_synth.CONFIGS[args.config]
+
+    res = measure_layer(env, cfg, args.flags, args.steps, args.warmup, args.small_m_max, args.replicas, warm=True)
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_bytes} bytes done")
+        del src, dst
+    probe = read_probe_gbps(env)
+    med = statistics.median
+    log(f"warm weights: median {med(res['warm_us']):.1f} us/layer eager; read probe {probe:.0f} GB/s")
+    router = router_timing(env, cfg, res["x"])
+
+    use_graph = args.mode == "graph" and res["graph_s"] is not None
+    s = summary(res, use_graph)
+    us_layer = s["us_per_layer"]
+    gbps = s["weight_stream_GBps"]
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, cfg, res["inp"])
+
+    others = {}
+    if not args.no_others:
+        for name, wl, flags in OTHER_WORKLOADS:
+            if wl == cfg.name and flags == args.flags:
+                continue
+            o = measure_layer(env, env.moe_synth.CONFIGS[wl], flags, args.other_steps, max(5, args.warmup // 2))
+            others[name] = summary(o, True)
+            others[name]["steps"] = args.other_steps
+            del o
 
     rec = {
         "metric": METRIC,
-        "value": round(us_layer, 2),
+        "value": us_layer,
         "unit": "µs/layer",
         "n_gpus": 1,
         "steps": args.steps,
@@ -351,43 +476,27 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4 weights, bf16 activations, fp32 accumulate",
         "data": "synthetic (seeded; random MXFP4 weights, no checkpoint)",
-        "config": {"workload": f"{cfg.name}: T={T} H={H} I={I} E={E} top-{k} "
-                               f"{'sigmoid' if cfg.score_fn else 'softmax'} renorm"
-                               + (f", clamp {cfg.clamp}" if cfg.clamp else ""),
-                   "timing": (f"hipGraph of {L} layers, median of {reps} replays" if use_graph
-                              else "eager, median step"),
-                   "flags": args.flags, "weight_replicas": R, "parallelism": "none (1 GPU)",
-                   "small_m_max": plan["small_m_max"]},
-        "weight_stream_GBps": round(gbps, 1),
-        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
-        "ffn_only_us": round(ffn_med, 2),
-        "weight_stream_GBps_ffn_only": round(weight_bytes / (ffn_med * 1e-6) / 1e9, 1),
-        "read_probe_GBps": round(read_probe_gbps, 1),
-        "pct_read_probe": round(100 * gbps / read_probe_gbps, 1),
-        "us_per_layer_warm_eager": {"median": round(med(warm_us), 2), "steps": n_warm,
+        "config": {"workload": workload_name(cfg), "timing": s["timing"], "flags": args.flags,
+                   "weight_replicas": res["R"], "parallelism": "none (1 GPU)",
+                   "small_m_max": res["plan"]["small_m_max"]},
+        "weight_stream_GBps": gbps,
+        "pct_hbm_peak": s["pct_hbm_peak"],
+        "ffn_only_us": s["ffn_only_us"],
+        "weight_stream_GBps_ffn_only": round(res["weight_bytes"] / (s["ffn_only_us"] * 1e-6) / 1e9, 1),
+        "read_probe_GBps": round(probe, 1),
+        "pct_read_probe": round(100 * gbps / probe, 1),
+        "us_per_layer_warm_eager": {"median": round(med(res["warm_us"]), 2), "steps": len(res["warm_us"]),
                                     "note": "one weight replica reused every step (not the metric)"},
-        "router_gemm_topk": (None if router_us is None else {
-            "us": round(router_us, 2),
-            "operand_GBps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
-            "pct_hbm_peak": round(100 * router_bytes / (router_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
-            "tflops": round(2 * T * E * H / (router_us * 1e-6) / 1e12, 2),
-            "us_warm": round(router_warm_us, 2),
-            "note": (f"logits = x . W_router^T (bf16 [E, H]) and top-k; us: one graph over {n_router} copies of "
-                     "(W_router, x), so every call reads cold operands (GB/s counts W_router and x once); "
-                     "us_warm: 50 calls on one copy; not part of value")}),
-        "stage_us_eager_median": {"route+group": round(med(route_group_us), 2), "gate_up": round(med(stage_us[0]), 2),
-                                  "down": round(med(stage_us[1]), 2), "combine": round(med(stage_us[2]), 2)},
-        "active_experts": n_active,
-        "weight_bytes_per_layer": weight_bytes,
-        "tflops": round(flops / (us_layer * 1e-6) / 1e12, 2),
-        "us_per_layer_eager": {"median": round(med(layer_us), 2),
-                               "p10": round(statistics.quantiles(layer_us, n=10)[0], 2) if len(layer_us) > 1 else None,
-                               "p90": round(statistics.quantiles(layer_us, n=10)[-1], 2) if len(layer_us) > 1 else None,
-                               "host_wall": round(eager_s / args.steps * 1e6, 2)},
-        "us_per_layer_graph": ({"median": round(med(graph_layer_us), 2), "min": round(min(graph_layer_us), 2),
-                                "max": round(max(graph_layer_us), 2)} if graph_layer_us else None),
-        "roofline": roofline,
+        "router_gemm_topk": router,
+        "stage_us_eager_median": s["stage_us_eager_median"],
+        "active_experts": res["n_active"],
+        "weight_bytes_per_layer": res["weight_bytes"],
+        "tflops": s["tflops"],
+        "us_per_layer_eager": s["us_per_layer_eager"],
+        "us_per_layer_graph": s["us_per_layer_graph"],
+        "roofline": s["roofline"],
         "cpu_baseline": cpu,
+        "other_workloads": others,
         "kernel_source_sha": kernel_source_hash(),
     }
     print(json.dumps(rec), flush=True)
