@@ -297,6 +297,29 @@ typedef struct {
 int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags,
                        const moe_ffn_options* opts /*[host]*/, moe_ffn_plan* plan /*[host]*/);
 
+/*
+ * moe_mxfp4_ffn_noalloc — moe_mxfp4_ffn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * without a workspace, the same kernels, limits and results (bitwise equal to moe_mxfp4_ffn). Its
+ * workspace is a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES (16 MiB) that every GPU the
+ * library runs on holds until the process ends; the call allocates and frees nothing. Shapes whose
+ * workspace (moe_mxfp4_ffn_workspace_size) exceeds that return MOE_ERR_WORKSPACE and enqueue
+ * nothing: at H = 4096, I = 2048, k = 8 that admits up to T = 85 tokens (63 with MOE_UNFUSED_GATE_UP),
+ * at H = 7168 up to T = 56. Nothing in the
+ * array needs to start at zero; each call overwrites what it reads. All calls on one GPU share that
+ * GPU's array, so calls that can overlap on one GPU (different streams, or different host threads
+ * without ordering) race: order them on one stream. moe_mxfp4_ffn_noalloc_max_bytes returns the
+ * array's size (host).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+size_t moe_mxfp4_ffn_noalloc_max_bytes(void);
+int moe_mxfp4_ffn_noalloc(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                          const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                          const uint8_t* w2_s, const float* topk_w, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* sorted_pair, const int32_t* pair_pos,
+                          const int32_t* active, const int32_t* n_active, float clamp_limit, int flags,
+                          uint16_t* out_bf16, void* stream);
+
 /* Human-readable name of a status code (host, static storage). */
 const char* moe_status_string(int status);
 

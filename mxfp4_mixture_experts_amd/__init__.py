@@ -104,6 +104,11 @@ def load_library(path: str | None = None):
     lib.moe_mxfp4_ffn_ex.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_float,
                                      i, V, V, ctypes.c_size_t, ctypes.POINTER(FfnOptions), V]
     lib.moe_mxfp4_ffn_ex.restype = i
+    lib.moe_mxfp4_ffn_noalloc.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_float,
+                                          i, V, V]
+    lib.moe_mxfp4_ffn_noalloc.restype = i
+    lib.moe_mxfp4_ffn_noalloc_max_bytes.argtypes = []
+    lib.moe_mxfp4_ffn_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.moe_ffn_options_init.argtypes = [ctypes.POINTER(FfnOptions)]
     lib.moe_ffn_options_init.restype = None
     lib.moe_mxfp4_ffn_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(FfnOptions), ctypes.POINTER(FfnPlan)]
@@ -367,6 +372,22 @@ def mxfp4_ffn(x: torch.Tensor, w: Mxfp4Weights, topk_w: torch.Tensor, grp: Group
         _ptr(grp.active), _ptr(grp.n_active), float(clamp_limit), int(flags), _ptr(out),
         _ptr(workspace), workspace.numel(), ctypes.byref(options) if options is not None else None,
         _stream(stream)), "moe_mxfp4_ffn_ex")
+    return out
+
+
+def mxfp4_ffn_noalloc(x: torch.Tensor, w: Mxfp4Weights, topk_w: torch.Tensor, grp: Grouping,
+                      clamp_limit: float = 0.0, flags: int = 0, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """mxfp4_ffn without a workspace argument: the library uses its own fixed device scratch
+    (moe_mxfp4_ffn_noalloc). Pass `out` to allocate nothing at all."""
+    x, T, H, k = ffn_check(x, w, topk_w, grp, out, None, flags)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().moe_mxfp4_ffn_noalloc(
+        _ptr(x), T, H, w.I, w.E, k, _ptr(w.w13_q), _ptr(w.w13_s), _ptr(w.w2_q), _ptr(w.w2_s),
+        _ptr(topk_w), _ptr(grp.counts), _ptr(grp.offsets), _ptr(grp.sorted_pair), _ptr(grp.pair_pos),
+        _ptr(grp.active), _ptr(grp.n_active), float(clamp_limit), int(flags), _ptr(out), _stream(stream)),
+        "moe_mxfp4_ffn_noalloc")
     return out
 
 

@@ -3,11 +3,18 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "moe_mxfp4.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
+
+// Workspace of moe_mxfp4_ffn_noalloc: a file-scope device array, one copy on every GPU the library
+// runs on, held until the process ends. On the host this name is only a stand-in for the symbol, not
+// a device address: host code reaches the array through the per-device address that
+// hipGetSymbolAddress returns (scratch_address below) and never passes `scratch` itself anywhere.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -112,6 +119,32 @@ void fill_plan(int T, int H, int I, int E, int k, int flags, const moe_ffn_optio
   const bool dense = plan->launch_large && T >= moe::kDenseMinRows;
   plan->n_launches = (plan->launch_small ? gu_launches + 1 : 0) + (plan->launch_large ? 3 : 0) +
                      (dense ? 3 : 0) + (T > 0 ? 1 : 0);
+}
+
+// Device address of `scratch` on the current device, looked up once per device with that device
+// current (each GPU holds its own copy at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return MOE_ERR_LAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 void record(const moe_ffn_options& o, int stage, bool start, hipStream_t stream) {
@@ -352,4 +385,27 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
   return moe_mxfp4_ffn_ex(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, topk_w, counts, offsets,
                           sorted_pair, pair_pos, active, n_active, clamp_limit, flags, out_bf16,
                           workspace, ws_bytes, nullptr, stream);
+}
+
+MOE_API size_t moe_mxfp4_ffn_noalloc_max_bytes(void) { return MOE_NOALLOC_SCRATCH_BYTES; }
+
+MOE_API int moe_mxfp4_ffn_noalloc(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                                  const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                                  const uint8_t* w2_s, const float* topk_w, const int32_t* counts,
+                                  const int32_t* offsets, const int32_t* sorted_pair,
+                                  const int32_t* pair_pos, const int32_t* active,
+                                  const int32_t* n_active, float clamp_limit, int flags,
+                                  uint16_t* out_bf16, void* stream) {
+  if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
+  if ((flags & ~kKnownFlags) || ((flags & MOE_FORCE_SMALL_M) && (flags & MOE_FORCE_LARGE_M)))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  // the same regions moe_mxfp4_ffn would take from a caller's workspace, here from `scratch`
+  if (ws_layout((long)T * k, H, I, E, k, flags).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  return moe_mxfp4_ffn_ex(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, topk_w, counts, offsets,
+                          sorted_pair, pair_pos, active, n_active, clamp_limit, flags, out_bf16, ws,
+                          MOE_NOALLOC_SCRATCH_BYTES, nullptr, stream);
 }

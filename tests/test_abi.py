@@ -206,3 +206,25 @@ def test_router_gemm_validation(lib):
     assert call(x=V(0x1008)) == -3          # x not 16-byte aligned
     assert call(ws=V(0x1010)) == -3         # workspace not 256-byte aligned
     assert call(ws_bytes=need - 1) == -4
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation entry point rejects bad sizes, and shapes whose workspace exceeds its fixed
+    scratch, before touching the GPU."""
+    lib.moe_mxfp4_ffn_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.moe_mxfp4_ffn_workspace_size.restype = ctypes.c_size_t
+    cap = lib.moe_mxfp4_ffn_noalloc_max_bytes()
+    assert cap == 16 << 20
+    assert lib.moe_mxfp4_ffn_workspace_size(85, 4096, 2048, 256, 8, 0) <= cap
+    assert lib.moe_mxfp4_ffn_workspace_size(86, 4096, 2048, 256, 8, 0) > cap
+    d = DUMMY
+
+    def call(T=8, H=4096, I=2048, E=256, k=8, flags=0):
+        return lib.moe_mxfp4_ffn_noalloc(d, T, H, I, E, k, d, d, d, d, d, d, d, d, d, d, d, ctypes.c_float(0.0),
+                                         flags, d, None)
+
+    assert call(T=86) == -4           # workspace beyond the scratch
+    assert call(T=1024, H=7168) == -4
+    assert call(H=4016) == -2
+    assert call(flags=8) == -3
+    assert call(T=0) == 0             # nothing to do
