@@ -31,9 +31,13 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 LLC_BYTES = 256 << 20           # MI355X Infinity Cache
 METRIC = "µs/MoE layer + weight-stream GB/s (% HBM peak) at M=8 decode, 1 GPU"
 
-# (name, workload, ffn flags) measured after the headline, fewer steps each, no CPU baseline
-OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0), ("decode_m2", "decode_m2", 0),
-                   ("decode_m8_unfused", "decode_m8", 1), ("m1024", "m1024", 0))
+# (name, workload, ffn flags, single launch) measured after the headline, fewer steps each, no CPU
+# baseline
+OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0, False), ("decode_m2", "decode_m2", 0, False),
+                   ("decode_m8_unfused", "decode_m8", 1, False), ("m1024", "m1024", 0, False),
+                   ("decode_c1_single_launch", "decode_c1", 0, True),
+                   ("decode_m2_single_launch", "decode_m2", 0, True),
+                   ("decode_m8_single_launch", "decode_m8", 0, True))
 
 
 def log(msg: str):
@@ -55,6 +59,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-others", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="headline through moe_layer_decode (the whole layer in one launch)")
     ap.add_argument("--other-steps", type=int, default=50, help="timed steps of each other workload")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain device copy of this many bytes (counter calibration)")
@@ -123,9 +129,10 @@ class Env:
 
 
 def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_max: int = -1,
-                  replicas_override: int = 0, warm: bool = False) -> dict:
+                  replicas_override: int = 0, warm: bool = False, single: bool = False) -> dict:
     """Eager (per-stage HIP events) and graph (L layers per hipGraph, timed replays) timings of one
-    layer workload with cold weights; optionally the warm-weight eager time."""
+    layer workload with cold weights; optionally the warm-weight eager time. `single`: the layer as
+    one moe_layer_decode launch (no stages: the launch is the whole layer)."""
     np, torch, moe, moe_synth = env.np, env.torch, env.moe, env.moe_synth
     stream = env.stream
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
@@ -140,7 +147,7 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
                           for _ in range(R - 1)]
     x = env.dev(inp["x"].view(np.int16)).view(torch.bfloat16)
     logits = env.dev(inp["logits"])
-    layer = moe.MoELayer(first, k, T, cfg.score_fn, cfg.renorm, cfg.clamp, flags)
+    layer = moe.MoELayer(first, k, T, cfg.score_fn, cfg.renorm, cfg.clamp, flags, single_launch=single)
     base_opts = moe.ffn_options(small_m_max=small_m_max)
     torch.cuda.synchronize()
     log(f"{cfg.name}: {R} weight replicas of {replica_bytes / 1e9:.2f} GB on device")
@@ -152,16 +159,16 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
         for i in range(warmup):
             step(i)
     torch.cuda.synchronize()
-    counts = layer.grp.counts.cpu().numpy()
+    counts = np.bincount(layer.ids[:T].cpu().numpy().ravel(), minlength=E)
     n_active = int(np.count_nonzero(counts))
     res = dict(cfg=cfg, flags=flags, R=R, inp=inp, n_active=n_active, weight_bytes=n_active * per_expert,
                gateup_bytes=n_active * 2 * I * (H // 2 + H // 32), flops=2 * T * k * 3 * H * I,
                gateup_flops=2 * T * k * 2 * I * H,
-               plan=moe.ffn_plan(T, H, I, E, k, flags, base_opts), steps=steps)
+               plan=moe.ffn_plan(T, H, I, E, k, flags, base_opts), steps=steps, single=single)
 
     # eager: per-step HIP events on the stream the kernels run on: around the whole layer (recorded
     # here) and around the gate_up, down and combine stages (recorded by the library)
-    stages = (moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE)
+    stages = () if single else (moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE)
     ev_layer = [(env.event(), env.event()) for _ in range(steps)]
     ev_stage = [[(env.event(), env.event()) for _ in stages] for _ in range(steps)]
     for i in range(steps):  # create the underlying events
@@ -181,13 +188,19 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
     res["eager_s"] = time.perf_counter() - t_start
     el = lambda a, b: a.elapsed_time(b) * 1e3  # noqa: E731  (µs)
     res["layer_us"] = [el(*ev_layer[i]) for i in range(steps)]
-    res["route_group_us"] = [el(ev_layer[i][0], ev_stage[i][0][0]) for i in range(steps)]
-    res["ffn_us"] = [el(ev_stage[i][0][0], ev_stage[i][2][1]) for i in range(steps)]
-    res["stage_us"] = [[el(*ev_stage[i][j]) for i in range(steps)] for j in range(len(stages))]
     med = statistics.median
-    log(f"{cfg.name} eager: {res['eager_s'] / steps * 1e6:.1f} us/layer wall, device median {med(res['layer_us']):.1f} us "
-        f"(route+group {med(res['route_group_us']):.1f}, gate_up {med(res['stage_us'][0]):.1f}, "
-        f"down {med(res['stage_us'][1]):.1f}, combine {med(res['stage_us'][2]):.1f})")
+    if single:
+        res["route_group_us"] = res["ffn_us"] = None
+        res["stage_us"] = None
+        log(f"{cfg.name} single launch eager: {res['eager_s'] / steps * 1e6:.1f} us/layer wall, device median "
+            f"{med(res['layer_us']):.1f} us")
+    else:
+        res["route_group_us"] = [el(ev_layer[i][0], ev_stage[i][0][0]) for i in range(steps)]
+        res["ffn_us"] = [el(ev_stage[i][0][0], ev_stage[i][2][1]) for i in range(steps)]
+        res["stage_us"] = [[el(*ev_stage[i][j]) for i in range(steps)] for j in range(len(stages))]
+        log(f"{cfg.name} eager: {res['eager_s'] / steps * 1e6:.1f} us/layer wall, device median "
+            f"{med(res['layer_us']):.1f} us (route+group {med(res['route_group_us']):.1f}, gate_up "
+            f"{med(res['stage_us'][0]):.1f}, down {med(res['stage_us'][1]):.1f}, combine {med(res['stage_us'][2]):.1f})")
 
     # graph: L consecutive layers captured in one hipGraph (layer j on replica j mod R), replayed
     # `reps` times with each replay timed; K = reps * L layers in all
@@ -243,6 +256,14 @@ def roofline_of(res: dict) -> dict:
     algorithmic weight bytes (HBM-bound decode) or flops (per-expert M = 1024) per launch over its
     mean event-timed duration on the stream it runs on."""
     cfg, plan = res["cfg"], res["plan"]
+    if res["single"]:
+        # the one launch streams every active expert's weights: all of them over its event-timed mean
+        mean_s = statistics.fmean(res["layer_us"]) / 1e6
+        achieved = res["weight_bytes"] / mean_s / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "layer_decode_kernel (route, group, gate_up, down, combine in one launch)",
+                "bytes_per_launch": res["weight_bytes"], "avg_launch_us": round(mean_s * 1e6, 2)}
     gateup_mean_s = statistics.fmean(res["stage_us"][0]) / 1e6
     large = plan["launch_large"]
     mfma_bound = cfg.name == "m1024"
@@ -281,6 +302,13 @@ def summary(res: dict, use_graph: bool) -> dict:
     gbps = res["weight_bytes"] / (us_layer * 1e-6) / 1e9
     tflops = res["flops"] / (us_layer * 1e-6) / 1e12
     stage = res["stage_us"]
+    if res["single"]:
+        stages = None
+        ffn_only = None
+    else:
+        stages = {"route+group": round(med(res["route_group_us"]), 2), "gate_up": round(med(stage[0]), 2),
+                  "down": round(med(stage[1]), 2), "combine": round(med(stage[2]), 2)}
+        ffn_only = round(med(res["ffn_us"]), 2)
     return {
         "us_per_layer": round(us_layer, 2),
         "timing": (f"hipGraph of {res['L']} layers, median of {res['reps']} replays" if use_graph
@@ -289,10 +317,8 @@ def summary(res: dict, use_graph: bool) -> dict:
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "tflops": round(tflops, 2),
         "pct_bf16_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 1),
-        "ffn_only_us": round(med(res["ffn_us"]), 2),
-        "stage_us_eager_median": {"route+group": round(med(res["route_group_us"]), 2),
-                                  "gate_up": round(med(stage[0]), 2), "down": round(med(stage[1]), 2),
-                                  "combine": round(med(stage[2]), 2)},
+        "ffn_only_us": ffn_only,
+        "stage_us_eager_median": stages,
         "us_per_layer_eager": {"median": round(med(res["layer_us"]), 2), "p10": quantile(res["layer_us"], 1),
                                "p90": quantile(res["layer_us"], 9),
                                "host_wall": round(res["eager_s"] / res["steps"] * 1e6, 2)},
@@ -304,7 +330,9 @@ def summary(res: dict, use_graph: bool) -> dict:
         "flops_per_layer": res["flops"],
         "roofline": roofline_of(res),
         "config": {"workload": workload_name(res["cfg"]), "flags": res["flags"], "weight_replicas": res["R"],
-                   "small_m_max": res["plan"]["small_m_max"]},
+                   "small_m_max": res["plan"]["small_m_max"],
+                   "path": "moe_layer_decode (one launch)" if res["single"] else
+                           "moe_route_group + moe_mxfp4_ffn (multi-launch)"},
     }
 
 
@@ -434,7 +462,8 @@ def main():
     env.moe.load_library()
     cfg = env.moe_synth.CONFIGS[args.config]
 
-    res = measure_layer(env, cfg, args.flags, args.steps, args.warmup, args.small_m_max, args.replicas, warm=True)
+    res = measure_layer(env, cfg, args.flags, args.steps, args.warmup, args.small_m_max, args.replicas, warm=True,
+                        single=args.single_launch)
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -455,10 +484,11 @@ def main():
 
     others = {}
     if not args.no_others:
-        for name, wl, flags in OTHER_WORKLOADS:
-            if wl == cfg.name and flags == args.flags:
+        for name, wl, flags, single in OTHER_WORKLOADS:
+            if wl == cfg.name and flags == args.flags and single == args.single_launch:
                 continue
-            o = measure_layer(env, env.moe_synth.CONFIGS[wl], flags, args.other_steps, max(5, args.warmup // 2))
+            o = measure_layer(env, env.moe_synth.CONFIGS[wl], flags, args.other_steps, max(5, args.warmup // 2),
+                              single=single)
             others[name] = summary(o, True)
             others[name]["steps"] = args.other_steps
             del o
@@ -477,12 +507,14 @@ def main():
         "dtype": "mxfp4 weights, bf16 activations, fp32 accumulate",
         "data": "synthetic (seeded; random MXFP4 weights, no checkpoint)",
         "config": {"workload": workload_name(cfg), "timing": s["timing"], "flags": args.flags,
+                   "path": s["config"]["path"],
                    "weight_replicas": res["R"], "parallelism": "none (1 GPU)",
                    "small_m_max": res["plan"]["small_m_max"]},
         "weight_stream_GBps": gbps,
         "pct_hbm_peak": s["pct_hbm_peak"],
         "ffn_only_us": s["ffn_only_us"],
-        "weight_stream_GBps_ffn_only": round(res["weight_bytes"] / (s["ffn_only_us"] * 1e-6) / 1e9, 1),
+        "weight_stream_GBps_ffn_only": (round(res["weight_bytes"] / (s["ffn_only_us"] * 1e-6) / 1e9, 1)
+                                        if s["ffn_only_us"] else None),
         "read_probe_GBps": round(probe, 1),
         "pct_read_probe": round(100 * gbps / probe, 1),
         "us_per_layer_warm_eager": {"median": round(med(res["warm_us"]), 2), "steps": len(res["warm_us"]),

@@ -298,6 +298,48 @@ int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags,
                        const moe_ffn_options* opts /*[host]*/, moe_ffn_plan* plan /*[host]*/);
 
 /*
+ * moe_layer_decode — the whole layer for decode batches in ONE kernel launch: router top-k and
+ * renormalisation (as moe_route_topk), grouping, gate_up + SwiGLU, down and the weighted combine
+ * (as moe_mxfp4_ffn), from logits to out. The pages point at persistent kernels and at merging
+ * producer/reduction/consumer launches as the lever at low concurrency ("Chunk 8.0", summary;
+ * "MTP1 Post-Portfolio Eager-Cycle Profile", Decision; launch cost per kernel in vllm.cpp PR #52).
+ *
+ * Every workgroup routes and groups all tokens itself (ids and weights bitwise equal to
+ * moe_route_topk's). The active experts' intermediate dimension is cut into 32-wide blocks shared
+ * out in contiguous ranges, one per workgroup: a workgroup computes h for its blocks (fp32, in LDS)
+ * and the down projection restricted to those blocks, a partial output per (range, expert, token),
+ * written to the workspace. After one grid barrier the partials are summed, in a fixed order, into
+ * out. The result is deterministic and within the same bar of the exact layer as moe_mxfp4_ffn, but
+ * not bitwise equal to it: h is not rounded to its bf16 pair, and the down sums are split over the
+ * ranges. On MI355X it is slower than moe_route_group + moe_mxfp4_ffn at every decode size measured
+ * (the exchange between workgroups across the eight XCDs' L2 caches costs more than the launches
+ * it saves), so the multi-launch path remains the default.
+ *
+ *   logits, score_fn, renorm, k      as moe_route_topk
+ *   x_bf16, weights, clamp_limit     as moe_mxfp4_ffn
+ *   topk_ids, topk_w                 [dev] i32[T, k], f32[T, k] (written), or NULL
+ *   out_bf16                         [dev] u16[T, H] (written), 16-byte aligned
+ *   workspace, ws_bytes              [dev] at least moe_layer_decode_workspace_size(T, H, I, E, k)
+ *                                    bytes, 256-byte aligned. Its first 256 bytes hold the barrier's
+ *                                    counter and must be ZERO before the first call on this workspace
+ *                                    (e.g. hipMemset once after allocating it); every call leaves
+ *                                    them in a valid state for the next. The rest is overwritten.
+ *                                    One workspace serves one device and one call at a time.
+ * Limits (MOE_ERR_UNSUPPORTED otherwise): 1 <= T <= 16, T*k <= 256, E <= 512, and each
+ * workgroup's share at most 32 blocks of 32 (min(E, T*k) * I/32 <= 32 * compute units); sizes as
+ * moe_mxfp4_ffn otherwise (MOE_ERR_SHAPE). The grid is one workgroup per compute unit and the
+ * barrier needs all of them resident at once: do not run it next to work that holds compute units
+ * for long. Should the barrier wait exceed about a second it gives up (results then undefined)
+ * and adds one to the 32-bit word at workspace byte 8. The workspace size is
+ * 256 + (T * CUs + 2 * T * k) * H * 4 bytes (CUs = compute units of the current device).
+ */
+size_t moe_layer_decode_workspace_size(int T, int H, int I, int E, int k);  /* host; 0 if unsupported */
+int moe_layer_decode(const float* logits, const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                     int score_fn, int renorm, const uint8_t* w13_q, const uint8_t* w13_s,
+                     const uint8_t* w2_q, const uint8_t* w2_s, float clamp_limit, int32_t* topk_ids,
+                     float* topk_w, uint16_t* out_bf16, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * moe_mxfp4_ffn_noalloc — moe_mxfp4_ffn for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments
  * without a workspace, the same kernels, limits and results (bitwise equal to moe_mxfp4_ffn). Its

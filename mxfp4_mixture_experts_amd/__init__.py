@@ -109,6 +109,11 @@ def load_library(path: str | None = None):
     lib.moe_mxfp4_ffn_noalloc.restype = i
     lib.moe_mxfp4_ffn_noalloc_max_bytes.argtypes = []
     lib.moe_mxfp4_ffn_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.moe_layer_decode_workspace_size.argtypes = [i, i, i, i, i]
+    lib.moe_layer_decode_workspace_size.restype = ctypes.c_size_t
+    lib.moe_layer_decode.argtypes = [V, V, i, i, i, i, i, i, i, V, V, V, V, ctypes.c_float, V, V, V, V,
+                                     ctypes.c_size_t, V]
+    lib.moe_layer_decode.restype = i
     lib.moe_ffn_options_init.argtypes = [ctypes.POINTER(FfnOptions)]
     lib.moe_ffn_options_init.restype = None
     lib.moe_mxfp4_ffn_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(FfnOptions), ctypes.POINTER(FfnPlan)]
@@ -391,6 +396,55 @@ def mxfp4_ffn_noalloc(x: torch.Tensor, w: Mxfp4Weights, topk_w: torch.Tensor, gr
     return out
 
 
+def layer_decode_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
+    """Bytes of workspace moe_layer_decode needs (0: the shape is not supported by the single launch)."""
+    return load_library().moe_layer_decode_workspace_size(T, H, I, E, k)
+
+
+def layer_decode_workspace(T: int, H: int, I: int, E: int, k: int, device="cuda") -> torch.Tensor:
+    """A workspace for layer_decode, zeroed (its barrier counter must start at zero)."""
+    n = layer_decode_workspace_size(T, H, I, E, k)
+    if n == 0:
+        raise MoeError(f"the single-launch layer does not support T={T} H={H} I={I} E={E} k={k}")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def layer_decode(logits: torch.Tensor, x: torch.Tensor, w: Mxfp4Weights, k: int, score_fn: int = SCORE_SOFTMAX,
+                 renorm: bool = True, clamp_limit: float = 0.0, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, ids: torch.Tensor | None = None,
+                 weights: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The whole layer in one launch (moe_layer_decode): logits f32 [T, E], x bf16 [T, H] -> bf16 [T, H].
+    `workspace` must come from layer_decode_workspace (or be zeroed before its first use); `ids` and
+    `weights` ([T, k]) receive the routing when given."""
+    x = _as_bf16(x)
+    T, H = x.shape
+    w.validate()
+    if H != w.H:
+        raise MoeError(f"x has hidden size {H}, the weights {w.H}")
+    _dev(logits, torch.float32, "logits")
+    if tuple(logits.shape) != (T, w.E):
+        raise MoeError(f"logits must be [{T}, {w.E}], got {tuple(logits.shape)}")
+    for t, name, dt in ((ids, "topk_ids", torch.int32), (weights, "topk_w", torch.float32)):
+        if t is not None:
+            _dev(t, dt, name)
+            if tuple(t.shape) != (T, k):
+                raise MoeError(f"{name} must be [{T}, {k}]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (T, H):
+            raise MoeError(f"out must be [{T}, {H}]")
+    if workspace is None:
+        workspace = layer_decode_workspace(T, H, w.I, w.E, k, x.device)
+    _dev(workspace, torch.uint8, "workspace")
+    _check(load_library().moe_layer_decode(
+        _ptr(logits), _ptr(x), T, H, w.I, w.E, int(k), int(score_fn), int(bool(renorm)), _ptr(w.w13_q),
+        _ptr(w.w13_s), _ptr(w.w2_q), _ptr(w.w2_s), float(clamp_limit), _ptr(ids), _ptr(weights), _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "moe_layer_decode")
+    return out
+
+
 class MoELayer:
     """One routed MXFP4 MoE layer with every buffer preallocated for up to ``max_tokens`` tokens.
 
@@ -399,7 +453,10 @@ class MoELayer:
     """
 
     def __init__(self, weights: Mxfp4Weights, k: int, max_tokens: int, score_fn: int = SCORE_SOFTMAX,
-                 renorm: bool = True, clamp_limit: float = 0.0, flags: int = 0, device="cuda"):
+                 renorm: bool = True, clamp_limit: float = 0.0, flags: int = 0, device="cuda",
+                 single_launch: bool = False):
+        """single_launch: run each forward as one moe_layer_decode launch (decode batches; every
+        token count up to max_tokens must be supported by it)."""
         weights.validate()
         self.w = weights
         self.k = k
@@ -415,6 +472,11 @@ class MoELayer:
         self.out = torch.empty((max_tokens, H), dtype=torch.bfloat16, device=device)
         ws = ffn_workspace_size(max_tokens, H, I, E, k, flags)
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.single_launch = single_launch
+        if single_launch:
+            # sized for max_tokens, which bounds every smaller batch's need (zeroed once: the
+            # barrier counter at its start must begin at zero)
+            self.layer_ws = layer_decode_workspace(max_tokens, H, I, E, k, device)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, weights: Mxfp4Weights | None = None,
                 stream=None, options: FfnOptions | None = None) -> torch.Tensor:
@@ -431,6 +493,9 @@ class MoELayer:
         if x.shape[1] != w.H:
             raise MoeError(f"x has hidden size {x.shape[1]}, the layer {w.H}")
         ids, tw = self.ids[:T], self.topk_w[:T]
+        if self.single_launch:
+            return layer_decode(logits, x, w, self.k, self.score_fn, self.renorm, self.clamp, self.out[:T],
+                                self.layer_ws, ids, tw, stream)
         route_group(logits, self.k, self.score_fn, self.renorm, ids, tw, self.grp, stream)
         return mxfp4_ffn(x, w, tw, self.grp, self.clamp, self.flags, self.out[:T], self.workspace, options,
                          stream)

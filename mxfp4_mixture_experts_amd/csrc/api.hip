@@ -409,3 +409,32 @@ MOE_API int moe_mxfp4_ffn_noalloc(const uint16_t* x_bf16, int T, int H, int I, i
                           sorted_pair, pair_pos, active, n_active, clamp_limit, flags, out_bf16, ws,
                           MOE_NOALLOC_SCRATCH_BYTES, nullptr, stream);
 }
+
+MOE_API size_t moe_layer_decode_workspace_size(int T, int H, int I, int E, int k) {
+  if (!ffn_sizes_ok(T, H, I, E, k) || T < 1) return 0;
+  const int cus = num_cus();
+  if (!moe::layer_supported(T, H, I, E, k, cus)) return 0;
+  return moe::layer_workspace_bytes(T, H, I, E, k, cus);
+}
+
+MOE_API int moe_layer_decode(const float* logits, const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                             int score_fn, int renorm, const uint8_t* w13_q, const uint8_t* w13_s,
+                             const uint8_t* w2_q, const uint8_t* w2_s, float clamp_limit, int32_t* topk_ids,
+                             float* topk_w, uint16_t* out_bf16, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const int cus = num_cus();
+  if (!moe::layer_supported(T, H, I, E, k, cus)) return MOE_ERR_UNSUPPORTED;
+  if (!logits || !x_bf16 || !w13_q || !w13_s || !w2_q || !w2_s || !out_bf16 || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(out_bf16, 16) || !aligned(w13_q, 16) || !aligned(w2_q, 16) ||
+      !aligned(workspace, kAlign))
+    return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < moe::layer_workspace_bytes(T, H, I, E, k, cus)) return MOE_ERR_WORKSPACE;
+  return moe::launch_layer_decode(logits, x_bf16, T, H, I, E, k, score_fn, renorm, w13_q, w13_s, w2_q, w2_s,
+                                  clamp_limit, topk_ids, topk_w, out_bf16, workspace, cus,
+                                  (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}

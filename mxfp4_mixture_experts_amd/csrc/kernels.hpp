@@ -149,6 +149,21 @@ hipError_t launch_dense_down(const DensePlan& dp, const Routed& r, int H, int I,
                              const uint8_t* w2_s, const int32_t* dense_e, const int32_t* dense_m0,
                              const uint16_t* h16, const uint8_t* rowf, float* y, hipStream_t stream);
 
+// The whole layer for decode in one launch (route, group, gate_up, down, combine); see layer_decode.hip.
+constexpr int kLayerMaxTokens = 16;
+constexpr int kLayerMaxPairs = 256;
+constexpr int kLayerMaxExperts = 512;
+constexpr int kLayerMaxRanges = 1024;           // workgroups (one per compute unit)
+constexpr size_t kLayerSyncBytes = 256;         // barrier counter and status word at the workspace start
+constexpr size_t kLayerMaxHLds = 92 * 1024;     // LDS for one workgroup's h (static LDS ~65 KB: 160 KB in all)
+bool layer_supported(int T, int H, int I, int E, int k, int num_cus);
+size_t layer_workspace_bytes(int T, int H, int I, int E, int k, int num_cus);
+size_t layer_h_lds_bytes(int T, int I, int E, int k, int num_cus);
+hipError_t launch_layer_decode(const float* logits, const uint16_t* x, int T, int H, int I, int E, int k,
+                               int score_fn, int renorm, const uint8_t* w13_q, const uint8_t* w13_s,
+                               const uint8_t* w2_q, const uint8_t* w2_s, float clamp, int32_t* ids_out,
+                               float* w_out, uint16_t* out, void* workspace, int num_cus, hipStream_t stream);
+
 // out[t] = bf16(sum_j topk_w[t, j] * y[pair_pos[t*k + j]])
 hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* pair_pos, int T, int H,
                           int k, uint16_t* out, int* grid_out, hipStream_t stream);

@@ -228,3 +228,30 @@ def test_noalloc_validation(lib):
     assert call(H=4016) == -2
     assert call(flags=8) == -3
     assert call(T=0) == 0             # nothing to do
+
+
+def test_layer_decode_validation(lib):
+    """moe_layer_decode: sizes, support limits, pointers and workspace are checked before any launch."""
+    lib.moe_layer_decode_workspace_size.restype = ctypes.c_size_t
+    need = lib.moe_layer_decode_workspace_size(8, 4096, 2048, 256, 8)
+    # 256 bytes of barrier state, then (T * CUs + 2 T k) rows of H fp32 partial outputs (256 CUs here)
+    assert need == 256 + (8 * 256 + 2 * 64) * 4096 * 4
+    assert lib.moe_layer_decode_workspace_size(17, 4096, 2048, 256, 8) == 0   # T > 16
+    assert lib.moe_layer_decode_workspace_size(16, 4096, 2048, 256, 16) == 0  # share > 32 blocks
+    assert lib.moe_layer_decode_workspace_size(8, 4016, 2048, 256, 8) == 0    # H % 32
+    d = DUMMY
+    sz = ctypes.c_size_t
+
+    def call(T=8, H=4096, I=2048, E=256, k=8, fn=0, logits=d, out=d, ws=V(0x10000), ws_bytes=need):
+        return lib.moe_layer_decode(logits, d, T, H, I, E, k, fn, 1, d, d, d, d, ctypes.c_float(0.0), None, None,
+                                    out, ws, sz(ws_bytes), None)
+
+    assert call(H=4016) == -2
+    assert call(k=9, E=8) == -2
+    assert call(fn=2) == -3
+    assert call(T=17) == -3
+    assert call(logits=None) == -1
+    assert call(out=None) == -1
+    assert call(ws=V(0x10010)) == -3
+    assert call(ws_bytes=need - 1) == -4
+    assert call(T=0) == 0
