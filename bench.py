@@ -336,6 +336,63 @@ def summary(res: dict, use_graph: bool) -> dict:
     }
 
 
+def forward_timing(env: Env, cfg, steps: int) -> dict | None:
+    """The layer from the activations and the router weights (moe_layer_forward: the router, its
+    selection and the grouping, then the FFN): one hipGraph of L layers on cold expert weights (the
+    same rotation as the headline), median over timed replays. Not part of `value`, which starts
+    from logits as the metric's layer does."""
+    np, torch, moe, moe_synth = env.np, env.torch, env.moe, env.moe_synth
+    stream = env.stream
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    inp = moe_synth.make_inputs(cfg)
+    per_expert = 3 * H * I // 2 + 3 * H * I // 32
+    R = max(2, math.ceil((2 << 30) / (E * per_expert)), math.ceil(8 * LLC_BYTES / (E * per_expert)))
+    first = moe.Mxfp4Weights(*(env.dev(inp[a]) for a in ("w13_q", "w13_s", "w2_q", "w2_s")))
+    replicas = [first] + [moe.Mxfp4Weights(*(t.clone() for t in (first.w13_q, first.w13_s, first.w2_q, first.w2_s)))
+                          for _ in range(R - 1)]
+    x = env.dev(inp["x"].view(np.int16)).view(torch.bfloat16)
+    wr = env.dev(moe_synth.make_router_weights(E, H, 20261203 + 99).view(np.int16)).view(torch.bfloat16)
+    ws = moe.layer_forward_workspace(T, H, I, E, k)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    fwd = lambda j: moe.layer_forward(x, wr, replicas[j % R], k, cfg.score_fn, cfg.renorm, cfg.clamp,  # noqa: E731
+                                      out=out, workspace=ws, stream=stream)
+    try:
+        with torch.cuda.stream(stream):
+            for j in range(5):
+                fwd(j)
+        torch.cuda.synchronize()
+        reps = 5
+        L = max(2, steps // reps)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for j in range(L):
+                fwd(j)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = env.event(), env.event()
+            with torch.cuda.stream(stream):
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / L)
+        del g
+    except Exception as exc:  # capture unsupported
+        log(f"layer_forward graph failed: {exc!r}")
+        return None
+    finally:
+        del replicas, first
+        torch.cuda.empty_cache()
+    us = statistics.median(times)
+    log(f"layer_forward (from x and W_router) {cfg.name}: {us:.1f} us/layer")
+    return {"us_per_layer": round(us, 2), "timing": f"hipGraph of {L} layers, median of {reps} replays",
+            "note": "x and bf16 W_router [E, H] to out: router projection + top-k + grouping (one launch up to "
+                    "32 tokens), gate_up, down, combine; cold expert weights; not part of value"}
+
+
 def read_probe_gbps(env: Env) -> float:
     """Attainable read bandwidth on this machine: a plain device reduction of 2 GiB in rows of 4096
     floats (one output per row; best of 5). A single whole-buffer sum reaches only about two thirds
@@ -370,7 +427,7 @@ def router_timing(env: Env, cfg, x) -> dict | None:
     w_router0 = env.dev(moe_synth.make_router_weights(E, H, 20261203 + 99).view(np.int16)).view(torch.bfloat16)
     r_ops = [(w_router0.clone(), x.clone()) for _ in range(n_router)]
     del w_router0
-    ws_router = torch.empty(moe.router_gemm_topk_workspace_size(T, H, E), dtype=torch.uint8, device="cuda")
+    ws_router = moe.router_workspace(T, H, E)
     with torch.cuda.stream(stream):
         moe.router_gemm_topk(r_ops[0][1], r_ops[0][0], k, cfg.score_fn, cfg.renorm, want_logits=False,
                              workspace=ws_router, stream=stream)
@@ -382,7 +439,7 @@ def router_timing(env: Env, cfg, x) -> dict | None:
         with torch.cuda.graph(gr, stream=stream):
             for wr_i, xr_i in ops:
                 moe.router_gemm_topk(xr_i, wr_i, k, cfg.score_fn, cfg.renorm, want_logits=False,
-                                     workspace=ws_router, stream=stream)
+                                     workspace=ws_router, stream=stream, split_launch=split[0])
         with torch.cuda.stream(stream):  # a replay runs on the current stream: make it `stream`
             gr.replay()
         torch.cuda.synchronize()
@@ -399,25 +456,38 @@ def router_timing(env: Env, cfg, x) -> dict | None:
         del gr
         return best
 
+    split = [False]
+
+    def graph_us_split(ops):
+        split[0] = True
+        try:
+            return graph_us(ops)
+        finally:
+            split[0] = False
+
     try:
         us = graph_us(r_ops)
         us_warm = graph_us([r_ops[0]] * 50)
+        us_two = graph_us_split(r_ops)
     except Exception as exc:  # capture unsupported: skip the router line
         log(f"router graph capture failed: {exc!r}")
         return None
     finally:
         del r_ops
         torch.cuda.empty_cache()
-    log(f"router gemm+top-k: {us:.2f} us per call cold ({n_router} operand copies), {us_warm:.2f} us warm")
+    log(f"router gemm+top-k: {us:.2f} us per call cold ({n_router} operand copies), {us_warm:.2f} us warm, "
+        f"{us_two:.2f} us cold as two launches")
     return {
         "us": round(us, 2),
         "operand_GBps": round(router_bytes / (us * 1e-6) / 1e9, 1),
         "pct_hbm_peak": round(100 * router_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
         "tflops": round(2 * T * E * H / (us * 1e-6) / 1e12, 2),
         "us_warm": round(us_warm, 2),
+        "us_two_launches": round(us_two, 2),
         "note": (f"logits = x . W_router^T (bf16 [E, H]) and top-k; us: one graph over {n_router} copies of "
                  "(W_router, x), so every call reads cold operands (GB/s counts W_router and x once); "
-                 "us_warm: 50 calls on one copy; not part of value")}
+                 "us_warm: 50 calls on one copy; us_two_launches: cold, the projection and the selection as "
+                 "two kernels (one launch is the default up to 32 tokens); not part of value")}
 
 
 def cpu_baseline(args, cfg, inp) -> dict:
@@ -475,6 +545,7 @@ def main():
     med = statistics.median
     log(f"warm weights: median {med(res['warm_us']):.1f} us/layer eager; read probe {probe:.0f} GB/s")
     router = router_timing(env, cfg, res["x"])
+    forward = forward_timing(env, cfg, args.steps) if args.flags == 0 and not args.single_launch else None
 
     use_graph = args.mode == "graph" and res["graph_s"] is not None
     s = summary(res, use_graph)
@@ -520,6 +591,7 @@ def main():
         "us_per_layer_warm_eager": {"median": round(med(res["warm_us"]), 2), "steps": len(res["warm_us"]),
                                     "note": "one weight replica reused every step (not the metric)"},
         "router_gemm_topk": router,
+        "layer_forward_from_x": forward,
         "stage_us_eager_median": s["stage_us_eager_median"],
         "active_experts": res["n_active"],
         "weight_bytes_per_layer": res["weight_bytes"],

@@ -115,21 +115,56 @@ int moe_route_topk(const float* logits, int T, int E, int k, int score_fn, int r
  * the projection before it undefined; here it is a dense bfloat16 matrix.
  * The projection runs on the matrix cores with K split into up to 16 slices (chosen from T, H and E
  * only); the slices' partial logits go to the workspace and are summed in slice order, so results
- * are deterministic for given sizes. Two kernels are enqueued.
+ * are deterministic for given sizes. For T <= 32 (decode) both steps run in ONE launch: the
+ * workgroup that completes the last slice (found with a device-scope counter at the workspace start)
+ * sums the partials and selects; above 32 tokens two kernels are enqueued. Both give the same bits.
  *
  *   x_bf16         [dev] u16[T, H]  bfloat16 activations, 16-byte aligned
  *   w_router_bf16  [dev] u16[E, H]  bfloat16 router weights (one row per expert), 16-byte aligned
  *   logits         [dev] f32[T, E]  (written) or NULL
  *   topk_ids, topk_w               as moe_route_topk (written)
  *   workspace, ws_bytes            [dev] at least moe_router_gemm_topk_workspace_size(T, H, E) bytes,
- *                                  256-byte aligned; contents on entry do not matter
+ *                                  256-byte aligned. Its first 256 bytes hold the one-launch
+ *                                  router's counter: ZERO them before the first call on this
+ *                                  workspace (e.g. hipMemset once after allocating it); every call
+ *                                  leaves them zero. The rest may hold anything on entry. One
+ *                                  workspace serves one call at a time.
  * Limits: T >= 0 (T == 0 enqueues nothing), 32 <= H <= MOE_MAX_HIDDEN, H % 32 == 0,
  * 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK), T*k <= MOE_MAX_PAIRS, score_fn in {0, 1}.
+ * moe_router_gemm_topk_ex adds flags: MOE_ROUTER_SPLIT_LAUNCH enqueues the two kernels at every T
+ * (the two-launch structure, bitwise the same results).
  */
+enum { MOE_ROUTER_SPLIT_LAUNCH = 1 };
 size_t moe_router_gemm_topk_workspace_size(int T, int H, int E);  /* host; 0 for invalid sizes */
 int moe_router_gemm_topk(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int E,
                          int k, int score_fn, int renorm, float* logits, int32_t* topk_ids,
                          float* topk_w, void* workspace, size_t ws_bytes, void* stream);
+int moe_router_gemm_topk_ex(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int E,
+                            int k, int score_fn, int renorm, float* logits, int32_t* topk_ids,
+                            float* topk_w, void* workspace, size_t ws_bytes, int flags, void* stream);
+
+/*
+ * moe_layer_forward — the whole layer from the activations and the router weights: the router
+ * projection and top-k, the grouping, and moe_mxfp4_ffn (the routed layer of the pages' Post-Portfolio
+ * Device Attribution table, "MTP1 Post-Portfolio Eager-Cycle Profile", from router to combine). For
+ * T <= 32 the router, its selection and the grouping are one launch, so decode runs in four
+ * (router+group, gate_up, down, combine). Results are bitwise those of moe_router_gemm_topk +
+ * moe_group_tokens + moe_mxfp4_ffn.
+ *   x_bf16, w_router_bf16, score_fn, renorm   as moe_router_gemm_topk
+ *   w13_q .. w2_s, clamp_limit, flags, out   as moe_mxfp4_ffn (flags: the MOE_* ffn flags)
+ *   logits, topk_ids, topk_w                  [dev] outputs of the router when not NULL
+ *   workspace, ws_bytes                       [dev] at least moe_layer_forward_workspace_size(T, H, I, E,
+ *                                             k, flags) bytes, 256-byte aligned; its first 256 bytes
+ *                                             must be ZERO before the first call (the router's counter,
+ *                                             left zero by every call)
+ * Limits and errors: as moe_mxfp4_ffn (and score_fn in {0, 1}).
+ */
+size_t moe_layer_forward_workspace_size(int T, int H, int I, int E, int k, int flags);  /* host; 0 if invalid */
+int moe_layer_forward(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int I, int E,
+                      int k, int score_fn, int renorm, const uint8_t* w13_q, const uint8_t* w13_s,
+                      const uint8_t* w2_q, const uint8_t* w2_s, float clamp_limit, int flags, float* logits,
+                      int32_t* topk_ids, float* topk_w, uint16_t* out_bf16, void* workspace,
+                      size_t ws_bytes, void* stream);
 
 /*
  * moe_group_tokens — token-to-expert grouping (expert histogram, exclusive prefix scan and a stable

@@ -90,6 +90,13 @@ def load_library(path: str | None = None):
     lib.moe_router_gemm_topk_workspace_size.restype = ctypes.c_size_t
     lib.moe_router_gemm_topk.argtypes = [V, V, i, i, i, i, i, i, V, V, V, V, ctypes.c_size_t, V]
     lib.moe_router_gemm_topk.restype = i
+    lib.moe_router_gemm_topk_ex.argtypes = [V, V, i, i, i, i, i, i, V, V, V, V, ctypes.c_size_t, i, V]
+    lib.moe_router_gemm_topk_ex.restype = i
+    lib.moe_layer_forward_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.moe_layer_forward_workspace_size.restype = ctypes.c_size_t
+    lib.moe_layer_forward.argtypes = [V, V, i, i, i, i, i, i, i, V, V, V, V, ctypes.c_float, i, V, V, V, V, V,
+                                      ctypes.c_size_t, V]
+    lib.moe_layer_forward.restype = i
     lib.moe_group_tokens_workspace_size.argtypes = [i, i, i]
     lib.moe_group_tokens_workspace_size.restype = ctypes.c_size_t
     lib.moe_group_tokens.argtypes = [V, i, i, i, V, V, V, V, V, V, V, ctypes.c_size_t, V]
@@ -193,11 +200,19 @@ def router_gemm_topk_workspace_size(T: int, H: int, E: int) -> int:
     return n
 
 
+ROUTER_SPLIT_LAUNCH = 1
+
+
+def router_workspace(T: int, H: int, E: int, device="cuda") -> torch.Tensor:
+    """A zeroed workspace for router_gemm_topk (its first bytes are a counter that must start at 0)."""
+    return torch.zeros(router_gemm_topk_workspace_size(T, H, E), dtype=torch.uint8, device=device)
+
+
 def router_gemm_topk(x: torch.Tensor, w_router: torch.Tensor, k: int, score_fn: int = SCORE_SOFTMAX,
                      renorm: bool = True, want_logits: bool = True, workspace: torch.Tensor | None = None,
-                     stream=None):
+                     stream=None, split_launch: bool = False):
     """logits = x . w_router^T (bf16, fp32 accumulation) and their top-k; returns
-    (topk_ids, topk_w, logits or None)."""
+    (topk_ids, topk_w, logits or None). `workspace` must come from router_workspace (zeroed once)."""
     _dev(x, torch.bfloat16, "x")
     _dev(w_router, torch.bfloat16, "w_router")
     T, H = x.shape
@@ -207,13 +222,14 @@ def router_gemm_topk(x: torch.Tensor, w_router: torch.Tensor, k: int, score_fn: 
     ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
     weights = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
-    need = router_gemm_topk_workspace_size(T, H, E)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _check(load_library().moe_router_gemm_topk(_ptr(x), _ptr(w_router), T, H, E, int(k), int(score_fn),
-                                               int(bool(renorm)), _ptr(logits), _ptr(ids), _ptr(weights),
-                                               _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                               _stream(stream)), "moe_router_gemm_topk")
+        workspace = router_workspace(T, H, E, x.device)
+    _dev(workspace, torch.uint8, "workspace")
+    _check(load_library().moe_router_gemm_topk_ex(_ptr(x), _ptr(w_router), T, H, E, int(k), int(score_fn),
+                                                  int(bool(renorm)), _ptr(logits), _ptr(ids), _ptr(weights),
+                                                  _ptr(workspace), workspace.numel(),
+                                                  ROUTER_SPLIT_LAUNCH if split_launch else 0, _stream(stream)),
+           "moe_router_gemm_topk_ex")
     return ids, weights, logits
 
 
@@ -442,6 +458,46 @@ def layer_decode(logits: torch.Tensor, x: torch.Tensor, w: Mxfp4Weights, k: int,
         _ptr(logits), _ptr(x), T, H, w.I, w.E, int(k), int(score_fn), int(bool(renorm)), _ptr(w.w13_q),
         _ptr(w.w13_s), _ptr(w.w2_q), _ptr(w.w2_s), float(clamp_limit), _ptr(ids), _ptr(weights), _ptr(out),
         _ptr(workspace), workspace.numel(), _stream(stream)), "moe_layer_decode")
+    return out
+
+
+def layer_forward_workspace(T: int, H: int, I: int, E: int, k: int, flags: int = 0, device="cuda") -> torch.Tensor:
+    """A zeroed workspace for layer_forward (its first bytes are the router's counter, which must start
+    at 0)."""
+    n = load_library().moe_layer_forward_workspace_size(T, H, I, E, k, flags)
+    if n == 0:
+        raise MoeError("invalid sizes for moe_layer_forward_workspace_size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def layer_forward(x: torch.Tensor, w_router: torch.Tensor, w: Mxfp4Weights, k: int, score_fn: int = SCORE_SOFTMAX,
+                  renorm: bool = True, clamp_limit: float = 0.0, flags: int = 0, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                  ids: torch.Tensor | None = None, weights: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The whole layer from x (bf16 [T, H]) and the router weights (bf16 [E, H]): moe_layer_forward."""
+    x = _as_bf16(x)
+    T, H = x.shape
+    w.validate()
+    _dev(w_router, torch.bfloat16, "w_router")
+    if tuple(w_router.shape) != (w.E, H) or H != w.H:
+        raise MoeError(f"w_router must be [{w.E}, {w.H}] and x [T, {w.H}]")
+    for t, name, dt, shape in ((logits, "logits", torch.float32, (T, w.E)), (ids, "topk_ids", torch.int32, (T, k)),
+                               (weights, "topk_w", torch.float32, (T, k))):
+        if t is not None:
+            _dev(t, dt, name)
+            if tuple(t.shape) != shape:
+                raise MoeError(f"{name} must be {list(shape)}")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    elif tuple(out.shape) != (T, H):
+        raise MoeError(f"out must be [{T}, {H}]")
+    if workspace is None:
+        workspace = layer_forward_workspace(T, H, w.I, w.E, k, flags, x.device)
+    _dev(workspace, torch.uint8, "workspace")
+    _check(load_library().moe_layer_forward(
+        _ptr(x), _ptr(w_router), T, H, w.I, w.E, int(k), int(score_fn), int(bool(renorm)), _ptr(w.w13_q),
+        _ptr(w.w13_s), _ptr(w.w2_q), _ptr(w.w2_s), float(clamp_limit), int(flags), _ptr(logits), _ptr(ids),
+        _ptr(weights), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)), "moe_layer_forward")
     return out
 
 

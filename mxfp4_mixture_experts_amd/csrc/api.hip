@@ -191,26 +191,46 @@ MOE_API int moe_route_topk(const float* logits, int T, int E, int k, int score_f
 
 MOE_API size_t moe_router_gemm_topk_workspace_size(int T, int H, int E) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || H < 32 || H > MOE_MAX_HIDDEN || H % 32) return 0;
-  const size_t b = moe::router_workspace_bytes(T, H, E);
-  return b > 0 ? b : 256;
+  return moe::router_workspace_bytes(T, H, E);
 }
 
-MOE_API int moe_router_gemm_topk(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int E,
-                                 int k, int score_fn, int renorm, float* logits, int32_t* topk_ids,
-                                 float* topk_w, void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+int router_check(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int E, int k, int score_fn,
+                 const void* workspace, size_t ws_bytes) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E ||
       (long)T * k > MOE_MAX_PAIRS || H < 32 || H > MOE_MAX_HIDDEN || H % 32)
     return MOE_ERR_SHAPE;
   if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!x_bf16 || !w_router_bf16 || !topk_ids || !topk_w || !workspace) return MOE_ERR_NULL;
+  if (!x_bf16 || !w_router_bf16 || !workspace) return MOE_ERR_NULL;
   if (!aligned(x_bf16, 16) || !aligned(w_router_bf16, 16) || !aligned(workspace, 256))
     return MOE_ERR_UNSUPPORTED;
-  if (ws_bytes < moe_router_gemm_topk_workspace_size(T, H, E)) return MOE_ERR_WORKSPACE;
-  if (moe::launch_router_gemm_topk(x_bf16, w_router_bf16, T, H, E, k, score_fn, renorm, (float*)workspace,
-                                   logits, topk_ids, topk_w, (hipStream_t)stream) != hipSuccess)
+  if (ws_bytes < moe::router_workspace_bytes(T, H, E)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API int moe_router_gemm_topk_ex(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int E,
+                                    int k, int score_fn, int renorm, float* logits, int32_t* topk_ids,
+                                    float* topk_w, void* workspace, size_t ws_bytes, int flags, void* stream) {
+  if (flags & ~MOE_ROUTER_SPLIT_LAUNCH) return MOE_ERR_UNSUPPORTED;
+  const int st = router_check(x_bf16, w_router_bf16, T, H, E, k, score_fn, workspace, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!topk_ids || !topk_w) return MOE_ERR_NULL;
+  if (moe::launch_router_gemm_topk(x_bf16, w_router_bf16, T, H, E, k, score_fn, renorm, workspace, logits,
+                                   topk_ids, topk_w, (flags & MOE_ROUTER_SPLIT_LAUNCH) != 0,
+                                   (hipStream_t)stream) != hipSuccess)
     return MOE_ERR_LAUNCH;
   return MOE_OK;
+}
+
+MOE_API int moe_router_gemm_topk(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int E,
+                                 int k, int score_fn, int renorm, float* logits, int32_t* topk_ids,
+                                 float* topk_w, void* workspace, size_t ws_bytes, void* stream) {
+  return moe_router_gemm_topk_ex(x_bf16, w_router_bf16, T, H, E, k, score_fn, renorm, logits, topk_ids, topk_w,
+                                 workspace, ws_bytes, 0, stream);
 }
 
 // The grouping is one workgroup with its histograms and scans in LDS: no device workspace.
@@ -437,4 +457,79 @@ MOE_API int moe_layer_decode(const float* logits, const uint16_t* x_bf16, int T,
                                   (hipStream_t)stream) == hipSuccess
              ? MOE_OK
              : MOE_ERR_LAUNCH;
+}
+
+namespace {
+
+// Workspace of moe_layer_forward: the router's (header first), the routing and grouping arrays, then
+// the FFN's.
+struct LayerWs {
+  size_t router, ids, w, counts, offsets, sorted_pair, pair_pos, active, n_active, ffn, total;
+};
+
+LayerWs layer_ws(int T, int H, int I, int E, int k, int flags) {
+  LayerWs l;
+  const size_t P = (size_t)T * k;
+  size_t off = 0;
+  l.router = off;
+  off = align_up(off + moe::router_workspace_bytes(T, H, E));
+  l.ids = off;
+  off = align_up(off + P * 4);
+  l.w = off;
+  off = align_up(off + P * 4);
+  l.counts = off;
+  off = align_up(off + (size_t)E * 4);
+  l.offsets = off;
+  off = align_up(off + (size_t)(E + 1) * 4);
+  l.sorted_pair = off;
+  off = align_up(off + P * 4);
+  l.pair_pos = off;
+  off = align_up(off + P * 4);
+  l.active = off;
+  off = align_up(off + (size_t)E * 4);
+  l.n_active = off;
+  off = align_up(off + 4);
+  l.ffn = off;
+  off += ws_layout((long)P, H, I, E, k, flags).total;
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+MOE_API size_t moe_layer_forward_workspace_size(int T, int H, int I, int E, int k, int flags) {
+  if (!ffn_sizes_ok(T, H, I, E, k) || (flags & ~kKnownFlags)) return 0;
+  return layer_ws(T, H, I, E, k, flags).total;
+}
+
+MOE_API int moe_layer_forward(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int H, int I, int E,
+                              int k, int score_fn, int renorm, const uint8_t* w13_q, const uint8_t* w13_s,
+                              const uint8_t* w2_q, const uint8_t* w2_s, float clamp_limit, int flags,
+                              float* logits, int32_t* topk_ids, float* topk_w, uint16_t* out_bf16,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if ((flags & ~kKnownFlags) || ((flags & MOE_FORCE_SMALL_M) && (flags & MOE_FORCE_LARGE_M)))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !w_router_bf16 || !w13_q || !w13_s || !w2_q || !w2_s || !out_bf16 || !workspace)
+    return MOE_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w_router_bf16, 16) || !aligned(out_bf16, 16) || !aligned(w13_q, 16) ||
+      !aligned(w2_q, 16) || !aligned(workspace, kAlign))
+    return MOE_ERR_UNSUPPORTED;
+  const LayerWs l = layer_ws(T, H, I, E, k, flags);
+  if (ws_bytes < l.total) return MOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(ws + l.ids);
+  float* tw = topk_w ? topk_w : reinterpret_cast<float*>(ws + l.w);
+  const moe::RouterGroupOut grp{reinterpret_cast<int32_t*>(ws + l.counts), reinterpret_cast<int32_t*>(ws + l.offsets),
+                                reinterpret_cast<int32_t*>(ws + l.sorted_pair),
+                                reinterpret_cast<int32_t*>(ws + l.pair_pos), reinterpret_cast<int32_t*>(ws + l.active),
+                                reinterpret_cast<int32_t*>(ws + l.n_active)};
+  if (moe::launch_router_group(x_bf16, w_router_bf16, T, H, E, k, score_fn, renorm, ws + l.router, logits, ids, tw,
+                               grp, (hipStream_t)stream) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  return moe_mxfp4_ffn_ex(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, tw, grp.counts, grp.offsets,
+                          grp.sorted_pair, grp.pair_pos, grp.active, grp.n_active, clamp_limit, flags, out_bf16,
+                          ws + l.ffn, ws_bytes - l.ffn, nullptr, stream);
 }

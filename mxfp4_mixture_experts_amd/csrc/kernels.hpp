@@ -17,10 +17,30 @@ struct RouterPlan {
   int blocks;           // workgroups of the GEMM
 };
 RouterPlan plan_router(int T, int H, int E);
+// Workspace: a 256-byte header (the one-launch router's completion counter, zero before the first
+// call and left zero by every call), then the partial logits.
+constexpr size_t kRouterHeaderBytes = 256;
+constexpr int kRouterMaxTopk = 16;
 size_t router_workspace_bytes(int T, int H, int E);
+bool router_fusable(int T);  // projection and selection in one launch
+// split_launch: the projection and the selection as two kernels even where one would do
 hipError_t launch_router_gemm_topk(const uint16_t* x, const uint16_t* w, int T, int H, int E, int k,
-                                   int score_fn, int renorm, float* part, float* logits, int32_t* ids,
-                                   float* weights, hipStream_t stream);
+                                   int score_fn, int renorm, void* workspace, float* logits, int32_t* ids,
+                                   float* weights, bool split_launch, hipStream_t stream);
+// Grouping outputs (moe_group_tokens's)
+struct RouterGroupOut {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  int32_t* active;
+  int32_t* n_active;
+};
+// The router and the grouping of its ids: one launch for T <= 32, else the two router kernels and
+// the grouping kernel.
+hipError_t launch_router_group(const uint16_t* x, const uint16_t* w, int T, int H, int E, int k, int score_fn,
+                               int renorm, void* workspace, float* logits, int32_t* ids, float* weights,
+                               const RouterGroupOut& grp, hipStream_t stream);
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int score_fn, int renorm,
                              int32_t* ids, float* weights, hipStream_t stream);

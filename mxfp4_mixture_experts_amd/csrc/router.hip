@@ -16,7 +16,10 @@
 //   - One wave per token then loads all its partial logits at once, sums them in slice order
 //     (deterministic, no atomics), optionally writes the logits, and runs the same selection code as
 //     the router kernel.
+#include <type_traits>
+
 #include "common.hpp"
+#include "group_dev.hpp"
 #include "kernels.hpp"
 #include "route_dev.hpp"
 
@@ -27,6 +30,8 @@ namespace {
 constexpr int kRouterTile = 64;      // experts per workgroup tile (16 per wave)
 constexpr int kRouterMaxSplits = 16;  // K slices at most
 constexpr int kRouterTargetBlocks = 512;  // about two workgroups per CU; more slices add partial-sum traffic
+constexpr int kRouterFusedMaxPairs = 32 * kRouterMaxTopk;  // T <= 32 tokens in the one-launch router
+constexpr int kRouterFusedThreads = 512;  // eight waves: four for the tile, all eight select
 
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
@@ -37,12 +42,12 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
 // at decode, where all four waves still stream their own expert rows). The operands of U steps are
 // loaded before any of their MFMAs, so a wave has U * (NB + 1) loads in flight; steps past the slice
 // re-read its last step and multiply by a zeroed weight operand, which leaves the accumulator
-// unchanged (for finite activations).
-template <int NB, int U>
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ w, int T, int H,
-                                                          int E, int tiles_t, int splits,
-                                                          int steps_per_split, float* __restrict__ part) {
+// unchanged (for finite activations). DEV_STORE: the partials are stored past the L2 (device scope),
+// for a workgroup on another XCD to read within the same launch.
+template <int NB, int U, bool DEV_STORE>
+__device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
+                                            int H, int E, int tiles_t, int splits, int steps_per_split,
+                                            float* __restrict__ part) {
   const int b = blockIdx.x;
   const int split = b % splits;
   const int tile = b / splits;
@@ -94,8 +99,22 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + tb * 16 + 4 * g + i;
-      if (t < T && e < E) part[((size_t)split * T + t) * E + e] = acc[tb][i];
+      if (t < T && e < E) {
+        float* dst = part + ((size_t)split * T + t) * E + e;
+        if constexpr (DEV_STORE)
+          __hip_atomic_store(dst, acc[tb][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *dst = acc[tb][i];
+      }
     }
+}
+
+template <int NB, int U>
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w, int T, int H,
+                                                          int E, int tiles_t, int splits,
+                                                          int steps_per_split, float* __restrict__ part) {
+  router_tile<NB, U, false>(x, w, T, H, E, tiles_t, splits, steps_per_split, part);
 }
 
 // T > 32: a workgroup owns 64 tokens x 64 experts and stages both operands through LDS, so every
@@ -206,15 +225,13 @@ __global__ __launch_bounds__(256) void router_gemm_lds_kernel(const uint16_t* __
   }
 }
 
-// One wave per token: the logits as the in-order sum of the slices' partials, then the selection.
-template <int EPL>
-__global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ part, int splits,
-                                                            int T, int E, int k, int score_fn, int renorm,
-                                                            float* __restrict__ logits,
-                                                            int32_t* __restrict__ ids,
-                                                            float* __restrict__ weights) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+// One wave, token t: the logits as the in-order sum of the slices' partials, then the selection.
+// DEV_LOAD: the partials are read past the L2 (device scope; written in the same launch).
+template <int EPL, bool DEV_LOAD>
+__device__ __forceinline__ void select_token(const float* __restrict__ part, int splits, int t, int T, int E,
+                                             int k, int score_fn, int renorm, float* __restrict__ logits,
+                                             int32_t* __restrict__ ids, float* __restrict__ weights,
+                                             int32_t* ids_copy) {
   const int lane = threadIdx.x & 63;
   const size_t slice = (size_t)T * E;
   // every partial in flight at once (slices past the last re-read it: loads under a branch would be
@@ -226,7 +243,13 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
     const int e = min(lane + 64 * i, E - 1);
     const float* p = part + (size_t)t * E + e;
 #pragma unroll
-    for (int sp = 0; sp < kRouterMaxSplits; ++sp) pv[i][sp] = p[min(sp, splits - 1) * slice];
+    for (int sp = 0; sp < kRouterMaxSplits; ++sp) {
+      const float* q = p + min(sp, splits - 1) * slice;
+      if constexpr (DEV_LOAD)
+        pv[i][sp] = __hip_atomic_load(const_cast<float*>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        pv[i][sp] = *q;
+    }
   }
   float v[EPL];
 #pragma unroll
@@ -239,7 +262,66 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
     else if (logits) logits[(size_t)t * E + e] = s;
     v[i] = s;
   }
-  route_dev::route_values<EPL>(v, t, E, k, score_fn, renorm, ids, weights, nullptr);
+  route_dev::route_values<EPL>(v, t, E, k, score_fn, renorm, ids, weights, ids_copy);
+}
+
+// One wave per token: the logits as the in-order sum of the slices' partials, then the selection.
+template <int EPL>
+__global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ part, int splits,
+                                                            int T, int E, int k, int score_fn, int renorm,
+                                                            float* __restrict__ logits,
+                                                            int32_t* __restrict__ ids,
+                                                            float* __restrict__ weights) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  select_token<EPL, false>(part, splits, t, T, E, k, score_fn, renorm, logits, ids, weights, nullptr);
+}
+
+// The projection and the selection in one launch (T <= 32): every workgroup computes its tile and
+// slice as router_gemm_kernel does, storing the partials past the L2, then adds one to a device-scope
+// counter; the workgroup that finds the count complete is the last, and runs the selection of every
+// token (a wave per token, the same code and order as router_select_kernel, so the results are
+// bitwise those of the two launches), then, with GROUP, the token grouping of the chosen ids (the
+// grouping kernel's device code), and resets the counter for the next call. The counter must be zero
+// before the first call.
+template <int NB, int U, int EPL, bool GROUP>
+__global__ __launch_bounds__(kRouterFusedThreads) void router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                           int T, int H, int E, int tiles_t, int splits,
+                                                           int steps_per_split, float* __restrict__ part,
+                                                           unsigned int* __restrict__ counter, int k, int score_fn,
+                                                           int renorm, float* __restrict__ logits,
+                                                           int32_t* __restrict__ ids, float* __restrict__ weights,
+                                                           RouterGroupOut grp) {
+  __shared__ int last;
+  __shared__ int32_t ids_lds[GROUP ? kRouterFusedMaxPairs : 1];
+  __shared__ std::conditional_t<GROUP, group_dev::Shared, char> gsh;  // LDS of the grouping, if any
+  // four waves compute the tile; the other four only join the selection in the last workgroup
+  if (threadIdx.x < 256) router_tile<NB, U, true>(x, w, T, H, E, tiles_t, splits, steps_per_split, part);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partials are stored
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int t = wave; t < T; t += kRouterFusedThreads / 64)
+    select_token<EPL, true>(part, splits, t, T, E, k, score_fn, renorm, logits, ids, weights,
+                            GROUP ? ids_lds : nullptr);
+  if constexpr (GROUP) {
+    __syncthreads();
+    const int P = T * k;
+    if (P <= 64) {
+      if (wave == 0)
+        group_dev::group_pairs_one_wave(static_cast<const int32_t*>(ids_lds), P, E, grp.counts, grp.offsets,
+                                        grp.sorted_pair, grp.pair_pos, grp.active, grp.n_active, gsh);
+    } else {
+      group_dev::group_pairs<1>(static_cast<const int32_t*>(ids_lds), P, E, grp.counts, grp.offsets,
+                                grp.sorted_pair, grp.pair_pos, grp.active, grp.n_active, gsh);
+    }
+  }
 }
 
 }  // namespace
@@ -260,13 +342,52 @@ RouterPlan plan_router(int T, int H, int E) {
 
 size_t router_workspace_bytes(int T, int H, int E) {
   const RouterPlan rp = plan_router(T, H, E);
-  return (size_t)rp.splits * T * E * sizeof(float);
+  return kRouterHeaderBytes + (size_t)rp.splits * T * E * sizeof(float);
 }
 
+bool router_fusable(int T) { return T <= 32; }
+
+namespace {
+
+template <bool GROUP>
+hipError_t launch_router_fused(const RouterPlan& rp, const uint16_t* x, const uint16_t* w, int T, int H, int E,
+                               int k, int score_fn, int renorm, void* workspace, float* logits, int32_t* ids,
+                               float* weights, const RouterGroupOut& grp, hipStream_t stream) {
+  unsigned int* counter = static_cast<unsigned int*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kRouterHeaderBytes);
+#define MOE_RF(NB, EPL)                                                                                   \
+  router_fused_kernel<NB, 8, EPL, GROUP><<<rp.blocks, kRouterFusedThreads, 0, stream>>>(x, w, T, H, E, rp.tiles_t, rp.splits, \
+                                                                        rp.steps_per_split, part, counter, k,   \
+                                                                        score_fn, renorm, logits, ids, weights, grp)
+#define MOE_RF_E(NB)  \
+  if (E <= 64)        \
+    MOE_RF(NB, 1);    \
+  else if (E <= 128)  \
+    MOE_RF(NB, 2);    \
+  else if (E <= 256)  \
+    MOE_RF(NB, 4);    \
+  else                \
+    MOE_RF(NB, 8);
+  if (rp.nb == 1) {
+    MOE_RF_E(1)
+  } else {
+    MOE_RF_E(2)
+  }
+#undef MOE_RF_E
+#undef MOE_RF
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_router_gemm_topk(const uint16_t* x, const uint16_t* w, int T, int H, int E, int k,
-                                   int score_fn, int renorm, float* part, float* logits, int32_t* ids,
-                                   float* weights, hipStream_t stream) {
+                                   int score_fn, int renorm, void* workspace, float* logits, int32_t* ids,
+                                   float* weights, bool split_launch, hipStream_t stream) {
   const RouterPlan rp = plan_router(T, H, E);
+  if (router_fusable(T) && !split_launch)
+    return launch_router_fused<false>(rp, x, w, T, H, E, k, score_fn, renorm, workspace, logits, ids, weights,
+                                      RouterGroupOut{}, stream);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kRouterHeaderBytes);
 #define MOE_RGEMM(NB, U)                                                                                 \
   router_gemm_kernel<NB, U><<<rp.blocks, 256, 0, stream>>>(x, w, T, H, E, rp.tiles_t, rp.splits,         \
                                                            rp.steps_per_split, part)
@@ -292,6 +413,19 @@ hipError_t launch_router_gemm_topk(const uint16_t* x, const uint16_t* w, int T, 
     MOE_RS(8);
 #undef MOE_RS
   return hipGetLastError();
+}
+
+hipError_t launch_router_group(const uint16_t* x, const uint16_t* w, int T, int H, int E, int k, int score_fn,
+                               int renorm, void* workspace, float* logits, int32_t* ids, float* weights,
+                               const RouterGroupOut& grp, hipStream_t stream) {
+  if (router_fusable(T))
+    return launch_router_fused<true>(plan_router(T, H, E), x, w, T, H, E, k, score_fn, renorm, workspace, logits,
+                                     ids, weights, grp, stream);
+  const hipError_t e = launch_router_gemm_topk(x, w, T, H, E, k, score_fn, renorm, workspace, logits, ids,
+                                               weights, true, stream);
+  if (e != hipSuccess) return e;
+  return launch_group_tokens(ids, T * k, E, grp.counts, grp.offsets, grp.sorted_pair, grp.pair_pos, grp.active,
+                             grp.n_active, stream);
 }
 
 }  // namespace moe

@@ -255,3 +255,28 @@ def test_layer_decode_validation(lib):
     assert call(ws=V(0x10010)) == -3
     assert call(ws_bytes=need - 1) == -4
     assert call(T=0) == 0
+
+
+def test_router_and_layer_forward_validation(lib):
+    lib.moe_router_gemm_topk_workspace_size.restype = ctypes.c_size_t
+    lib.moe_layer_forward_workspace_size.restype = ctypes.c_size_t
+    # a 256-byte header (the one-launch router's counter) before the partial logits
+    assert lib.moe_router_gemm_topk_workspace_size(8, 4096, 256) >= 256 + 8 * 256 * 4
+    need = lib.moe_layer_forward_workspace_size(8, 4096, 2048, 256, 8, 0)
+    assert need > lib.moe_mxfp4_ffn_workspace_size(8, 4096, 2048, 256, 8, 0)
+    assert lib.moe_layer_forward_workspace_size(8, 4016, 2048, 256, 8, 0) == 0
+    d = DUMMY
+    sz = ctypes.c_size_t
+    assert lib.moe_router_gemm_topk_ex(d, d, 8, 4096, 256, 8, 0, 1, None, d, d, d, sz(1 << 30), 2, None) == -3
+
+    def call(T=8, H=4096, I=2048, E=256, k=8, fn=0, flags=0, out=d, ws=V(0x10000), ws_bytes=need):
+        return lib.moe_layer_forward(d, d, T, H, I, E, k, fn, 1, d, d, d, d, ctypes.c_float(0.0), flags, None, None,
+                                     None, out, ws, sz(ws_bytes), None)
+
+    assert call(H=4016) == -2
+    assert call(fn=2) == -3
+    assert call(flags=6) == -3
+    assert call(out=None) == -1
+    assert call(ws=V(0x10010)) == -3
+    assert call(ws_bytes=need - 1) == -4
+    assert call(T=0) == 0
