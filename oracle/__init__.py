@@ -11,7 +11,10 @@ Steps and their sources (page title, then section or element):
   * group   — same table, direct M=2 route remap row;
   * ffn     — same table, compact routed MXFP4 GEMM and routed clamp-SwiGLU rows; the MXFP4 element
               format is the OCP Microscaling Formats (MX) v1.0 MXFP4 definition;
-  * combine — the routing-weighted sum of each token's k expert outputs.
+  * combine — the routing-weighted sum of each token's k expert outputs;
+  * activation quantisation (the W4A8 / W4A4 mode) — the OCP Microscaling Formats (MX) v1.0
+              specification: the MXFP8 (E4M3) and MXFP4 (E2M1) element formats and its shared-scale
+              computation for a block of 32 values.
 """
 from __future__ import annotations
 
@@ -28,6 +31,10 @@ _lib = None
 
 SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
+
+ACT_NONE = 0
+ACT_MXFP8 = 1
+ACT_MXFP4 = 2
 
 
 def compile_oracle(src: str, out: str) -> str:
@@ -71,6 +78,19 @@ class OracleLib:
         lib.oracle_mxfp4_ffn.argtypes = [P, i, i, i, i, i, P, P, P, P, P, P, ctypes.c_double, i,
                                          P, P, P]
         lib.oracle_mxfp4_ffn.restype = i
+        lib.oracle_mxfp4_ffn_act.argtypes = [P, i, i, i, i, i, P, P, P, P, P, P, ctypes.c_double, i,
+                                             i, P, P, P]
+        lib.oracle_mxfp4_ffn_act.restype = i
+        lib.oracle_e4m3_value.argtypes = [i]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_e4m3_encode.restype = i
+        lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+        lib.oracle_e2m1_encode.restype = i
+        lib.oracle_mx_element.argtypes = [i, i]
+        lib.oracle_mx_element.restype = ctypes.c_double
+        lib.oracle_mx_quantize_block.argtypes = [P, i, P]
+        lib.oracle_mx_quantize_block.restype = i
         lib.oracle_router_logits.argtypes = [P, P, i, i, i, i, P]
         lib.oracle_router_logits.restype = i
         lib.oracle_num_threads.argtypes = [i]
@@ -95,6 +115,37 @@ class OracleLib:
         q = _c(q, np.uint8)
         s = _c(s, np.uint8)
         return self.lib.oracle_mxfp4_element(_ptr(q), _ptr(s), int(K), int(n), int(kk))
+
+    def e4m3_value(self, code: int) -> float:
+        return self.lib.oracle_e4m3_value(int(code))
+
+    def e4m3_encode(self, v: float) -> int:
+        return int(self.lib.oracle_e4m3_encode(float(v)))
+
+    def e2m1_encode(self, v: float) -> int:
+        return int(self.lib.oracle_e2m1_encode(float(v)))
+
+    def mx_element(self, fmt: int, code: int) -> float:
+        return self.lib.oracle_mx_element(int(fmt), int(code))
+
+    def mx_quantize_block(self, v, fmt: int):
+        """Quantise 32 values to an MX block: returns (E8M0 scale byte, uint8[32] element codes)."""
+        v = _c(v, np.float64)
+        assert v.shape == (32,)
+        codes = np.zeros(32, np.uint8)
+        s = self.lib.oracle_mx_quantize_block(_ptr(v), int(fmt), _ptr(codes))
+        return int(s), codes
+
+    def mx_dequantize(self, v, fmt: int) -> np.ndarray:
+        """Each consecutive 32-value block of v (float64, last axis a multiple of 32) quantised and
+        decoded back, through mx_quantize_block."""
+        v = _c(v, np.float64)
+        flat = v.reshape(-1, 32)
+        out = np.empty_like(flat)
+        for b in range(flat.shape[0]):
+            s, codes = self.mx_quantize_block(flat[b], fmt)
+            out[b] = [self.mx_element(fmt, c) * self.e8m0_value(s) for c in codes]
+        return out.reshape(v.shape)
 
     def route_topk(self, logits: np.ndarray, k: int, score_fn: int = SCORE_SOFTMAX,
                    renorm: bool = True):
@@ -141,8 +192,10 @@ class OracleLib:
         return out
 
     def mxfp4_ffn(self, x_bf16: np.ndarray, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w,
-                  clamp_limit: float = 0.0, nthreads: int = 0, want_pairs: bool = False) -> dict:
-        """Expert FFN plus combine. Returns dict(out_ref f64[T,H], out_bf16 u16[T,H], y_pairs?)."""
+                  clamp_limit: float = 0.0, nthreads: int = 0, want_pairs: bool = False,
+                  act_fmt: int = ACT_NONE) -> dict:
+        """Expert FFN plus combine. Returns dict(out_ref f64[T,H], out_bf16 u16[T,H], y_pairs?).
+        act_fmt ACT_MXFP8 / ACT_MXFP4 quantises x (per 32 along H) and h (per 32 along I) first."""
         x = _c(x_bf16, np.uint16)
         T, H = x.shape
         w13_q = _c(w13_q, np.uint8)
@@ -160,11 +213,18 @@ class OracleLib:
         out_ref = np.zeros((T, H), np.float64)
         out_bf16 = np.zeros((T, H), np.uint16)
         y = np.zeros((T * k, H), np.float64) if want_pairs else None
-        rc = self.lib.oracle_mxfp4_ffn(_ptr(x), T, H, I, E, k, _ptr(w13_q), _ptr(w13_s),
-                                       _ptr(w2_q), _ptr(w2_s), _ptr(ids), _ptr(w),
-                                       float(clamp_limit), int(nthreads),
-                                       _ptr(y) if y is not None else None, _ptr(out_ref),
-                                       _ptr(out_bf16))
+        if act_fmt == ACT_NONE:
+            rc = self.lib.oracle_mxfp4_ffn(_ptr(x), T, H, I, E, k, _ptr(w13_q), _ptr(w13_s),
+                                           _ptr(w2_q), _ptr(w2_s), _ptr(ids), _ptr(w),
+                                           float(clamp_limit), int(nthreads),
+                                           _ptr(y) if y is not None else None, _ptr(out_ref),
+                                           _ptr(out_bf16))
+        else:
+            rc = self.lib.oracle_mxfp4_ffn_act(_ptr(x), T, H, I, E, k, _ptr(w13_q), _ptr(w13_s),
+                                               _ptr(w2_q), _ptr(w2_s), _ptr(ids), _ptr(w),
+                                               float(clamp_limit), int(act_fmt), int(nthreads),
+                                               _ptr(y) if y is not None else None, _ptr(out_ref),
+                                               _ptr(out_bf16))
         if rc != 0:
             raise ValueError(f"oracle_mxfp4_ffn failed with {rc}")
         res = dict(out_ref=out_ref, out_bf16=out_bf16)
@@ -173,12 +233,13 @@ class OracleLib:
         return res
 
     def moe_layer(self, logits, x_bf16, w13_q, w13_s, w2_q, w2_s, k, score_fn=SCORE_SOFTMAX,
-                  renorm=True, clamp_limit=0.0, nthreads=0) -> dict:
+                  renorm=True, clamp_limit=0.0, nthreads=0, act_fmt=ACT_NONE) -> dict:
         """The whole path: route, group, expert FFN and combine."""
         E = np.asarray(logits).shape[1]
         ids, w = self.route_topk(logits, k, score_fn, renorm)
         grp = self.group_tokens(ids, E)
-        ffn = self.mxfp4_ffn(x_bf16, w13_q, w13_s, w2_q, w2_s, ids, w, clamp_limit, nthreads)
+        ffn = self.mxfp4_ffn(x_bf16, w13_q, w13_s, w2_q, w2_s, ids, w, clamp_limit, nthreads,
+                             act_fmt=act_fmt)
         return dict(topk_ids=ids, topk_w=w, **grp, **ffn)
 
     def num_threads(self, nthreads: int = 0) -> int:
@@ -223,6 +284,30 @@ def mxfp4_element(q, s, K, n, kk):
     return default().mxfp4_element(q, s, K, n, kk)
 
 
+def e4m3_value(code):
+    return default().e4m3_value(code)
+
+
+def e4m3_encode(v):
+    return default().e4m3_encode(v)
+
+
+def e2m1_encode(v):
+    return default().e2m1_encode(v)
+
+
+def mx_element(fmt, code):
+    return default().mx_element(fmt, code)
+
+
+def mx_quantize_block(v, fmt):
+    return default().mx_quantize_block(v, fmt)
+
+
+def mx_dequantize(v, fmt):
+    return default().mx_dequantize(v, fmt)
+
+
 def route_topk(logits, k, score_fn=SCORE_SOFTMAX, renorm=True):
     return default().route_topk(logits, k, score_fn, renorm)
 
@@ -236,15 +321,15 @@ def router_logits(x_bf16, w_bf16, nthreads=0):
 
 
 def mxfp4_ffn(x_bf16, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, clamp_limit=0.0, nthreads=0,
-              want_pairs=False):
+              want_pairs=False, act_fmt=ACT_NONE):
     return default().mxfp4_ffn(x_bf16, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, clamp_limit,
-                               nthreads, want_pairs)
+                               nthreads, want_pairs, act_fmt)
 
 
 def moe_layer(logits, x_bf16, w13_q, w13_s, w2_q, w2_s, k, score_fn=SCORE_SOFTMAX, renorm=True,
-              clamp_limit=0.0, nthreads=0):
+              clamp_limit=0.0, nthreads=0, act_fmt=ACT_NONE):
     return default().moe_layer(logits, x_bf16, w13_q, w13_s, w2_q, w2_s, k, score_fn, renorm,
-                               clamp_limit, nthreads)
+                               clamp_limit, nthreads, act_fmt)
 
 
 def num_threads(nthreads: int = 0) -> int:

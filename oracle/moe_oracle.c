@@ -110,6 +110,94 @@ double oracle_mxfp4_element(const uint8_t* q, const uint8_t* s, int K, long n, l
   return oracle_e2m1_value(code) * oracle_e8m0_value(s[n * (long)(K / 32) + kk / 32]);
 }
 
+/* ---- activation formats (MX) --------------------------------------------------------------- */
+
+/* E4M3 (the OCP 8-bit floating point format MXFP8 uses, "FN": no infinities): bit 7 sign, bits 6..3
+ * exponent with bias 7, bits 2..0 mantissa. An exponent field of zero is the subnormal 0.m * 2^-6;
+ * S.1111.111 is NaN; the largest finite magnitude is 1.75 * 2^8 = 448. */
+double oracle_e4m3_value(int code) {
+  int sign = (code >> 7) & 1;
+  int expo = (code >> 3) & 15;
+  int mant = code & 7;
+  double mag;
+  if (expo == 15 && mant == 7) return NAN;
+  if (expo == 0)
+    mag = ldexp((double)mant / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)mant / 8.0, expo - 7);
+  return sign ? -mag : mag;
+}
+
+/* The nearest representable magnitude of |v| (ties to even) on a grid with `mbits` mantissa bits,
+ * smallest normal exponent emin and largest finite magnitude vmax (saturating there). */
+static double round_to_grid(double a, int mbits, int emin, double vmax) {
+  int e;
+  if (a == 0.0) return 0.0;
+  frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int ex = e - 1;
+  if (ex < emin) ex = emin; /* subnormal range: the spacing of the smallest binade */
+  double ulp = ldexp(1.0, ex - mbits);
+  double r = nearbyint(a / ulp) * ulp; /* default rounding: ties to even */
+  return r > vmax ? vmax : r;
+}
+
+/* E4M3 code nearest to a finite v (ties to even), saturating at +-448. */
+int oracle_e4m3_encode(double v) {
+  double r = round_to_grid(fabs(v), 3, -6, 448.0);
+  int code = 0;
+  for (int c = 0; c < 127; ++c)  /* the non-negative codes in increasing value; 127 is NaN */
+    if (oracle_e4m3_value(c) == r) code = c;
+  return (signbit(v) ? 0x80 : 0) | code;
+}
+
+/* E2M1 code nearest to a finite v (ties to even), saturating at +-6. */
+int oracle_e2m1_encode(double v) {
+  double r = round_to_grid(fabs(v), 1, 0, 6.0);
+  int code = 0;
+  for (int c = 0; c < 8; ++c)
+    if (oracle_e2m1_value(c) == r) code = c;
+  return (signbit(v) ? 8 : 0) | code;
+}
+
+double oracle_mx_element(int fmt, int code) {
+  return fmt == ORACLE_ACT_MXFP8 ? oracle_e4m3_value(code) : oracle_e2m1_value(code);
+}
+
+/* One 32-value block quantised to an MX format (OCP MX v1.0, the shared-scale computation): with
+ * amax the largest magnitude, the shared exponent is floor(log2(amax)) - emax_elem, where emax_elem
+ * is the exponent of the element format's largest normal (8 for E4M3, 2 for E2M1), clamped to the
+ * E8M0 range [-127, 127]; each element is v / 2^shared_exp converted to the element format, nearest
+ * with ties to even, saturating at its largest finite magnitude. A block of zeros gets the scale
+ * byte 0 and zero elements. Returns the E8M0 scale byte; codes[0..31] receive the elements. */
+int oracle_mx_quantize_block(const double* v, int fmt, uint8_t* codes) {
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i)
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  if (amax == 0.0) {
+    for (int i = 0; i < 32; ++i) codes[i] = 0;
+    return 0;
+  }
+  int e;
+  frexp(amax, &e);
+  int shared = (e - 1) - (fmt == ORACLE_ACT_MXFP8 ? 8 : 2);
+  if (shared < -127) shared = -127;
+  if (shared > 127) shared = 127;
+  for (int i = 0; i < 32; ++i) {
+    double q = ldexp(v[i], -shared); /* exact: a power-of-two scaling */
+    codes[i] = (uint8_t)(fmt == ORACLE_ACT_MXFP8 ? oracle_e4m3_encode(q) : oracle_e2m1_encode(q));
+  }
+  return shared + 127;
+}
+
+/* Replace v[0 .. 32*nblocks) by its MX-quantised values (the dequantised blocks). */
+static void mx_fake_quantize(double* v, long nblocks, int fmt) {
+  uint8_t codes[32];
+  for (long b = 0; b < nblocks; ++b) {
+    int s = oracle_mx_quantize_block(v + 32 * b, fmt, codes);
+    for (int i = 0; i < 32; ++i) v[32 * b + i] = oracle_mx_element(fmt, codes[i]) * oracle_e8m0_value(s);
+  }
+}
+
 /* ---- routing -------------------------------------------------------------------------------- */
 
 int oracle_route_topk(const float* logits, int T, int E, int k, int score_fn, int renorm,
@@ -201,7 +289,23 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
                      const uint8_t* w2_s, const int32_t* topk_ids, const double* topk_w,
                      double clamp_limit, int nthreads, double* y_pairs, double* out_ref,
                      uint16_t* out_bf16) {
+  return oracle_mxfp4_ffn_act(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, clamp_limit,
+                              ORACLE_ACT_NONE, nthreads, y_pairs, out_ref, out_bf16);
+}
+
+/* The FFN with the activations of both GEMMs quantised to an MX format (act_fmt ORACLE_ACT_MXFP8 or
+ * ORACLE_ACT_MXFP4; ORACLE_ACT_NONE computes the plain FFN): each token's x is quantised per 32-value
+ * block along H before the gate/up projection, and each pair's h, rounded to binary32 first (the
+ * precision in which a GPU computes it, so that both take each element's rounding decision from a
+ * binary32 value), per 32-value block along I before the down projection. Everything else is as
+ * oracle_mxfp4_ffn, in fp64. */
+int oracle_mxfp4_ffn_act(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                         const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                         const uint8_t* w2_s, const int32_t* topk_ids, const double* topk_w,
+                         double clamp_limit, int act_fmt, int nthreads, double* y_pairs, double* out_ref,
+                         uint16_t* out_bf16) {
   if (T < 0 || H < 32 || I < 32 || H % 32 || I % 32 || E < 1 || k < 1) return -2;
+  if (act_fmt != ORACLE_ACT_NONE && act_fmt != ORACLE_ACT_MXFP8 && act_fmt != ORACLE_ACT_MXFP4) return -2;
   long P = (long)T * k;
   const long w13_qe = (long)2 * I * (H / 2), w13_se = (long)2 * I * (H / 32);
   const long w2_qe = (long)H * (I / 2), w2_se = (long)H * (I / 32);
@@ -233,6 +337,7 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
       continue;
     }
     for (int hh = 0; hh < H; ++hh) xd[hh] = oracle_bf16_to_double(x_bf16[t * H + hh]);
+    if (act_fmt != ORACLE_ACT_NONE) mx_fake_quantize(xd, H / 32, act_fmt);
     const uint8_t* q13 = w13_q + e * w13_qe;
     const uint8_t* s13 = w13_s + e * w13_se;
     for (int i = 0; i < I; ++i) {
@@ -246,6 +351,10 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
         u = fmin(fmax(u, -clamp_limit), clamp_limit);
       }
       hv[i] = g / (1.0 + exp(-g)) * u;
+    }
+    if (act_fmt != ORACLE_ACT_NONE) {
+      for (int i = 0; i < I; ++i) hv[i] = (double)(float)hv[i];
+      mx_fake_quantize(hv, I / 32, act_fmt);
     }
     const uint8_t* q2 = w2_q + e * w2_qe;
     const uint8_t* s2 = w2_s + e * w2_se;

@@ -17,12 +17,19 @@ extern "C" {
 #endif
 
 enum { ORACLE_SCORE_SOFTMAX = 0, ORACLE_SCORE_SIGMOID = 1 };
+enum { ORACLE_ACT_NONE = 0, ORACLE_ACT_MXFP8 = 1, ORACLE_ACT_MXFP4 = 2 };
 
 double oracle_e2m1_value(int code);
 double oracle_e8m0_value(int byte);
 double oracle_bf16_to_double(uint16_t bits);
 uint16_t oracle_double_to_bf16(double v);
 double oracle_mxfp4_element(const uint8_t* q, const uint8_t* s, int K, long n, long kk);
+
+double oracle_e4m3_value(int code);
+int oracle_e4m3_encode(double v);
+int oracle_e2m1_encode(double v);
+double oracle_mx_element(int fmt, int code);
+int oracle_mx_quantize_block(const double* v, int fmt, uint8_t* codes);
 
 int oracle_route_topk(const float* logits, int T, int E, int k, int score_fn, int renorm,
                       int32_t* topk_ids, double* topk_w);
@@ -40,6 +47,13 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
                      const uint8_t* w2_s, const int32_t* topk_ids, const double* topk_w,
                      double clamp_limit, int nthreads, double* y_pairs, double* out_ref,
                      uint16_t* out_bf16);
+
+/* As oracle_mxfp4_ffn with the GEMMs' activations quantised to an MX format (act_fmt); see the .c. */
+int oracle_mxfp4_ffn_act(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                         const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                         const uint8_t* w2_s, const int32_t* topk_ids, const double* topk_w,
+                         double clamp_limit, int act_fmt, int nthreads, double* y_pairs, double* out_ref,
+                         uint16_t* out_bf16);
 
 /* Router logits f64[T,E] = x . w^T for bfloat16 x[T,H] and w[E,H] (fp64, h ascending). */
 int oracle_router_logits(const uint16_t* x_bf16, const uint16_t* w_bf16, int T, int H, int E,

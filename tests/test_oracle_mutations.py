@@ -43,10 +43,25 @@ MUTANTS = {
     "x_decode_shift": ("uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
     "router_last_term_dropped": ("for (long h = 0; h < H; ++h) acc +=", "for (long h = 0; h < H - 1; ++h) acc +="),
     "router_k_reversed": ("oracle_bf16_to_double(wr[h]);", "oracle_bf16_to_double(wr[H - 1 - h]);"),
+    "e4m3_bias": ("mag = ldexp(1.0 + (double)mant / 8.0, expo - 7);", "mag = ldexp(1.0 + (double)mant / 8.0, expo - 8);"),
+    "e4m3_subnormal_exponent": ("mag = ldexp((double)mant / 8.0, -6);", "mag = ldexp((double)mant / 8.0, -7);"),
+    "e4m3_min_normal": ("round_to_grid(fabs(v), 3, -6, 448.0)", "round_to_grid(fabs(v), 3, -7, 448.0)"),
+    "round_ties_away": ("double r = nearbyint(a / ulp) * ulp;", "double r = round(a / ulp) * ulp;"),
+    "e2m1_no_saturation": ("round_to_grid(fabs(v), 1, 0, 6.0)", "round_to_grid(fabs(v), 1, 0, 8.0)"),
+    "mx_emax_fp8": ("(fmt == ORACLE_ACT_MXFP8 ? 8 : 2)", "(fmt == ORACLE_ACT_MXFP8 ? 7 : 2)"),
+    "mx_emax_fp4": ("(fmt == ORACLE_ACT_MXFP8 ? 8 : 2)", "(fmt == ORACLE_ACT_MXFP8 ? 8 : 1)"),
+    "mx_shared_exponent_ceil": ("int shared = (e - 1) - ", "int shared = e - "),
+    "mx_no_low_clamp": ("if (shared < -127) shared = -127;", ";"),
+    "mx_last_element_ignored": ("for (int i = 0; i < 32; ++i)\n    if (fabs(v[i]) > amax)",
+                                "for (int i = 0; i < 31; ++i)\n    if (fabs(v[i]) > amax)"),
+    "mx_block_offset": ("oracle_mx_quantize_block(v + 32 * b, fmt, codes)", "oracle_mx_quantize_block(v, fmt, codes)"),
+    "x_not_quantised": ("if (act_fmt != ORACLE_ACT_NONE) mx_fake_quantize(xd, H / 32, act_fmt);", ";"),
+    "h_not_quantised": ("      mx_fake_quantize(hv, I / 32, act_fmt);", ";"),
+    "h_not_rounded_to_binary32": ("hv[i] = (double)(float)hv[i];", "hv[i] = hv[i];"),
 }
 
 PIN_MODULES = ["test_oracle_formats.py", "test_oracle_route.py", "test_oracle_group.py", "test_oracle_ffn.py",
-               "test_oracle_router.py"]
+               "test_oracle_router.py", "test_oracle_act_quant.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
