@@ -31,13 +31,16 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 LLC_BYTES = 256 << 20           # MI355X Infinity Cache
 METRIC = "µs/MoE layer + weight-stream GB/s (% HBM peak) at M=8 decode, 1 GPU"
 
-# (name, workload, ffn flags, single launch) measured after the headline, fewer steps each, no CPU
-# baseline
-OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0, False), ("decode_m2", "decode_m2", 0, False),
-                   ("decode_m8_unfused", "decode_m8", 1, False), ("m1024", "m1024", 0, False),
-                   ("decode_c1_single_launch", "decode_c1", 0, True),
-                   ("decode_m2_single_launch", "decode_m2", 0, True),
-                   ("decode_m8_single_launch", "decode_m8", 0, True))
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (also E4M3 x E2M1 on the scaled MFMA)
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
+# (name, workload, ffn flags, single launch, activation format) measured after the headline, fewer
+# steps each, no CPU baseline. Activation format 1 / 2: the W4A8 / W4A4 FFN (moe_mxfp4_ffn_mx).
+OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0, False, 0), ("decode_m2", "decode_m2", 0, False, 0),
+                   ("decode_m8_unfused", "decode_m8", 1, False, 0), ("m1024", "m1024", 0, False, 0),
+                   ("m1024_w4a8", "m1024", 0, False, 1), ("m1024_w4a4", "m1024", 0, False, 2),
+                   ("decode_c1_single_launch", "decode_c1", 0, True, 0),
+                   ("decode_m2_single_launch", "decode_m2", 0, True, 0),
+                   ("decode_m8_single_launch", "decode_m8", 0, True, 0))
 
 
 def log(msg: str):
@@ -53,6 +56,8 @@ def parse():
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="which timing is reported as value (both are measured)")
     ap.add_argument("--flags", type=int, default=0, help="moe_mxfp4_ffn flags (1 = unfused gate/up)")
+    ap.add_argument("--act", type=int, default=0, choices=(0, 1, 2),
+                    help="headline FFN with MX activations: 1 = W4A8 (MXFP8), 2 = W4A4 (MXFP4)")
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough for cold weights)")
     ap.add_argument("--small-m-max", type=int, default=-1,
                     help="launch-table threshold override (moe_ffn_options.small_m_max; -1 = the library's table)")
@@ -129,10 +134,11 @@ class Env:
 
 
 def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_max: int = -1,
-                  replicas_override: int = 0, warm: bool = False, single: bool = False) -> dict:
+                  replicas_override: int = 0, warm: bool = False, single: bool = False, act: int = 0) -> dict:
     """Eager (per-stage HIP events) and graph (L layers per hipGraph, timed replays) timings of one
     layer workload with cold weights; optionally the warm-weight eager time. `single`: the layer as
-    one moe_layer_decode launch (no stages: the launch is the whole layer)."""
+    one moe_layer_decode launch (no stages: the launch is the whole layer). `act` 1 / 2: the FFN with
+    MXFP8 / MXFP4 activations (moe_mxfp4_ffn_mx)."""
     np, torch, moe, moe_synth = env.np, env.torch, env.moe, env.moe_synth
     stream = env.stream
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
@@ -147,7 +153,8 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
                           for _ in range(R - 1)]
     x = env.dev(inp["x"].view(np.int16)).view(torch.bfloat16)
     logits = env.dev(inp["logits"])
-    layer = moe.MoELayer(first, k, T, cfg.score_fn, cfg.renorm, cfg.clamp, flags, single_launch=single)
+    layer = moe.MoELayer(first, k, T, cfg.score_fn, cfg.renorm, cfg.clamp, flags, single_launch=single,
+                         act_format=act)
     base_opts = moe.ffn_options(small_m_max=small_m_max)
     torch.cuda.synchronize()
     log(f"{cfg.name}: {R} weight replicas of {replica_bytes / 1e9:.2f} GB on device")
@@ -164,7 +171,7 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
     res = dict(cfg=cfg, flags=flags, R=R, inp=inp, n_active=n_active, weight_bytes=n_active * per_expert,
                gateup_bytes=n_active * 2 * I * (H // 2 + H // 32), flops=2 * T * k * 3 * H * I,
                gateup_flops=2 * T * k * 2 * I * H,
-               plan=moe.ffn_plan(T, H, I, E, k, flags, base_opts), steps=steps, single=single)
+               plan=moe.ffn_plan(T, H, I, E, k, flags, base_opts), steps=steps, single=single, act=act)
 
     # eager: per-step HIP events on the stream the kernels run on: around the whole layer (recorded
     # here) and around the gate_up, down and combine stages (recorded by the library)
@@ -265,6 +272,14 @@ def roofline_of(res: dict) -> dict:
                 "kernel": "layer_decode_kernel (route, group, gate_up, down, combine in one launch)",
                 "bytes_per_launch": res["weight_bytes"], "avg_launch_us": round(mean_s * 1e6, 2)}
     gateup_mean_s = statistics.fmean(res["stage_us"][0]) / 1e6
+    if res["act"]:
+        peak = FP8_MFMA_PEAK_TFLOPS if res["act"] == 1 else FP4_MFMA_PEAK_TFLOPS
+        achieved = res["gateup_flops"] / gateup_mean_s / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "mx_gemm_kernel gate_up (block-scaled MFMA, " +
+                          ("E4M3" if res["act"] == 1 else "E2M1") + " activations x E2M1 weights)",
+                "flops_per_launch": res["gateup_flops"], "avg_launch_us": round(gateup_mean_s * 1e6, 2)}
     large = plan["launch_large"]
     mfma_bound = cfg.name == "m1024"
     if mfma_bound:
@@ -332,7 +347,9 @@ def summary(res: dict, use_graph: bool) -> dict:
         "config": {"workload": workload_name(res["cfg"]), "flags": res["flags"], "weight_replicas": res["R"],
                    "small_m_max": res["plan"]["small_m_max"],
                    "path": "moe_layer_decode (one launch)" if res["single"] else
-                           "moe_route_group + moe_mxfp4_ffn (multi-launch)"},
+                           ("moe_route_group + moe_mxfp4_ffn_mx (" + ("W4A8: MXFP8" if res["act"] == 1 else
+                                                                      "W4A4: MXFP4") + " activations)")
+                           if res["act"] else "moe_route_group + moe_mxfp4_ffn (multi-launch)"},
     }
 
 
@@ -533,7 +550,7 @@ def main():
     cfg = env.moe_synth.CONFIGS[args.config]
 
     res = measure_layer(env, cfg, args.flags, args.steps, args.warmup, args.small_m_max, args.replicas, warm=True,
-                        single=args.single_launch)
+                        single=args.single_launch, act=args.act)
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -545,7 +562,8 @@ def main():
     med = statistics.median
     log(f"warm weights: median {med(res['warm_us']):.1f} us/layer eager; read probe {probe:.0f} GB/s")
     router = router_timing(env, cfg, res["x"])
-    forward = forward_timing(env, cfg, args.steps) if args.flags == 0 and not args.single_launch else None
+    forward = (forward_timing(env, cfg, args.steps) if args.flags == 0 and not args.single_launch and not args.act
+               else None)
 
     use_graph = args.mode == "graph" and res["graph_s"] is not None
     s = summary(res, use_graph)
@@ -555,11 +573,11 @@ def main():
 
     others = {}
     if not args.no_others:
-        for name, wl, flags, single in OTHER_WORKLOADS:
-            if wl == cfg.name and flags == args.flags and single == args.single_launch:
+        for name, wl, flags, single, act in OTHER_WORKLOADS:
+            if wl == cfg.name and flags == args.flags and single == args.single_launch and act == args.act:
                 continue
             o = measure_layer(env, env.moe_synth.CONFIGS[wl], flags, args.other_steps, max(5, args.warmup // 2),
-                              single=single)
+                              single=single, act=act)
             others[name] = summary(o, True)
             others[name]["steps"] = args.other_steps
             del o

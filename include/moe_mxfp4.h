@@ -333,6 +333,70 @@ int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags,
                        const moe_ffn_options* opts /*[host]*/, moe_ffn_plan* plan /*[host]*/);
 
 /*
+ * Activation-quantised expert feed-forward (W4A8 / W4A4).
+ * (The FP4 activation-quantise step of the FP4 GEMM path named in "Chunk 8.0", its summary;
+ * read as OCP Microscaling Formats (MX) v1.0 blocks: 32 values along the reduction axis sharing an
+ * E8M0 scale, with MXFP8 E4M3 or MXFP4 E2M1 elements.)
+ *
+ * A block's scale byte is floor(log2 amax) - emax + 127 (emax = 8 for E4M3, 2 for E2M1; amax the
+ * block's largest magnitude), clamped to [0, 254]; each element is v / 2^(byte - 127) rounded to the
+ * nearest element value (ties to even), saturating at +-448 (E4M3) or +-6 (E2M1); a zero block gets
+ * byte 0. A value that rounds to zero keeps its sign bit.
+ */
+enum { MOE_ACT_MXFP8 = 1, MOE_ACT_MXFP4 = 2 };
+
+/*
+ * moe_mx_quantize — quantise bfloat16 rows to MX blocks.
+ *   x_bf16        [dev] u16[rows, cols], 16-byte aligned; cols % 32 == 0, rows * cols < 2^31
+ *   act_format    MOE_ACT_MXFP8 or MOE_ACT_MXFP4
+ *   codes         [dev] u8[rows, cols] (E4M3 bytes) or u8[rows, cols / 2] (two E2M1 codes per byte, the
+ *                 even element in the low nibble), 16-byte aligned (written)
+ *   scales        [dev] u8[rows, cols / 32] (written)
+ * The codes and bytes are exact functions of x (no rounding but the element rounding defined above).
+ */
+int moe_mx_quantize(const uint16_t* x_bf16, int rows, int cols, int act_format, uint8_t* codes,
+                    uint8_t* scales, void* stream);
+
+size_t moe_mxfp4_ffn_mx_workspace_size(int T, int H, int I, int E, int k, int act_format);  /* 0 if invalid */
+
+/*
+ * moe_mxfp4_ffn_mx — moe_mxfp4_ffn with both GEMMs' activations quantised to MX blocks: x per 32
+ * values along H before gate_up, h per 32 values along I before down (h is computed in fp32 and its
+ * codes are decided from that value). The GEMMs run the gfx950 block-scaled MFMA directly on the
+ * MXFP4 weights and the activation codes (fp32 accumulation); every active expert runs on 256-row
+ * tiles, so this is the large-batch variant (decode batches waste most of each tile). The result is
+ * that of the FFN on the quantised activations, not of moe_mxfp4_ffn: the quantisation error is part
+ * of the method. Deterministic (repeated calls give bitwise-identical outputs).
+ *   arguments as moe_mxfp4_ffn (no active list or flags), plus
+ *   act_format                   MOE_ACT_MXFP8 (W4A8) or MOE_ACT_MXFP4 (W4A4)
+ *   w13_s, w2_s                  4-byte aligned (in addition to moe_mxfp4_ffn's alignments)
+ *   workspace, ws_bytes          [dev] at least moe_mxfp4_ffn_mx_workspace_size(...) bytes, 256-byte
+ *                                aligned; contents on entry do not matter
+ *   opts                         NULL, or per-call options of which only the stage events are used
+ *                                (gate_up: the gate_up GEMM after the x quantisation; down; combine)
+ * Limits: as moe_mxfp4_ffn, and H % 128 == 0, I % 128 == 0 (MOE_ERR_SHAPE otherwise); act_format
+ * otherwise is MOE_ERR_UNSUPPORTED.
+ */
+int moe_mxfp4_ffn_mx(const uint16_t* x_bf16, int T, int H, int I, int E, int k, const uint8_t* w13_q,
+                     const uint8_t* w13_s, const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_w,
+                     const int32_t* counts, const int32_t* offsets, const int32_t* sorted_pair,
+                     const int32_t* pair_pos, float clamp_limit, int act_format, uint16_t* out_bf16,
+                     void* workspace, size_t ws_bytes, const moe_ffn_options* opts, void* stream);
+
+/*
+ * moe_mxfp4_ffn_mx_h_offsets — where moe_mxfp4_ffn_mx leaves the quantised h in its workspace.
+ * After a call completes (and until the workspace is reused), h's codes u8[T*k, I] (E4M3) or
+ * u8[T*k, I/2] (E2M1, even element in the low nibble) start at byte *codes_offset of the workspace
+ * and its scale bytes u8[T*k, I/32] at *scales_offset, rows in the grouping's sorted order (row
+ * pair_pos[p] holds pair p). For inspecting the decisions the GPU took (e.g. against a reference
+ * quantiser); the call itself does not need it. Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (the sizes
+ * moe_mxfp4_ffn_mx rejects).
+ */
+int moe_mxfp4_ffn_mx_h_offsets(int T, int H, int I, int E, int k, int act_format, size_t* codes_offset,
+                               size_t* scales_offset);
+
+
+/*
  * moe_layer_decode — the whole layer for decode batches in ONE kernel launch: router top-k and
  * renormalisation (as moe_route_topk), grouping, gate_up + SwiGLU, down and the weighted combine
  * (as moe_mxfp4_ffn), from logits to out. The pages point at persistent kernels and at merging

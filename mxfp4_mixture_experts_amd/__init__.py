@@ -27,6 +27,8 @@ SCORE_SIGMOID = 1
 UNFUSED_GATE_UP = 1
 FORCE_SMALL_M = 2
 FORCE_LARGE_M = 4
+ACT_MXFP8 = 1  # W4A8: activations as MXFP8 (E4M3) blocks
+ACT_MXFP4 = 2  # W4A4: activations as MXFP4 (E2M1) blocks
 STAGE_GATE_UP = 0
 STAGE_DOWN = 1
 STAGE_COMBINE = 2
@@ -121,6 +123,16 @@ def load_library(path: str | None = None):
     lib.moe_layer_decode.argtypes = [V, V, i, i, i, i, i, i, i, V, V, V, V, ctypes.c_float, V, V, V, V,
                                      ctypes.c_size_t, V]
     lib.moe_layer_decode.restype = i
+    lib.moe_mx_quantize.argtypes = [V, i, i, i, V, V, V]
+    lib.moe_mx_quantize.restype = i
+    lib.moe_mxfp4_ffn_mx_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.moe_mxfp4_ffn_mx_workspace_size.restype = ctypes.c_size_t
+    lib.moe_mxfp4_ffn_mx.argtypes = [V, i, i, i, i, i, V, V, V, V, V, V, V, V, V, ctypes.c_float, i, V, V,
+                                     ctypes.c_size_t, ctypes.POINTER(FfnOptions), V]
+    lib.moe_mxfp4_ffn_mx.restype = i
+    lib.moe_mxfp4_ffn_mx_h_offsets.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t),
+                                               ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_mxfp4_ffn_mx_h_offsets.restype = i
     lib.moe_ffn_options_init.argtypes = [ctypes.POINTER(FfnOptions)]
     lib.moe_ffn_options_init.restype = None
     lib.moe_mxfp4_ffn_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(FfnOptions), ctypes.POINTER(FfnPlan)]
@@ -412,6 +424,71 @@ def mxfp4_ffn_noalloc(x: torch.Tensor, w: Mxfp4Weights, topk_w: torch.Tensor, gr
     return out
 
 
+def mx_quantize(x: torch.Tensor, act_format: int = ACT_MXFP8, codes: torch.Tensor | None = None,
+                scales: torch.Tensor | None = None, stream=None):
+    """Quantise bf16 rows x [R, C] (C % 32 == 0) to MX blocks (moe_mx_quantize). Returns (codes u8
+    [R, C] for MXFP8 or [R, C/2] for MXFP4, scale bytes u8 [R, C/32])."""
+    x = _as_bf16(x)
+    R, C = x.shape
+    cw = C if act_format == ACT_MXFP8 else C // 2
+    if codes is None:
+        codes = torch.empty((R, cw), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, max(C // 32, 1)), dtype=torch.uint8, device=x.device)
+    _dev(codes, torch.uint8, "codes")
+    _dev(scales, torch.uint8, "scales")
+    if tuple(codes.shape) != (R, cw) or tuple(scales.shape) != (R, C // 32):
+        raise MoeError(f"codes must be [{R}, {cw}] and scales [{R}, {C // 32}]")
+    _check(load_library().moe_mx_quantize(_ptr(x), R, C, int(act_format), _ptr(codes), _ptr(scales),
+                                          _stream(stream)), "moe_mx_quantize")
+    return codes, scales
+
+
+def ffn_mx_workspace_size(T: int, H: int, I: int, E: int, k: int, act_format: int = ACT_MXFP8) -> int:
+    n = load_library().moe_mxfp4_ffn_mx_workspace_size(T, H, I, E, k, int(act_format))
+    if n == 0:
+        raise MoeError(f"invalid sizes for moe_mxfp4_ffn_mx: T={T} H={H} I={I} E={E} k={k} act={act_format}")
+    return n
+
+
+def ffn_mx_h_view(workspace: torch.Tensor, T: int, H: int, I: int, E: int, k: int, act_format: int = ACT_MXFP8):
+    """Views of the quantised h that moe_mxfp4_ffn_mx left in `workspace`: (codes u8 [T*k, I] or
+    [T*k, I/2], scale bytes u8 [T*k, I/32]), rows in sorted order (moe_mxfp4_ffn_mx_h_offsets)."""
+    co, so = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().moe_mxfp4_ffn_mx_h_offsets(T, H, I, E, k, int(act_format), ctypes.byref(co),
+                                                     ctypes.byref(so)), "moe_mxfp4_ffn_mx_h_offsets")
+    P = T * k
+    cw = I if act_format == ACT_MXFP8 else I // 2
+    codes = workspace[co.value:co.value + P * cw].view(P, cw)
+    scales = workspace[so.value:so.value + P * (I // 32)].view(P, I // 32)
+    return codes, scales
+
+
+def mxfp4_ffn_mx(x: torch.Tensor, w: Mxfp4Weights, topk_w: torch.Tensor, grp: Grouping,
+                 clamp_limit: float = 0.0, act_format: int = ACT_MXFP8, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, options: FfnOptions | None = None,
+                 stream=None) -> torch.Tensor:
+    """The expert FFN with MX-quantised activations (moe_mxfp4_ffn_mx): W4A8 for ACT_MXFP8, W4A4 for
+    ACT_MXFP4. Returns bf16 [T, H]. With a `workspace`, ffn_mx_h_view shows the quantised h after the
+    call. Of `options` only the stage events are used."""
+    x, T, H, k = ffn_check(x, w, topk_w, grp, out, None, 0)
+    E, I = w.E, w.I
+    need = ffn_mx_workspace_size(T, H, I, E, k, act_format)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _dev(workspace, torch.uint8, "workspace")
+    if workspace.numel() < need:
+        raise MoeError(f"workspace holds {workspace.numel()} bytes, needs {need}")
+    _check(load_library().moe_mxfp4_ffn_mx(
+        _ptr(x), T, H, I, E, k, _ptr(w.w13_q), _ptr(w.w13_s), _ptr(w.w2_q), _ptr(w.w2_s), _ptr(topk_w),
+        _ptr(grp.counts), _ptr(grp.offsets), _ptr(grp.sorted_pair), _ptr(grp.pair_pos), float(clamp_limit),
+        int(act_format), _ptr(out), _ptr(workspace), workspace.numel(),
+        ctypes.byref(options) if options is not None else None, _stream(stream)), "moe_mxfp4_ffn_mx")
+    return out
+
+
 def layer_decode_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
     """Bytes of workspace moe_layer_decode needs (0: the shape is not supported by the single launch)."""
     return load_library().moe_layer_decode_workspace_size(T, H, I, E, k)
@@ -510,9 +587,10 @@ class MoELayer:
 
     def __init__(self, weights: Mxfp4Weights, k: int, max_tokens: int, score_fn: int = SCORE_SOFTMAX,
                  renorm: bool = True, clamp_limit: float = 0.0, flags: int = 0, device="cuda",
-                 single_launch: bool = False):
+                 single_launch: bool = False, act_format: int = 0):
         """single_launch: run each forward as one moe_layer_decode launch (decode batches; every
-        token count up to max_tokens must be supported by it)."""
+        token count up to max_tokens must be supported by it). act_format ACT_MXFP8 / ACT_MXFP4: the
+        FFN with MX-quantised activations (moe_mxfp4_ffn_mx; flags must be 0)."""
         weights.validate()
         self.w = weights
         self.k = k
@@ -526,7 +604,11 @@ class MoELayer:
         self.topk_w = torch.empty((max_tokens, k), dtype=torch.float32, device=device)
         self.grp = Grouping.empty(max_tokens, k, E, device)
         self.out = torch.empty((max_tokens, H), dtype=torch.bfloat16, device=device)
-        ws = ffn_workspace_size(max_tokens, H, I, E, k, flags)
+        self.act_format = act_format
+        if act_format and (flags or single_launch):
+            raise MoeError("the activation-quantised FFN takes no flags and has no single-launch form")
+        ws = (ffn_mx_workspace_size(max_tokens, H, I, E, k, act_format) if act_format
+              else ffn_workspace_size(max_tokens, H, I, E, k, flags))
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
         self.single_launch = single_launch
         if single_launch:
@@ -553,5 +635,8 @@ class MoELayer:
             return layer_decode(logits, x, w, self.k, self.score_fn, self.renorm, self.clamp, self.out[:T],
                                 self.layer_ws, ids, tw, stream)
         route_group(logits, self.k, self.score_fn, self.renorm, ids, tw, self.grp, stream)
+        if self.act_format:
+            return mxfp4_ffn_mx(x, w, tw, self.grp, self.clamp, self.act_format, self.out[:T], self.workspace,
+                                options, stream)
         return mxfp4_ffn(x, w, tw, self.grp, self.clamp, self.flags, self.out[:T], self.workspace, options,
                          stream)

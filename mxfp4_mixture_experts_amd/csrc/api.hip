@@ -409,6 +409,119 @@ MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, in
 
 MOE_API size_t moe_mxfp4_ffn_noalloc_max_bytes(void) { return MOE_NOALLOC_SCRATCH_BYTES; }
 
+// ---- activation-quantised FFN (W4A8 / W4A4) ---------------------------------------------------
+
+namespace {
+
+struct MxLayout {
+  size_t sched, xq, xs, hq, hs, y, total;
+  int slots;
+};
+
+bool mx_sizes_ok(int T, int H, int I, int E, int k, int act) {
+  return ffn_sizes_ok(T, H, I, E, k) && H % 128 == 0 && I % 128 == 0 &&
+         (act == MOE_ACT_MXFP8 || act == MOE_ACT_MXFP4);
+}
+
+// tile_e[slots], tile_m0[slots] | x codes | x scales | h codes | h scales | y f32[P, H]
+MxLayout mx_layout(int T, int H, int I, int E, int k, int act) {
+  MxLayout w;
+  const size_t P = (size_t)T * k;
+  const size_t ebits = act == MOE_ACT_MXFP8 ? 8 : 4;
+  w.slots = moe::mx_slots_bound(T, E, k);
+  size_t off = 0;
+  w.sched = off;
+  off = align_up(off + sizeof(int32_t) * 2 * (size_t)w.slots);
+  w.xq = off;
+  off = align_up(off + (size_t)T * H * ebits / 8);
+  w.xs = off;
+  off = align_up(off + (size_t)T * (H / 32));
+  w.hq = off;
+  off = align_up(off + P * I * ebits / 8);
+  w.hs = off;
+  off = align_up(off + P * (I / 32));
+  w.y = off;
+  off = align_up(off + P * H * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+MOE_API int moe_mx_quantize(const uint16_t* x_bf16, int rows, int cols, int act_format, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 32 || cols % 32 || (long)rows * cols > (1L << 31) - 1) return MOE_ERR_SHAPE;
+  if (act_format != MOE_ACT_MXFP8 && act_format != MOE_ACT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x_bf16 || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 16)) return MOE_ERR_UNSUPPORTED;
+  return moe::launch_mx_quant_x(x_bf16, rows, cols, act_format, codes, scales, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API size_t moe_mxfp4_ffn_mx_workspace_size(int T, int H, int I, int E, int k, int act_format) {
+  if (!mx_sizes_ok(T, H, I, E, k, act_format)) return 0;
+  return mx_layout(T, H, I, E, k, act_format).total;
+}
+
+MOE_API int moe_mxfp4_ffn_mx_h_offsets(int T, int H, int I, int E, int k, int act_format, size_t* codes_offset,
+                                      size_t* scales_offset) {
+  if (!codes_offset || !scales_offset) return MOE_ERR_NULL;
+  if (!mx_sizes_ok(T, H, I, E, k, act_format)) return MOE_ERR_SHAPE;
+  const MxLayout wl = mx_layout(T, H, I, E, k, act_format);
+  *codes_offset = wl.hq;
+  *scales_offset = wl.hs;
+  return MOE_OK;
+}
+
+MOE_API int moe_mxfp4_ffn_mx(const uint16_t* x_bf16, int T, int H, int I, int E, int k, const uint8_t* w13_q,
+                             const uint8_t* w13_s, const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_w,
+                             const int32_t* counts, const int32_t* offsets, const int32_t* sorted_pair,
+                             const int32_t* pair_pos, float clamp_limit, int act_format, uint16_t* out_bf16,
+                             void* workspace, size_t ws_bytes, const moe_ffn_options* opts, void* stream) {
+  if (!ffn_sizes_ok(T, H, I, E, k) || H % 128 || I % 128) return MOE_ERR_SHAPE;
+  if (act_format != MOE_ACT_MXFP8 && act_format != MOE_ACT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  moe_ffn_options o;
+  {
+    const int st = read_options(opts, o);
+    if (st != MOE_OK) return st;
+  }
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !w13_q || !w13_s || !w2_q || !w2_s || !topk_w || !counts || !offsets || !sorted_pair ||
+      !pair_pos || !out_bf16 || !workspace)
+    return MOE_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(out_bf16, 16) || !aligned(w13_q, 16) || !aligned(w2_q, 16) ||
+      !aligned(w13_s, 4) || !aligned(w2_s, 4) || !aligned(workspace, kAlign))
+    return MOE_ERR_UNSUPPORTED;
+  const MxLayout wl = mx_layout(T, H, I, E, k, act_format);
+  if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* tile_e = (int32_t*)(ws + wl.sched);
+  int32_t* tile_m0 = tile_e + wl.slots;
+  uint8_t* xq = (uint8_t*)(ws + wl.xq);
+  uint8_t* xs = (uint8_t*)(ws + wl.xs);
+  uint8_t* hq = (uint8_t*)(ws + wl.hq);
+  uint8_t* hs = (uint8_t*)(ws + wl.hs);
+  float* y = (float*)(ws + wl.y);
+  const moe::MxPlan mp = moe::plan_mx(T, H, I, E, k);
+  bool ok = moe::launch_mx_schedule(counts, E, mp, tile_e, tile_m0, s) == hipSuccess;
+  ok &= moe::launch_mx_quant_x(x_bf16, T, H, act_format, xq, xs, s) == hipSuccess;
+  record(o, MOE_STAGE_GATE_UP, true, s);
+  ok &= moe::launch_mx_gateup(mp, act_format, xq, xs, counts, offsets, sorted_pair, k, H, I, tile_e, tile_m0, w13_q,
+                              w13_s, clamp_limit, hq, hs, s) == hipSuccess;
+  record(o, MOE_STAGE_GATE_UP, false, s);
+  record(o, MOE_STAGE_DOWN, true, s);
+  ok &= moe::launch_mx_down(mp, act_format, hq, hs, counts, offsets, k, H, I, tile_e, tile_m0, w2_q, w2_s, y, s) ==
+        hipSuccess;
+  record(o, MOE_STAGE_DOWN, false, s);
+  record(o, MOE_STAGE_COMBINE, true, s);
+  ok &= moe::launch_combine(y, topk_w, pair_pos, T, H, k, out_bf16, nullptr, s) == hipSuccess;
+  record(o, MOE_STAGE_COMBINE, false, s);
+  return ok ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 MOE_API int moe_mxfp4_ffn_noalloc(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
                                   const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                                   const uint8_t* w2_s, const float* topk_w, const int32_t* counts,

@@ -184,6 +184,34 @@ hipError_t launch_layer_decode(const float* logits, const uint16_t* x, int T, in
                                const uint8_t* w2_q, const uint8_t* w2_s, float clamp, int32_t* ids_out,
                                float* w_out, uint16_t* out, void* workspace, int num_cus, hipStream_t stream);
 
+// Activation-quantised GEMMs (W4A8 / W4A4; see ffn_mx.hip): x and h as MX blocks, block-scaled MFMA on
+// the packed weights, 256-row tiles of every active expert.
+constexpr int kActFp8 = 1;  // MXFP8 (E4M3) activations
+constexpr int kActFp4 = 2;  // MXFP4 (E2M1) activations
+constexpr int kMxTileM = 256;
+constexpr int kMxTileN = 256;
+struct MxPlan {
+  int slots;                 // bound on the number of (expert, 256-row tile) pairs
+  int gu_grid_x, dn_grid_x;  // column tiles: 128 h columns (gate_up), 256 output columns (down)
+  int gu_blocks, dn_blocks;  // one-dimensional grids (XCD-interleaved tile order)
+};
+int mx_slots_bound(int T, int E, int k);
+MxPlan plan_mx(int T, int H, int I, int E, int k);
+hipError_t launch_mx_schedule(const int32_t* counts, int E, const MxPlan& mp, int32_t* tile_e, int32_t* tile_m0,
+                              hipStream_t stream);
+// rows x cols bf16 (cols % 32 == 0) -> codes [rows, cols] (E4M3) or [rows, cols/2] (E2M1) and scale
+// bytes [rows, cols/32]
+hipError_t launch_mx_quant_x(const uint16_t* x, int rows, int cols, int act, uint8_t* xq, uint8_t* xs,
+                             hipStream_t stream);
+hipError_t launch_mx_gateup(const MxPlan& mp, int act, const uint8_t* xq, const uint8_t* xs, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* sorted_pair, int k, int H, int I,
+                            const int32_t* tile_e, const int32_t* tile_m0, const uint8_t* w13_q,
+                            const uint8_t* w13_s, float clamp, uint8_t* hq, uint8_t* hs, hipStream_t stream);
+hipError_t launch_mx_down(const MxPlan& mp, int act, const uint8_t* hq, const uint8_t* hs, const int32_t* counts,
+                          const int32_t* offsets, int k, int H, int I, const int32_t* tile_e,
+                          const int32_t* tile_m0, const uint8_t* w2_q, const uint8_t* w2_s, float* y,
+                          hipStream_t stream);
+
 // out[t] = bf16(sum_j topk_w[t, j] * y[pair_pos[t*k + j]])
 hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* pair_pos, int T, int H,
                           int k, uint16_t* out, int* grid_out, hipStream_t stream);

@@ -79,7 +79,7 @@ class OracleLib:
                                          P, P, P]
         lib.oracle_mxfp4_ffn.restype = i
         lib.oracle_mxfp4_ffn_act.argtypes = [P, i, i, i, i, i, P, P, P, P, P, P, ctypes.c_double, i,
-                                             i, P, P, P]
+                                             i, P, P, P, P]
         lib.oracle_mxfp4_ffn_act.restype = i
         lib.oracle_e4m3_value.argtypes = [i]
         lib.oracle_e4m3_value.restype = ctypes.c_double
@@ -193,9 +193,10 @@ class OracleLib:
 
     def mxfp4_ffn(self, x_bf16: np.ndarray, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w,
                   clamp_limit: float = 0.0, nthreads: int = 0, want_pairs: bool = False,
-                  act_fmt: int = ACT_NONE) -> dict:
-        """Expert FFN plus combine. Returns dict(out_ref f64[T,H], out_bf16 u16[T,H], y_pairs?).
-        act_fmt ACT_MXFP8 / ACT_MXFP4 quantises x (per 32 along H) and h (per 32 along I) first."""
+                  act_fmt: int = ACT_NONE, want_h: bool = False) -> dict:
+        """Expert FFN plus combine. Returns dict(out_ref f64[T,H], out_bf16 u16[T,H], y_pairs?, h_pairs?).
+        act_fmt ACT_MXFP8 / ACT_MXFP4 quantises x (per 32 along H) and h (per 32 along I) first;
+        want_h returns each pair's h before that quantisation (f64[T*k, I])."""
         x = _c(x_bf16, np.uint16)
         T, H = x.shape
         w13_q = _c(w13_q, np.uint8)
@@ -213,7 +214,8 @@ class OracleLib:
         out_ref = np.zeros((T, H), np.float64)
         out_bf16 = np.zeros((T, H), np.uint16)
         y = np.zeros((T * k, H), np.float64) if want_pairs else None
-        if act_fmt == ACT_NONE:
+        hp = np.zeros((T * k, I), np.float64) if want_h else None
+        if act_fmt == ACT_NONE and not want_h:
             rc = self.lib.oracle_mxfp4_ffn(_ptr(x), T, H, I, E, k, _ptr(w13_q), _ptr(w13_s),
                                            _ptr(w2_q), _ptr(w2_s), _ptr(ids), _ptr(w),
                                            float(clamp_limit), int(nthreads),
@@ -223,13 +225,16 @@ class OracleLib:
             rc = self.lib.oracle_mxfp4_ffn_act(_ptr(x), T, H, I, E, k, _ptr(w13_q), _ptr(w13_s),
                                                _ptr(w2_q), _ptr(w2_s), _ptr(ids), _ptr(w),
                                                float(clamp_limit), int(act_fmt), int(nthreads),
-                                               _ptr(y) if y is not None else None, _ptr(out_ref),
+                                               _ptr(y) if y is not None else None,
+                                               _ptr(hp) if hp is not None else None, _ptr(out_ref),
                                                _ptr(out_bf16))
         if rc != 0:
             raise ValueError(f"oracle_mxfp4_ffn failed with {rc}")
         res = dict(out_ref=out_ref, out_bf16=out_bf16)
         if y is not None:
             res["y_pairs"] = y
+        if hp is not None:
+            res["h_pairs"] = hp
         return res
 
     def moe_layer(self, logits, x_bf16, w13_q, w13_s, w2_q, w2_s, k, score_fn=SCORE_SOFTMAX,
@@ -321,9 +326,9 @@ def router_logits(x_bf16, w_bf16, nthreads=0):
 
 
 def mxfp4_ffn(x_bf16, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, clamp_limit=0.0, nthreads=0,
-              want_pairs=False, act_fmt=ACT_NONE):
+              want_pairs=False, act_fmt=ACT_NONE, want_h=False):
     return default().mxfp4_ffn(x_bf16, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, clamp_limit,
-                               nthreads, want_pairs, act_fmt)
+                               nthreads, want_pairs, act_fmt, want_h)
 
 
 def moe_layer(logits, x_bf16, w13_q, w13_s, w2_q, w2_s, k, score_fn=SCORE_SOFTMAX, renorm=True,

@@ -290,7 +290,7 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
                      double clamp_limit, int nthreads, double* y_pairs, double* out_ref,
                      uint16_t* out_bf16) {
   return oracle_mxfp4_ffn_act(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, clamp_limit,
-                              ORACLE_ACT_NONE, nthreads, y_pairs, out_ref, out_bf16);
+                              ORACLE_ACT_NONE, nthreads, y_pairs, NULL, out_ref, out_bf16);
 }
 
 /* The FFN with the activations of both GEMMs quantised to an MX format (act_fmt ORACLE_ACT_MXFP8 or
@@ -302,8 +302,8 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
 int oracle_mxfp4_ffn_act(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
                          const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                          const uint8_t* w2_s, const int32_t* topk_ids, const double* topk_w,
-                         double clamp_limit, int act_fmt, int nthreads, double* y_pairs, double* out_ref,
-                         uint16_t* out_bf16) {
+                         double clamp_limit, int act_fmt, int nthreads, double* y_pairs, double* h_pairs,
+                         double* out_ref, uint16_t* out_bf16) {
   if (T < 0 || H < 32 || I < 32 || H % 32 || I % 32 || E < 1 || k < 1) return -2;
   if (act_fmt != ORACLE_ACT_NONE && act_fmt != ORACLE_ACT_MXFP8 && act_fmt != ORACLE_ACT_MXFP4) return -2;
   long P = (long)T * k;
@@ -352,10 +352,12 @@ int oracle_mxfp4_ffn_act(const uint16_t* x_bf16, int T, int H, int I, int E, int
       }
       hv[i] = g / (1.0 + exp(-g)) * u;
     }
-    if (act_fmt != ORACLE_ACT_NONE) {
+    if (act_fmt != ORACLE_ACT_NONE)
       for (int i = 0; i < I; ++i) hv[i] = (double)(float)hv[i];
+    if (h_pairs)
+      for (int i = 0; i < I; ++i) h_pairs[p * (long)I + i] = hv[i];
+    if (act_fmt != ORACLE_ACT_NONE)
       mx_fake_quantize(hv, I / 32, act_fmt);
-    }
     const uint8_t* q2 = w2_q + e * w2_qe;
     const uint8_t* s2 = w2_s + e * w2_se;
     for (int n = 0; n < H; ++n) {

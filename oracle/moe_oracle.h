@@ -48,12 +48,14 @@ int oracle_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
                      double clamp_limit, int nthreads, double* y_pairs, double* out_ref,
                      uint16_t* out_bf16);
 
-/* As oracle_mxfp4_ffn with the GEMMs' activations quantised to an MX format (act_fmt); see the .c. */
+/* As oracle_mxfp4_ffn with the GEMMs' activations quantised to an MX format (act_fmt); see the .c.
+ * h_pairs (optional): f64[T*k, I], each pair's h before its quantisation (rounded to binary32 when
+ * act_fmt quantises). */
 int oracle_mxfp4_ffn_act(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
                          const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                          const uint8_t* w2_s, const int32_t* topk_ids, const double* topk_w,
-                         double clamp_limit, int act_fmt, int nthreads, double* y_pairs, double* out_ref,
-                         uint16_t* out_bf16);
+                         double clamp_limit, int act_fmt, int nthreads, double* y_pairs, double* h_pairs,
+                         double* out_ref, uint16_t* out_bf16);
 
 /* Router logits f64[T,E] = x . w^T for bfloat16 x[T,H] and w[E,H] (fp64, h ascending). */
 int oracle_router_logits(const uint16_t* x_bf16, const uint16_t* w_bf16, int T, int H, int E,

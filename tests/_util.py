@@ -120,3 +120,44 @@ def parity_metrics(out_bf16_bits, ref):
     return dict(max_raw=float(err.max()) / rms if rms > 0 else float(err.max()),
                 max_excess=float((err - own).max()) / rms if rms > 0 else float((err - own).max()),
                 l1=float(err.sum()) / den if den > 0 else float(err.sum()))
+
+
+# ---- MX activation quantisers of the tests (independent of the oracle's) -------------------------
+
+ACT_MXFP8 = 1
+ACT_MXFP4 = 2
+
+
+def e4m3_torch(v):
+    """Nearest E4M3 values (ties to even) of v, saturating at 448, via torch's conversion. torch
+    converts a float64 through binary32, so v must be binary32 values for a single rounding."""
+    import torch
+
+    v = np.clip(np.asarray(v, np.float64), -448.0, 448.0)
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def e2m1_bruteforce(v):
+    """Nearest E2M1 values by a search over the eight magnitudes (a tie, always between neighbouring
+    codes, goes to the even code), saturating at 6."""
+    v = np.asarray(v, np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[..., None] - E2M1_TABLE)
+    cand = d == d.min(axis=-1, keepdims=True)
+    rank = np.where(cand, np.arange(8) % 2, 2)  # an even candidate first, else the only one
+    return np.copysign(E2M1_TABLE[rank.argmin(axis=-1)], v)
+
+
+def mx_fake_quant(v, fmt):
+    """Blocks of 32 along the last axis: scale 2^(floor(log2 amax) - emax), clamped to [-127, 127],
+    then each element rounded by the element quantiser above."""
+    v = np.asarray(v, np.float64)
+    b = v.reshape(-1, 32)
+    amax = np.abs(b).max(axis=1)
+    emax = 8 if fmt == ACT_MXFP8 else 2
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    shared = np.clip(e - 1 - emax, -127, 127).astype(np.float64)
+    X = np.exp2(shared)[:, None]
+    q = e4m3_torch(b / X) if fmt == ACT_MXFP8 else e2m1_bruteforce(b / X)
+    q = np.where(amax[:, None] > 0, q * X, 0.0)
+    return q.reshape(v.shape)

@@ -280,3 +280,43 @@ def test_router_and_layer_forward_validation(lib):
     assert call(ws=V(0x10010)) == -3
     assert call(ws_bytes=need - 1) == -4
     assert call(T=0) == 0
+
+
+def test_mx_quantize_validation(lib):
+    s = None
+    assert lib.moe_mx_quantize(DUMMY, -1, 64, 1, DUMMY, DUMMY, s) == -2
+    assert lib.moe_mx_quantize(DUMMY, 4, 48, 1, DUMMY, DUMMY, s) == -2   # cols % 32
+    assert lib.moe_mx_quantize(DUMMY, 4, 0, 1, DUMMY, DUMMY, s) == -2
+    assert lib.moe_mx_quantize(DUMMY, 4, 64, 3, DUMMY, DUMMY, s) == -3   # unknown format
+    assert lib.moe_mx_quantize(DUMMY, 4, 64, 0, DUMMY, DUMMY, s) == -3
+    assert lib.moe_mx_quantize(None, 0, 64, 2, None, None, s) == 0       # nothing to do
+    assert lib.moe_mx_quantize(None, 4, 64, 1, DUMMY, DUMMY, s) == -1
+    assert lib.moe_mx_quantize(DUMMY, 4, 64, 1, DUMMY, None, s) == -1
+    assert lib.moe_mx_quantize(V(0x1008), 4, 64, 1, DUMMY, DUMMY, s) == -3  # x not 16-byte aligned
+    assert lib.moe_mx_quantize(DUMMY, 4, 64, 2, V(0x1004), DUMMY, s) == -3  # codes not 16-byte aligned
+
+
+def test_ffn_mx_workspace_and_validation(lib):
+    q = lib.moe_mxfp4_ffn_mx_workspace_size
+    assert q(8, 96, 128, 4, 2, 1) == 0      # H % 128
+    assert q(8, 128, 160, 4, 2, 1) == 0     # I % 128
+    assert q(8, 128, 128, 4, 2, 0) == 0     # format
+    assert q(8, 128, 128, 4, 5, 1) == 0     # k > E
+    w8, w4 = q(1024, 7168, 2048, 8, 8, 1), q(1024, 7168, 2048, 8, 8, 2)
+    assert w8 > w4 > 1024 * 8 * 7168 * 4   # y alone is P*H fp32
+    s = None
+
+    def call(T=8, H=256, I=256, E=4, k=2, act=1, x=DUMMY, w13s=DUMMY, ws=DUMMY, wsb=1 << 30, out=DUMMY):
+        return lib.moe_mxfp4_ffn_mx(x, T, H, I, E, k, DUMMY, w13s, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                    DUMMY, ctypes.c_float(0.0), act, out, ws, wsb, None, s)
+    assert call(H=96) == -2
+    assert call(I=160) == -2
+    assert call(k=5) == -2
+    assert call(act=0) == -3
+    assert call(act=3) == -3
+    assert call(T=0, x=None, out=None, ws=None) == 0
+    assert call(x=None) == -1
+    assert call(ws=None) == -1
+    assert call(w13s=V(0x1002)) == -3       # scales not 4-byte aligned
+    assert call(ws=V(0x1080)) == -3         # workspace not 256-byte aligned
+    assert call(wsb=q(8, 256, 256, 4, 2, 1) - 1) == -4

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import moe_synth
-from _gpu import assert_output_parity, dev, run_layer, weights_to_device, x_to_device, out_bits
+from _gpu import assert_output_parity, dev, out_bits, run_layer, sample_tokens, weights_to_device, x_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -153,26 +153,6 @@ def test_threshold_sweep_same_result(orc):
         print(f"threshold {thr}", flush=True)
         g = run_layer(inp, cfg.k, cfg.score_fn, cfg.clamp, 0, w=w, options=moe.ffn_options(small_m_max=thr))
         assert_output_parity(g["out_bf16"], ref["out_ref"], f"thr={thr}")
-
-
-def sample_tokens(ref_ids, grp, T, k, n=20):
-    """Tokens to check at full size: first, last, tokens routed to the most and least loaded active
-    experts, and the tokens at the row-tile edges (rows 0, 63, 64, 127, 128, 255, 256, 511, 512,
-    767, 768 and the last) of the most loaded expert, so every 64-row MFMA tile boundary and every
-    256-row dense tile of it is reached (with one token per row of every expert, as at m1024, of
-    every expert); the rest seeded at random."""
-    counts, offsets, sorted_pair = grp["counts"], grp["offsets"], grp["sorted_pair"]
-    loads = counts[ref_ids].max(axis=1)
-    picks = {0, T - 1, int(np.argmax(loads)), int(np.argmin(loads))}
-    e = int(np.argmax(counts))
-    M = int(counts[e])
-    for r in (0, 63, 64, 127, 128, 255, 256, 511, 512, 767, 768, M - 1):
-        if 0 <= r < M:
-            picks.add(int(sorted_pair[offsets[e] + r]) // k)
-    rng = np.random.default_rng(T)
-    while len(picks) < n:
-        picks.add(int(rng.integers(0, T)))
-    return np.array(sorted(picks))
 
 
 @pytest.mark.parametrize("name", ["medium_zipf", "high_c4", "m1024"])

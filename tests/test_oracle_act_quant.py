@@ -21,46 +21,11 @@ import pytest
 import torch
 
 import moe_synth
-from _util import GOLDEN, E2M1_TABLE, bf16_to_f64, dequant
+from _util import GOLDEN, E2M1_TABLE, bf16_to_f64, dequant, e2m1_bruteforce, e4m3_torch, mx_fake_quant
 
-ACT_MXFP8 = 1
-ACT_MXFP4 = 2
+from _util import ACT_MXFP4, ACT_MXFP8
+
 FMT = {"mxfp8": ACT_MXFP8, "mxfp4": ACT_MXFP4}
-
-
-# ---- the test's own element quantisers ------------------------------------------------------------
-
-def e4m3_torch(v):
-    """Nearest E4M3 values (ties to even) of v, saturating at 448, via torch's conversion. torch
-    converts a float64 through binary32, so v must be binary32 values for a single rounding."""
-    v = np.clip(np.asarray(v, np.float64), -448.0, 448.0)
-    return torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
-
-
-def e2m1_bruteforce(v):
-    """Nearest E2M1 values by a search over the eight magnitudes (a tie, always between neighbouring
-    codes, goes to the even code), saturating at 6."""
-    v = np.asarray(v, np.float64)
-    a = np.minimum(np.abs(v), 6.0)
-    d = np.abs(a[..., None] - E2M1_TABLE)
-    cand = d == d.min(axis=-1, keepdims=True)
-    rank = np.where(cand, np.arange(8) % 2, 2)  # an even candidate first, else the only one
-    return np.copysign(E2M1_TABLE[rank.argmin(axis=-1)], v)
-
-
-def mx_fake_quant(v, fmt):
-    """Blocks of 32 along the last axis: scale 2^(floor(log2 amax) - emax), clamped to [-127, 127],
-    then each element rounded by the element quantiser above."""
-    v = np.asarray(v, np.float64)
-    b = v.reshape(-1, 32)
-    amax = np.abs(b).max(axis=1)
-    emax = 8 if fmt == ACT_MXFP8 else 2
-    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
-    shared = np.clip(e - 1 - emax, -127, 127).astype(np.float64)
-    X = np.exp2(shared)[:, None]
-    q = e4m3_torch(b / X) if fmt == ACT_MXFP8 else e2m1_bruteforce(b / X)
-    q = np.where(amax[:, None] > 0, q * X, 0.0)
-    return q.reshape(v.shape)
 
 
 def test_e2m1_bruteforce_itself_on_ties():
@@ -297,3 +262,24 @@ def test_h_is_rounded_to_binary32_before_its_quantisation(orc):
     assert hq == -2.0 ** -7
     # from fp64, |h| at the block scale lies above the tie 272, so the nearest E4M3 value is 288
     assert 272.0 < abs(h) * 2.0 ** 15 < 288.0 and abs(h) * 2.0 ** 15 - 272.0 > 1e-6
+
+
+def test_h_pairs_output(orc):
+    """The optional h output is each pair's h before quantisation: binary32 values that quantise to the
+    h the down projection uses (checked through y), and, unquantised, the plain FFN's h."""
+    cfg, inp = moe_synth.small_case(3, 64, 64, 4, 2, 12)
+    ids, w = orc.route_topk(inp["logits"], 2)
+    res = orc.mxfp4_ffn(inp["x"], inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"], ids, w, act_fmt=ACT_MXFP8,
+                        want_pairs=True, want_h=True)
+    h = res["h_pairs"]
+    np.testing.assert_array_equal(h, _h32(h))
+    for p in range(h.shape[0]):
+        W2 = dequant(inp["w2_q"][ids.flat[p]], inp["w2_s"][ids.flat[p]])
+        np.testing.assert_allclose(res["y_pairs"][p], W2 @ mx_fake_quant(h[p], ACT_MXFP8), rtol=1e-12,
+                                   atol=1e-12 * np.abs(res["y_pairs"][p]).max())
+    plain = orc.mxfp4_ffn(inp["x"], inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"], ids, w, want_h=True)
+    xd = bf16_to_f64(inp["x"])
+    for p in range(h.shape[0]):
+        W13 = dequant(inp["w13_q"][ids.flat[p]], inp["w13_s"][ids.flat[p]])
+        g, u = W13[:64] @ xd[p // 2], W13[64:] @ xd[p // 2]
+        np.testing.assert_allclose(plain["h_pairs"][p], g / (1 + np.exp(-g)) * u, rtol=1e-12, atol=1e-14)
