@@ -74,7 +74,7 @@ def parse():
 
 # Sources of the weight-streaming kernels (the gate_up stage at decode): the file that defines them and
 # the headers it includes. A counter measurement of those kernels stays valid while these are unchanged.
-STREAMING_SOURCES = ("common.hpp", "ffn_small.hip", "kernels.hpp")
+STREAMING_SOURCES = ("common.hpp", "ffn_small.hip", "kernels.hpp", "stream_dev.hpp")
 
 
 def kernel_source_hash(names=None) -> str:

@@ -4,7 +4,7 @@
 // (v_mfma_scale_f32_32x32x64_f8f6f4), which takes codes and scale bytes as they are: no weight is
 // decoded anywhere.
 //
-//   quantise x   one lane per 32-value block of a token's x: amax, the scale byte
+//   quantise x   four lanes per 32-value block of a token's x: amax, the scale byte
 //                (biased exponent of amax minus the element format's largest exponent, at least 0),
 //                the codes (nearest-even, saturating), written as [T, H] (E4M3) or [T, H/2] (E2M1)
 //                plus [T, H/32] scale bytes;
@@ -88,51 +88,40 @@ __device__ __forceinline__ uint32_t mx_code(float v, float mult) {
 
 // ---- x quantisation ---------------------------------------------------------------------------
 
+// Four consecutive lanes hold one 32-value block, 8 values (16 bytes) each, so a wave's loads and
+// stores are contiguous; the block maximum is a two-step shuffle max within the four lanes.
 template <int AF>
-__global__ __launch_bounds__(256) void mx_quant_x_kernel(const uint16_t* __restrict__ x, int nblocks,
+__global__ __launch_bounds__(256) void mx_quant_x_kernel(const uint16_t* __restrict__ x, int nchunks,
                                                          uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
-  const int i = blockIdx.x * 256 + threadIdx.x;  // block of 32 values, over T * H / 32
-  if (i >= nblocks) return;
-  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)i * 32);
-  uint32_t w[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint4 v = src[q];
-    w[4 * q + 0] = v.x;
-    w[4 * q + 1] = v.y;
-    w[4 * q + 2] = v.z;
-    w[4 * q + 3] = v.w;
-  }
+  const int i = blockIdx.x * 256 + threadIdx.x;  // 8-value chunk, over T * H / 8 (a multiple of 4)
+  const bool valid = i < nchunks;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (valid) v = *reinterpret_cast<const uint4*>(x + (size_t)i * 8);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo_f32(w[j])), fabsf(bf16_hi_f32(w[j]))));
+  for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo_f32(w[j])), fabsf(bf16_hi_f32(w[j]))));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
   const uint32_t sb = mx_scale_byte<AF>(amax);
   const float mult = mx_inv_scale(sb);
-  xs[i] = (uint8_t)sb;
+  if (!valid) return;
+  if ((i & 3) == 0) xs[i >> 2] = (uint8_t)sb;
   if (AF == kActFp8) {
-    uint32_t o[8];
+    uint32_t o[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const uint32_t a = w[2 * j], b = w[2 * j + 1];
       o[j] = mx_code<AF>(bf16_lo_f32(a), mult) | (mx_code<AF>(bf16_hi_f32(a), mult) << 8) |
              (mx_code<AF>(bf16_lo_f32(b), mult) << 16) | (mx_code<AF>(bf16_hi_f32(b), mult) << 24);
     }
-    uint4* dst = reinterpret_cast<uint4*>(xq + (size_t)i * 32);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    *reinterpret_cast<uint2*>(xq + (size_t)i * 8) = make_uint2(o[0], o[1]);
   } else {
-    uint32_t o[4];
+    uint32_t d = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t d = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t v = w[4 * j + q];
-        d |= (mx_code<AF>(bf16_lo_f32(v), mult) | (mx_code<AF>(bf16_hi_f32(v), mult) << 4)) << (8 * q);
-      }
-      o[j] = d;
-    }
-    *reinterpret_cast<uint4*>(xq + (size_t)i * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int q = 0; q < 4; ++q)
+      d |= (mx_code<AF>(bf16_lo_f32(w[q]), mult) | (mx_code<AF>(bf16_hi_f32(w[q]), mult) << 4)) << (8 * q);
+    *reinterpret_cast<uint32_t*>(xq + (size_t)i * 4) = d;
   }
 }
 
@@ -503,12 +492,12 @@ hipError_t launch_mx_schedule(const int32_t* counts, int E, const MxPlan& mp, in
 
 hipError_t launch_mx_quant_x(const uint16_t* x, int T, int H, int act, uint8_t* xq, uint8_t* xs,
                              hipStream_t stream) {
-  const int nblocks = T * (H / 32);
-  const int grid = (nblocks + 255) / 256;
+  const int nchunks = T * (H / 8);
+  const int grid = (nchunks + 255) / 256;
   if (act == kActFp8)
-    mx_quant_x_kernel<kActFp8><<<grid, 256, 0, stream>>>(x, nblocks, xq, xs);
+    mx_quant_x_kernel<kActFp8><<<grid, 256, 0, stream>>>(x, nchunks, xq, xs);
   else
-    mx_quant_x_kernel<kActFp4><<<grid, 256, 0, stream>>>(x, nblocks, xq, xs);
+    mx_quant_x_kernel<kActFp4><<<grid, 256, 0, stream>>>(x, nchunks, xq, xs);
   return hipGetLastError();
 }
 
