@@ -133,6 +133,30 @@ class Env:
         return self.torch.from_numpy(self.np.ascontiguousarray(a)).cuda()
 
 
+def cold_replicas(cfg) -> int:
+    """Weight replicas for cold-weight timing. A layer reads only its active experts (at most
+    min(E, T*k) of them), so the replicas are counted on those bytes: consecutive layers rotate over
+    the replicas, and one full rotation reads at least 8x the 256 MB Infinity Cache, so no layer finds
+    its weights there. (Counted on whole replicas, a one-token layer that reads 20 MB of a 0.32 GB
+    replica would cycle through 140 MB and run from the cache.)"""
+    per_expert = 3 * cfg.H * cfg.I // 2 + 3 * cfg.H * cfg.I // 32
+    layer_bytes = min(cfg.E, cfg.T * cfg.k) * per_expert
+    return max(2, math.ceil(8 * LLC_BYTES / layer_bytes))
+
+
+def capture_rotation(torch, stream, L: int, R: int, layer_fn) -> list:
+    """hipGraphs of L consecutive layers each, enough of them that replaying them in turn walks over
+    all R weight replicas (graph i runs layers i*L .. i*L + L - 1, layer j on replica j mod R)."""
+    graphs = []
+    for gi in range(max(1, math.ceil(R / L))):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for j in range(L):
+                layer_fn((gi * L + j) % R)
+        graphs.append(g)
+    return graphs
+
+
 def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_max: int = -1,
                   replicas_override: int = 0, warm: bool = False, single: bool = False, act: int = 0) -> dict:
     """Eager (per-stage HIP events) and graph (L layers per hipGraph, timed replays) timings of one
@@ -147,7 +171,7 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
     log(f"{cfg.name} flags={flags}: inputs in {time.time() - t0:.1f}s")
     per_expert = 3 * H * I // 2 + 3 * H * I // 32
     replica_bytes = E * per_expert
-    R = replicas_override or max(2, math.ceil((2 << 30) / replica_bytes), math.ceil(8 * LLC_BYTES / replica_bytes))
+    R = replicas_override or cold_replicas(cfg)
     first = moe.Mxfp4Weights(*(env.dev(inp[a]) for a in ("w13_q", "w13_s", "w2_q", "w2_s")))
     replicas = [first] + [moe.Mxfp4Weights(*(t.clone() for t in (first.w13_q, first.w13_s, first.w2_q, first.w2_s)))
                           for _ in range(R - 1)]
@@ -209,32 +233,31 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
             f"{med(res['layer_us']):.1f} us (route+group {med(res['route_group_us']):.1f}, gate_up "
             f"{med(res['stage_us'][0]):.1f}, down {med(res['stage_us'][1]):.1f}, combine {med(res['stage_us'][2]):.1f})")
 
-    # graph: L consecutive layers captured in one hipGraph (layer j on replica j mod R), replayed
-    # `reps` times with each replay timed; K = reps * L layers in all
+    # graph: L consecutive layers captured per hipGraph, graphs in turn covering all R replicas;
+    # `reps` replays (graph r mod G) with each replay timed; K = reps * L layers in all
     reps = next(r for r in (5, 4, 2, 1) if steps % r == 0 and steps // r >= 2) if steps >= 2 else 1
     L = steps // reps
     res.update(graph_s=None, graph_layer_us=[], L=L, reps=reps)
     try:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for j in range(L):
-                layer.forward(x, logits, replicas[j % R], stream=stream, options=base_opts)
+        graphs = capture_rotation(torch, stream, L, R, lambda r: layer.forward(x, logits, replicas[r], stream=stream,
+                                                                              options=base_opts))
         with torch.cuda.stream(stream):
-            g.replay()  # warm-up replay
+            for g in graphs:
+                g.replay()  # warm-up replays
         torch.cuda.synchronize()
         ev_g = [(env.event(), env.event()) for _ in range(reps)]
         t_start = time.perf_counter()
         with torch.cuda.stream(stream):
             for r_ in range(reps):
                 ev_g[r_][0].record(stream)
-                g.replay()
+                graphs[r_ % len(graphs)].replay()
                 ev_g[r_][1].record(stream)
         torch.cuda.synchronize()
         res["graph_s"] = time.perf_counter() - t_start
         res["graph_layer_us"] = [el(*ev_g[r_]) / L for r_ in range(reps)]
         log(f"{cfg.name} graph ({L} layers per graph, {reps} replays): median {med(res['graph_layer_us']):.1f} "
             f"us/layer, range {min(res['graph_layer_us']):.1f}-{max(res['graph_layer_us']):.1f}")
-        del g
+        del graphs
     except Exception as exc:  # capture unsupported: report eager
         log(f"graph capture failed: {exc!r}")
 
@@ -362,8 +385,7 @@ def forward_timing(env: Env, cfg, steps: int) -> dict | None:
     stream = env.stream
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     inp = moe_synth.make_inputs(cfg)
-    per_expert = 3 * H * I // 2 + 3 * H * I // 32
-    R = max(2, math.ceil((2 << 30) / (E * per_expert)), math.ceil(8 * LLC_BYTES / (E * per_expert)))
+    R = cold_replicas(cfg)
     first = moe.Mxfp4Weights(*(env.dev(inp[a]) for a in ("w13_q", "w13_s", "w2_q", "w2_s")))
     replicas = [first] + [moe.Mxfp4Weights(*(t.clone() for t in (first.w13_q, first.w13_s, first.w2_q, first.w2_s)))
                           for _ in range(R - 1)]
@@ -380,23 +402,21 @@ def forward_timing(env: Env, cfg, steps: int) -> dict | None:
         torch.cuda.synchronize()
         reps = 5
         L = max(2, steps // reps)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for j in range(L):
-                fwd(j)
+        graphs = capture_rotation(torch, stream, L, R, fwd)
         with torch.cuda.stream(stream):
-            g.replay()
+            for g in graphs:
+                g.replay()
         torch.cuda.synchronize()
         times = []
-        for _ in range(reps):
+        for r_ in range(reps):
             a, b = env.event(), env.event()
             with torch.cuda.stream(stream):
                 a.record(stream)
-                g.replay()
+                graphs[r_ % len(graphs)].replay()
                 b.record(stream)
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b) * 1e3 / L)
-        del g
+        del graphs
     except Exception as exc:  # capture unsupported
         log(f"layer_forward graph failed: {exc!r}")
         return None

@@ -253,11 +253,11 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
         const uint32_t oq = rr * qrow + kb * 16;
         const uint32_t os = rr * srow + kb;
         if (kGate) {
-          w[d][s][0][b] = ld16(pf.q, oq);
+          w[d][s][0][b] = ld_stream16(pf.q, oq);
           sc[d][s][0][b] = ld8(pf.s, os);
         }
         if (kUp) {
-          w[d][s][1][b] = ld16(pf.q, oq + up_q);
+          w[d][s][1][b] = ld_stream16(pf.q, oq + up_q);
           sc[d][s][1][b] = ld8(pf.s, os + up_s);
         }
       }
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
 #pragma unroll
       for (int b = 0; b < BPL; ++b) {
         const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
-        w[d][s][b] = ld16(pf.q, rr * qrow + kb * 16);
+        w[d][s][b] = ld_stream16(pf.q, rr * qrow + kb * 16);
         sc[d][s][b] = ld8(pf.s, rr * srow + kb);
       }
     }
