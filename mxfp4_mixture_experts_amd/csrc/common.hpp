@@ -89,13 +89,27 @@ __device__ __forceinline__ float clampf(float v, float c) { return fminf(fmaxf(v
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Lane 63's value, uniform (a scalar read of the lane, no LDS traffic); every lane must be active.
+__device__ __forceinline__ int wave_last(int v) { return __builtin_amdgcn_readlane(v, 63); }
+
+// v plus a DPP-moved copy of v; lanes whose source is outside the row or the row mask add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add_i32(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (all active), in registers: within each row of 16 lanes by
+// shifts of 1, 2, 4 and 8 lanes (row_shr), then the last lane of row 0 into row 1 and of row 2 into
+// row 3 (row_bcast:15), then the last lane of row 1 into rows 2 and 3 (row_bcast:31). `lane` is
+// unused (kept for the call sites).
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  (void)lane;
+  v = dpp_add_i32<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add_i32<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add_i32<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add_i32<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add_i32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add_i32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
         tile_m0[slot] = t * kTileM;
       }
     }
-    nt += __shfl(incl, 63, 64);
+    nt += wave_last(incl);
     const int dtiles = dense ? (c + kDenseRows - 1) / kDenseRows : 0;
     const int dincl = wave_inclusive_scan(dtiles, lane);
     for (int t = 0; t < dtiles; ++t) {
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64) void schedule_kernel(const int32_t* __restrict_
         dense_m0[slot] = t * kDenseRows;
       }
     }
-    nd += __shfl(dincl, 63, 64);
+    nd += wave_last(dincl);
   }
   for (int i = ns + lane; i < E; i += 64) small_list[i] = -1;
   for (int i = nt + lane; i < tile_slots; i += 64) tile_e[i] = -1;

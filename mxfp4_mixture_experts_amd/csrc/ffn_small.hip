@@ -104,7 +104,7 @@ __device__ __forceinline__ bool my_items(const int32_t* list, const int* count_p
   for (int base = 0; base < n; base += 64) {
     const int i = base + lane;
     const int c = i < n ? item_cost(counts[list[i]], MT) : 0;
-    total += (long)uniform(__shfl(wave_inclusive_scan(c, lane), 63, 64));
+    total += (long)wave_last(wave_inclusive_scan(c, lane));
   }
   total *= tiles;
   const long p0 = total * b / G, p1 = total * (b + 1) / G;
@@ -131,7 +131,7 @@ __device__ __forceinline__ bool my_items(const int32_t* list, const int* count_p
       const int v = i * tiles + (int)((p1 - excl + c - 1) / (c > 0 ? c : 1));
       end = min(end, uniform(__shfl(v, src, 64)));
     }
-    run += (long)tiles * uniform(__shfl(scan, 63, 64));
+    run += (long)tiles * wave_last(scan);
   }
   ir.begin = begin;
   ir.end = end;

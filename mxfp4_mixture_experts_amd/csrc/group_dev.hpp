@@ -102,7 +102,7 @@ __device__ __forceinline__ void group_pairs(IdPtr ids, int P, int E, int32_t* __
         counts[e] = c;
         offsets[e] = carry + incl - c;
       }
-      carry += __shfl(incl, 63, 64);
+      carry += wave_last(incl);
       const bool act = e < E && c > 0;
       const uint64_t am = __ballot(act);
       if (act) active[acarry + __popcll(am & lanemask_lt(lane))] = e;
@@ -173,7 +173,7 @@ __device__ __forceinline__ void group_pairs_one_wave(IdPtr ids, int P, int E, in
       offsets[e] = carry + incl - c;
       cnt[e] = carry + incl - c;
     }
-    carry += __shfl(incl, 63, 64);
+    carry += wave_last(incl);
     const bool act = e < E && c > 0;
     const uint64_t am = __ballot(act);
     if (act) active[acarry + __popcll(am & lanemask_lt(lane))] = e;

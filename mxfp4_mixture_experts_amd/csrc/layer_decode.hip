@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64 * NW, 1) void layer_decode_kernel(LayerArgs a) {
         L.range_base[s] = carry + incl - rows;
         L.rrow0[s] = carry + incl - rows - first_off;
       }
-      carry += __shfl(incl, 63, 64);
+      carry += wave_last(incl);
     }
     if (lane == 0) L.range_base[R] = carry;
   }
