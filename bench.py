@@ -6,8 +6,8 @@ T=8 tokens, H=4096, I=2048, E=256 experts, top-8 softmax routing (the c8 decode 
 PR #52 node-trace diff measures). Weights are random MXFP4 of that shape, rotated over enough
 device replicas that every step streams them cold from HBM (no step finds its weights in the 256 MB
 last-level cache). Prints one JSON line: the headline workload's numbers, then the same layer
-measurement for the other workloads (one token, two tokens, decode M=8 with the unfused gate/up,
-and per-expert M=1024 on the matrix cores) under "other_workloads".
+measurement for the other workloads (one token, two tokens, decode M=2 and M=8 with the unfused
+gate/up, and per-expert M=1024 on the matrix cores) under "other_workloads".
 
   python bench.py [--steps K] [--warmup W] [--config decode_m8] [--mode graph|eager] [--no-others]
 """
@@ -36,6 +36,7 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
 # (name, workload, ffn flags, single launch, activation format) measured after the headline, fewer
 # steps each, no CPU baseline. Activation format 1 / 2: the W4A8 / W4A4 FFN (moe_mxfp4_ffn_mx).
 OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0, False, 0), ("decode_m2", "decode_m2", 0, False, 0),
+                   ("decode_m2_unfused", "decode_m2", 1, False, 0),
                    ("decode_m8_unfused", "decode_m8", 1, False, 0), ("m1024", "m1024", 0, False, 0),
                    ("m1024_w4a8", "m1024", 0, False, 1), ("m1024_w4a4", "m1024", 0, False, 2),
                    ("decode_c1_single_launch", "decode_c1", 0, True, 0),
