@@ -36,6 +36,8 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
 # (name, workload, ffn flags, single launch, activation format) measured after the headline, fewer
 # steps each, no CPU baseline. Activation format 1 / 2: the W4A8 / W4A4 FFN (moe_mxfp4_ffn_mx).
 OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0, False, 0), ("decode_m2", "decode_m2", 0, False, 0),
+                   ("decode_c1_separate_combine", "decode_c1", 8, False, 0),
+                   ("decode_m2_separate_combine", "decode_m2", 8, False, 0),
                    ("decode_m2_unfused", "decode_m2", 1, False, 0),
                    ("decode_m8_unfused", "decode_m8", 1, False, 0), ("m1024", "m1024", 0, False, 0),
                    ("m1024_w4a8", "m1024", 0, False, 1), ("m1024_w4a4", "m1024", 0, False, 2),
@@ -56,7 +58,7 @@ def parse():
     ap.add_argument("--config", default="decode_m8")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="which timing is reported as value (both are measured)")
-    ap.add_argument("--flags", type=int, default=0, help="moe_mxfp4_ffn flags (1 = unfused gate/up)")
+    ap.add_argument("--flags", type=int, default=0, help="moe_mxfp4_ffn flags (1 = unfused gate/up, 8 = separate combine launch)")
     ap.add_argument("--act", type=int, default=0, choices=(0, 1, 2),
                     help="headline FFN with MX activations: 1 = W4A8 (MXFP8), 2 = W4A4 (MXFP4)")
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough for cold weights)")

@@ -73,7 +73,12 @@ enum {
   /* Force every active expert onto the weight-streaming small-M kernels, whatever its row count. */
   MOE_FORCE_SMALL_M = 2,
   /* Force every active expert onto the MFMA kernels (row-tile, or dense from 256 rows). */
-  MOE_FORCE_LARGE_M = 4
+  MOE_FORCE_LARGE_M = 4,
+  /* Run the weighted combine as a launch of its own. Without it, when only the weight-streaming
+   * kernels run and there are at most 32 routed pairs (T * k) whose activations fit one
+   * workgroup's LDS, the combine is folded into the down launch. The result is bitwise identical
+   * either way; only the launch structure changes. */
+  MOE_SEPARATE_COMBINE = 8
 };
 
 /* Limits checked on the host. */
@@ -251,7 +256,8 @@ size_t moe_mxfp4_ffn_workspace_size(int T, int H, int I, int E, int k, int flags
  *                                an argument, since the grouping carries everything the kernels
  *                                read of them (rows per expert, pair of each row, row of each pair)
  *   clamp_limit                  <= 0 disables the clamp
- *   flags                        MOE_UNFUSED_GATE_UP | MOE_FORCE_SMALL_M | MOE_FORCE_LARGE_M
+ *   flags                        MOE_UNFUSED_GATE_UP | MOE_FORCE_SMALL_M | MOE_FORCE_LARGE_M |
+ *                                MOE_SEPARATE_COMBINE
  *                                (the two FORCE flags are mutually exclusive)
  *   out_bf16                     [dev] u16[T, H]  (written), 16-byte aligned
  *   workspace, ws_bytes          [dev] at least moe_mxfp4_ffn_workspace_size(T, H, I, E, k, flags)
@@ -285,7 +291,9 @@ int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k, con
  *   stage_start/stop  hipEvent_t handles (caller-owned) or NULL: when set, the call records
  *                     stage_start[s] before the first kernel of stage s and stage_stop[s] after its
  *                     last kernel, on the call's stream (stages MOE_STAGE_*), so one stage can be
- *                     timed on the stream its kernels run on.
+ *                     timed on the stream its kernels run on. When the combine is folded into the
+ *                     down launch (moe_ffn_plan.fold_combine), the down stage holds it and the
+ *                     combine stage's two events bracket no work.
  */
 enum { MOE_STAGE_GATE_UP = 0, MOE_STAGE_DOWN = 1, MOE_STAGE_COMBINE = 2, MOE_NUM_STAGES = 3 };
 typedef struct {
@@ -325,8 +333,10 @@ typedef struct {
   int small_down_grid;   /* workgroups of the weight-streaming down launch */
   int large_gateup_grid; /* workgroups of the MFMA gate_up launch */
   int large_down_grid;   /* workgroups of the MFMA down launch */
-  int combine_grid;      /* workgroups of the combine launch */
+  int combine_grid;      /* workgroups of the combine launch (0 when folded into down) */
   int n_launches;        /* kernels enqueued by one call */
+  int fold_combine;      /* 1 if the weighted combine runs inside the weight-streaming down launch
+                            (small_down_grid is then that launch's grid) */
 } moe_ffn_plan;
 
 int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags,

@@ -27,6 +27,7 @@ SCORE_SIGMOID = 1
 UNFUSED_GATE_UP = 1
 FORCE_SMALL_M = 2
 FORCE_LARGE_M = 4
+SEPARATE_COMBINE = 8  # the combine as a launch of its own (never folded into down)
 ACT_MXFP8 = 1  # W4A8: activations as MXFP8 (E4M3) blocks
 ACT_MXFP4 = 2  # W4A4: activations as MXFP4 (E2M1) blocks
 STAGE_GATE_UP = 0
@@ -65,7 +66,7 @@ def ffn_options(small_m_max: int = -1, dense_down_cols: int = 0, stage_events: d
 class FfnPlan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int) for name in (
         "small_m_max", "launch_small", "launch_large", "small_gateup_grid", "small_down_grid",
-        "large_gateup_grid", "large_down_grid", "combine_grid", "n_launches")]
+        "large_gateup_grid", "large_down_grid", "combine_grid", "n_launches", "fold_combine")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

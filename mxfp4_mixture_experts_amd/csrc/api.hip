@@ -80,7 +80,7 @@ bool ffn_sizes_ok(int T, int H, int I, int E, int k) {
   return true;
 }
 
-constexpr int kKnownFlags = MOE_UNFUSED_GATE_UP | MOE_FORCE_SMALL_M | MOE_FORCE_LARGE_M;
+constexpr int kKnownFlags = MOE_UNFUSED_GATE_UP | MOE_FORCE_SMALL_M | MOE_FORCE_LARGE_M | MOE_SEPARATE_COMBINE;
 
 int effective_small_m_max(int T, int flags, const moe_ffn_options& o) {
   if (flags & MOE_FORCE_SMALL_M) return INT_MAX;
@@ -108,17 +108,21 @@ void fill_plan(int T, int H, int I, int E, int k, int flags, const moe_ffn_optio
   plan->launch_large = (flags & MOE_FORCE_LARGE_M) ? 1 : ((flags & MOE_FORCE_SMALL_M) ? 0 : (T > thr));
   if (T == 0) plan->launch_small = plan->launch_large = 0;
   const int gu_launches = (flags & MOE_UNFUSED_GATE_UP) ? 2 : 1;
+  // the combine folds into the streaming down launch when that launch sees every pair
+  const bool fold = plan->launch_small && !plan->launch_large && !(flags & MOE_SEPARATE_COMBINE) &&
+                    moe::down_combine_fits(sp, H, I);
+  plan->fold_combine = fold ? 1 : 0;
   plan->small_gateup_grid = plan->launch_small ? sp.gu_grid : 0;
-  plan->small_down_grid = plan->launch_small ? sp.dn_grid : 0;
+  plan->small_down_grid = plan->launch_small ? (fold ? sp.fold_grid : sp.dn_grid) : 0;
   plan->large_gateup_grid = plan->launch_large ? lp.gu_blocks : 0;
   plan->large_down_grid = plan->launch_large ? lp.dn_blocks : 0;
-  plan->combine_grid = T > 0 ? moe::combine_grid(T, H) : 0;
+  plan->combine_grid = (T > 0 && !fold) ? moe::combine_grid(T, H) : 0;
   // the MFMA kernels need the schedule kernel's tile lists first; the dense kernels (gate_up, the
   // fp16 rewrite of their h rows, down) run only when an expert can have kDenseMinRows rows (an
   // expert has at most T)
   const bool dense = plan->launch_large && T >= moe::kDenseMinRows;
   plan->n_launches = (plan->launch_small ? gu_launches + 1 : 0) + (plan->launch_large ? 3 : 0) +
-                     (dense ? 3 : 0) + (T > 0 ? 1 : 0);
+                     (dense ? 3 : 0) + (T > 0 && !fold ? 1 : 0);
 }
 
 // Device address of `scratch` on the current device, looked up once per device with that device
@@ -380,7 +384,10 @@ MOE_API int moe_mxfp4_ffn_ex(const uint16_t* x_bf16, int T, int H, int I, int E,
   record(o, MOE_STAGE_DOWN, true, s);
   if (dense)
     ok &= moe::launch_dense_h16(dp, r, I, dense_e, dense_m0, h_hi, h_lo, rowf, s) == hipSuccess;
-  if (plan.launch_small)
+  if (plan.launch_small && plan.fold_combine)
+    ok &= moe::launch_small_down_combine(sp, r, list, list_count, pair_pos, topk_w, H, I, w2_q, w2_s, h_hi,
+                                         h_lo, out_bf16, s) == hipSuccess;
+  else if (plan.launch_small)
     ok &= moe::launch_small_down(sp, r, list, list_count, !plan.launch_large, H, I, w2_q, w2_s, h_hi, h_lo, y,
                                  s) == hipSuccess;
   if (plan.launch_large)
@@ -389,8 +396,10 @@ MOE_API int moe_mxfp4_ffn_ex(const uint16_t* x_bf16, int T, int H, int I, int E,
     ok &= moe::launch_dense_down(dp, r, H, I, w2_q, w2_s, dense_e, dense_m0, h_hi, rowf, y, s) == hipSuccess;
   record(o, MOE_STAGE_DOWN, false, s);
 
+  // (folded into the down launch: the combine stage's events bracket no work)
   record(o, MOE_STAGE_COMBINE, true, s);
-  ok &= moe::launch_combine(y, topk_w, pair_pos, T, H, k, out_bf16, nullptr, s) == hipSuccess;
+  if (!plan.fold_combine)
+    ok &= moe::launch_combine(y, topk_w, pair_pos, T, H, k, out_bf16, nullptr, s) == hipSuccess;
   record(o, MOE_STAGE_COMBINE, false, s);
   return ok ? MOE_OK : MOE_ERR_LAUNCH;
 }

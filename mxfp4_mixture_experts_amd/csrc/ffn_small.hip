@@ -594,6 +594,226 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// down with the weighted combine folded in, for few routed pairs (P <= kCombinePairsMax, every active
+// expert on these kernels, P rows of h within the LDS a workgroup can have). A workgroup owns whole
+// tiles of output rows, for every pair: its items are (output-row tile, expert slot), tile outermost,
+// and its range is a contiguous run of whole tiles. Every pair's h blocks are built once, at the start,
+// into LDS in the down kernel's fp16 format (the same conversion, so the same values), the y values of
+// the workgroup's rows stay in LDS, and at the end the workgroup sums topk_w[t, j] * y[pair_pos[t, j]]
+// over j in order in fp32 and rounds once to bfloat16: the combine kernel's arithmetic, bit for bit.
+// The layer then has one launch, and one round trip of y through memory, fewer.
+
+template <int BPL, int MT, int S, int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void small_down_combine_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count,
+    const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int T, int k, int H, int I,
+    int ntiles, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s, int lpr,
+    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, uint16_t* __restrict__ out) {
+  __shared__ int counter;
+  __shared__ int s_n;
+  __shared__ int32_t s_e[kCombinePairsMax], s_m[kCombinePairsMax], s_r0[kCombinePairsMax];
+  __shared__ int32_t s_pp[kCombinePairsMax];
+  __shared__ float s_w[kCombinePairsMax];
+  // dynamic LDS: h blocks as fp16 pairs (P * NB * 64 bytes), their inverse scales [P][NB], y [P][NR]
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+
+  const int P = T * k;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int nt0 = (int)((long)wg * ntiles / G), nt1 = (int)((long)(wg + 1) * ntiles / G);
+  if (nt0 >= nt1) return;  // (uniform; the grid has at most ntiles workgroups)
+
+  const int lane = threadIdx.x & 63;
+  const int lg = ilog2(lpr);
+  const int q = lane & (lpr - 1);
+  const int sub = lane >> lg;
+  const int rpw = 64 >> lg;
+  const int NB = I >> 5;
+  const int tile_rows = S * rpw;
+  const int NR = (nt1 - nt0) * tile_rows;  // output rows of this workgroup (past H at the end: not used)
+  const int nbase = nt0 * tile_rows;
+  const uint32_t qrow = (uint32_t)(I >> 1), srow = (uint32_t)NB;
+  const size_t qexp = (size_t)H * qrow, sexp = (size_t)H * srow;
+  const bool k_exact = (NB % lpr) == 0;
+  // quarter i of block kb of row r at h16[(r * 4 + i) * NB + kb]: the lanes of a wave read
+  // consecutive 16-byte words
+  uint4* h16 = reinterpret_cast<uint4*>(dyn);
+  float* hinv_l = reinterpret_cast<float*>(dyn + (size_t)P * NB * 64);
+  float* y_l = hinv_l + (size_t)P * NB;
+
+  // the work list and each pair's weight and row, to LDS (n <= P <= kCombinePairsMax)
+  if (threadIdx.x < 64) {
+    const int n = min(uniform(*list_count), kCombinePairsMax);  // (at most P, by the grouping)
+    if (lane < n) {
+      const int e = list[lane];
+      s_e[lane] = e;
+      s_m[lane] = counts[e];
+      s_r0[lane] = offsets[e];
+    }
+    if (lane < P && lane < kCombinePairsMax) {
+      s_pp[lane] = pair_pos[lane];
+      s_w[lane] = topk_w[lane];
+    }
+    if (lane == 0) {
+      s_n = n;
+      counter = 0;
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  if (n <= 0) return;  // (uniform)
+  const int nitems = (nt1 - nt0) * n;
+  const ItemRange ir{0, nitems};
+
+  uint4 w[D][S][BPL];
+  uint32_t sc[D][S][BPL];
+  int ring_item[D];
+
+  auto prefetch = [&](int d) {
+    ring_item[d] = take_item(&counter, ir);
+    const int it = min(ring_item[d], nitems - 1);
+    const int tl = uniform(it / n);
+    const int slot = uniform(it - tl * n);
+    const int e = uniform(s_e[slot]);
+    const uint8_t* pq = w2_q + (size_t)e * qexp;
+    const uint8_t* ps = w2_s + (size_t)e * sexp;
+    const int n0 = (nt0 + tl) * tile_rows;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint32_t rr = (uint32_t)min(n0 + s * rpw + sub, H - 1);
+#pragma unroll
+      for (int b = 0; b < BPL; ++b) {
+        const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
+        w[d][s][b] = ld_stream16(pq, rr * qrow + kb * 16);
+        sc[d][s][b] = ld8(ps, rr * srow + kb);
+      }
+    }
+  };
+
+  uint32_t hh[MT][BPL][16];  // h blocks as scaled fp16 pairs
+  float hinv[MT][BPL];       // their inverse power-of-two scales
+
+  auto consume = [&](int d) {
+    const int item = ring_item[d];
+    const int tl = uniform(item / n);
+    const int slot = uniform(item - tl * n);
+    const int M = uniform(s_m[slot]);
+    const int row0 = uniform(s_r0[slot]);
+    const int n0 = (nt0 + tl) * tile_rows;
+    const bool full = n0 + tile_rows <= H;
+    for (int m0 = 0; m0 < M; m0 += MT) {
+      const int mc = min(MT, M - m0);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int row = row0 + m0 + min(m, mc - 1);
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+          const int kb = min(q + lpr * b, NB - 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 v = h16[((size_t)row * 4 + i) * NB + kb];
+            hh[m][b][4 * i] = v.x, hh[m][b][4 * i + 1] = v.y, hh[m][b][4 * i + 2] = v.z, hh[m][b][4 * i + 3] = v.w;
+          }
+          hinv[m][b] = hinv_l[(size_t)row * NB + kb];
+        }
+      }
+      float acc[S][MT];
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[s][m] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int nn = n0 + s * rpw + sub;
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+          float scale = e8m0_to_float(sc[d][s][b]);
+          if (!(full && k_exact) && !(nn < H && q + lpr * b < NB)) scale = 0.0f;
+          if (MT == 1 || mc == MT) {
+            uint32_t hs[MT][16];
+            float bs[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              bs[m] = scale * hinv[m][b];
+#pragma unroll
+              for (int i = 0; i < 16; ++i) hs[m][i] = hh[m][b][i];
+            }
+            dot_block_f16s<MT>(w[d][s][b], bs, hs, acc[s]);
+          } else {
+            uint32_t hs[1][16];
+            float bs[1] = {scale * hinv[0][b]};
+            float a1[1];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) hs[0][i] = hh[0][b][i];
+            a1[0] = acc[s][0];
+            dot_block_f16s<1>(w[d][s][b], bs, hs, a1);
+            acc[s][0] = a1[0];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int nn = n0 + s * rpw + sub;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m >= mc) break;
+          const float v = segment_sum(acc[s][m], lpr);
+          if (q == lpr - 1 && nn < H) y_l[(size_t)(row0 + m0 + m) * NR + (nn - nbase)] = v;
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d) prefetch(d);
+  // every pair's h blocks, as the down kernel builds them (after the first weight loads, so both
+  // round trips overlap)
+  for (int i = threadIdx.x; i < P * NB; i += blockDim.x) {
+    const int row = i / NB, kb = i - row * NB;
+    const uint8_t* hib = reinterpret_cast<const uint8_t*>(h_hi + (size_t)row * I) + kb * 64;
+    const uint8_t* lob = reinterpret_cast<const uint8_t*>(h_lo + (size_t)row * I) + kb * 64;
+    uint4 hv[4], lv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hv[j] = ld16(hib, j * 16);
+      lv[j] = ld16(lob, j * 16);
+    }
+    uint32_t blk[16];
+    const float inv = h_planes_to_f16(hv, lv, blk);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      h16[((size_t)row * 4 + j) * NB + kb] = make_uint4(blk[4 * j], blk[4 * j + 1], blk[4 * j + 2], blk[4 * j + 3]);
+    hinv_l[i] = inv;
+  }
+  __syncthreads();
+  bool more = true;
+  while (more) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (more) {
+        if (ring_item[d] >= nitems) {
+          more = false;
+        } else {
+          consume(d);
+          prefetch(d);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // the weighted combine of this workgroup's output rows: out[t, n] = bf16(sum_j w[t, j] * y[pair, n])
+  for (int i = threadIdx.x; i < T * NR; i += blockDim.x) {
+    const int t = i / NR, nn = i - t * NR;
+    const int nr = nbase + nn;
+    if (nr >= H) continue;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) acc = fmaf(s_w[t * k + j], y_l[(size_t)s_pp[t * k + j] * NR + nn], acc);
+    out[(size_t)t * H + nr] = f32_to_bf16_rne(acc);
+  }
+}
+
 template <int MODE>
 hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* list,
                            const int32_t* list_count, int H, int I, const uint8_t* wq,
@@ -651,6 +871,7 @@ SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
   const long gu_items = (long)sp.slots * sp.gu_tiles, dn_items = (long)sp.slots * sp.dn_tiles;
   sp.gu_grid = (int)(gu_items < num_cus ? gu_items : num_cus);
   sp.dn_grid = (int)(dn_items < num_cus ? dn_items : num_cus);
+  sp.fold_grid = sp.dn_tiles < num_cus ? sp.dn_tiles : num_cus;
   sp.gu_block = 256 * gu_waves(sp.gu.bpl, sp.mt_gu);
   sp.dn_block = 256 * dn_waves(sp.dn.bpl, sp.mt_dn);
   return sp;
@@ -745,6 +966,64 @@ hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t
   }
 #undef MOE_DN
 #undef MOE_DN_K
+  return hipGetLastError();
+}
+
+// LDS of the folded down + combine kernel: fp16 h blocks and their scales for every pair, and the y
+// values of one workgroup's output rows for every pair.
+size_t down_combine_lds(const SmallPlan& sp, int H, int I) {
+  const int grid = sp.fold_grid;
+  if (grid <= 0) return 0;
+  const size_t rows = (size_t)((sp.dn_tiles + grid - 1) / grid) * sp.dn_tile;
+  (void)H;
+  return (size_t)sp.P * (I / 32) * 68 + (size_t)sp.P * rows * 4;
+}
+
+bool down_combine_fits(const SmallPlan& sp, int H, int I) {
+  return sp.P >= 1 && sp.P <= kCombinePairsMax && sp.fold_grid > 0 &&
+         down_combine_lds(sp, H, I) <= stage_limit();
+}
+
+hipError_t launch_small_down_combine(const SmallPlan& sp, const Routed& r, const int32_t* list,
+                                     const int32_t* list_count, const int32_t* pair_pos,
+                                     const float* topk_w, int H, int I, const uint8_t* w2_q,
+                                     const uint8_t* w2_s, const uint16_t* h_hi, const uint16_t* h_lo,
+                                     uint16_t* out, hipStream_t stream) {
+  if (!down_combine_fits(sp, H, I)) return hipErrorInvalidValue;
+  const dim3 grid(sp.fold_grid);
+  const int lpr = sp.dn.lpr, ntiles = sp.dn_tiles;
+  const size_t lds = down_combine_lds(sp, H, I);
+#define MOE_DC(BPL, MT)                                                                              \
+  {                                                                                                 \
+    auto kern = small_down_combine_kernel<BPL, MT, down_slots(BPL), down_ring(BPL), 4 * dn_waves(BPL, MT)>; \
+    static std::atomic<bool> lds_attr_set{false};                                                   \
+    if (lds > 65536 && !lds_attr_set.load()) {                                                      \
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                                  \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageMaxBytes) !=   \
+          hipSuccess)                                                                               \
+        return hipErrorInvalidValue;                                                                \
+      lds_attr_set.store(true);                                                                     \
+    }                                                                                               \
+    kern<<<grid, 256 * dn_waves(BPL, MT), lds, stream>>>(r.counts, r.offsets, list, list_count, pair_pos, \
+                                                         topk_w, sp.T, r.k, H, I, ntiles, w2_q, w2_s, lpr, \
+                                                         h_hi, h_lo, out);                           \
+  }
+  switch (sp.dn.bpl) {
+    case 1:
+      if (sp.mt_dn == 2) MOE_DC(1, 2) else MOE_DC(1, 1)
+      break;
+    case 2:
+      if (sp.mt_dn == 2) MOE_DC(2, 2) else MOE_DC(2, 1)
+      break;
+    case 3: MOE_DC(3, 1) break;
+    case 4: MOE_DC(4, 1) break;
+    case 5: MOE_DC(5, 1) break;
+    case 6: MOE_DC(6, 1) break;
+    case 7: MOE_DC(7, 1) break;
+    case 8: MOE_DC(8, 1) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_DC
   return hipGetLastError();
 }
 

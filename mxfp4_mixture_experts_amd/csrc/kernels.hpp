@@ -88,6 +88,7 @@ struct SmallPlan {
   int gu_tile, dn_tile;    // rows per item, one wave's share (gate rows for gate_up, output rows for down)
   int gu_tiles, dn_tiles;  // items per expert
   int gu_grid, dn_grid;    // persistent workgroups (one per CU)
+  int fold_grid;           // workgroups of down with the combine folded in (whole output-row tiles each)
   int gu_block, dn_block;  // threads per workgroup
   int slots;               // bound on the number of experts in the list (min(E, P))
   int T, P;                // tokens, routed pairs
@@ -107,6 +108,17 @@ hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t
                              const int32_t* list_count, bool list_is_active, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const uint16_t* h_hi, const uint16_t* h_lo, float* y,
                              hipStream_t stream);
+
+// Down with the weighted combine folded in (one launch instead of two; results identical to
+// launch_small_down followed by launch_combine, bit for bit). Only for lists holding every active
+// expert, at most kCombinePairsMax routed pairs, and when down_combine_fits.
+constexpr int kCombinePairsMax = 32;
+bool down_combine_fits(const SmallPlan& sp, int H, int I);
+hipError_t launch_small_down_combine(const SmallPlan& sp, const Routed& r, const int32_t* list,
+                                     const int32_t* list_count, const int32_t* pair_pos,
+                                     const float* topk_w, int H, int I, const uint8_t* w2_q,
+                                     const uint8_t* w2_s, const uint16_t* h_hi, const uint16_t* h_lo,
+                                     uint16_t* out, hipStream_t stream);
 
 // bf16-MFMA kernels for experts with more than `small_m_max` rows: tiles of up to 64 rows of one
 // expert; the weight rows are decoded from MXFP4 to bf16 in registers, the activation tile is staged

@@ -24,9 +24,10 @@ def out_bits(out: torch.Tensor) -> np.ndarray:
 
 
 def run_layer(inp: dict, k: int, score_fn: int, clamp: float, flags: int = 0, w=None, renorm=True,
-              options=None, ids=None):
+              options=None, ids=None, topk_w=None):
     """The whole path on the GPU; returns numpy copies of every intermediate the ABI exposes. With
-    `ids` (numpy [T, k]) the router is skipped and those ids are grouped with uniform weights 1/k."""
+    `ids` (numpy [T, k]) the router is skipped and those ids are grouped with the weights `topk_w`
+    (numpy [T, k], as float32), uniform 1/k by default."""
     x = x_to_device(inp["x"])
     w = w if w is not None else weights_to_device(inp)
     E = w.E
@@ -34,7 +35,10 @@ def run_layer(inp: dict, k: int, score_fn: int, clamp: float, flags: int = 0, w=
         ids, tw = moe.route_topk(dev(inp["logits"]), k, score_fn, renorm)
     else:
         ids = dev(np.asarray(ids, np.int32))
-        tw = torch.full(tuple(ids.shape), 1.0 / k, dtype=torch.float32, device="cuda")
+        if topk_w is None:
+            tw = torch.full(tuple(ids.shape), 1.0 / k, dtype=torch.float32, device="cuda")
+        else:
+            tw = dev(np.asarray(topk_w, np.float32))
     grp = moe.group_tokens(ids, E)
     out = moe.mxfp4_ffn(x, w, tw, grp, clamp, flags, options=options)
     torch.cuda.synchronize()

@@ -125,7 +125,7 @@ def test_ffn_pointer_alignment_and_flags(lib):
     assert ffn(lib, out=None) == -1
     assert ffn(lib, x=V(0x1008)) == -3  # x not 16-byte aligned
     assert ffn(lib, ws=V(0x10010)) == -3  # workspace not 256-byte aligned
-    assert ffn(lib, flags=8) == -3  # unknown flag
+    assert ffn(lib, flags=16) == -3  # unknown flag
     assert ffn(lib, flags=2 | 4) == -3  # both FORCE flags
 
 
@@ -152,6 +152,16 @@ def test_launch_plan(lib):
     assert m.ffn_plan(1, 2048, 768, 128, 8)["small_gateup_grid"] <= 8 * 768
     p = m.ffn_plan(8, 4096, 2048, 256, 8, m.UNFUSED_GATE_UP)
     assert p["n_launches"] == 4
+    assert m.ffn_plan(8, 4096, 2048, 256, 8)["fold_combine"] == 0  # 64 pairs: too many to fold
+    # one token, 8 pairs: the combine runs inside the down launch, whose workgroups own whole
+    # output-row tiles (7168 rows in tiles of 4)
+    p = m.ffn_plan(1, 7168, 2048, 256, 8)
+    assert p["fold_combine"] == 1 and p["n_launches"] == 2 and p["combine_grid"] == 0
+    assert p["small_down_grid"] == min(7168 // 4, 256)
+    p = m.ffn_plan(1, 7168, 2048, 256, 8, m.SEPARATE_COMBINE)
+    assert p["fold_combine"] == 0 and p["n_launches"] == 3 and p["combine_grid"] > 0
+    assert m.ffn_plan(1, 7168, 2048, 256, 8, m.UNFUSED_GATE_UP)["n_launches"] == 3
+    assert m.ffn_plan(1, 7168, 2048, 256, 8, m.FORCE_LARGE_M)["fold_combine"] == 0
     p = m.ffn_plan(1024, 7168, 2048, 256, 8)
     # schedule, streaming gate_up + down, row-tile gate_up + down, dense gate_up + h rewrite + down,
     # combine
@@ -226,7 +236,7 @@ def test_noalloc_validation(lib):
     assert call(T=86) == -4           # workspace beyond the scratch
     assert call(T=1024, H=7168) == -4
     assert call(H=4016) == -2
-    assert call(flags=8) == -3
+    assert call(flags=16) == -3
     assert call(T=0) == 0             # nothing to do
 
 

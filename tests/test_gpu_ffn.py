@@ -17,7 +17,11 @@ pytestmark = pytest.mark.gpu
 moe = pytest.importorskip("mxfp4_mixture_experts_amd")
 
 FLAG_SETS = {"default": 0, "small": moe.FORCE_SMALL_M, "large": moe.FORCE_LARGE_M,
-             "unfused": moe.UNFUSED_GATE_UP, "unfused_small": moe.UNFUSED_GATE_UP | moe.FORCE_SMALL_M}
+             "unfused": moe.UNFUSED_GATE_UP, "unfused_small": moe.UNFUSED_GATE_UP | moe.FORCE_SMALL_M,
+             "separate": moe.SEPARATE_COMBINE, "separate_small": moe.SEPARATE_COMBINE | moe.FORCE_SMALL_M}
+# pairs of flag sets whose outputs must be bitwise equal: only the launch structure differs
+SAME_BITS = (("unfused", "default"), ("unfused_small", "small"), ("separate", "default"),
+             ("separate_small", "small"))
 
 
 def oracle_full(orc, inp, cfg):
@@ -36,10 +40,9 @@ def check_full(orc, cfg, inp, flags_names=tuple(FLAG_SETS)):
         np.testing.assert_array_equal(g["sorted_pair"], ref["sorted_pair"])
         assert_output_parity(g["out_bf16"], ref["out_ref"], f"{cfg.name}/{fname}")
         outs[fname] = g["out_bf16"]
-    if "unfused" in outs and "default" in outs:
-        np.testing.assert_array_equal(outs["unfused"], outs["default"])  # fused == unfused bitwise
-    if "unfused_small" in outs and "small" in outs:
-        np.testing.assert_array_equal(outs["unfused_small"], outs["small"])
+    for a, b in SAME_BITS:
+        if a in outs and b in outs:
+            np.testing.assert_array_equal(outs[a], outs[b], err_msg=f"{a} vs {b}")
     return outs
 
 
@@ -52,6 +55,41 @@ def test_configs_full(orc, name):
 def test_decode_m8_full(orc):
     cfg = moe_synth.CONFIGS["decode_m8"]
     check_full(orc, cfg, moe_synth.make_inputs(cfg), ("default", "large", "unfused"))
+
+
+FOLD_CASES = [
+    # T, H, I, E, k, ids of every token (None: routed by the logits): the combine folded into down
+    (1, 96, 160, 6, 1, [2]),                      # one pair; 64-row output tiles, the last ragged
+    (2, 4096, 2048, 8, 8, [0, 0, 1, 0, 2, 0, 0, 7]),  # mixed multiplicities, 16 pairs
+    (4, 256, 8192, 3, 2, None),                   # 4 blocks per lane, 8 pairs, h 139 KB in LDS
+    (32, 224, 96, 40, 1, None),                   # 32 pairs (the most that fold), ragged tiles
+    (16, 512, 256, 4, 2, [3, 3]),                 # 32 rows in one expert, tokens per pass 2
+]
+
+
+@pytest.mark.parametrize("case", FOLD_CASES, ids=lambda c: "T%d_H%d_I%d_E%d_k%d" % c[:5])
+def test_folded_combine(orc, case):
+    """Down with the combine folded in: the same bits as down + the separate combine launch, and the
+    oracle's result within the tolerance."""
+    T, H, I, E, k, row = case
+    cfg, inp = moe_synth.small_case(T, H, I, E, k, 90 + T)
+    if row is None:
+        ids, wts = orc.route_topk(inp["logits"], k, cfg.score_fn, cfg.renorm)
+    else:
+        ids = np.tile(np.array(row, np.int32), (T, 1))
+        wts = np.random.default_rng(T).uniform(0.05, 1.0, (T, k))
+    wts = np.asarray(wts, np.float32).astype(np.float64)  # the weights the GPU is given, exactly
+    ref = orc.mxfp4_ffn(inp["x"], inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"], ids, wts)
+    assert moe.ffn_plan(T, H, I, E, k, moe.FORCE_SMALL_M)["fold_combine"] == 1
+    assert moe.ffn_plan(T, H, I, E, k, moe.FORCE_SMALL_M | moe.SEPARATE_COMBINE)["fold_combine"] == 0
+    w = weights_to_device(inp)
+    outs = {}
+    for fname in ("small", "separate_small"):
+        print(f"folded combine T={T} H={H} I={I} E={E} k={k} flags={fname}", flush=True)
+        g = run_layer(inp, k, 0, 0.0, FLAG_SETS[fname], w=w, ids=ids, topk_w=wts)
+        assert_output_parity(g["out_bf16"], ref["out_ref"], f"fold T{T} I{I}/{fname}")
+        outs[fname] = g["out_bf16"]
+    np.testing.assert_array_equal(outs["small"], outs["separate_small"])
 
 
 CASES = [
