@@ -147,6 +147,41 @@ def cold_replicas(cfg) -> int:
     return max(2, math.ceil(8 * LLC_BYTES / layer_bytes))
 
 
+def library_gemm_reference(env, cfg, iters: int = 20) -> dict:
+    """Context for the MFMA roofline at large per-expert M: the vendor library's bf16 GEMM (torch.bmm,
+    hipBLASLt on ROCm) on the same per-expert shapes as the layer's two GEMMs, with plain bf16
+    operands (no FP4 decode), both operands contiguous, timed on the bench stream. Only for
+    workloads where every expert holds every token (E == k), so the shapes are exact."""
+    torch = env.torch
+    E, M, H, I = cfg.E, cfg.T, cfg.H, cfg.I
+    out = {"note": "torch.bmm bf16 (hipBLASLt), plain bf16 operands, same per-expert GEMM shapes; "
+                   "not part of the layer"}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    with torch.cuda.stream(env.stream):
+        for name, (kdim, ndim) in (("gate_up", (H, 2 * I)), ("down", (I, H))):
+            a = torch.randn(E, M, kdim, device="cuda", dtype=torch.bfloat16, generator=g).contiguous()
+            b = torch.randn(E, kdim, ndim, device="cuda", dtype=torch.bfloat16, generator=g).contiguous()
+            c = torch.empty(E, M, ndim, device="cuda", dtype=torch.bfloat16)
+            for _ in range(5):
+                torch.bmm(a, b, out=c)
+            ev = [env.event() for _ in range(iters + 1)]
+            for i in range(iters):
+                ev[i].record(env.stream)
+                torch.bmm(a, b, out=c)
+                ev[i + 1].record(env.stream)
+            env.stream.synchronize()
+            ts = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(iters))
+            flops = 2.0 * E * M * kdim * ndim
+            med_us = statistics.median(ts)
+            out[name] = {"us_median": round(med_us, 1), "us_min": round(ts[0], 1),
+                         "tflops": round(flops / (med_us * 1e-6) / 1e12, 1),
+                         "pct_bf16_mfma_peak": round(100 * flops / (med_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 1)}
+            del a, b, c
+    log(f"{cfg.name} library bf16 GEMM reference: gate_up {out['gate_up']['us_median']} us "
+        f"({out['gate_up']['tflops']} TFLOP/s), down {out['down']['us_median']} us ({out['down']['tflops']} TFLOP/s)")
+    return out
+
+
 def capture_rotation(torch, stream, L: int, R: int, layer_fn) -> list:
     """hipGraphs of L consecutive layers each, enough of them that replaying them in turn walks over
     all R weight replicas (graph i runs layers i*L .. i*L + L - 1, layer j on replica j mod R)."""
@@ -604,6 +639,8 @@ def main():
             others[name] = summary(o, True)
             others[name]["steps"] = args.other_steps
             del o
+            if name == "m1024":
+                others[name]["library_bf16_gemm"] = library_gemm_reference(env, env.moe_synth.CONFIGS[wl])
 
     rec = {
         "metric": METRIC,
