@@ -48,6 +48,19 @@ RowSplit choose_row_split(int K) {
   return s;
 }
 
+// LDS a workgroup can hold on the current device (at most kStageMaxBytes)
+constexpr size_t kStageMaxBytes = 150 * 1024;
+size_t stage_limit() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) {
+    (void)hipGetLastError();
+    return 65536;
+  }
+  const size_t lim = (size_t)v - 1024;  // the kernel's own LDS variables
+  return lim < kStageMaxBytes ? lim : kStageMaxBytes;
+}
+
 namespace {
 
 using namespace stream_dev;
@@ -197,10 +210,18 @@ __device__ __forceinline__ int take_item(int* counter, const ItemRange& ir) {
 // ---------------------------------------------------------------------------------------------
 // gate_up: an item is S (gate row, up row) slot pairs.
 
-template <int BPL, int MT, int S, int D, int NW, int MODE>
+// STX: all T rows of x and the token of each of the P sorted rows are copied to LDS at the start by
+// the waves that do not compute the workgroup's range (so the copy overlaps that computation and
+// waiting for it never waits for weight loads), and a wave reads its activation slices from there
+// at every change of expert instead of fetching them from L2 behind its weight ring. The host
+// enables it when both fit kXStageBytes + kTokStageBytes.
+constexpr int kXStageBytes = 65536;
+constexpr int kTokStageBytes = 4096;
+
+template <int BPL, int MT, int S, int D, int NW, int MODE, bool STX>
 __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k, int T,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
     int tiles, int weighted, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s,
     int lpr, float clamp, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
@@ -209,8 +230,37 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
   constexpr bool kUp = MODE != kGateOnly;
   __shared__ int counter;
   __shared__ int range[2];
+  extern __shared__ __attribute__((aligned(16))) uint8_t x_stage[];  // STX: x [T][H] bf16, tokens [P]
   ItemRange ir;
   if (threadIdx.x == 0) counter = 0;
+  if constexpr (STX) {
+    if (threadIdx.x >= 64) {  // waves 1..NW-1; wave 0 computes the range meanwhile
+      constexpr int kStagers = 64 * (NW - 1);
+      constexpr int NXL = (kXStageBytes / 16 + kStagers - 1) / kStagers;
+      const int st = threadIdx.x - 64;
+      const int n16 = T * H / 8;
+      const int P = T * k;
+      const uint4* src = reinterpret_cast<const uint4*>(x);
+      // every load is issued (indices clamped into the arrays), so they are in flight together;
+      // only the stores are conditional
+      uint4 v[NXL];
+#pragma unroll
+      for (int j = 0; j < NXL; ++j) v[j] = src[min(st + kStagers * j, n16 - 1)];
+      constexpr int NTL = kTokStageBytes / 4 / kStagers + 1;
+      int tok[NTL];
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) tok[j] = sorted_pair[min(st + kStagers * j, P - 1)];
+      uint4* dst = reinterpret_cast<uint4*>(x_stage);
+#pragma unroll
+      for (int j = 0; j < NXL; ++j)
+        if (st + kStagers * j < n16) dst[st + kStagers * j] = v[j];
+      int32_t* tdst = reinterpret_cast<int32_t*>(x_stage + (size_t)T * H * 2);
+#pragma unroll
+      for (int j = 0; j < NTL; ++j)
+        if (st + kStagers * j < P) tdst[st + kStagers * j] = tok[j] / k;
+    }
+  }
+  // (the barrier inside makes the staged rows visible too)
   if (!my_items_wg(list, list_count, counts, tiles, MT, weighted, range, ir)) return;
 
   const int lane = threadIdx.x & 63;
@@ -282,17 +332,29 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     const bool full = n0 + tile_rows <= I;
     for (int m0 = 0; m0 < cur.M; m0 += MT) {
       const int mc = min(MT, cur.M - m0);
-      if (m0 != cur.a_m0) {  // activation slices of this token chunk (L2 hits)
+      if (m0 != cur.a_m0) {  // activation slices of this token chunk (LDS with STX, else L2 hits)
         cur.a_m0 = m0;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const int t = uniform(sorted_pair[cur.row0 + m0 + min(m, mc - 1)]) / k;
-          const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
+          const int row = cur.row0 + m0 + min(m, mc - 1);
+          if constexpr (STX) {
+            const int t = uniform(reinterpret_cast<const int32_t*>(x_stage + (size_t)T * H * 2)[row]);
+            const uint8_t* xbase = x_stage + (size_t)t * H * 2;
 #pragma unroll
-          for (int b = 0; b < BPL; ++b) {
-            const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
+            for (int b = 0; b < BPL; ++b) {
+              const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xb[m][b][i] = ld16(xbase, kb * 64 + i * 16);
+              for (int i = 0; i < 4; ++i) xb[m][b][i] = *reinterpret_cast<const uint4*>(xbase + kb * 64 + i * 16);
+            }
+          } else {
+            const int t = uniform(sorted_pair[row]) / k;
+            const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+              const uint32_t kb = (uint32_t)min(q + lpr * b, NB - 1);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) xb[m][b][i] = ld16(xbase, kb * 64 + i * 16);
+            }
           }
         }
 #pragma unroll
@@ -814,6 +876,13 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_combine_kernel(
   }
 }
 
+// x and the row tokens in LDS (STX) when they fit the staging bounds and there are at least 8 waves
+// to copy them
+bool gateup_stx(const SmallPlan& sp, int H) {
+  return (size_t)sp.T * H * 2 <= (size_t)kXStageBytes && (size_t)sp.P * 4 <= (size_t)kTokStageBytes &&
+         sp.gu_block >= 512 && (size_t)sp.T * H * 2 + (size_t)sp.P * 4 <= stage_limit();
+}
+
 template <int MODE>
 hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* list,
                            const int32_t* list_count, int H, int I, const uint8_t* wq,
@@ -821,11 +890,31 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
                            float* g_ws, hipStream_t stream) {
   const dim3 grid(sp.gu_grid);
   const int lpr = sp.gu.lpr, tiles = sp.gu_tiles;
-#define MOE_GU(BPL, MT)                                                                          \
-  small_gateup_kernel<BPL, MT, gateup_slots(BPL), gateup_ring(BPL), 4 * gu_waves(BPL, MT), MODE> \
-      <<<grid, 256 * gu_waves(BPL, MT), 0, stream>>>(r.x, r.counts, r.offsets, r.sorted_pair, r.k,   \
-                                                     list, list_count, H, I, tiles, sp.weighted, wq, \
-                                                     ws, lpr, clamp, h_hi, h_lo, g_ws)
+  const bool stx = gateup_stx(sp, H);
+  const size_t lds = stx ? (size_t)sp.T * H * 2 + (size_t)sp.P * 4 : 0;
+#define MOE_GU_K(BPL, MT, STX)                                                                           \
+  {                                                                                                      \
+    auto kern = small_gateup_kernel<BPL, MT, gateup_slots(BPL), gateup_ring(BPL), 4 * gu_waves(BPL, MT), \
+                                    MODE, STX>;                                                          \
+    static std::atomic<bool> lds_attr_set{false};                                                        \
+    if (STX && lds > 65536 && !lds_attr_set.load()) {                                                    \
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                                       \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageMaxBytes) !=        \
+          hipSuccess)                                                                                    \
+        return hipErrorInvalidValue;                                                                     \
+      lds_attr_set.store(true);                                                                          \
+    }                                                                                                    \
+    kern<<<grid, 256 * gu_waves(BPL, MT), STX ? lds : 0, stream>>>(                                      \
+        r.x, r.counts, r.offsets, r.sorted_pair, r.k, sp.T, list, list_count, H, I, tiles, sp.weighted,  \
+        wq, ws, lpr, clamp, h_hi, h_lo, g_ws);                                                           \
+  }
+#define MOE_GU(BPL, MT)          \
+  do {                           \
+    if (stx && 4 * gu_waves(BPL, MT) >= 8) \
+      MOE_GU_K(BPL, MT, true)    \
+    else                         \
+      MOE_GU_K(BPL, MT, false)   \
+  } while (0)
 #define MOE_GU_MT(BPL) \
   if (sp.mt_gu == 2)   \
     MOE_GU(BPL, 2);    \
@@ -844,6 +933,7 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
   }
 #undef MOE_GU_MT
 #undef MOE_GU
+#undef MOE_GU_K
   return hipGetLastError();
 }
 
@@ -904,18 +994,6 @@ hipError_t launch_small_gateup(const SmallPlan& sp, const Routed& r, const int32
 // routing.
 int down_stage_rows(const SmallPlan& sp) { return sp.P; }
 
-// LDS a workgroup can hold on the current device (at most kStageMaxBytes)
-constexpr size_t kStageMaxBytes = 150 * 1024;
-size_t stage_limit() {
-  int dev = 0, v = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) {
-    (void)hipGetLastError();
-    return 65536;
-  }
-  const size_t lim = (size_t)v - 1024;  // the kernel's own LDS variables
-  return lim < kStageMaxBytes ? lim : kStageMaxBytes;
-}
 
 hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t* list,
                              const int32_t* list_count, bool list_is_active, int H, int I,
