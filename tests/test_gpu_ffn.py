@@ -217,6 +217,9 @@ DUP_IDS = [
     (8, 4096, 2048, 8, 8, [0] * 8),                   # one expert with all 64 rows
     (2, 4096, 2048, 8, 8, [0] * 8),                   # 16 rows: all of h fits the LDS (staged down)
     (8, 1024, 512, 8, 8, [0, 0, 0, 1, 1, 2, 4, 0]),   # mixed multiplicities
+    (8, 4096, 2048, 8, 8, [0, 0, 0, 0, 1, 2, 3, 4]),  # h too big for LDS: workgroups within experts 1-4
+                                                      # stage their rows, those in expert 0 (32 rows,
+                                                      # 256 KB) read them from L2
     (300, 256, 128, 3, 2, [1, 1]),                     # 600 rows in one expert: dense kernels
 ]
 
