@@ -101,15 +101,34 @@ __device__ __forceinline__ int item_cost(int M, int MT) { return 3 * ((M + MT - 
 // position p is the first item whose cost interval starts at or after p; every workgroup evaluates
 // it the same way, so the end of one range is the begin of the next.
 __device__ __forceinline__ bool my_items(const int32_t* list, const int* count_ptr,
-                                         const int32_t* counts, int tiles, int MT, int weighted,
-                                         ItemRange& ir) {
+                                         const int32_t* counts, int list_cap, int tiles, int MT,
+                                         int weighted, ItemRange& ir) {
   const int lane = threadIdx.x & 63;
+  // the list's first 64 entries are loaded with its length (entries past the length are stale or
+  // unwritten: clamped into the expert range, never used), so a list of at most 64 experts costs
+  // two dependent round trips: length and entries, then row counts
+  const int e_pre = weighted ? list[min(lane, list_cap - 1)] : 0;
   const int n = uniform(*count_ptr);
   if (n <= 0) return false;
   const int G = gridDim.x, b = blockIdx.x;
   if (!weighted) {  // every expert has the same row count: equal item counts, no count loads
     ir.begin = (int)((long)b * n * tiles / G);
     ir.end = (int)((long)(b + 1) * n * tiles / G);
+    return ir.begin < ir.end;
+  }
+  if (n <= 64) {
+    const int c = lane < n ? item_cost(counts[min(max(e_pre, 0), list_cap - 1)], MT) : 0;
+    const int scan = wave_inclusive_scan(c, lane);
+    const long total = (long)tiles * wave_last(scan);
+    const long p0 = total * b / G, p1 = total * (b + 1) / G;
+    const long incl = (long)tiles * scan, excl = incl - (long)tiles * c;
+    const bool has0 = lane < n && p0 >= excl && p0 < incl;
+    const bool has1 = lane < n && p1 >= excl && p1 < incl;
+    const uint64_t m0 = __ballot(has0), m1 = __ballot(has1);
+    const int v0 = lane * tiles + (int)((p0 - excl + c - 1) / (c > 0 ? c : 1));
+    const int v1 = lane * tiles + (int)((p1 - excl + c - 1) / (c > 0 ? c : 1));
+    ir.begin = m0 ? uniform(__shfl(v0, __ffsll((unsigned long long)m0) - 1, 64)) : n * tiles;
+    ir.end = m1 ? uniform(__shfl(v1, __ffsll((unsigned long long)m1) - 1, 64)) : n * tiles;
     return ir.begin < ir.end;
   }
   // total cost
@@ -155,11 +174,11 @@ __device__ __forceinline__ bool my_items(const int32_t* list, const int* count_p
 // (every wave of the GPU loading the same few lines of the list and the counts at once would queue
 // on those lines). Returns false, in every wave, for an empty range.
 __device__ __forceinline__ bool my_items_wg(const int32_t* list, const int* count_ptr,
-                                            const int32_t* counts, int tiles, int MT, int weighted,
-                                            int* shared_range, ItemRange& ir) {
+                                            const int32_t* counts, int list_cap, int tiles, int MT,
+                                            int weighted, int* shared_range, ItemRange& ir) {
   if (threadIdx.x < 64) {
     ItemRange r{0, 0};
-    if (!my_items(list, count_ptr, counts, tiles, MT, weighted, r)) r = ItemRange{0, 0};
+    if (!my_items(list, count_ptr, counts, list_cap, tiles, MT, weighted, r)) r = ItemRange{0, 0};
     if (threadIdx.x == 0) {
       shared_range[0] = r.begin;
       shared_range[1] = r.end;
@@ -222,7 +241,7 @@ template <int BPL, int MT, int S, int D, int NW, int MODE, bool STX>
 __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k, int T,
-    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int list_cap, int H, int I,
     int tiles, int weighted, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s,
     int lpr, float clamp, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
     float* __restrict__ g_ws) {
@@ -261,7 +280,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     }
   }
   // (the barrier inside makes the staged rows visible too)
-  if (!my_items_wg(list, list_count, counts, tiles, MT, weighted, range, ir)) return;
+  if (!my_items_wg(list, list_count, counts, list_cap, tiles, MT, weighted, range, ir)) return;
 
   const int lane = threadIdx.x & 63;
   const int lg = ilog2(lpr);
@@ -460,7 +479,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
 template <int BPL, int MT, int S, int D, int NW, bool STAGED>
 __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int H, int I,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int list_cap, int H, int I,
     int tiles, int weighted, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s,
     int lpr, const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo,
     float* __restrict__ y) {
@@ -469,7 +488,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t h_stage[];  // STAGED: hi plane, then lo plane
   ItemRange ir;
   if (threadIdx.x == 0) counter = 0;
-  if (!my_items_wg(list, list_count, counts, tiles, MT, weighted, range, ir)) return;
+  if (!my_items_wg(list, list_count, counts, list_cap, tiles, MT, weighted, range, ir)) return;
 
   const int lane = threadIdx.x & 63;
   const int lg = ilog2(lpr);
@@ -669,7 +688,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
 template <int BPL, int MT, int S, int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void small_down_combine_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int list_cap,
     const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int T, int k, int H, int I,
     int ntiles, const uint8_t* __restrict__ w2_q, const uint8_t* __restrict__ w2_s, int lpr,
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, uint16_t* __restrict__ out) {
@@ -706,9 +725,11 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_combine_kernel(
 
   // the work list and each pair's weight and row, to LDS (n <= P <= kCombinePairsMax)
   if (threadIdx.x < 64) {
+    // the list's entries are loaded with its length (entries past it are never used)
+    const int e_pre = list[min(lane, list_cap - 1)];
     const int n = min(uniform(*list_count), kCombinePairsMax);  // (at most P, by the grouping)
     if (lane < n) {
-      const int e = list[lane];
+      const int e = e_pre;
       s_e[lane] = e;
       s_m[lane] = counts[e];
       s_r0[lane] = offsets[e];
@@ -905,7 +926,8 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
       lds_attr_set.store(true);                                                                          \
     }                                                                                                    \
     kern<<<grid, 256 * gu_waves(BPL, MT), STX ? lds : 0, stream>>>(                                      \
-        r.x, r.counts, r.offsets, r.sorted_pair, r.k, sp.T, list, list_count, H, I, tiles, sp.weighted,  \
+        r.x, r.counts, r.offsets, r.sorted_pair, r.k, sp.T, list, list_count, sp.E, H, I, tiles,         \
+        sp.weighted,                                                                                     \
         wq, ws, lpr, clamp, h_hi, h_lo, g_ws);                                                           \
   }
 #define MOE_GU(BPL, MT)          \
@@ -952,6 +974,7 @@ SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
   sp.slots = (int)(P < E ? P : E);
   sp.T = T;
   sp.P = (int)P;
+  sp.E = E;
   sp.mt_gu = (T >= 2 && sp.gu.bpl <= 2) ? 2 : 1;
   sp.mt_dn = (T >= 2 && sp.dn.bpl <= 2) ? 2 : 1;
   // with T <= 2 every expert has one or two rows and costs about the same per item
@@ -1016,7 +1039,7 @@ hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t
         return hipErrorInvalidValue;                                                                  \
       lds_attr_set.store(true);                                                                       \
     }                                                                                                 \
-    kern<<<grid, 256 * dn_waves(BPL, MT), lds, stream>>>(r.counts, r.offsets, list, list_count, H, I,   \
+    kern<<<grid, 256 * dn_waves(BPL, MT), lds, stream>>>(r.counts, r.offsets, list, list_count, sp.E, H, I, \
                                                          tiles, sp.weighted, w2_q, w2_s, lpr, h_hi,    \
                                                          h_lo, y);                                     \
   }
@@ -1082,7 +1105,7 @@ hipError_t launch_small_down_combine(const SmallPlan& sp, const Routed& r, const
         return hipErrorInvalidValue;                                                                \
       lds_attr_set.store(true);                                                                     \
     }                                                                                               \
-    kern<<<grid, 256 * dn_waves(BPL, MT), lds, stream>>>(r.counts, r.offsets, list, list_count, pair_pos, \
+    kern<<<grid, 256 * dn_waves(BPL, MT), lds, stream>>>(r.counts, r.offsets, list, list_count, sp.E, pair_pos, \
                                                          topk_w, sp.T, r.k, H, I, ntiles, w2_q, w2_s, lpr, \
                                                          h_hi, h_lo, out);                           \
   }

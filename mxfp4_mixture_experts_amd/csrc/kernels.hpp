@@ -92,6 +92,7 @@ struct SmallPlan {
   int gu_block, dn_block;  // threads per workgroup
   int slots;               // bound on the number of experts in the list (min(E, P))
   int T, P;                // tokens, routed pairs
+  int E;                   // experts (entries of the work list)
   int mt_gu, mt_dn;        // tokens per pass
   int weighted;            // workgroup ranges weighted by the experts' row counts
 };
