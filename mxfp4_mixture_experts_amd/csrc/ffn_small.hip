@@ -212,11 +212,12 @@ struct Prefetch {
   int slot;                  // expert slot whose bases are cached
   const uint8_t* q;          // that expert's code and scale bases
   const uint8_t* s;
+  int M, row0;               // that expert's row count and first sorted row
 };
 
 // Expert state of the item being consumed.
 struct Current {
-  int slot, e, M, row0, a_m0;
+  int slot, M, row0, a_m0;
 };
 
 // Next item of the workgroup's range for this wave (uniform); >= ir.end once the range is drained.
@@ -297,7 +298,8 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
   uint4 w[D][S][2][BPL];
   uint32_t sc[D][S][2][BPL];
   int ring_item[D];
-  Prefetch pf{-1, w13_q, w13_s};
+  int ring_m[D], ring_r0[D];  // the entry's expert: row count and first row, read when its item is taken
+  Prefetch pf{-1, w13_q, w13_s, 0, 0};
 
   // take an item into ring entry d and issue its loads; rows of a partial last tile are clamped
   // (their results are never stored)
@@ -311,7 +313,11 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
       const int e = uniform(list[slot]);
       pf.q = w13_q + (size_t)e * qexp;
       pf.s = w13_s + (size_t)e * sexp;
+      pf.M = uniform(counts[e]);
+      pf.row0 = uniform(offsets[e]);
     }
+    ring_m[d] = pf.M;
+    ring_r0[d] = pf.row0;
     const int n0 = tile * tile_rows;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     }
   };
 
-  Current cur{-1, -1, 0, 0, -1};
+  Current cur{-1, 0, 0, -1};
   uint4 xb[MT][BPL][4];
 
   auto consume = [&](int d) {
@@ -342,9 +348,8 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     const int tile = uniform(item - slot * tiles);
     if (slot != cur.slot) {  // new expert
       cur.slot = slot;
-      cur.e = uniform(list[slot]);
-      cur.M = uniform(counts[cur.e]);
-      cur.row0 = uniform(offsets[cur.e]);
+      cur.M = ring_m[d];
+      cur.row0 = ring_r0[d];
       cur.a_m0 = -1;
     }
     const int n0 = tile * tile_rows;
@@ -514,7 +519,8 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
   uint4 w[D][S][BPL];
   uint32_t sc[D][S][BPL];
   int ring_item[D];
-  Prefetch pf{-1, w2_q, w2_s};
+  int ring_m[D], ring_r0[D];  // the entry's expert: row count and first row, read when its item is taken
+  Prefetch pf{-1, w2_q, w2_s, 0, 0};
 
   auto prefetch = [&](int d) {
     ring_item[d] = take_item(&counter, ir);
@@ -526,7 +532,11 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
       const int e = uniform(list[slot]);
       pf.q = w2_q + (size_t)e * qexp;
       pf.s = w2_s + (size_t)e * sexp;
+      pf.M = uniform(counts[e]);
+      pf.row0 = uniform(offsets[e]);
     }
+    ring_m[d] = pf.M;
+    ring_r0[d] = pf.row0;
     const int n0 = tile * tile_rows;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -540,7 +550,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     }
   };
 
-  Current cur{-1, -1, 0, 0, -1};
+  Current cur{-1, 0, 0, -1};
   uint32_t hh[MT][BPL][16];  // h blocks as scaled fp16 pairs
   float hinv[MT][BPL];       // their inverse power-of-two scales
 
@@ -550,9 +560,8 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     const int tile = uniform(item - slot * tiles);
     if (slot != cur.slot) {
       cur.slot = slot;
-      cur.e = uniform(list[slot]);
-      cur.M = uniform(counts[cur.e]);
-      cur.row0 = uniform(offsets[cur.e]);
+      cur.M = ring_m[d];
+      cur.row0 = ring_r0[d];
       cur.a_m0 = -1;
     }
     const int n0 = tile * tile_rows;
