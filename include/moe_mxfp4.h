@@ -336,7 +336,9 @@ typedef struct {
   int combine_grid;      /* workgroups of the combine launch (0 when folded into down) */
   int n_launches;        /* kernels enqueued by one call */
   int fold_combine;      /* 1 if the weighted combine runs inside the weight-streaming down launch
-                            (small_down_grid is then that launch's grid) */
+                            (small_down_grid is then that launch's grid); decided from the LDS a
+                            workgroup can have on the current device (64 KB assumed when no device
+                            can be queried), so a plan made without a GPU can differ here */
 } moe_ffn_plan;
 
 int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags,
