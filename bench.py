@@ -33,17 +33,21 @@ METRIC = "µs/MoE layer + weight-stream GB/s (% HBM peak) at M=8 decode, 1 GPU"
 
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (also E4M3 x E2M1 on the scaled MFMA)
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
-# (name, workload, ffn flags, single launch, activation format) measured after the headline, fewer
-# steps each, no CPU baseline. Activation format 1 / 2: the W4A8 / W4A4 FFN (moe_mxfp4_ffn_mx).
-OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0, False, 0), ("decode_m2", "decode_m2", 0, False, 0),
-                   ("decode_c1_separate_combine", "decode_c1", 8, False, 0),
-                   ("decode_m2_separate_combine", "decode_m2", 8, False, 0),
-                   ("decode_m2_unfused", "decode_m2", 1, False, 0),
-                   ("decode_m8_unfused", "decode_m8", 1, False, 0), ("m1024", "m1024", 0, False, 0),
-                   ("m1024_w4a8", "m1024", 0, False, 1), ("m1024_w4a4", "m1024", 0, False, 2),
-                   ("decode_c1_single_launch", "decode_c1", 0, True, 0),
-                   ("decode_m2_single_launch", "decode_m2", 0, True, 0),
-                   ("decode_m8_single_launch", "decode_m8", 0, True, 0))
+# (name, workload, ffn flags, single launch, activation format, from logits) measured after the
+# headline, fewer steps each, no CPU baseline. Activation format 1 / 2: the W4A8 / W4A4 FFN
+# (moe_mxfp4_ffn_mx). From logits: the layer as one moe_layer_from_logits call.
+OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0, False, 0, False), ("decode_m2", "decode_m2", 0, False, 0, False),
+                   ("decode_c1_from_logits", "decode_c1", 0, False, 0, True),
+                   ("decode_m2_from_logits", "decode_m2", 0, False, 0, True),
+                   ("decode_m8_from_logits", "decode_m8", 0, False, 0, True),
+                   ("decode_c1_separate_combine", "decode_c1", 8, False, 0, False),
+                   ("decode_m2_separate_combine", "decode_m2", 8, False, 0, False),
+                   ("decode_m2_unfused", "decode_m2", 1, False, 0, False),
+                   ("decode_m8_unfused", "decode_m8", 1, False, 0, False), ("m1024", "m1024", 0, False, 0, False),
+                   ("m1024_w4a8", "m1024", 0, False, 1, False), ("m1024_w4a4", "m1024", 0, False, 2, False),
+                   ("decode_c1_single_launch", "decode_c1", 0, True, 0, False),
+                   ("decode_m2_single_launch", "decode_m2", 0, True, 0, False),
+                   ("decode_m8_single_launch", "decode_m8", 0, True, 0, False))
 
 
 def log(msg: str):
@@ -69,6 +73,8 @@ def parse():
     ap.add_argument("--no-others", action="store_true", help="measure the headline workload only")
     ap.add_argument("--single-launch", action="store_true",
                     help="headline through moe_layer_decode (the whole layer in one launch)")
+    ap.add_argument("--from-logits", action="store_true",
+                    help="headline through moe_layer_from_logits (routing inside the gate_up launch)")
     ap.add_argument("--other-steps", type=int, default=50, help="timed steps of each other workload")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain device copy of this many bytes (counter calibration)")
@@ -196,11 +202,13 @@ def capture_rotation(torch, stream, L: int, R: int, layer_fn) -> list:
 
 
 def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_max: int = -1,
-                  replicas_override: int = 0, warm: bool = False, single: bool = False, act: int = 0) -> dict:
+                  replicas_override: int = 0, warm: bool = False, single: bool = False, act: int = 0,
+                  from_logits: bool = False) -> dict:
     """Eager (per-stage HIP events) and graph (L layers per hipGraph, timed replays) timings of one
     layer workload with cold weights; optionally the warm-weight eager time. `single`: the layer as
     one moe_layer_decode launch (no stages: the launch is the whole layer). `act` 1 / 2: the FFN with
-    MXFP8 / MXFP4 activations (moe_mxfp4_ffn_mx)."""
+    MXFP8 / MXFP4 activations (moe_mxfp4_ffn_mx). `from_logits`: the layer as one moe_layer_from_logits
+    call (stage events as for the FFN; route+group then times what runs before the gate_up launch)."""
     np, torch, moe, moe_synth = env.np, env.torch, env.moe, env.moe_synth
     stream = env.stream
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
@@ -216,7 +224,7 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
     x = env.dev(inp["x"].view(np.int16)).view(torch.bfloat16)
     logits = env.dev(inp["logits"])
     layer = moe.MoELayer(first, k, T, cfg.score_fn, cfg.renorm, cfg.clamp, flags, single_launch=single,
-                         act_format=act)
+                         act_format=act, from_logits=from_logits)
     base_opts = moe.ffn_options(small_m_max=small_m_max)
     torch.cuda.synchronize()
     log(f"{cfg.name}: {R} weight replicas of {replica_bytes / 1e9:.2f} GB on device")
@@ -233,7 +241,9 @@ def measure_layer(env: Env, cfg, flags: int, steps: int, warmup: int, small_m_ma
     res = dict(cfg=cfg, flags=flags, R=R, inp=inp, n_active=n_active, weight_bytes=n_active * per_expert,
                gateup_bytes=n_active * 2 * I * (H // 2 + H // 32), flops=2 * T * k * 3 * H * I,
                gateup_flops=2 * T * k * 2 * I * H,
-               plan=moe.ffn_plan(T, H, I, E, k, flags, base_opts), steps=steps, single=single, act=act)
+               plan=moe.ffn_plan(T, H, I, E, k, flags, base_opts), steps=steps, single=single, act=act,
+               from_logits=from_logits,
+               routed=from_logits and moe.layer_from_logits_routed(T, H, I, E, k, flags, base_opts))
 
     # eager: per-step HIP events on the stream the kernels run on: around the whole layer (recorded
     # here) and around the gate_up, down and combine stages (recorded by the library)
@@ -408,6 +418,9 @@ def summary(res: dict, use_graph: bool) -> dict:
         "config": {"workload": workload_name(res["cfg"]), "flags": res["flags"], "weight_replicas": res["R"],
                    "small_m_max": res["plan"]["small_m_max"],
                    "path": "moe_layer_decode (one launch)" if res["single"] else
+                           ("moe_layer_from_logits (" + ("routing and grouping inside the gate_up launch)"
+                                                         if res["routed"] else "routing launch first)"))
+                           if res["from_logits"] else
                            ("moe_route_group + moe_mxfp4_ffn_mx (" + ("W4A8: MXFP8" if res["act"] == 1 else
                                                                       "W4A4: MXFP4") + " activations)")
                            if res["act"] else "moe_route_group + moe_mxfp4_ffn (multi-launch)"},
@@ -608,7 +621,7 @@ def main():
     cfg = env.moe_synth.CONFIGS[args.config]
 
     res = measure_layer(env, cfg, args.flags, args.steps, args.warmup, args.small_m_max, args.replicas, warm=True,
-                        single=args.single_launch, act=args.act)
+                        single=args.single_launch, act=args.act, from_logits=args.from_logits)
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -631,11 +644,12 @@ def main():
 
     others = {}
     if not args.no_others:
-        for name, wl, flags, single, act in OTHER_WORKLOADS:
-            if wl == cfg.name and flags == args.flags and single == args.single_launch and act == args.act:
+        for name, wl, flags, single, act, lg in OTHER_WORKLOADS:
+            if (wl == cfg.name and flags == args.flags and single == args.single_launch and act == args.act
+                    and lg == args.from_logits):
                 continue
             o = measure_layer(env, env.moe_synth.CONFIGS[wl], flags, args.other_steps, max(5, args.warmup // 2),
-                              single=single, act=act)
+                              single=single, act=act, from_logits=lg)
             others[name] = summary(o, True)
             others[name]["steps"] = args.other_steps
             del o

@@ -345,6 +345,35 @@ int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags,
                        const moe_ffn_options* opts /*[host]*/, moe_ffn_plan* plan /*[host]*/);
 
 /*
+ * moe_layer_from_logits — the whole layer from the router logits: top-k routing, grouping, expert
+ * FFN and combine (the routed layer of the Post-Portfolio Device Attribution table, "MTP1
+ * Post-Portfolio Eager-Cycle Profile", from the router's select/normalize step to the combine).
+ * Results are bitwise those of moe_route_group + moe_mxfp4_ffn with the same flags. When
+ * moe_layer_from_logits_routed(T, H, I, E, k, flags, opts) returns 1 (decode batches: only the
+ * weight-streaming kernels run with the fused gate/up pass, T*k <= 64, E <= 256, the activations fit
+ * the gate_up kernel's LDS staging and T is at most its waves), every gate_up workgroup routes and
+ * groups the batch itself from the logits and the first one writes the routing and grouping for the
+ * launches that follow: the routing launch and a memory round trip before the first weight load are
+ * saved. Otherwise the routing and grouping launches run first.
+ *   logits, score_fn, renorm                  as moe_route_topk (logits [dev] f32[T, E])
+ *   x_bf16, w13_q .. w2_s, clamp_limit, flags, out   as moe_mxfp4_ffn
+ *   topk_ids, topk_w                          [dev] outputs of the routing when not NULL
+ *   workspace, ws_bytes                       [dev] at least moe_layer_from_logits_workspace_size(T, H,
+ *                                             I, E, k, flags) bytes, 256-byte aligned (no contents
+ *                                             required)
+ *   opts                                      [host] as moe_mxfp4_ffn_ex (NULL = the defaults)
+ * Limits and errors: as moe_mxfp4_ffn (and score_fn in {0, 1}).
+ */
+size_t moe_layer_from_logits_workspace_size(int T, int H, int I, int E, int k, int flags);  /* host; 0 if invalid */
+int moe_layer_from_logits_routed(int T, int H, int I, int E, int k, int flags,
+                                 const moe_ffn_options* opts /*[host]*/);  /* host: 1 if routed in gate_up */
+int moe_layer_from_logits(const float* logits, const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                          int score_fn, int renorm, const uint8_t* w13_q, const uint8_t* w13_s,
+                          const uint8_t* w2_q, const uint8_t* w2_s, float clamp_limit, int flags,
+                          int32_t* topk_ids, float* topk_w, uint16_t* out_bf16, void* workspace,
+                          size_t ws_bytes, const moe_ffn_options* opts, void* stream);
+
+/*
  * Activation-quantised expert feed-forward (W4A8 / W4A4).
  * (The FP4 activation-quantise step of the FP4 GEMM path named in "Chunk 8.0", its summary;
  * read as OCP Microscaling Formats (MX) v1.0 blocks: 32 values along the reduction axis sharing an

@@ -100,6 +100,13 @@ def load_library(path: str | None = None):
     lib.moe_layer_forward.argtypes = [V, V, i, i, i, i, i, i, i, V, V, V, V, ctypes.c_float, i, V, V, V, V, V,
                                       ctypes.c_size_t, V]
     lib.moe_layer_forward.restype = i
+    lib.moe_layer_from_logits_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.moe_layer_from_logits_workspace_size.restype = ctypes.c_size_t
+    lib.moe_layer_from_logits_routed.argtypes = [i, i, i, i, i, i, V]
+    lib.moe_layer_from_logits_routed.restype = i
+    lib.moe_layer_from_logits.argtypes = [V, V, i, i, i, i, i, i, i, V, V, V, V, ctypes.c_float, i, V, V, V, V,
+                                          ctypes.c_size_t, V, V]
+    lib.moe_layer_from_logits.restype = i
     lib.moe_group_tokens_workspace_size.argtypes = [i, i, i]
     lib.moe_group_tokens_workspace_size.restype = ctypes.c_size_t
     lib.moe_group_tokens.argtypes = [V, i, i, i, V, V, V, V, V, V, V, ctypes.c_size_t, V]
@@ -579,6 +586,53 @@ def layer_forward(x: torch.Tensor, w_router: torch.Tensor, w: Mxfp4Weights, k: i
     return out
 
 
+def layer_from_logits_workspace(T: int, H: int, I: int, E: int, k: int, flags: int = 0, device="cuda") -> torch.Tensor:
+    """A workspace for moe_layer_from_logits (no contents required)."""
+    n = load_library().moe_layer_from_logits_workspace_size(T, H, I, E, k, flags)
+    if n == 0:
+        raise MoeError("invalid sizes for moe_layer_from_logits")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def layer_from_logits_routed(T: int, H: int, I: int, E: int, k: int, flags: int = 0,
+                             options: FfnOptions | None = None) -> bool:
+    """Whether moe_layer_from_logits routes and groups inside the gate_up launch for these sizes."""
+    return bool(load_library().moe_layer_from_logits_routed(T, H, I, E, k, flags,
+                                                            ctypes.byref(options) if options is not None else None))
+
+
+def layer_from_logits(logits: torch.Tensor, x: torch.Tensor, w: Mxfp4Weights, k: int,
+                      score_fn: int = SCORE_SOFTMAX, renorm: bool = True, clamp_limit: float = 0.0,
+                      flags: int = 0, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      ids: torch.Tensor | None = None, weights: torch.Tensor | None = None,
+                      options: FfnOptions | None = None, stream=None) -> torch.Tensor:
+    """The whole layer from router logits (f32 [T, E]) and x (bf16 [T, H]): moe_layer_from_logits."""
+    x = _as_bf16(x)
+    T, H = x.shape
+    w.validate()
+    _dev(logits, torch.float32, "logits")
+    if tuple(logits.shape) != (T, w.E) or H != w.H:
+        raise MoeError(f"logits must be [{T}, {w.E}] and x [T, {w.H}]")
+    for t, name, dt, shape in ((ids, "topk_ids", torch.int32, (T, k)), (weights, "topk_w", torch.float32, (T, k))):
+        if t is not None:
+            _dev(t, dt, name)
+            if tuple(t.shape) != shape:
+                raise MoeError(f"{name} must be {list(shape)}")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    elif tuple(out.shape) != (T, H):
+        raise MoeError(f"out must be [{T}, {H}]")
+    if workspace is None:
+        workspace = layer_from_logits_workspace(T, H, w.I, w.E, k, flags, x.device)
+    _dev(workspace, torch.uint8, "workspace")
+    _check(load_library().moe_layer_from_logits(
+        _ptr(logits), _ptr(x), T, H, w.I, w.E, int(k), int(score_fn), int(bool(renorm)), _ptr(w.w13_q),
+        _ptr(w.w13_s), _ptr(w.w2_q), _ptr(w.w2_s), float(clamp_limit), int(flags), _ptr(ids), _ptr(weights),
+        _ptr(out), _ptr(workspace), workspace.numel(), ctypes.byref(options) if options is not None else None,
+        _stream(stream)), "moe_layer_from_logits")
+    return out
+
+
 class MoELayer:
     """One routed MXFP4 MoE layer with every buffer preallocated for up to ``max_tokens`` tokens.
 
@@ -588,10 +642,12 @@ class MoELayer:
 
     def __init__(self, weights: Mxfp4Weights, k: int, max_tokens: int, score_fn: int = SCORE_SOFTMAX,
                  renorm: bool = True, clamp_limit: float = 0.0, flags: int = 0, device="cuda",
-                 single_launch: bool = False, act_format: int = 0):
+                 single_launch: bool = False, act_format: int = 0, from_logits: bool = False):
         """single_launch: run each forward as one moe_layer_decode launch (decode batches; every
         token count up to max_tokens must be supported by it). act_format ACT_MXFP8 / ACT_MXFP4: the
-        FFN with MX-quantised activations (moe_mxfp4_ffn_mx; flags must be 0)."""
+        FFN with MX-quantised activations (moe_mxfp4_ffn_mx; flags must be 0). from_logits: run each
+        forward as one moe_layer_from_logits call (the routing inside the gate_up launch where it
+        fits; the grouping then lives in the call's workspace and `grp` is not written)."""
         weights.validate()
         self.w = weights
         self.k = k
@@ -612,6 +668,11 @@ class MoELayer:
               else ffn_workspace_size(max_tokens, H, I, E, k, flags))
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
         self.single_launch = single_launch
+        self.from_logits = from_logits
+        if from_logits:
+            if single_launch or act_format:
+                raise MoeError("from_logits excludes single_launch and act_format")
+            self.lf_ws = layer_from_logits_workspace(max_tokens, H, I, E, k, flags, device)
         if single_launch:
             # sized for max_tokens, which bounds every smaller batch's need (zeroed once: the
             # barrier counter at its start must begin at zero)
@@ -635,6 +696,9 @@ class MoELayer:
         if self.single_launch:
             return layer_decode(logits, x, w, self.k, self.score_fn, self.renorm, self.clamp, self.out[:T],
                                 self.layer_ws, ids, tw, stream)
+        if self.from_logits:
+            return layer_from_logits(logits, x, w, self.k, self.score_fn, self.renorm, self.clamp, self.flags,
+                                     self.out[:T], self.lf_ws, ids, tw, options, stream)
         route_group(logits, self.k, self.score_fn, self.renorm, ids, tw, self.grp, stream)
         if self.act_format:
             return mxfp4_ffn_mx(x, w, tw, self.grp, self.clamp, self.act_format, self.out[:T], self.workspace,

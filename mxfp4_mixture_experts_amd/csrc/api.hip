@@ -303,13 +303,17 @@ MOE_API int moe_mxfp4_ffn_plan(int T, int H, int I, int E, int k, int flags, con
   return MOE_OK;
 }
 
-MOE_API int moe_mxfp4_ffn_ex(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
-                             const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
-                             const uint8_t* w2_s, const float* topk_w, const int32_t* counts,
-                             const int32_t* offsets, const int32_t* sorted_pair,
-                             const int32_t* pair_pos, const int32_t* active, const int32_t* n_active,
-                             float clamp_limit, int flags, uint16_t* out_bf16, void* workspace,
-                             size_t ws_bytes, const moe_ffn_options* opts, void* stream) {
+namespace {
+
+// moe_mxfp4_ffn_ex; with `ro`, the gate_up launch is the routed variant, which also produces the
+// routing and the grouping (ids, topk_w and the grouping arrays passed here are its outputs; the
+// caller checks routed_ffn_ok first).
+int ffn_impl(const uint16_t* x_bf16, int T, int H, int I, int E, int k, const uint8_t* w13_q,
+             const uint8_t* w13_s, const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_w,
+             const int32_t* counts, const int32_t* offsets, const int32_t* sorted_pair, const int32_t* pair_pos,
+             const int32_t* active, const int32_t* n_active, float clamp_limit, int flags, uint16_t* out_bf16,
+             void* workspace, size_t ws_bytes, const moe_ffn_options* opts, void* stream,
+             const moe::RouteOut* ro) {
   if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
   if ((flags & ~kKnownFlags) || ((flags & MOE_FORCE_SMALL_M) && (flags & MOE_FORCE_LARGE_M)))
     return MOE_ERR_UNSUPPORTED;
@@ -368,6 +372,9 @@ MOE_API int moe_mxfp4_ffn_ex(const uint16_t* x_bf16, int T, int H, int I, int E,
                                      moe::kGateOnly, h_hi, h_lo, g_f32, s) == hipSuccess;
       ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
                                      moe::kUpWithGate, h_hi, h_lo, g_f32, s) == hipSuccess;
+    } else if (ro) {
+      ok &= moe::launch_small_gateup_routed(sp, r, *ro, H, I, w13_q, w13_s, clamp_limit, h_hi, h_lo, s) ==
+            hipSuccess;
     } else {
       ok &= moe::launch_small_gateup(sp, r, list, list_count, H, I, w13_q, w13_s, clamp_limit,
                                      moe::kGateUpFused, h_hi, h_lo, g_f32, s) == hipSuccess;
@@ -402,6 +409,30 @@ MOE_API int moe_mxfp4_ffn_ex(const uint16_t* x_bf16, int T, int H, int I, int E,
     ok &= moe::launch_combine(y, topk_w, pair_pos, T, H, k, out_bf16, nullptr, s) == hipSuccess;
   record(o, MOE_STAGE_COMBINE, false, s);
   return ok ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+// Whether the routed gate_up variant serves a call: only the weight-streaming kernels run, the
+// gate/up pass is fused, and the batch fits the variant (gateup_routed_ok).
+bool routed_ffn_ok(int T, int H, int I, int E, int k, int flags, const moe_ffn_options& o) {
+  if (T < 1 || (flags & MOE_UNFUSED_GATE_UP)) return false;
+  moe_ffn_plan plan;
+  fill_plan(T, H, I, E, k, flags, o, &plan);
+  if (!plan.launch_small || plan.launch_large) return false;
+  return moe::gateup_routed_ok(moe::plan_small(T, H, I, E, k, num_cus()), H, E);
+}
+
+}  // namespace
+
+MOE_API int moe_mxfp4_ffn_ex(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                             const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                             const uint8_t* w2_s, const float* topk_w, const int32_t* counts,
+                             const int32_t* offsets, const int32_t* sorted_pair,
+                             const int32_t* pair_pos, const int32_t* active, const int32_t* n_active,
+                             float clamp_limit, int flags, uint16_t* out_bf16, void* workspace,
+                             size_t ws_bytes, const moe_ffn_options* opts, void* stream) {
+  return ffn_impl(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, topk_w, counts, offsets, sorted_pair,
+                  pair_pos, active, n_active, clamp_limit, flags, out_bf16, workspace, ws_bytes, opts, stream,
+                  nullptr);
 }
 
 MOE_API int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k,
@@ -618,6 +649,99 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int flags) {
 }
 
 }  // namespace
+
+namespace {
+
+// Workspace of moe_layer_from_logits: the routing and grouping arrays, then the FFN's.
+struct LogitsWs {
+  size_t ids, w, counts, offsets, sorted_pair, pair_pos, active, n_active, ffn, total;
+};
+
+LogitsWs logits_ws(int T, int H, int I, int E, int k, int flags) {
+  LogitsWs l;
+  const size_t P = (size_t)T * k;
+  size_t off = 0;
+  l.ids = off;
+  off = align_up(off + P * 4);
+  l.w = off;
+  off = align_up(off + P * 4);
+  l.counts = off;
+  off = align_up(off + (size_t)E * 4);
+  l.offsets = off;
+  off = align_up(off + (size_t)(E + 1) * 4);
+  l.sorted_pair = off;
+  off = align_up(off + P * 4);
+  l.pair_pos = off;
+  off = align_up(off + P * 4);
+  l.active = off;
+  off = align_up(off + (size_t)E * 4);
+  l.n_active = off;
+  off = align_up(off + 4);
+  l.ffn = off;
+  off += ws_layout((long)P, H, I, E, k, flags).total;
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+MOE_API size_t moe_layer_from_logits_workspace_size(int T, int H, int I, int E, int k, int flags) {
+  if (!ffn_sizes_ok(T, H, I, E, k) || (flags & ~kKnownFlags)) return 0;
+  return logits_ws(T, H, I, E, k, flags).total;
+}
+
+MOE_API int moe_layer_from_logits_routed(int T, int H, int I, int E, int k, int flags,
+                                         const moe_ffn_options* opts) {
+  moe_ffn_options o;
+  if (!ffn_sizes_ok(T, H, I, E, k) || (flags & ~kKnownFlags) || read_options(opts, o) != MOE_OK) return 0;
+  return routed_ffn_ok(T, H, I, E, k, flags, o) ? 1 : 0;
+}
+
+MOE_API int moe_layer_from_logits(const float* logits, const uint16_t* x_bf16, int T, int H, int I, int E, int k,
+                                  int score_fn, int renorm, const uint8_t* w13_q, const uint8_t* w13_s,
+                                  const uint8_t* w2_q, const uint8_t* w2_s, float clamp_limit, int flags,
+                                  int32_t* topk_ids, float* topk_w, uint16_t* out_bf16, void* workspace,
+                                  size_t ws_bytes, const moe_ffn_options* opts, void* stream) {
+  if (!ffn_sizes_ok(T, H, I, E, k)) return MOE_ERR_SHAPE;
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if ((flags & ~kKnownFlags) || ((flags & MOE_FORCE_SMALL_M) && (flags & MOE_FORCE_LARGE_M)))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !x_bf16 || !w13_q || !w13_s || !w2_q || !w2_s || !out_bf16 || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(out_bf16, 16) || !aligned(w13_q, 16) || !aligned(w2_q, 16) ||
+      !aligned(workspace, kAlign))
+    return MOE_ERR_UNSUPPORTED;
+  const LogitsWs l = logits_ws(T, H, I, E, k, flags);
+  if (ws_bytes < l.total) return MOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(ws + l.ids);
+  float* tw = topk_w ? topk_w : reinterpret_cast<float*>(ws + l.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + l.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + l.offsets);
+  int32_t* sorted_pair = reinterpret_cast<int32_t*>(ws + l.sorted_pair);
+  int32_t* pair_pos = reinterpret_cast<int32_t*>(ws + l.pair_pos);
+  int32_t* active = reinterpret_cast<int32_t*>(ws + l.active);
+  int32_t* n_active = reinterpret_cast<int32_t*>(ws + l.n_active);
+  hipStream_t s = (hipStream_t)stream;
+  moe_ffn_options o;
+  {
+    const int st = read_options(opts, o);
+    if (st != MOE_OK) return st;
+  }
+  if (routed_ffn_ok(T, H, I, E, k, flags, o)) {
+    const moe::RouteOut ro{logits, E, score_fn, renorm, ids, tw, counts, offsets, sorted_pair, pair_pos, active,
+                           n_active};
+    return ffn_impl(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, tw, counts, offsets, sorted_pair, pair_pos,
+                    active, n_active, clamp_limit, flags, out_bf16, ws + l.ffn, ws_bytes - l.ffn, opts, stream,
+                    &ro);
+  }
+  const int st = moe_route_group(logits, T, E, k, score_fn, renorm, ids, tw, counts, offsets, sorted_pair, pair_pos,
+                                 active, n_active, s);
+  if (st != MOE_OK) return st;
+  return ffn_impl(x_bf16, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, tw, counts, offsets, sorted_pair, pair_pos,
+                  active, n_active, clamp_limit, flags, out_bf16, ws + l.ffn, ws_bytes - l.ffn, opts, stream,
+                  nullptr);
+}
 
 MOE_API size_t moe_layer_forward_workspace_size(int T, int H, int I, int E, int k, int flags) {
   if (!ffn_sizes_ok(T, H, I, E, k) || (flags & ~kKnownFlags)) return 0;

@@ -29,7 +29,9 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "group_dev.hpp"
 #include "kernels.hpp"
+#include "route_dev.hpp"
 #include "stream_dev.hpp"
 
 namespace moe {
@@ -238,21 +240,69 @@ __device__ __forceinline__ int take_item(int* counter, const ItemRange& ir) {
 constexpr int kXStageBytes = 65536;
 constexpr int kTokStageBytes = 4096;
 
-template <int BPL, int MT, int S, int D, int NW, int MODE, bool STX>
+// EPL > 0 (routed variant, decode): every workgroup first routes the T tokens itself (a wave per
+// token, EPL logits per lane: the router top-k device code) and groups the T*k <= kRoutePairs pairs
+// (one wave: the grouping device code) into LDS, and reads its work list, the experts' counts and
+// offsets and the rows' tokens from there; workgroup 0 also writes the ids, weights and grouping to
+// memory for the launches that follow. The routing and grouping are the separate kernels' code on
+// the same inputs, so every workgroup holds the same result, bitwise that of those kernels. The
+// layer then needs no routing launch and no memory round trip before the first weight load.
+template <int BPL, int MT, int S, int D, int NW, int MODE, bool STX, int EPL>
 __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, int k, int T,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_count, int list_cap, int H, int I,
     int tiles, int weighted, const uint8_t* __restrict__ w13_q, const uint8_t* __restrict__ w13_s,
     int lpr, float clamp, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
-    float* __restrict__ g_ws) {
+    float* __restrict__ g_ws, RouteOut ro) {
   constexpr bool kGate = MODE != kUpWithGate;
   constexpr bool kUp = MODE != kGateOnly;
+  constexpr bool ROUTE = EPL > 0;
+  static_assert(!ROUTE || STX, "the routed variant reads the rows' tokens from LDS");
   __shared__ int counter;
   __shared__ int range[2];
   extern __shared__ __attribute__((aligned(16))) uint8_t x_stage[];  // STX: x [T][H] bf16, tokens [P]
+  // ROUTE: the ids, weights and grouping of the batch
+  __shared__ int32_t r_ids[ROUTE ? kRoutePairs : 1], r_sorted[ROUTE ? kRoutePairs : 1],
+      r_pair_pos[ROUTE ? kRoutePairs : 1];
+  __shared__ float r_w[ROUTE ? kRoutePairs : 1];
+  __shared__ int32_t r_cnt[ROUTE ? kRouteExperts : 1], r_counts[ROUTE ? kRouteExperts : 1],
+      r_offsets[ROUTE ? kRouteExperts + 1 : 1], r_active[ROUTE ? kRouteExperts : 1], r_n_active[1];
   ItemRange ir;
   if (threadIdx.x == 0) counter = 0;
+  if constexpr (ROUTE) {
+    const int wv = threadIdx.x >> 6;
+    const bool first = blockIdx.x == 0;
+    if (wv < T)  // a wave per token (the host checks T <= NW)
+      route_dev::route_token<EPL>(ro.logits, wv, ro.E, k, ro.score_fn, ro.renorm, first ? ro.ids : r_ids,
+                                  first ? ro.weights : r_w, first ? r_ids : nullptr);
+    __syncthreads();
+    if (threadIdx.x < 64)
+      group_dev::group_pairs_one_wave<const int32_t*, int32_t*>(r_ids, T * k, ro.E, r_counts, r_offsets, r_sorted,
+                                                                r_pair_pos, r_active, r_n_active, r_cnt);
+    __syncthreads();
+    if (first) {  // the grouping, for the launches that follow
+      for (int i = threadIdx.x; i < ro.E; i += blockDim.x) {
+        ro.counts[i] = r_counts[i];
+        ro.offsets[i] = r_offsets[i];
+        ro.active[i] = r_active[i];
+      }
+      for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+        ro.sorted_pair[i] = r_sorted[i];
+        ro.pair_pos[i] = r_pair_pos[i];
+      }
+      if (threadIdx.x == 0) {
+        ro.offsets[ro.E] = r_offsets[ro.E];
+        *ro.n_active = r_n_active[0];
+      }
+    }
+  }
+  // the work list, the experts' row counts and first rows, and the rows' pairs: in LDS when routed
+  const int32_t* Lst = ROUTE ? r_active : list;
+  const int32_t* Lcnt = ROUTE ? r_n_active : list_count;
+  const int32_t* Cnt = ROUTE ? r_counts : counts;
+  const int32_t* Off = ROUTE ? r_offsets : offsets;
+  const int32_t* Srt = ROUTE ? r_sorted : sorted_pair;
   if constexpr (STX) {
     if (threadIdx.x >= 64) {  // waves 1..NW-1; wave 0 computes the range meanwhile
       constexpr int kStagers = 64 * (NW - 1);
@@ -269,7 +319,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
       constexpr int NTL = kTokStageBytes / 4 / kStagers + 1;
       int tok[NTL];
 #pragma unroll
-      for (int j = 0; j < NTL; ++j) tok[j] = sorted_pair[min(st + kStagers * j, P - 1)];
+      for (int j = 0; j < NTL; ++j) tok[j] = Srt[min(st + kStagers * j, P - 1)];
       uint4* dst = reinterpret_cast<uint4*>(x_stage);
 #pragma unroll
       for (int j = 0; j < NXL; ++j)
@@ -281,7 +331,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     }
   }
   // (the barrier inside makes the staged rows visible too)
-  if (!my_items_wg(list, list_count, counts, list_cap, tiles, MT, weighted, range, ir)) return;
+  if (!my_items_wg(Lst, Lcnt, Cnt, list_cap, tiles, MT, weighted, range, ir)) return;
 
   const int lane = threadIdx.x & 63;
   const int lg = ilog2(lpr);
@@ -310,11 +360,11 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
     const int tile = uniform(it - slot * tiles);
     if (slot != pf.slot) {
       pf.slot = slot;
-      const int e = uniform(list[slot]);
+      const int e = uniform(Lst[slot]);
       pf.q = w13_q + (size_t)e * qexp;
       pf.s = w13_s + (size_t)e * sexp;
-      pf.M = uniform(counts[e]);
-      pf.row0 = uniform(offsets[e]);
+      pf.M = uniform(Cnt[e]);
+      pf.row0 = uniform(Off[e]);
     }
     ring_m[d] = pf.M;
     ring_r0[d] = pf.row0;
@@ -371,7 +421,7 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
               for (int i = 0; i < 4; ++i) xb[m][b][i] = *reinterpret_cast<const uint4*>(xbase + kb * 64 + i * 16);
             }
           } else {
-            const int t = uniform(sorted_pair[row]) / k;
+            const int t = uniform(Srt[row]) / k;
             const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
 #pragma unroll
             for (int b = 0; b < BPL; ++b) {
@@ -925,7 +975,7 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
 #define MOE_GU_K(BPL, MT, STX)                                                                           \
   {                                                                                                      \
     auto kern = small_gateup_kernel<BPL, MT, gateup_slots(BPL), gateup_ring(BPL), 4 * gu_waves(BPL, MT), \
-                                    MODE, STX>;                                                          \
+                                    MODE, STX, 0>;                                                       \
     static std::atomic<bool> lds_attr_set{false};                                                        \
     if (STX && lds > 65536 && !lds_attr_set.load()) {                                                    \
       if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                                       \
@@ -937,7 +987,7 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
     kern<<<grid, 256 * gu_waves(BPL, MT), STX ? lds : 0, stream>>>(                                      \
         r.x, r.counts, r.offsets, r.sorted_pair, r.k, sp.T, list, list_count, sp.E, H, I, tiles,         \
         sp.weighted,                                                                                     \
-        wq, ws, lpr, clamp, h_hi, h_lo, g_ws);                                                           \
+        wq, ws, lpr, clamp, h_hi, h_lo, g_ws, RouteOut{});                                               \
   }
 #define MOE_GU(BPL, MT)          \
   do {                           \
@@ -969,6 +1019,59 @@ hipError_t gateup_dispatch(const SmallPlan& sp, const Routed& r, const int32_t* 
 }
 
 }  // namespace
+
+bool gateup_routed_ok(const SmallPlan& sp, int H, int E) {
+  return gateup_stx(sp, H) && sp.gu.bpl <= 2 && sp.gu_grid > 0 && sp.T >= 1 && sp.T <= sp.gu_block / 64 &&
+         sp.P <= kRoutePairs && E >= 1 && E <= kRouteExperts;
+}
+
+hipError_t launch_small_gateup_routed(const SmallPlan& sp, const Routed& r, const RouteOut& ro, int H, int I,
+                                      const uint8_t* w13_q, const uint8_t* w13_s, float clamp,
+                                      uint16_t* h_hi, uint16_t* h_lo, hipStream_t stream) {
+  if (!gateup_routed_ok(sp, H, ro.E)) return hipErrorInvalidValue;
+  const dim3 grid(sp.gu_grid);
+  const int lpr = sp.gu.lpr, tiles = sp.gu_tiles;
+  const size_t lds = (size_t)sp.T * H * 2 + (size_t)sp.P * 4;
+#define MOE_GUR(BPL, MT, EPL)                                                                             \
+  {                                                                                                       \
+    auto kern = small_gateup_kernel<BPL, MT, gateup_slots(BPL), gateup_ring(BPL), 4 * gu_waves(BPL, MT),  \
+                                    kGateUpFused, true, EPL>;                                             \
+    static std::atomic<bool> lds_attr_set{false};                                                         \
+    if (lds > 65536 && !lds_attr_set.load()) {                                                            \
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                                        \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageMaxBytes) != hipSuccess) \
+        return hipErrorInvalidValue;                                                                      \
+      lds_attr_set.store(true);                                                                           \
+    }                                                                                                     \
+    kern<<<grid, 256 * gu_waves(BPL, MT), lds, stream>>>(r.x, ro.counts, ro.offsets, ro.sorted_pair, r.k,  \
+                                                         sp.T, ro.active, ro.n_active, sp.E, H, I, tiles,  \
+                                                         sp.weighted, w13_q, w13_s, lpr, clamp, h_hi, h_lo, \
+                                                         nullptr, ro);                                     \
+  }
+#define MOE_GUR_E(BPL, MT)          \
+  if (ro.E <= 64)                   \
+    MOE_GUR(BPL, MT, 1)             \
+  else if (ro.E <= 128)             \
+    MOE_GUR(BPL, MT, 2)             \
+  else                              \
+    MOE_GUR(BPL, MT, 4)
+  if (sp.gu.bpl == 1) {
+    if (sp.mt_gu == 2) {
+      MOE_GUR_E(1, 2)
+    } else {
+      MOE_GUR_E(1, 1)
+    }
+  } else {
+    if (sp.mt_gu == 2) {
+      MOE_GUR_E(2, 2)
+    } else {
+      MOE_GUR_E(2, 1)
+    }
+  }
+#undef MOE_GUR_E
+#undef MOE_GUR
+  return hipGetLastError();
+}
 
 SmallPlan plan_small(int T, int H, int I, int E, int k, int num_cus) {
   SmallPlan sp;

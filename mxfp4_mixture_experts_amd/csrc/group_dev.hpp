@@ -146,15 +146,12 @@ __device__ __forceinline__ void group_pairs(IdPtr ids, int P, int E, int32_t* __
 // holding it, one wave-wide scan over the experts gives counts, offsets and the active list (and
 // turns the LDS counts into base rows), and each pair's row is its expert's base plus the number of
 // lower lanes holding the same expert — the definition above, so the outputs are the same.
-template <typename IdPtr>
-__device__ __forceinline__ void group_pairs_one_wave(IdPtr ids, int P, int E, int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ sorted_pair,
-                                                     int32_t* __restrict__ pair_pos,
-                                                     int32_t* __restrict__ active,
-                                                     int32_t* __restrict__ n_active, Shared& sh) {
+// (cnt: E ints of LDS, per expert its count, then its base row)
+template <typename IdPtr, typename OutPtr>
+__device__ __forceinline__ void group_pairs_one_wave(IdPtr ids, int P, int E, OutPtr counts, OutPtr offsets,
+                                                     OutPtr sorted_pair, OutPtr pair_pos, OutPtr active,
+                                                     OutPtr n_active, int* cnt) {
   const int lane = threadIdx.x & 63;
-  int* cnt = sh.total;  // per expert: count, then base row
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
   const bool valid = lane < P;
   const int my_e = valid ? ids[lane] : 0;
@@ -189,6 +186,17 @@ __device__ __forceinline__ void group_pairs_one_wave(IdPtr ids, int P, int E, in
     sorted_pair[pos] = lane;
     pair_pos[lane] = pos;
   }
+}
+
+template <typename IdPtr>
+__device__ __forceinline__ void group_pairs_one_wave(IdPtr ids, int P, int E, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_pair,
+                                                     int32_t* __restrict__ pair_pos,
+                                                     int32_t* __restrict__ active,
+                                                     int32_t* __restrict__ n_active, Shared& sh) {
+  group_pairs_one_wave<IdPtr, int32_t*>(ids, P, E, counts, offsets, sorted_pair, pair_pos, active, n_active,
+                                        sh.total);
 }
 
 }  // namespace group_dev

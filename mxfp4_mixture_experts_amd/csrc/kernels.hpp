@@ -57,6 +57,19 @@ hipError_t launch_route_group(const float* logits, int T, int E, int k, int scor
                               int32_t* n_active, hipStream_t stream);
 
 // Grouping results and activations every FFN kernel reads.
+// Outputs of the routed gate_up variant (written by its first workgroup): the router's ids and
+// weights [P] and the grouping (counts [E], offsets [E + 1], sorted_pair [P], pair_pos [P], active [E],
+// n_active [1]), from router logits f32 [T, E].
+struct RouteOut {
+  const float* logits;
+  int E, score_fn, renorm;
+  int32_t* ids;
+  float* weights;
+  int32_t *counts, *offsets, *sorted_pair, *pair_pos, *active, *n_active;
+};
+constexpr int kRoutePairs = 64;     // the routed variant groups at most 64 pairs (one wave)
+constexpr int kRouteExperts = 256;  // and at most 256 experts (4 logits per lane)
+
 struct Routed {
   const uint16_t* x;         // bf16 [T, H]
   const int32_t* counts;     // [E]
@@ -109,6 +122,14 @@ hipError_t launch_small_down(const SmallPlan& sp, const Routed& r, const int32_t
                              const int32_t* list_count, bool list_is_active, int H, int I, const uint8_t* w2_q,
                              const uint8_t* w2_s, const uint16_t* h_hi, const uint16_t* h_lo, float* y,
                              hipStream_t stream);
+
+// gate_up with the routing and grouping done by every workgroup (see RouteOut): for decode batches
+// whose activations fit the LDS staging, T <= the workgroup's waves, T*k <= kRoutePairs and
+// E <= kRouteExperts, the fused gate/up pass only (gateup_routed_ok says whether a plan qualifies).
+bool gateup_routed_ok(const SmallPlan& sp, int H, int E);
+hipError_t launch_small_gateup_routed(const SmallPlan& sp, const Routed& r, const RouteOut& ro, int H, int I,
+                                      const uint8_t* w13_q, const uint8_t* w13_s, float clamp,
+                                      uint16_t* h_hi, uint16_t* h_lo, hipStream_t stream);
 
 // Down with the weighted combine folded in (one launch instead of two; results identical to
 // launch_small_down followed by launch_combine, bit for bit). Only for lists holding every active

@@ -240,6 +240,53 @@ def test_noalloc_validation(lib):
     assert call(T=0) == 0             # nothing to do
 
 
+def test_layer_from_logits_validation(lib):
+    """moe_layer_from_logits: sizes, flags, pointers and workspace are checked before any launch; the
+    routed query follows the gate_up variant's limits."""
+    lib.moe_layer_from_logits_workspace_size.restype = ctypes.c_size_t
+    lib.moe_mxfp4_ffn_workspace_size.restype = ctypes.c_size_t
+    need = lib.moe_layer_from_logits_workspace_size(8, 4096, 2048, 256, 8, 0)
+    # routing and grouping arrays (P ids, P weights, E counts, E + 1 offsets, P sorted pairs, P positions,
+    # E active, 1 count, each 256-byte aligned), then the FFN's workspace
+    assert need > lib.moe_mxfp4_ffn_workspace_size(8, 4096, 2048, 256, 8, 0)
+    assert lib.moe_layer_from_logits_workspace_size(8, 4016, 2048, 256, 8, 0) == 0   # H % 32
+    assert lib.moe_layer_from_logits_workspace_size(8, 4096, 2048, 256, 8, 16) == 0  # unknown flag
+    # one token, 8 pairs, 128 experts, x in 4 KB: routed inside gate_up (also with no device to ask)
+    assert lib.moe_layer_from_logits_routed(1, 2048, 768, 128, 8, 0, None) == 1
+    assert lib.moe_layer_from_logits_routed(1, 2048, 768, 128, 8, 1, None) == 0     # unfused gate/up
+    assert lib.moe_layer_from_logits_routed(1, 2048, 768, 128, 8, 4, None) == 0     # MFMA kernels
+    assert lib.moe_layer_from_logits_routed(16, 2048, 768, 128, 8, 0, None) == 0    # 128 pairs
+    assert lib.moe_layer_from_logits_routed(1, 2048, 768, 512, 8, 0, None) == 0     # more than 256 experts
+    assert lib.moe_layer_from_logits_routed(0, 2048, 768, 128, 8, 0, None) == 0
+    from mxfp4_mixture_experts_amd import FfnOptions
+
+    opts = FfnOptions()
+    lib.moe_ffn_options_init(ctypes.byref(opts))
+    opts.small_m_max = 0                                                          # MFMA kernels
+    assert lib.moe_layer_from_logits_routed(1, 2048, 768, 128, 8, 0, ctypes.byref(opts)) == 0
+    opts.small_m_max = -2                                                         # invalid options
+    assert lib.moe_layer_from_logits_routed(1, 2048, 768, 128, 8, 0, ctypes.byref(opts)) == 0
+    d = DUMMY
+    sz = ctypes.c_size_t
+
+    def call(T=8, H=4096, I=2048, E=256, k=8, fn=0, flags=0, logits=d, out=d, ws=V(0x10000), ws_bytes=need,
+             o=None):
+        return lib.moe_layer_from_logits(logits, d, T, H, I, E, k, fn, 1, d, d, d, d, ctypes.c_float(0.0), flags,
+                                         None, None, out, ws, sz(ws_bytes), o, None)
+
+    assert call(H=4016) == -2
+    assert call(k=9, E=8) == -2
+    assert call(fn=2) == -3
+    assert call(flags=16) == -3
+    assert call(flags=2 | 4) == -3
+    assert call(logits=None) == -1
+    assert call(out=None) == -1
+    assert call(ws=V(0x10010)) == -3
+    assert call(ws_bytes=need - 1) == -4
+    assert call(o=ctypes.byref(opts)) == -2                                       # small_m_max -2
+    assert call(T=0) == 0
+
+
 def test_layer_decode_validation(lib):
     """moe_layer_decode: sizes, support limits, pointers and workspace are checked before any launch."""
     lib.moe_layer_decode_workspace_size.restype = ctypes.c_size_t
