@@ -192,8 +192,9 @@ int moe_layer_forward(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int
  * T == 0. Ids need not be distinct within a token (an expert then holds several of its pairs).
  *
  * Workspace: moe_group_tokens_workspace_size(T, k, E) returns the device bytes a call needs for
- * these sizes, or (size_t)-1 for invalid sizes. The grouping runs in one workgroup whose
- * histograms and scans live in LDS, so the size is 0 for every valid shape and `workspace` may be
+ * these sizes, or (size_t)-1 for invalid sizes. The grouping runs in one workgroup up to 1024
+ * pairs and over up to 64 workgroups beyond (each counts every expert over all the ids itself, so
+ * they exchange nothing); histograms and scans live in LDS, so the size is 0 for every valid shape and `workspace` may be
  * NULL; a caller that passes a buffer keeps working if a later version needs one (the size is a
  * function of T, k and E only, the worst case over every routing, as tokenspeed PR #661 "The
  * workspace contract" requires). ws_bytes below the query's result returns MOE_ERR_WORKSPACE.

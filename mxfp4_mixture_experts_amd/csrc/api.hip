@@ -237,7 +237,8 @@ MOE_API int moe_router_gemm_topk(const uint16_t* x_bf16, const uint16_t* w_route
                                  workspace, ws_bytes, 0, stream);
 }
 
-// The grouping is one workgroup with its histograms and scans in LDS: no device workspace.
+// The grouping keeps its histograms and scans in LDS (each workgroup counts all the ids itself when
+// there are several): no device workspace.
 MOE_API size_t moe_group_tokens_workspace_size(int T, int k, int E) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || (long)T * k > MOE_MAX_PAIRS)
     return (size_t)-1;

@@ -188,6 +188,135 @@ __device__ __forceinline__ void group_pairs_one_wave(IdPtr ids, int P, int E, Ou
   }
 }
 
+// The same grouping over several workgroups, for many pairs (one workgroup places 64-pair chunks at
+// roughly one per wave every microsecond, so 8192 pairs took 16 us alone). Workgroup g owns the
+// chunks [g * cpw, (g + 1) * cpw). No device scratch and no communication between workgroups:
+// each one counts every expert over all P ids and over the ids before its own chunks with LDS
+// atomics (integer counts, so the order of the additions does not matter), which gives it every
+// expert's offset and the number of its pairs that precede the workgroup. Its waves then count and
+// place their own chunks exactly as group_pairs does, starting from those numbers, so every pair
+// gets the same row: offsets[e] + (pairs of e at lower p). Workgroup 0 writes counts, offsets and
+// the active list. kIdGroup ids per thread are loaded together.
+struct SharedMulti {
+  int hist[kMaxWaves * kMaxExperts];  // per-wave counts of the workgroup's chunks, then running rows
+  int total[kMaxExperts];             // pairs of each expert over all P
+  int before[kMaxExperts];            // pairs of each expert before the workgroup's first chunk
+  int base[kMaxExperts];              // offsets
+};
+
+template <int kIdGroup>
+__device__ __forceinline__ void group_pairs_multi(const int32_t* __restrict__ ids, int P, int E, int cpw,
+                                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ sorted_pair,
+                                                  int32_t* __restrict__ pair_pos, int32_t* __restrict__ active,
+                                                  int32_t* __restrict__ n_active, SharedMulti& sh) {
+  const int nw = blockDim.x >> 6;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x;
+
+  for (int i = threadIdx.x; i < nw * E; i += blockDim.x) sh.hist[i] = 0;
+  for (int i = threadIdx.x; i < E; i += blockDim.x) sh.total[i] = 0, sh.before[i] = 0;
+  __syncthreads();
+
+  const int chunks = (P + 63) >> 6;
+  const int wg_c0 = min(chunks, g * cpw);
+  const int wg_c1 = min(chunks, wg_c0 + cpw);
+  const int p_first = wg_c0 << 6;  // first pair of the workgroup
+
+  // 1. every expert's count over all P, and over the pairs before the workgroup's chunks
+  for (int p0 = 0; p0 < P; p0 += kIdGroup * (int)blockDim.x) {
+    int ev[kIdGroup];
+#pragma unroll
+    for (int j = 0; j < kIdGroup; ++j) {
+      const int p = p0 + j * (int)blockDim.x + (int)threadIdx.x;
+      ev[j] = p < P ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kIdGroup; ++j) {
+      const int p = p0 + j * (int)blockDim.x + (int)threadIdx.x;
+      if (ev[j] >= 0) {
+        atomicAdd(&sh.total[ev[j]], 1);
+        if (p < p_first) atomicAdd(&sh.before[ev[j]], 1);
+      }
+    }
+  }
+
+  // the wave's chunks: a contiguous share of the workgroup's
+  const int per_wave = (wg_c1 - wg_c0 + nw - 1) / nw;
+  const int c_begin = min(wg_c1, wg_c0 + w * per_wave);
+  const int c_end = min(wg_c1, c_begin + per_wave);
+  int* my_hist = sh.hist + w * E;
+
+  // 2. per-wave counts of its chunks (the lowest lane of each expert adds the expert's lanes)
+  for (int c = c_begin; c < c_end; ++c) {
+    const int p = (c << 6) + lane;
+    const bool valid = p < P;
+    const int e = valid ? ids[p] : 0;
+    const uint64_t peers = match_key(e, valid);
+    if (valid && lane == __ffsll((unsigned long long)peers) - 1) my_hist[e] += __popcll(peers);
+  }
+  __syncthreads();
+
+  // 3. per expert: rows before each wave's chunks = before + counts of the earlier waves
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = sh.before[e];
+    for (int v = 0; v < nw; ++v) {
+      const int c = sh.hist[v * E + e];
+      sh.hist[v * E + e] = run;
+      run += c;
+    }
+  }
+
+  // 4. exclusive scan over experts (wave 0); workgroup 0 also writes counts, offsets, the active list
+  if (w == 0) {
+    const bool writer = g == 0;
+    int carry = 0, acarry = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < E ? sh.total[e] : 0;
+      const int incl = wave_inclusive_scan(c, lane);
+      if (e < E) {
+        sh.base[e] = carry + incl - c;
+        if (writer) {
+          counts[e] = c;
+          offsets[e] = carry + incl - c;
+        }
+      }
+      carry += wave_last(incl);
+      const bool act = e < E && c > 0;
+      const uint64_t am = __ballot(act);
+      if (writer && act) active[acarry + __popcll(am & lanemask_lt(lane))] = e;
+      acarry += __popcll(am);
+    }
+    if (writer) {
+      if (lane == 0) {
+        offsets[E] = carry;
+        *n_active = acarry;
+      }
+      for (int i = acarry + lane; i < E; i += 64) active[i] = -1;
+    }
+  }
+  __syncthreads();
+
+  // 5. stable placement of the wave's chunks
+  for (int c = c_begin; c < c_end; ++c) {
+    const int p = (c << 6) + lane;
+    const bool valid = p < P;
+    const int e = valid ? ids[p] : 0;
+    const uint64_t peers = match_key(e, valid);
+    if (valid) {
+      const int pos = sh.base[e] + my_hist[e] + __popcll(peers & lanemask_lt(lane));
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+    }
+    // every lane of this wave has read my_hist[e] above before the leader advances it
+    __builtin_amdgcn_wave_barrier();
+    if (valid && lane == __ffsll((unsigned long long)peers) - 1) my_hist[e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <typename IdPtr>
 __device__ __forceinline__ void group_pairs_one_wave(IdPtr ids, int P, int E, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,

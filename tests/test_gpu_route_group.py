@@ -89,7 +89,9 @@ def test_group_configs(orc, name):
 
 
 @pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (3, 2, 5, 1), (64, 8, 256, 2), (1000, 16, 512, 3),
-                                        (8192, 8, 256, 4), (4097, 3, 16, 5), (20000, 8, 512, 6)])
+                                        (8192, 8, 256, 4), (4097, 3, 16, 5), (20000, 8, 512, 6),
+                                        (1024, 2, 3, 12), (2049, 1, 7, 13), (1025, 2, 64, 14),
+                                        (131072, 8, 64, 15), (1025, 1, 9, 19), (512, 2, 9, 20)])
 def test_group_random(orc, T, k, E, seed):
     rng = np.random.default_rng(seed)
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
@@ -100,6 +102,15 @@ def test_group_skewed(orc):
     rng = np.random.default_rng(11)
     ids = np.stack([rng.choice(4, size=2, replace=False) for _ in range(3000)]).astype(np.int32)
     check_group(orc, ids, 512, "skewed")
+
+
+@pytest.mark.parametrize("T,k,E,seed", [(3000, 4, 1, 16), (5000, 8, 8, 17), (700, 16, 3, 18)])
+def test_group_repeated_ids(orc, T, k, E, seed):
+    """ids drawn with repetition (an expert holds several pairs of one token), past the
+    single-workgroup size; E = 1 puts every pair on one expert."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    check_group(orc, ids, E, "repeated")
 
 
 def test_group_empty(orc):
