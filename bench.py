@@ -7,7 +7,8 @@ PR #52 node-trace diff measures). Weights are random MXFP4 of that shape, rotate
 device replicas that every step streams them cold from HBM (no step finds its weights in the 256 MB
 last-level cache). Prints one JSON line: the headline workload's numbers, then the same layer
 measurement for the other workloads (one token, two tokens, decode M=2 and M=8 with the unfused
-gate/up, and per-expert M=1024 on the matrix cores) under "other_workloads".
+gate/up, per-expert M=1024 on the matrix cores, and the medium (T=256, Zipf-skewed) and high (T=1024)
+concurrency batches) under "other_workloads".
 
   python bench.py [--steps K] [--warmup W] [--config decode_m8] [--mode graph|eager] [--no-others]
 """
@@ -45,6 +46,7 @@ OTHER_WORKLOADS = (("decode_c1", "decode_c1", 0, False, 0, False), ("decode_m2",
                    ("decode_m2_unfused", "decode_m2", 1, False, 0, False),
                    ("decode_m8_unfused", "decode_m8", 1, False, 0, False), ("m1024", "m1024", 0, False, 0, False),
                    ("m1024_w4a8", "m1024", 0, False, 1, False), ("m1024_w4a4", "m1024", 0, False, 2, False),
+                   ("medium_zipf", "medium_zipf", 0, False, 0, False), ("high_c4", "high_c4", 0, False, 0, False),
                    ("decode_c1_single_launch", "decode_c1", 0, True, 0, False),
                    ("decode_m2_single_launch", "decode_m2", 0, True, 0, False),
                    ("decode_m8_single_launch", "decode_m8", 0, True, 0, False))
