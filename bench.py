@@ -597,11 +597,19 @@ def cpu_baseline(args, cfg, inp) -> dict:
         log(f"oracle rep {rep}: {times[-1]:.2f}s")
     per_layer_us = statistics.median(times) * 1e6 * (cfg.T / sample_tokens)
     used = oracle.num_threads(threads)
+    # one thread, on one token (a layer's cost is proportional to its routed pairs), once
+    t_c = time.perf_counter()
+    oracle.moe_layer(inp["logits"][:1], inp["x"][:1], inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"], cfg.k,
+                     cfg.score_fn, cfg.renorm, cfg.clamp, 1)
+    one_us = (time.perf_counter() - t_c) * 1e6 * cfg.T
+    log(f"oracle, one thread, one token: {one_us / cfg.T / 1e6:.2f}s")
     return {"value": round(per_layer_us, 1), "unit": "µs/layer", "cores": used, "kind": "oracle",
             "threads_used": used, "host_cores": host_cores,
             "sample": (f"{sample_tokens} of {cfg.T} tokens of one {cfg.name} layer (route+group+ffn+combine, "
                        f"fp64, {used} OpenMP threads on a host reporting {host_cores} cores), median of "
-                       f"{args.cpu_reps}, scaled to the whole layer")}
+                       f"{args.cpu_reps}, scaled to the whole layer"),
+            "single_thread": {"value": round(one_us, 1), "unit": "µs/layer", "threads_used": 1,
+                              "sample": f"1 of {cfg.T} tokens, one run, scaled to the whole layer"}}
 
 
 def main():
