@@ -201,6 +201,20 @@ struct MxSrc {
 constexpr int kScaleGroupSteps = 4;
 constexpr int kScaleGroupBytes = (kMxTileM + kMxTileN) * 16;
 
+// One direct global -> LDS load (16 or 4 bytes a lane, lane l at lds + l * bytes), written as inline
+// assembly so that the compiler, which cannot tell the LDS it writes apart from the LDS the step reads,
+// does not wait for it before every later LDS read: the step issues the loads of step s + 1 first and
+// waits for them itself (s_waitcnt vmcnt(0) and the barrier at the start of step s + 1). The wave-uniform
+// LDS address goes to M0 (one wait state before the load uses it).
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* g, void* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  if (BYTES == 16)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
+}
+
 // Direct global -> LDS loads of step s into one stage: one instruction puts the wave's 64 x 16 bytes at
 // 1 KB of consecutive LDS, lane l at 16 l. Load j of wave w fills kilobyte w * loads + j of its tile.
 // With scale groups (SG) the scales of steps s .. s + 3 go to `sgrp` when s is a multiple of four;
@@ -211,31 +225,29 @@ __device__ __forceinline__ void mx_gload(const MxSrc<AF>& src, int s, int wave, 
   using S = MxShape<AF>;
 #pragma unroll
   for (int j = 0; j < S::kALoads; ++j)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src.a[j] + (size_t)s * S::kABytes),
-                                     reinterpret_cast<void*>(base + (wave * S::kALoads + j) * 1024), 16, 0, 0);
+    lds_dma<16>(src.a[j] + (size_t)s * S::kABytes, base + (wave * S::kALoads + j) * 1024);
 #pragma unroll
   for (int j = 0; j < S::kBLoads; ++j)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src.b[j] + (size_t)s * (kMxBK / 2)),
-                                     reinterpret_cast<void*>(base + S::kATile + (wave * S::kBLoads + j) * 1024), 16,
-                                     0, 0);
+    lds_dma<16>(src.b[j] + (size_t)s * (kMxBK / 2), base + S::kATile + (wave * S::kBLoads + j) * 1024);
   if (SG) {
     if ((s & (kScaleGroupSteps - 1)) == 0)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src.s + (size_t)s * (kMxBK / 32)),
-                                       reinterpret_cast<void*>(sgrp + wave * 1024), 16, 0, 0);
+      lds_dma<16>(src.s + (size_t)s * (kMxBK / 32), sgrp + wave * 1024);
   } else {
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src.s + (size_t)s * (kMxBK / 32)),
-                                     reinterpret_cast<void*>(base + S::kATile + S::kBTile + wave * 256), 4, 0, 0);
+    lds_dma<4>(src.s + (size_t)s * (kMxBK / 32), base + S::kATile + S::kBTile + wave * 256);
   }
 }
 
 // One K-step of one wave: 64 rows x 128 weight rows, K = 128 as two halves of 64 (16 MFMAs). Two LDS
 // stages alternate. At step s every wave waits for its own loads of step s (issued during step s - 1)
-// and one barrier makes all of them visible; the wave then reads every operand of step s from `cur`
-// into registers, and only after that issues the loads of step s + 1 into `next`, which every wave
-// finished reading before the barrier (its reads of it had returned: its MFMAs of step s - 1 consumed
-// them). So the loads of step s + 1 overlap the MFMAs of step s, and no read of a stage ever waits on
-// loads into it that are still in flight. The barrier carries no memory fence; the empty asm
-// statements keep the compiler from moving LDS accesses across it or the reads past the loads.
+// and one barrier makes all of them visible; the wave then at once issues the loads of step s + 1 into
+// `next`, which every wave finished reading before the barrier (its reads of it had returned: its MFMAs
+// of step s - 1 consumed them), and reads the operands of step s from `cur`, each MFMA waiting only for
+// its own operands. So the loads of step s + 1 have the whole step to arrive, and no read of a stage
+// ever waits on loads into it that are still in flight (the loads are inline assembly, so the compiler
+// adds no wait for them before the reads). The barrier carries no memory fence; the empty asm
+// statements keep the compiler from moving LDS accesses across it. (With the loads issued after the
+// reads, as built-ins, every MFMA of the step waited for all of the step's reads: W4A8 gate_up 248-251
+// against 237-238 us, W4A4 216 against 202 us at m1024, same box, two alternations.)
 template <int AF, bool SG>
 __device__ __forceinline__ void mx_step(const MxSrc<AF>& src, int s, int nsteps, int wave, int wr, int wc, int g,
                                         int r, const uint8_t* cur, uint8_t* next, uint8_t* sg0, uint8_t* sg1,
@@ -245,6 +257,7 @@ __device__ __forceinline__ void mx_step(const MxSrc<AF>& src, int s, int nsteps,
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  if (s + 1 < nsteps) mx_gload<AF, SG>(src, s + 1, wave, next, (((s + 1) >> 2) & 1) ? sg1 : sg0);
 
   const uint8_t* A = cur;
   const uint8_t* B = A + S::kATile;
@@ -279,8 +292,6 @@ __device__ __forceinline__ void mx_step(const MxSrc<AF>& src, int s, int nsteps,
       bv[ks][ni] = *reinterpret_cast<const uint4*>(B + n * (kMxBK / 2) + swz<4>(n, ks * 2 + g) * 16);
     }
   }
-  asm volatile("" ::: "memory");
-  if (s + 1 < nsteps) mx_gload<AF, SG>(src, s + 1, wave, next, (((s + 1) >> 2) & 1) ? sg1 : sg0);
 
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
@@ -387,6 +398,7 @@ __global__ __launch_bounds__(kMxThreads, 1) void mx_gemm_kernel(
     mx_step<AF, SG>(src, s, nsteps, wave, wr, wc, g, r, st0, st1, sg0, sg1, acc);
     if (s + 1 < nsteps) mx_step<AF, SG>(src, s + 1, nsteps, wave, wr, wc, g, r, st1, st0, sg0, sg1, acc);
   }
+  __builtin_amdgcn_s_waitcnt(kVmcntWaitAll);  // no load into LDS outlives the loop
 
   if (GATEUP) {
     // h = silu(g) * u per element, then each row's 32-column block quantised: the block is column r
