@@ -8,14 +8,13 @@
 //     matching 128 up columns; down: 256 or 224 output columns, whichever fills the compute units
 //     in fewer, fuller rounds); its eight waves (two per SIMD) each compute 64 rows x 128 (or 112)
 //     weight rows with 16x16x32 MFMAs (32 or 28 accumulator blocks);
-//   - per K-step of 64 every thread loads 16-byte chunks of the activation rows and one MX block of
-//     one weight row (16 bytes of E2M1 codes + the E8M0 scale), decodes the block exactly with the
-//     scaled FP4 conversion and writes both to LDS; the staging of step s + 1 is interleaved with
-//     the MFMAs of step s, and each chunk's loads for step s + 2 are issued as soon as its
-//     registers are free;
-//   - LDS rows are padded to 16 bytes past a multiple of 64 so the MFMA operand reads (16 rows x
-//     16 bytes per lane group) hit 64 distinct banks; two LDS buffers alternate, one barrier per
-//     K-step.
+//   - per K-step of 64 the activation rows go straight from memory to LDS (direct loads) and every
+//     thread loads one MX block of one weight row (16 bytes of E2M1 codes + the E8M0 scale), decodes
+//     it exactly with the scaled FP4 conversion and writes it to LDS; the loads of step s + 1 are
+//     issued while step s runs its MFMAs;
+//   - weight rows in LDS are padded to 16 bytes past a multiple of 64 and activation rows have their
+//     16-byte chunks permuted, so the MFMA operand reads (16 rows x 16 bytes per lane group) hit 64
+//     distinct banks; two LDS buffers alternate, one barrier per K-step.
 // gate_up multiplies bf16 x with bf16 weights (E2M1 x E8M0 is exact in bf16). Gate columns and the
 // matching up columns land in the same lanes of a wave, so the clamp-SwiGLU epilogue runs in
 // registers; it writes h as its two bf16 planes.
@@ -35,6 +34,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace moe {
 
@@ -76,17 +76,18 @@ struct DenseShape {
   static constexpr int kTN = 2 * kNW;
   static constexpr int kBK = 64;                        // K elements per step (two MX blocks)
   static constexpr int kBlocks = kBK / 32;              // MX blocks per weight row and step
-  static constexpr int kRow = kBK * 2 + 16;             // LDS bytes per row (16-bit values + padding)
-  static constexpr int kATileBytes = kDM * kRow;
+  static constexpr int kRow = kBK * 2 + 16;             // LDS bytes per weight row (16-bit values + padding)
+  static constexpr int kARow = kBK * 2;                 // LDS bytes per activation row (chunks permuted)
+  static constexpr int kATileBytes = kDM * kARow;
   static constexpr int kBTileBytes = kTN * kRow;
   static constexpr int kStage = kATileBytes + kBTileBytes;
   // LDS bytes past the two stages: down keeps the row and column exponents there
   static constexpr int kExtra = GATEUP ? 0 : (kDM + kTN) * 4;
   static constexpr int kLds = 2 * kStage + kExtra;
-  // 16-byte LDS chunks per activation row and step (each one global 16-byte load), per thread and
-  // step, and weight-block chunks per thread and step
+  // 16-byte LDS chunks per activation row and step, direct loads per wave and step (each puts 1 KB,
+  // eight rows, into LDS), and weight-block chunks per thread and step
   static constexpr int kCpr = kBK * 2 / 16;
-  static constexpr int kAChunks = kDM * kCpr / kDThreads;
+  static constexpr int kAChunks = kATileBytes / (kDW * 1024);
   static constexpr int kBChunks = (kTN * kBlocks + kDThreads - 1) / kDThreads;
 };
 
@@ -154,14 +155,20 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   const int wc = wave / (kDW / 2);  // column group: B-tile rows wc*kNW .. +kNW
 
   // ---- staging assignments
-  // activations: chunk c = tid + kDThreads * i covers elements 8 (c % kCpr) .. +8 of row c / kCpr
-  // (of x for gate_up; of the fp16 h row for down)
+  // activations (x for gate_up, the fp16 h rows for down) go straight from memory to LDS: direct load
+  // i of wave w fills LDS kilobyte w * NA + i of the tile, lane l the 16 bytes at 16 l, i.e. position
+  // l % 8 of tile row r = 8 (w * NA + i) + l / 8. Rows are unpadded and a row's chunk c sits at position
+  // c ^ ((r >> 1) & 7), so the operand reads of 16 consecutive rows (one chunk each) hit 64 distinct
+  // banks; the lane therefore fetches the chunk that belongs at its position.
   constexpr int kCpr = S::kCpr;
+  static_assert(kCpr == 8, "activation rows of 128 bytes");
   const uint8_t* arow[NA];
+  int achunk[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int c = tid + kDThreads * i;
-    const int lr = min(c / kCpr, rows - 1);
+    const int r = 8 * (wave * NA + i) + lane / 8;
+    achunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+    const int lr = min(r, rows - 1);
     if (GATEUP) {
       const int t = sorted_pair[row0 + lr] / k;
       arow[i] = reinterpret_cast<const uint8_t*>(x + (size_t)t * H);
@@ -182,18 +189,24 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     bs[jw] = wrow * srow;
   }
 
-  // one register set of loads: activation chunk i and the weight block(s) of one K-step
-  uint4 ra[NA];
+  // one register set of loads: the weight block(s) of one K-step
   uint4 rb[NBW];
   uint32_t rs[NBW];
 
-  // loads of K-step `step` (steps past the end re-load the last one, never used)
-  auto load_a = [&](int i, int step) {
-    const int st = min(step, nsteps - 1);
-    const int c = tid + kDThreads * i;
-    const int elc = min(st * S::kBK + (c % kCpr) * 8, K - 8);  // first element of the chunk
-    ra[i] = ld16(arow[i], (uint32_t)elc * 2);
+  // activations of K-step `step` -> LDS buffer step & 1 (direct loads, waited for by the caller). Past K
+  // (a last step of 32 when K is not a multiple of 64) a chunk repeats the row's last eight finite
+  // values: the weights there decode with a zero scale, so those products are exact zeros and no
+  // masking is needed.
+  auto dma_a = [&](int step) {
+    uint8_t* st_a = lds + (step & 1) * S::kStage;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int elc = min(step * S::kBK + achunk[i] * 8, K - 8);  // first element of the chunk
+      lds_dma16(arow[i] + (size_t)elc * 2, st_a + (wave * NA + i) * 1024);
+    }
   };
+  // VMEM instructions of one load_b (a 16-byte code load and a scale byte per block)
+  constexpr int kBOps = 2 * NBW;
   auto load_b = [&](int step) {
     const int st = min(step, nsteps - 1);
     const uint32_t blk = (uint32_t)min(st * S::kBlocks + bblk, NB - 1);
@@ -210,8 +223,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[ms][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int i = 0; i < NA; ++i) load_a(i, 0);
+  dma_a(0);
   load_b(0);
 
   // down: the row scales of this tile and the column shifts of this column tile
@@ -227,14 +239,6 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     __syncthreads();
   }
 
-  // activation chunk i of K-step `step` -> LDS buffer step & 1. Past K (a last step of 32 when K is
-  // not a multiple of 64) the chunk repeats the row's last eight finite values: the weights there
-  // decode with a zero scale, so those products are exact zeros and no masking is needed.
-  auto stage_a = [&](int i, int step) {
-    uint8_t* st_a = lds + (step & 1) * S::kStage;
-    const int c = tid + kDThreads * i;
-    *reinterpret_cast<uint4*>(st_a + (c / kCpr) * S::kRow + (c % kCpr) * 16) = ra[i];
-  };
   // weight blocks of K-step `step` -> 32 16-bit values each in LDS buffer step & 1 (a zero scale
   // past K): bf16 with the block scale for gate_up, fp16 with the block scale relative to the
   // column's for down
@@ -275,22 +279,20 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
     }
   };
 
-  // software pipeline: step 0 staged and step 1 in flight before the loop; during step s the MFMA
-  // groups read buffer s & 1 while, between them, the chunks of step s + 1 go to buffer (s + 1) & 1
-  // (last read in step s - 1, before the barrier that opened step s) and each chunk's registers are
-  // refilled at once with step s + 2, so every load has a whole step to arrive. One barrier per step.
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    stage_a(i, 0);
-    load_a(i, 1);
-  }
+  // software pipeline: step 0 staged and step 1's weights in flight before the loop. Step s opens by
+  // issuing the activation loads of step s + 1 into buffer (s + 1) & 1 (last read in step s - 1,
+  // before the barrier that opened step s); its MFMA passes read buffer s & 1; its last pass decodes
+  // the weights of step s + 1 into buffer (s + 1) & 1 and refills their registers with step s + 2.
+  // Every load has about a step to arrive. One barrier per step, after the wait for the activations.
   stage_b(0);
   load_b(1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(kBOps));  // step 0's activations (step 1's weights may fly)
   __syncthreads();
 
   // operand reads from LDS (lane: row / column j16, K elements 8g .. 8g+7 of 32-wide slice kk)
   auto read_a = [&](const uint8_t* st_a, int kk, int ms) {
-    return *reinterpret_cast<const op_t*>(st_a + (wr * kWM + ms * 16 + j16) * S::kRow + kk * 64 + g * 16);
+    const int r = wr * kWM + ms * 16 + j16;
+    return *reinterpret_cast<const op_t*>(st_a + r * S::kARow + (((kk * 4 + g) ^ ((r >> 1) & 7)) * 16));
   };
   auto read_b = [&](const uint8_t* st_b, int kk, int cb) {
     return *reinterpret_cast<const op_t*>(st_b + (wc * kNW + cb * 16 + j16) * S::kRow + kk * 64 + g * 16);
@@ -298,6 +300,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
   constexpr int kQ = S::kBlocks * NCB;  // column-block passes per step (slice-major)
 
   for (int step = 0; step < nsteps; ++step) {
+    if (step + 1 < nsteps) dma_a(step + 1);
     const uint8_t* st_a = lds + (step & 1) * S::kStage;
     const uint8_t* st_b = st_a + S::kATileBytes;
     // Column-block-major passes: pass q = 8 kk + cb multiplies the slice's four A operands (held in
@@ -321,11 +324,9 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
         else
           acc[ms][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[ms], bring[q % 3], acc[ms][cb], 0, 0, 0);
       }
-      // one staging piece of the next step after every other pass
-      if ((q & 1) && (q >> 1) < NA) {
-        stage_a(q >> 1, step + 1);
-        load_a(q >> 1, step + 2);
-      } else if ((q & 1) && (q >> 1) == NA) {
+      // the weights of the next step in the last pass, as late as possible behind the activation loads
+      // (the compiler's wait for their registers also waits for those)
+      if (q == kQ - 1) {
         stage_b(step + 1);
         load_b(step + 2);
       }
@@ -335,6 +336,7 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kBOps));  // the activations of step + 1 have landed
     __syncthreads();
   }
 

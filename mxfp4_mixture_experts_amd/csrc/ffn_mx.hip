@@ -30,6 +30,7 @@
 //   result: lane l holds column r, rows 8 * (i / 4) + 4 * g + i % 4 in element i.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace moe {
 
@@ -201,20 +202,6 @@ struct MxSrc {
 constexpr int kScaleGroupSteps = 4;
 constexpr int kScaleGroupBytes = (kMxTileM + kMxTileN) * 16;
 
-// One direct global -> LDS load (16 or 4 bytes a lane, lane l at lds + l * bytes), written as inline
-// assembly so that the compiler, which cannot tell the LDS it writes apart from the LDS the step reads,
-// does not wait for it before every later LDS read: the step issues the loads of step s + 1 first and
-// waits for them itself (s_waitcnt vmcnt(0) and the barrier at the start of step s + 1). The wave-uniform
-// LDS address goes to M0 (one wait state before the load uses it).
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(const void* g, void* lds) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  if (BYTES == 16)
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
-  else
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
-}
-
 // Direct global -> LDS loads of step s into one stage: one instruction puts the wave's 64 x 16 bytes at
 // 1 KB of consecutive LDS, lane l at 16 l. Load j of wave w fills kilobyte w * loads + j of its tile.
 // With scale groups (SG) the scales of steps s .. s + 3 go to `sgrp` when s is a multiple of four;
@@ -225,15 +212,15 @@ __device__ __forceinline__ void mx_gload(const MxSrc<AF>& src, int s, int wave, 
   using S = MxShape<AF>;
 #pragma unroll
   for (int j = 0; j < S::kALoads; ++j)
-    lds_dma<16>(src.a[j] + (size_t)s * S::kABytes, base + (wave * S::kALoads + j) * 1024);
+    lds_dma16(src.a[j] + (size_t)s * S::kABytes, base + (wave * S::kALoads + j) * 1024);
 #pragma unroll
   for (int j = 0; j < S::kBLoads; ++j)
-    lds_dma<16>(src.b[j] + (size_t)s * (kMxBK / 2), base + S::kATile + (wave * S::kBLoads + j) * 1024);
+    lds_dma16(src.b[j] + (size_t)s * (kMxBK / 2), base + S::kATile + (wave * S::kBLoads + j) * 1024);
   if (SG) {
     if ((s & (kScaleGroupSteps - 1)) == 0)
-      lds_dma<16>(src.s + (size_t)s * (kMxBK / 32), sgrp + wave * 1024);
+      lds_dma16(src.s + (size_t)s * (kMxBK / 32), sgrp + wave * 1024);
   } else {
-    lds_dma<4>(src.s + (size_t)s * (kMxBK / 32), base + S::kATile + S::kBTile + wave * 256);
+    lds_dma4(src.s + (size_t)s * (kMxBK / 32), base + S::kATile + S::kBTile + wave * 256);
   }
 }
 
