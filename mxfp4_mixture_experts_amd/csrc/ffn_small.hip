@@ -504,20 +504,19 @@ __global__ __launch_bounds__(64 * NW, 1) void small_gateup_kernel(
 #pragma unroll
   for (int d = 0; d < D; ++d) prefetch(d);
   // items are taken in increasing order, so the first entry past the range ends the wave's work
-  bool more = true;
-  while (more) {
+  // The loop leaves by a jump straight out of the unrolled ring walk: with a flag tested again at the
+  // top, the control flow kept a path from a refill of entry d back to the consumption of entry d
+  // with the other entry not refilled in between, and along it the compiler's wait before each
+  // consumption covered every load in flight, the other entry's too (the ring drained at every item).
+  for (;;) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (more) {
-        if (ring_item[d] >= ir.end) {
-          more = false;
-        } else {
-          consume(d);
-          prefetch(d);
-        }
-      }
+      if (ring_item[d] >= ir.end) goto drained;
+      consume(d);
+      prefetch(d);
     }
   }
+drained:;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -718,20 +717,19 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_kernel(
     }
     __syncthreads();
   }
-  bool more = true;
-  while (more) {
+  // The loop leaves by a jump straight out of the unrolled ring walk: with a flag tested again at the
+  // top, the control flow kept a path from a refill of entry d back to the consumption of entry d
+  // with the other entry not refilled in between, and along it the compiler's wait before each
+  // consumption covered every load in flight, the other entry's too (the ring drained at every item).
+  for (;;) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (more) {
-        if (ring_item[d] >= ir.end) {
-          more = false;
-        } else {
-          consume(d);
-          prefetch(d);
-        }
-      }
+      if (ring_item[d] >= ir.end) goto drained;
+      consume(d);
+      prefetch(d);
     }
   }
+drained:;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -930,20 +928,16 @@ __global__ __launch_bounds__(64 * NW, 1) void small_down_combine_kernel(
     hinv_l[i] = inv;
   }
   __syncthreads();
-  bool more = true;
-  while (more) {
+  // (the ring walk leaves by a jump, as in the kernels above)
+  for (;;) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (more) {
-        if (ring_item[d] >= nitems) {
-          more = false;
-        } else {
-          consume(d);
-          prefetch(d);
-        }
-      }
+      if (ring_item[d] >= nitems) goto drained;
+      consume(d);
+      prefetch(d);
     }
   }
+drained:
   __syncthreads();
   // the weighted combine of this workgroup's output rows: out[t, n] = bf16(sum_j w[t, j] * y[pair, n])
   for (int i = threadIdx.x; i < T * NR; i += blockDim.x) {
