@@ -408,20 +408,17 @@ __global__ __launch_bounds__(64 * NW, 1) void layer_decode_kernel(LayerArgs a) {
 
 #pragma unroll
     for (int d = 0; d < kLRing; ++d) prefetch(d);
-    bool more = true;
-    while (more) {
+    // the ring walk leaves by a jump (with a flag tested again at the top, the compiler's wait before
+    // consuming an entry also covered the other entry's loads, draining the ring at every item)
+    for (;;) {
 #pragma unroll
       for (int d = 0; d < kLRing; ++d) {
-        if (more) {
-          if (ring_item[d] >= n_items) {
-            more = false;
-          } else {
-            consume(d);
-            prefetch(d);
-          }
-        }
+        if (ring_item[d] >= n_items) goto gate_up_drained;
+        consume(d);
+        prefetch(d);
       }
     }
+  gate_up_drained:;
   }
   __syncthreads();
 
@@ -540,20 +537,16 @@ __global__ __launch_bounds__(64 * NW, 1) void layer_decode_kernel(LayerArgs a) {
 
 #pragma unroll
     for (int d = 0; d < kLRing; ++d) prefetch(d);
-    bool more = true;
-    while (more) {
+    // (the ring walk leaves by a jump, as above)
+    for (;;) {
 #pragma unroll
       for (int d = 0; d < kLRing; ++d) {
-        if (more) {
-          if (ring_item[d] >= n_items) {
-            more = false;
-          } else {
-            consume(d);
-            prefetch(d);
-          }
-        }
+        if (ring_item[d] >= n_items) goto down_drained;
+        consume(d);
+        prefetch(d);
       }
     }
+  down_drained:;
   }
 
   // ---- 3. grid barrier: this workgroup's partial rows are complete at the device level -----------
