@@ -281,8 +281,9 @@ int moe_mxfp4_ffn(const uint16_t* x_bf16, int T, int H, int I, int E, int k, con
  *   small_m_max       launch-table threshold: experts with at most this many rows run on the
  *                     weight-streaming kernels, the others on the MFMA kernels. -1 (default) follows
  *                     the table keyed by token count (tokenspeed PR #661, "What the sweep found"):
- *                     8 for T <= 8 (every expert streams), 2 above. Values below -1 are rejected
- *                     (MOE_ERR_SHAPE). The FORCE flags take precedence.
+ *                     8 for T <= 8 (every expert streams), 2 for 8 < T < 256, 0 from 256 tokens on
+ *                     (every expert on the MFMA kernels). 0 launches no weight-streaming kernel.
+ *                     Values below -1 are rejected (MOE_ERR_SHAPE). The FORCE flags take precedence.
  *   dense_down_cols   column tile of the dense (>= 256 rows per expert) down GEMM: 0 (default)
  *                     picks 256 or 224 output columns per workgroup, whichever finishes the expected
  *                     ceil(T*k/256) x ceil(H/width) tiles in fewer, fuller rounds over the compute

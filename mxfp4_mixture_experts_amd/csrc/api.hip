@@ -24,7 +24,14 @@ namespace {
 // that, experts with more than 2 rows go to the MFMA kernels (the streaming kernels hold two
 // tokens' activations in registers, and each further pair of tokens costs another decode pass and a
 // reload). A call's options may override the threshold.
-int table_small_m_max(int T) { return T <= 8 ? 8 : 2; }
+// Launch table keyed by the token count (a launch structure chosen by M, as in tokenspeed PR #661,
+// "What the sweep found"): up to 8 tokens every expert has at most 8 rows and streams; in between,
+// experts of one or two rows stream and the rest run on the MFMA kernels; from 256 tokens on every
+// active expert runs on the MFMA kernels and the weight-streaming launches are skipped (MI355X, same
+// box, two alternations: medium_zipf, T = 256, 777-778 us per layer against 797-824 with experts of
+// up to two rows streaming; high_c4, T = 1024, 1692-1702 against 1700-1719).
+constexpr int kTableAllMfmaTokens = 256;
+int table_small_m_max(int T) { return T <= 8 ? 8 : T < kTableAllMfmaTokens ? 2 : 0; }
 
 constexpr size_t kAlign = 256;
 
@@ -104,7 +111,8 @@ void fill_plan(int T, int H, int I, int E, int k, int flags, const moe_ffn_optio
   const moe::SmallPlan sp = moe::plan_small(T, H, I, E, k, num_cus());
   const moe::LargePlan lp = moe::plan_large(T, H, I, E, k, thr == INT_MAX ? INT_MAX - 1 : thr);
   plan->small_m_max = thr;
-  plan->launch_small = (flags & MOE_FORCE_LARGE_M) ? 0 : 1;
+  // a threshold of 0 leaves no active expert (every one has a row) to the weight-streaming kernels
+  plan->launch_small = thr > 0 ? 1 : 0;
   plan->launch_large = (flags & MOE_FORCE_LARGE_M) ? 1 : ((flags & MOE_FORCE_SMALL_M) ? 0 : (T > thr));
   if (T == 0) plan->launch_small = plan->launch_large = 0;
   const int gu_launches = (flags & MOE_UNFUSED_GATE_UP) ? 2 : 1;

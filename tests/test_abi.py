@@ -163,9 +163,14 @@ def test_launch_plan(lib):
     assert m.ffn_plan(1, 7168, 2048, 256, 8, m.UNFUSED_GATE_UP)["n_launches"] == 3
     assert m.ffn_plan(1, 7168, 2048, 256, 8, m.FORCE_LARGE_M)["fold_combine"] == 0
     p = m.ffn_plan(1024, 7168, 2048, 256, 8)
-    # schedule, streaming gate_up + down, row-tile gate_up + down, dense gate_up + h rewrite + down,
-    # combine
-    assert p["launch_small"] == 1 and p["launch_large"] == 1 and p["n_launches"] == 9
+    # from 256 tokens every expert runs on the MFMA kernels: schedule, row-tile gate_up + down, dense
+    # gate_up + h rewrite + down, combine
+    assert p["small_m_max"] == 0 and p["launch_small"] == 0 and p["launch_large"] == 1 and p["n_launches"] == 7
+    p = m.ffn_plan(255, 7168, 2048, 256, 8)
+    # streaming gate_up + down as well, and no dense kernels below 256 tokens
+    assert p["small_m_max"] == 2 and p["launch_small"] == 1 and p["launch_large"] == 1 and p["n_launches"] == 6
+    p = m.ffn_plan(64, 4096, 2048, 256, 8, options=m.ffn_options(small_m_max=0))
+    assert p["launch_small"] == 0 and p["launch_large"] == 1
     p = m.ffn_plan(1024, 7168, 2048, 256, 8, m.FORCE_LARGE_M)
     assert p["launch_small"] == 0 and p["launch_large"] == 1 and p["small_m_max"] == 0
     p = m.ffn_plan(1024, 7168, 2048, 256, 8, m.FORCE_SMALL_M)
@@ -173,7 +178,8 @@ def test_launch_plan(lib):
     p = m.ffn_plan(0, 4096, 2048, 256, 8)
     assert p["n_launches"] == 0
     assert m.ffn_plan(8, 4096, 2048, 256, 8)["small_m_max"] == 8
-    assert m.ffn_plan(256, 4096, 2048, 256, 8)["small_m_max"] == 2
+    assert m.ffn_plan(9, 4096, 2048, 256, 8)["small_m_max"] == 2
+    assert m.ffn_plan(256, 4096, 2048, 256, 8)["small_m_max"] == 0
     assert m.ffn_plan(8, 4096, 2048, 256, 8, options=m.ffn_options(small_m_max=2))["launch_large"] == 1
     assert m.ffn_plan(8, 4096, 2048, 256, 8)["launch_large"] == 0  # nothing persists between calls
     with pytest.raises(m.MoeError):
